@@ -1,0 +1,242 @@
+/*
+ * hstu_oracle.c -- plain fp64 CPU oracle for jagged HSTU attention (forward).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may call, link or
+ * load this file or the library built from it; it exists so that the tests,
+ * the smoke check and the benchmark's CPU-baseline leg can compare the HIP
+ * path against an obviously correct definition.  It shares no code, header,
+ * table or helper with the HIP sources.
+ *
+ * What it computes, per sequence b, head h and row i of the sequence
+ * (definitions from the pages; citations name page title and section):
+ *
+ *   s_ij = alpha * <q_i, k_j> + pos[min(|i-j|, P-1)]
+ *                 + time[min(floor(log2(1 + |t_i - t_j|)), Tt-1)]
+ *       The biased score: relative-position and relative-time bias
+ *       ("HSTU tensor by tensor: SiLU aggregation, temporal bias and gating",
+ *       sections "Relative time adds information content similarity lacks"
+ *       and "Similar shape, different aggregation").
+ *   a_ij = SiLU(s_ij) / n_scale   for allowed (i,j), and exactly 0 otherwise.
+ *       Pointwise SiLU aggregation with no row normalisation (same page,
+ *       "SiLU aggregation coefficients are not probabilities" and "Similar
+ *       shape, different aggregation"); illegal pairs are zeroed after the
+ *       nonlinearity ("Do not copy softmax masking mechanically") -- here they
+ *       are simply never evaluated, which is the same value and cannot make NaN.
+ *   o_i  = sum_j a_ij v_j
+ *   out_i = LayerNorm(o_i) * u_i   (or o_i itself with epilogue NONE)
+ *       The norm-then-gate step U_i (.) Norm(sum_j A_ij V_j) of the teaching
+ *       equation ("Similar shape, different aggregation"; "Follow the U, V, Q
+ *       and K branches").
+ *
+ * The allowed set combines the four rules the "HSTU-MUSA" page names in
+ * "Mathematical Equivalence" (contextual bidirectional prefix, candidate
+ * position clamping, target-group masking, max attention length) with the
+ * causal indicator 1_{j<=i} of the teaching equation.  Readings taken where the
+ * pages are silent (all listed with the design notes):
+ *   - L = seq length, T = clamp(num_targets[b], 0, L), n_h = L - T history
+ *     tokens, c = clamp(contextual_len, 0, n_h) prefix tokens.
+ *   - prefix rows i < c see j < c (bidirectional);
+ *     history rows c <= i < n_h see j <= i;
+ *     candidate rows i >= n_h see every history token j < n_h, plus j == i.
+ *   - window W > 0: additionally p_i - j <= W, where p_i = min(i, n_h) is the
+ *     clamped candidate position (candidates all sit at the history end).
+ *   - the bias uses the raw |i-j| and |t_i - t_j| (symmetric inside the prefix).
+ *   - floor(log2(1+dt)) is taken in exact integer arithmetic.
+ *   - LayerNorm per (token, head) over d_v, no affine weights, biased
+ *     variance, epsilon given by the caller.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_EPILOGUE_LN_U 0
+#define ORACLE_EPILOGUE_NONE 1
+
+static int64_t clamp64(int64_t x, int64_t lo, int64_t hi) {
+  return x < lo ? lo : (x > hi ? hi : x);
+}
+
+/* Geometry of one sequence: length, history length, prefix length. */
+typedef struct {
+  int64_t L, n_h, c, W;
+} seq_geom;
+
+static seq_geom geometry(const int32_t* offsets, const int32_t* num_targets, int b,
+                         int contextual_len, int max_attn_len) {
+  seq_geom g;
+  g.L = (int64_t)offsets[b + 1] - (int64_t)offsets[b];
+  int64_t T = num_targets ? clamp64(num_targets[b], 0, g.L) : 0;
+  g.n_h = g.L - T;
+  g.c = clamp64(contextual_len, 0, g.n_h);
+  g.W = max_attn_len;
+  return g;
+}
+
+/* Whether query row i may aggregate key j (both local to the sequence). */
+static int allowed(const seq_geom* g, int64_t i, int64_t j) {
+  int ok;
+  if (i < g->c) {
+    ok = j < g->c;                              /* bidirectional prefix     */
+  } else if (i < g->n_h) {
+    ok = j <= i;                                /* causal history           */
+  } else {
+    ok = (j < g->n_h) || (j == i);              /* target group: history+self */
+  }
+  if (ok && g->W > 0) {
+    int64_t p = i < g->n_h ? i : g->n_h;        /* candidate position clamp */
+    ok = (p - j) <= g->W;
+  }
+  return ok;
+}
+
+/* floor(log2(x)) for x >= 1 by repeated halving: plain integer arithmetic. */
+static int floor_log2_u64(uint64_t x) {
+  int b = 0;
+  while (x > 1) {
+    x >>= 1;
+    ++b;
+  }
+  return b;
+}
+
+int hstu_oracle_time_bucket(int64_t t_i, int64_t t_j) {
+  uint64_t dt = t_i >= t_j ? (uint64_t)t_i - (uint64_t)t_j : (uint64_t)t_j - (uint64_t)t_i;
+  return floor_log2_u64(1u + dt);
+}
+
+double hstu_oracle_silu(double x) { return x / (1.0 + exp(-x)); }
+
+int hstu_oracle_allowed(int64_t L, int64_t num_targets, int64_t contextual_len,
+                        int64_t max_attn_len, int64_t i, int64_t j) {
+  seq_geom g;
+  g.L = L;
+  g.n_h = L - clamp64(num_targets, 0, L);
+  g.c = clamp64(contextual_len, 0, g.n_h);
+  g.W = max_attn_len;
+  if (i < 0 || j < 0 || i >= L || j >= L) return 0;
+  return allowed(&g, i, j);
+}
+
+/* Number of allowed (i, j) pairs over the batch, counted one pair at a time. */
+int64_t hstu_oracle_count_allowed(int num_seqs, const int32_t* offsets,
+                                  const int32_t* num_targets, int contextual_len,
+                                  int max_attn_len) {
+  int64_t n = 0;
+  for (int b = 0; b < num_seqs; ++b) {
+    seq_geom g = geometry(offsets, num_targets, b, contextual_len, max_attn_len);
+    for (int64_t i = 0; i < g.L; ++i)
+      for (int64_t j = 0; j < g.L; ++j) n += allowed(&g, i, j);
+  }
+  return n;
+}
+
+typedef struct {
+  int b, h;
+  int64_t work;
+} oracle_item;
+
+static int cmp_item_desc(const void* a, const void* b) {
+  const oracle_item* x = (const oracle_item*)a;
+  const oracle_item* y = (const oracle_item*)b;
+  if (x->work != y->work) return x->work < y->work ? 1 : -1;
+  if (x->b != y->b) return x->b - y->b;
+  return x->h - y->h;
+}
+
+/*
+ * Full forward.  Tensors are [total_tokens, H, d] with a token stride `ld_*`
+ * (in elements) and head stride d.  All floating inputs are fp64 copies of the
+ * exact values the device sees.  Returns 0, or -1 on a bad argument.
+ */
+int hstu_oracle_fwd(int num_seqs, const int32_t* offsets, int num_heads, int d_qk, int d_v,
+                    const double* q, int64_t ld_q, const double* k, int64_t ld_k,
+                    const double* v, int64_t ld_v, const double* u, int64_t ld_u,
+                    const int64_t* timestamps, const int32_t* num_targets,
+                    int contextual_len, int max_attn_len, double alpha, double n_scale,
+                    const double* pos_table, int pos_len, const double* time_table,
+                    int time_len, double eps, int epilogue, double* out, int64_t ld_out,
+                    int nthreads) {
+  if (num_seqs < 0 || num_heads <= 0 || d_qk <= 0 || d_v <= 0) return -1;
+  if ((pos_table == NULL) != (pos_len == 0) || (time_table == NULL) != (time_len == 0)) return -1;
+  if (time_table && !timestamps) return -1;
+  if (!(n_scale > 0.0)) return -1;
+  int n_items = num_seqs * num_heads;
+  oracle_item* items = (oracle_item*)malloc(sizeof(oracle_item) * (size_t)(n_items > 0 ? n_items : 1));
+  if (!items) return -1;
+  for (int b = 0; b < num_seqs; ++b) {
+    int64_t L = (int64_t)offsets[b + 1] - (int64_t)offsets[b];
+    for (int h = 0; h < num_heads; ++h) {
+      items[b * num_heads + h].b = b;
+      items[b * num_heads + h].h = h;
+      items[b * num_heads + h].work = L * L;
+    }
+  }
+  qsort(items, (size_t)n_items, sizeof(oracle_item), cmp_item_desc);
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+  (void)nthreads;
+#endif
+
+#pragma omp parallel
+  {
+    double* o = (double*)malloc(sizeof(double) * (size_t)d_v);
+#pragma omp for schedule(dynamic, 1)
+    for (int it = 0; it < n_items; ++it) {
+      int b = items[it].b, h = items[it].h;
+      seq_geom g = geometry(offsets, num_targets, b, contextual_len, max_attn_len);
+      int64_t base = offsets[b];
+      for (int64_t i = 0; i < g.L; ++i) {
+        const double* qi = q + (base + i) * ld_q + (int64_t)h * d_qk;
+        for (int e = 0; e < d_v; ++e) o[e] = 0.0;
+        for (int64_t j = 0; j < g.L; ++j) {
+          if (!allowed(&g, i, j)) continue;
+          const double* kj = k + (base + j) * ld_k + (int64_t)h * d_qk;
+          double dot = 0.0;
+          for (int e = 0; e < d_qk; ++e) dot += qi[e] * kj[e];
+          double s = alpha * dot;
+          if (pos_table) {
+            int64_t rel = i >= j ? i - j : j - i;
+            s += pos_table[rel < pos_len - 1 ? rel : pos_len - 1];
+          }
+          if (time_table) {
+            int bucket = hstu_oracle_time_bucket(timestamps[base + i], timestamps[base + j]);
+            s += time_table[bucket < time_len - 1 ? bucket : time_len - 1];
+          }
+          double a = hstu_oracle_silu(s) / n_scale;
+          const double* vj = v + (base + j) * ld_v + (int64_t)h * d_v;
+          for (int e = 0; e < d_v; ++e) o[e] += a * vj[e];
+        }
+        double* dst = out + (base + i) * ld_out + (int64_t)h * d_v;
+        if (epilogue == ORACLE_EPILOGUE_NONE) {
+          for (int e = 0; e < d_v; ++e) dst[e] = o[e];
+        } else {
+          double mean = 0.0;
+          for (int e = 0; e < d_v; ++e) mean += o[e];
+          mean /= d_v;
+          double var = 0.0;
+          for (int e = 0; e < d_v; ++e) var += (o[e] - mean) * (o[e] - mean);
+          var /= d_v;
+          double rstd = 1.0 / sqrt(var + eps);
+          const double* ui = u + (base + i) * ld_u + (int64_t)h * d_v;
+          for (int e = 0; e < d_v; ++e) dst[e] = (o[e] - mean) * rstd * ui[e];
+        }
+      }
+    }
+    free(o);
+  }
+  free(items);
+  return 0;
+}
+
+int hstu_oracle_max_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
