@@ -1,0 +1,256 @@
+#!/usr/bin/env python3
+"""Throughput of the jagged HSTU attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload ranking]
+
+A step is one pass of the whole hot path (scheduler kernel + attention kernel)
+over one batch of seeded synthetic inputs already resident in HBM.  Before
+every timed step a 1 GiB buffer is rewritten (outside the timed events) so
+that the 256 MB last-level cache holds none of the inputs.  Prints one JSON
+line with valid-pair TFLOP/s, tokens/s, the attention kernel's roofline
+position and the fp64 CPU oracle timed on this host as a baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "jagged HSTU attn fwd TFLOP/s (valid pairs) + % bf16 MFMA peak; tokens/s"
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}      # dense MFMA peaks, MI355X
+PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCES = ["jagged_hstu_attention_attn_amd/csrc/attn_fwd.hip",
+                  "jagged_hstu_attention_attn_amd/csrc/hstu_device.hpp"]
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic(inp, valid_pairs: int):
+    """Algorithmic flops and HBM bytes of one forward (definitions in the
+    design notes): 2*(d_qk+d_v) flops per valid pair and head; q, k, v, u read
+    once, out written once, plus timestamps, metadata and bias tables."""
+    H, dqk, dv, N, B = inp.num_heads, inp.d_qk, inp.d_v, inp.total_tokens, inp.num_seqs
+    es = 2 if inp.dtype == "bf16" else 4
+    flops = 2.0 * (dqk + dv) * H * valid_pairs
+    byts = N * H * (2 * dqk + 3 * dv) * es
+    if inp.timestamps is not None:
+        byts += 8 * N
+    byts += 4 * (B + 1) + (4 * B if inp.num_targets is not None else 0)
+    byts += 4 * (0 if inp.pos_table is None else inp.pos_table.shape[0])
+    byts += 4 * (0 if inp.time_table is None else inp.time_table.shape[0])
+    return flops, byts
+
+
+def traffic_from_profile(workload: str):
+    """HBM bytes per attention launch from the committed counter summary, if
+    it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"attn_fwd_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_sha = re.search(r"kernel_source_sha:\s*([0-9a-f]+)", text)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_sha or not m_bytes or m_sha.group(1) != kernel_source_hash():
+        return None
+    return float(m_bytes.group(1))
+
+
+def cpu_baseline(inp, flops_per_pair_head: float, budget_s: float):
+    """The fp64 oracle, as it stands, on this host's cores over a bounded
+    prefix of the batch (whole sequences), in the metric's unit."""
+    import numpy as np
+    import oracle
+    oracle.build(force=False)
+    from jagged_hstu_attention_attn_amd.inputs import make_inputs
+    # estimate from a small prefix, then take the largest prefix within budget
+    nthreads = oracle.default_threads()
+    B = inp.num_seqs
+    probe = make_inputs(inp.workload, num_seqs=max(1, min(B, 4)), dtype=inp.dtype)
+    _, t_probe, _ = oracle.timed_forward(probe, nthreads=nthreads)
+    pairs_probe = oracle.count_allowed(probe.offsets, probe.num_targets, probe.contextual_len,
+                                       probe.max_attn_len)
+    rate = pairs_probe / max(t_probe, 1e-6)
+    lens = inp.lengths
+    nb = B
+    total_pairs = oracle.count_allowed(inp.offsets, inp.num_targets, inp.contextual_len,
+                                       inp.max_attn_len)
+    if total_pairs / rate > budget_s:
+        lo, hi = 1, B
+        while lo < hi:
+            mid = (lo + hi + 1) // 2
+            off = np.concatenate([[0], np.cumsum(lens[:mid])]).astype(np.int32)
+            nt = None if inp.num_targets is None else inp.num_targets[:mid]
+            p = oracle.count_allowed(off, nt, inp.contextual_len, inp.max_attn_len)
+            if p / rate <= budget_s:
+                lo = mid
+            else:
+                hi = mid - 1
+        nb = lo
+    sample = make_inputs(inp.workload, num_seqs=nb, dtype=inp.dtype) if nb < B else inp
+    pairs = oracle.count_allowed(sample.offsets, sample.num_targets, sample.contextual_len,
+                                 sample.max_attn_len)
+    _, secs, used = oracle.timed_forward(sample, nthreads=nthreads)
+    tflops = flops_per_pair_head * sample.num_heads * pairs / secs / 1e12
+    return {
+        "value": tflops, "unit": "TFLOP/s", "cores": used, "kind": "oracle",
+        "sample": (f"{nb} of {B} sequences of the {inp.workload} batch "
+                   f"({sample.total_tokens} tokens, {sample.num_heads} heads, fp64 C loop, "
+                   f"OpenMP over (sequence, head)), {secs:.2f} s"),
+        "seconds": secs, "tokens_per_s": sample.total_tokens / secs,
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="ranking",
+                    choices=["tiny", "ranking", "longtail", "windowed", "layer"])
+    ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--no-flush", action="store_true", help="keep inputs cache-resident")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 256 MiB device copy (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the forward shards by sequence with no exchange; see the design notes)",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    if args.copy_calibration:
+        n = 256 << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copied {n} bytes 5 times")
+        return 0
+
+    from jagged_hstu_attention_attn_amd.api import JaggedAttnCall, valid_pairs
+    from jagged_hstu_attention_attn_amd.device_inputs import call_kwargs, to_device
+    from jagged_hstu_attention_attn_amd.inputs import WORKLOADS, make_inputs
+
+    log(f"workload {args.workload}: generating inputs")
+    inp = make_inputs(args.workload, seed=args.seed)
+    dev = to_device(inp, "cuda")
+    call = JaggedAttnCall(dev["q"], dev["k"], dev["v"], dev["u"], dev["offsets"],
+                          **call_kwargs(inp, dev))
+    pairs = valid_pairs(inp.offsets, inp.num_targets, inp.contextual_len, inp.max_attn_len)
+    flops, byts = algorithmic(inp, pairs)
+    flush = None if args.no_flush else torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+
+    log(f"{inp.num_seqs} sequences, {inp.total_tokens} tokens, {pairs} valid pairs/head; "
+        f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for s in range(args.steps):
+        if flush is not None:
+            flush.fill_(s & 0xFF)
+        e0, e1, e2 = evs[s]
+        e0.record(stream)
+        call.plan()
+        e1.record(stream)
+        call.run()
+        e2.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    step_ms = [e0.elapsed_time(e2) for e0, _, e2 in evs]
+    plan_ms = [e0.elapsed_time(e1) for e0, e1, _ in evs]
+    attn_ms = [e1.elapsed_time(e2) for _, e1, e2 in evs]
+    ms = sum(step_ms) / len(step_ms)
+    attn = sum(attn_ms) / len(attn_ms)
+    plan = sum(plan_ms) / len(plan_ms)
+    log(f"step {ms * 1e3:.1f} us (plan {plan * 1e3:.1f} us, attention {attn * 1e3:.1f} us), "
+        f"wall {wall:.3f} s")
+
+    tflops = flops / (ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[inp.dtype]
+    ai = flops / byts
+    ridge = peak * 1e12 / (PEAK_HBM_GBS * 1e9)
+    bound = "mfma" if ai >= ridge else "hbm"
+    if bound == "hbm":
+        achieved = byts / (attn * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS}
+    else:
+        achieved = flops / (attn * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                "frac": achieved / peak}
+    roof["traffic"] = traffic_from_profile(args.workload)
+    roof["kernel"] = "hstu_attn_fwd_kernel"
+    roof["kernel_us"] = attn * 1e3
+    roof["algorithmic_bytes"] = byts
+    roof["algorithmic_flops"] = flops
+
+    result = {
+        "metric": METRIC,
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": inp.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": args.workload,
+            "num_seqs": inp.num_seqs,
+            "total_tokens": inp.total_tokens,
+            "num_heads": inp.num_heads,
+            "d_qk": inp.d_qk,
+            "d_v": inp.d_v,
+            "valid_pairs_per_head": pairs,
+            "seed": args.seed if args.seed is not None else WORKLOADS[args.workload].seed,
+            "cache_flushed": flush is not None,
+            "parallelism": "single GPU",
+        },
+        "tokens_per_s": inp.total_tokens / (ms * 1e-3),
+        "pct_bf16_mfma_peak": 100.0 * tflops / PEAK_TFLOPS["bf16"],
+        "pct_hbm_peak": 100.0 * byts / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "plan_us": plan * 1e3,
+        "wall_s": wall,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the fp64 CPU oracle")
+        result["cpu_baseline"] = cpu_baseline(inp, 2.0 * (inp.d_qk + inp.d_v), args.cpu_budget)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,176 @@
+/*
+ * hstu_attn.h -- C ABI of the MI355X (gfx950) jagged HSTU attention library.
+ *
+ * Operation (forward only).  Sequences are stored jagged: the tokens of all
+ * sequences are concatenated and an int32 offsets array marks where each
+ * sequence starts ("Scaling HSTU: ragged execution, candidate amortization and
+ * content features", section "Variable length is a central systems issue").
+ * For every sequence b, head h and query row i of the sequence:
+ *
+ *   s_ij  = alpha * <q_i, k_j> + pos_table[min(|i-j|, P-1)]
+ *                 + time_table[min(floor(log2(1 + |t_i - t_j|)), Tt-1)]
+ *   a_ij  = SiLU(s_ij) / n_scale  if (i, j) is allowed, else exactly 0
+ *   o_i   = sum_j a_ij * v_j
+ *   out_i = LayerNorm(o_i) * u_i        (HSTU_EPILOGUE_LN_U)
+ *         = o_i                         (HSTU_EPILOGUE_NONE)
+ *
+ * This is the pointwise SiLU aggregation with relative position / time bias
+ * and the norm-then-U gating of "HSTU tensor by tensor: SiLU aggregation,
+ * temporal bias and gating" (sections "SiLU aggregation coefficients are not
+ * probabilities", "Relative time adds information content similarity lacks",
+ * "Similar shape, different aggregation"); illegal coefficients are zeroed
+ * after the nonlinearity (section "Do not copy softmax masking mechanically"),
+ * so a masked score that overflows can never turn into NaN.
+ *
+ * Allowed pairs combine the causal rule with the four rules named on the
+ * "HSTU-MUSA" page, section "Mathematical Equivalence".  With L the sequence
+ * length, T = clamp(num_targets[b], 0, L) candidates at the end, n_h = L - T
+ * history tokens and c = clamp(contextual_len, 0, n_h) prefix tokens:
+ *   prefix rows    i <  c        : j < c          (bidirectional)
+ *   history rows   c <= i < n_h  : j <= i         (causal)
+ *   candidate rows i >= n_h      : j < n_h, or j == i   (target group)
+ *   if max_attn_len W > 0, also p_i - j <= W with p_i = min(i, n_h)
+ *   (candidate position clamping: every candidate sits at the history end).
+ * The bias always uses the raw |i-j| and |t_i - t_j|.  LayerNorm is taken per
+ * (token, head) over d_v, without affine weights, with biased variance and
+ * epsilon desc->ln_eps.
+ *
+ * Memory layout.  q, k: [total_tokens, H, d_qk]; v, u, out: [total_tokens, H,
+ * d_v].  Element (t, h, e) of tensor x lives at x + t*ld_x + h*d + e (ld_x in
+ * elements, head stride d).  All of q, k, v, u, out share desc->dtype.
+ * offsets: int32 [num_seqs+1], offsets[0] = 0, nondecreasing, offsets[num_seqs]
+ * = total_tokens.  timestamps: int64 [total_tokens], seconds.  num_targets:
+ * int32 [num_seqs].  pos_table, time_table: float32.
+ *
+ * Ownership and asynchrony.  Every tensor pointer is device memory owned by
+ * the caller.  The library allocates no device memory and keeps no pointer
+ * after a call returns; scratch space comes from the caller's `workspace`.
+ * Calls only enqueue kernels on `stream` (a hipStream_t; NULL = the default
+ * stream) and never synchronise: the caller keeps every buffer alive until
+ * the stream has passed the call.
+ *
+ * Errors.  Functions return an hstu_status.  Every condition the host can
+ * check (null pointers, sizes, alignment, strides, table lengths, n_scale,
+ * workspace size, unsupported shapes) is checked before any HIP call; a
+ * failing call enqueues nothing.  A failure sets a thread-local message that
+ * hstu_last_error() returns.  Nothing aborts or throws across the ABI.
+ * Device data is trusted: non-monotone offsets, offsets[num_seqs] !=
+ * total_tokens or non-finite inputs give undefined results (checking them
+ * would need a synchronisation).  num_targets[b] and contextual_len are
+ * clamped as described above.
+ */
+#ifndef HSTU_ATTN_H_
+#define HSTU_ATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  HSTU_OK = 0,
+  HSTU_ERR_INVALID_ARG = -1,  /* null pointer, bad size, stride or alignment     */
+  HSTU_ERR_UNSUPPORTED = -2,  /* valid but not built: (dtype, d_qk, d_v) etc.    */
+  HSTU_ERR_WORKSPACE = -3,    /* workspace null or smaller than required         */
+  HSTU_ERR_HIP = -4           /* a HIP runtime call or kernel launch failed      */
+} hstu_status;
+
+typedef enum { HSTU_DTYPE_F32 = 0, HSTU_DTYPE_BF16 = 1 } hstu_dtype;
+
+typedef enum { HSTU_EPILOGUE_LN_U = 0, HSTU_EPILOGUE_NONE = 1 } hstu_epilogue;
+
+/* Shapes, element type and strides of one call. */
+typedef struct {
+  int32_t num_seqs;       /* B >= 0                                               */
+  int32_t total_tokens;   /* N >= 0, equals offsets[B] on the device              */
+  int32_t num_heads;      /* H >= 1                                               */
+  int32_t d_qk;           /* head dim of q and k                                  */
+  int32_t d_v;            /* head dim of v, u and out                             */
+  int32_t dtype;          /* hstu_dtype of q, k, v, u, out                        */
+  int64_t ld_q, ld_k, ld_v, ld_u, ld_out;  /* token strides in elements           */
+  int32_t pos_table_len;  /* P; 0 iff pos_table is NULL                           */
+  int32_t time_table_len; /* Tt; 0 iff time_table is NULL (then no timestamps)    */
+  float ln_eps;           /* LayerNorm epsilon (> 0 and finite)                   */
+  int32_t epilogue;       /* hstu_epilogue                                        */
+} hstu_attn_desc;
+
+/*
+ * Supported (dtype, d_qk, d_v): (BF16,128,128), (BF16,64,64), (F32,128,128),
+ * (F32,64,64), (F32,8,8).  Alignment: q, k, v, u, out 16-byte aligned and
+ * ld_x * sizeof(element) a multiple of 16 bytes with ld_x >= H * d.
+ * Returns 1 if supported, 0 if not (no message is set).
+ */
+int hstu_jagged_attn_supported(int32_t dtype, int32_t d_qk, int32_t d_v);
+
+/*
+ * Workspace bytes the call needs for `desc` (the work list of the scheduler).
+ * Depends on num_seqs, total_tokens and num_heads only.  Returns 0 and sets
+ * the error message if desc is invalid.
+ */
+size_t hstu_jagged_attn_workspace_bytes(const hstu_attn_desc* desc);
+
+/*
+ * The full forward: hstu_jagged_attn_plan followed by hstu_jagged_attn_run on
+ * the same stream.  Arguments are as described for those two calls.
+ * B == 0 or total_tokens == 0 returns HSTU_OK and enqueues nothing.
+ */
+int hstu_jagged_attn_fwd(const hstu_attn_desc* desc,
+                         const void* q, const void* k, const void* v, const void* u,
+                         const int32_t* offsets, const int64_t* timestamps,
+                         const int32_t* num_targets, int32_t contextual_len,
+                         int32_t max_attn_len, float alpha, float n_scale,
+                         const float* pos_table, const float* time_table, void* out,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Scheduler: enqueues one kernel that reads offsets / num_targets on the
+ * device, splits every (sequence, head) into query tiles, estimates each tile's
+ * work from the mask geometry (number of key tiles it must visit) and writes a
+ * work list sorted by decreasing work into `workspace` ("Scaling HSTU",
+ * section "Variable length is a central systems issue": kernels must handle
+ * boundaries, grouping and balance).  The plan depends only on offsets,
+ * num_targets, contextual_len, max_attn_len and the shapes in desc, so it can
+ * be reused by several hstu_jagged_attn_run calls (e.g. every layer of a
+ * stack sharing one batch).  num_targets may be NULL (no candidates);
+ * contextual_len >= 0; max_attn_len >= 0 (0 = unlimited).
+ */
+int hstu_jagged_attn_plan(const hstu_attn_desc* desc, const int32_t* offsets,
+                          const int32_t* num_targets, int32_t contextual_len,
+                          int32_t max_attn_len, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/*
+ * Attention: enqueues the attention kernel, which walks the work list that a
+ * previous hstu_jagged_attn_plan call on the same stream wrote into
+ * `workspace` with the same offsets, num_targets, contextual_len,
+ * max_attn_len and shapes.  Requires n_scale > 0 and finite, alpha finite;
+ * timestamps non-NULL iff time_table non-NULL.  Writes every row of `out`
+ * exactly once and nothing else.
+ */
+int hstu_jagged_attn_run(const hstu_attn_desc* desc,
+                         const void* q, const void* k, const void* v, const void* u,
+                         const int32_t* offsets, const int64_t* timestamps,
+                         const int32_t* num_targets, int32_t contextual_len,
+                         int32_t max_attn_len, float alpha, float n_scale,
+                         const float* pos_table, const float* time_table, void* out,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Host helper for throughput accounting: the exact number of allowed (i, j)
+ * pairs of the batch, per head, from HOST copies of offsets and num_targets
+ * (num_targets may be NULL).  Returns -1 and sets the message on bad input.
+ */
+int64_t hstu_jagged_attn_valid_pairs(int32_t num_seqs, const int32_t* offsets_host,
+                                     const int32_t* num_targets_host,
+                                     int32_t contextual_len, int32_t max_attn_len);
+
+/* Thread-local message for the last failing call of this thread ("" if none). */
+const char* hstu_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HSTU_ATTN_H_ */

@@ -1,0 +1,186 @@
+"""Python binding of the jagged HSTU attention library.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libhstu_attn.so.  PyTorch supplies device memory and the current
+stream; nothing here computes on tensors.
+
+    out = jagged_attn_fwd(q, k, v, u, offsets, timestamps=ts, num_targets=nt,
+                          contextual_len=0, max_attn_len=0, alpha=a, n_scale=n,
+                          pos_table=pos, time_table=tim)
+
+q, k: [N, H, d_qk]; v, u: [N, H, d_v]; bf16 or fp32 CUDA (HIP) tensors whose
+last two dimensions are contiguous (the token stride may be larger, e.g. views
+into a fused projection output).  offsets: int32 [B+1]; timestamps: int64 [N];
+num_targets: int32 [B]; tables: float32.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import _lib
+
+__all__ = ["jagged_attn_fwd", "plan", "run", "make_desc", "workspace_bytes", "valid_pairs",
+           "JaggedAttnCall"]
+
+_DTYPES = {torch.float32: _lib.HSTU_DTYPE_F32, torch.bfloat16: _lib.HSTU_DTYPE_BF16}
+_EPILOGUES = {"ln_u": _lib.HSTU_EPILOGUE_LN_U, "none": _lib.HSTU_EPILOGUE_NONE}
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _token_stride(t: torch.Tensor, name: str) -> int:
+    if t.dim() != 3:
+        raise ValueError(f"{name} must be [tokens, heads, dim], got shape {tuple(t.shape)}")
+    if t.stride(2) != 1 or t.stride(1) != t.shape[2]:
+        raise ValueError(f"{name}: the head and feature dimensions must be contiguous")
+    return int(t.stride(0)) if t.shape[0] > 1 else int(t.shape[1] * t.shape[2])
+
+
+def make_desc(q, k, v, u, out, num_seqs: int, *, pos_table=None, time_table=None,
+              eps: float = 1e-5, epilogue: str = "ln_u") -> _lib.HstuAttnDesc:
+    if q.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    for name, t in (("k", k), ("v", v), ("out", out)) + ((("u", u),) if u is not None else ()):
+        if t.dtype != q.dtype:
+            raise TypeError(f"{name} has dtype {t.dtype}, q has {q.dtype}")
+    d = _lib.HstuAttnDesc()
+    d.num_seqs = int(num_seqs)
+    d.total_tokens = int(q.shape[0])
+    d.num_heads = int(q.shape[1])
+    d.d_qk = int(q.shape[2])
+    d.d_v = int(v.shape[2])
+    d.dtype = _DTYPES[q.dtype]
+    d.ld_q = _token_stride(q, "q")
+    d.ld_k = _token_stride(k, "k")
+    d.ld_v = _token_stride(v, "v")
+    d.ld_u = _token_stride(u, "u") if u is not None else d.num_heads * d.d_v
+    d.ld_out = _token_stride(out, "out")
+    d.pos_table_len = 0 if pos_table is None else int(pos_table.numel())
+    d.time_table_len = 0 if time_table is None else int(time_table.numel())
+    d.ln_eps = float(eps)
+    d.epilogue = _EPILOGUES[epilogue]
+    return d
+
+
+def workspace_bytes(desc: _lib.HstuAttnDesc) -> int:
+    n = _lib.load().hstu_jagged_attn_workspace_bytes(ctypes.byref(desc))
+    if n == 0:
+        raise _lib.HstuError(_lib.HSTU_ERR_INVALID_ARG, _lib.last_error())
+    return int(n)
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def plan(desc, offsets, num_targets, contextual_len, max_attn_len, workspace) -> None:
+    """Enqueue the scheduler kernel (writes the work list into `workspace`)."""
+    _lib.check(_lib.load().hstu_jagged_attn_plan(
+        ctypes.byref(desc), _ptr(offsets), _ptr(num_targets), int(contextual_len),
+        int(max_attn_len), _ptr(workspace), int(workspace.numel()), _stream(workspace.device)))
+
+
+def _run_like(fn_name, desc, q, k, v, u, offsets, timestamps, num_targets, contextual_len,
+              max_attn_len, alpha, n_scale, pos_table, time_table, out, workspace):
+    fn = getattr(_lib.load(), fn_name)
+    _lib.check(fn(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(u), _ptr(offsets),
+                  _ptr(timestamps), _ptr(num_targets), int(contextual_len), int(max_attn_len),
+                  float(alpha), float(n_scale), _ptr(pos_table), _ptr(time_table), _ptr(out),
+                  _ptr(workspace), int(workspace.numel()), _stream(q.device)))
+
+
+def run(desc, q, k, v, u, offsets, timestamps, num_targets, contextual_len, max_attn_len,
+        alpha, n_scale, pos_table, time_table, out, workspace) -> None:
+    """Enqueue the attention kernel on a work list made by `plan`."""
+    _run_like("hstu_jagged_attn_run", desc, q, k, v, u, offsets, timestamps, num_targets,
+              contextual_len, max_attn_len, alpha, n_scale, pos_table, time_table, out,
+              workspace)
+
+
+def _check_aux(offsets, timestamps, num_targets, pos_table, time_table, device):
+    if offsets.dtype != torch.int32 or offsets.dim() != 1 or not offsets.is_contiguous():
+        raise TypeError("offsets must be a contiguous int32 vector")
+    if timestamps is not None and (timestamps.dtype != torch.int64 or not timestamps.is_contiguous()):
+        raise TypeError("timestamps must be a contiguous int64 vector")
+    if num_targets is not None and (num_targets.dtype != torch.int32 or not num_targets.is_contiguous()):
+        raise TypeError("num_targets must be a contiguous int32 vector")
+    for name, t in (("pos_table", pos_table), ("time_table", time_table)):
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
+            raise TypeError(f"{name} must be a contiguous float32 vector")
+    for t in (offsets, timestamps, num_targets, pos_table, time_table):
+        if t is not None and t.device != device:
+            raise ValueError("all tensors must live on the same GPU")
+
+
+class JaggedAttnCall:
+    """A reusable call: owns its descriptor and workspace, so the work list
+    built by `plan()` can serve several `run()` calls on the same batch."""
+
+    def __init__(self, q, k, v, u, offsets, *, timestamps=None, num_targets=None,
+                 contextual_len=0, max_attn_len=0, alpha, n_scale, pos_table=None,
+                 time_table=None, eps=1e-5, epilogue="ln_u", out=None):
+        if not q.is_cuda:
+            raise ValueError("tensors must be on a GPU")
+        _check_aux(offsets, timestamps, num_targets, pos_table, time_table, q.device)
+        self.q, self.k, self.v, self.u = q, k, v, u
+        self.offsets, self.timestamps, self.num_targets = offsets, timestamps, num_targets
+        self.contextual_len, self.max_attn_len = int(contextual_len), int(max_attn_len)
+        self.alpha, self.n_scale = float(alpha), float(n_scale)
+        self.pos_table, self.time_table = pos_table, time_table
+        if out is None:
+            out = torch.empty((q.shape[0], q.shape[1], v.shape[2]), dtype=q.dtype,
+                              device=q.device)
+        self.out = out
+        self.desc = make_desc(q, k, v, u, out, offsets.numel() - 1, pos_table=pos_table,
+                              time_table=time_table, eps=eps, epilogue=epilogue)
+        self.workspace = torch.empty(workspace_bytes(self.desc), dtype=torch.uint8,
+                                     device=q.device)
+
+    def plan(self) -> None:
+        plan(self.desc, self.offsets, self.num_targets, self.contextual_len, self.max_attn_len,
+             self.workspace)
+
+    def run(self) -> torch.Tensor:
+        run(self.desc, self.q, self.k, self.v, self.u, self.offsets, self.timestamps,
+            self.num_targets, self.contextual_len, self.max_attn_len, self.alpha, self.n_scale,
+            self.pos_table, self.time_table, self.out, self.workspace)
+        return self.out
+
+    def __call__(self) -> torch.Tensor:
+        _run_like("hstu_jagged_attn_fwd", self.desc, self.q, self.k, self.v, self.u,
+                  self.offsets, self.timestamps, self.num_targets, self.contextual_len,
+                  self.max_attn_len, self.alpha, self.n_scale, self.pos_table, self.time_table,
+                  self.out, self.workspace)
+        return self.out
+
+
+def jagged_attn_fwd(q, k, v, u, offsets, *, timestamps=None, num_targets=None,
+                    contextual_len: int = 0, max_attn_len: int = 0, alpha: float,
+                    n_scale: float, pos_table=None, time_table=None, eps: float = 1e-5,
+                    epilogue: str = "ln_u", out=None) -> torch.Tensor:
+    """One full forward (scheduler + attention) on the current stream."""
+    call = JaggedAttnCall(q, k, v, u, offsets, timestamps=timestamps, num_targets=num_targets,
+                          contextual_len=contextual_len, max_attn_len=max_attn_len,
+                          alpha=alpha, n_scale=n_scale, pos_table=pos_table,
+                          time_table=time_table, eps=eps, epilogue=epilogue, out=out)
+    return call()
+
+
+def valid_pairs(offsets, num_targets=None, contextual_len: int = 0, max_attn_len: int = 0) -> int:
+    """Exact allowed-pair count per head, from host copies of the metadata."""
+    off = np.ascontiguousarray(np.asarray(offsets), dtype=np.int32)
+    nt = None if num_targets is None else np.ascontiguousarray(np.asarray(num_targets),
+                                                                dtype=np.int32)
+    n = _lib.load().hstu_jagged_attn_valid_pairs(
+        off.shape[0] - 1, off.ctypes.data_as(ctypes.c_void_p),
+        None if nt is None else nt.ctypes.data_as(ctypes.c_void_p),
+        int(contextual_len), int(max_attn_len))
+    if n < 0:
+        raise _lib.HstuError(_lib.HSTU_ERR_INVALID_ARG, _lib.last_error())
+    return int(n)

@@ -1,0 +1,258 @@
+// hstu_attn.hip -- host side of the C ABI declared in include/hstu_attn.h:
+// argument validation (before any HIP call), workspace sizing, launches of the
+// scheduler and attention kernels on the caller's stream, error reporting.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "hstu_attn.h"
+#include "hstu_device.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+size_t elem_size(int32_t dtype) { return dtype == HSTU_DTYPE_BF16 ? 2 : 4; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_desc(const hstu_attn_desc* d) {
+  if (!d) return fail(HSTU_ERR_INVALID_ARG, "desc is NULL");
+  if (d->num_seqs < 0) return fail(HSTU_ERR_INVALID_ARG, "num_seqs < 0 (%d)", d->num_seqs);
+  if (d->total_tokens < 0)
+    return fail(HSTU_ERR_INVALID_ARG, "total_tokens < 0 (%d)", d->total_tokens);
+  if (d->num_heads < 1) return fail(HSTU_ERR_INVALID_ARG, "num_heads < 1 (%d)", d->num_heads);
+  if (d->dtype != HSTU_DTYPE_F32 && d->dtype != HSTU_DTYPE_BF16)
+    return fail(HSTU_ERR_INVALID_ARG, "unknown dtype %d", d->dtype);
+  if (d->epilogue != HSTU_EPILOGUE_LN_U && d->epilogue != HSTU_EPILOGUE_NONE)
+    return fail(HSTU_ERR_INVALID_ARG, "unknown epilogue %d", d->epilogue);
+  if (d->d_qk <= 0 || d->d_v <= 0)
+    return fail(HSTU_ERR_INVALID_ARG, "d_qk and d_v must be positive (%d, %d)", d->d_qk, d->d_v);
+  if (!hstu::attn_supported(d->dtype, d->d_qk, d->d_v))
+    return fail(HSTU_ERR_UNSUPPORTED, "unsupported (dtype=%d, d_qk=%d, d_v=%d)", d->dtype,
+                d->d_qk, d->d_v);
+  if (d->pos_table_len < 0 || d->time_table_len < 0)
+    return fail(HSTU_ERR_INVALID_ARG, "negative table length");
+  if (d->pos_table_len > hstu::kPosMax)
+    return fail(HSTU_ERR_UNSUPPORTED, "pos_table_len %d exceeds %d", d->pos_table_len,
+                hstu::kPosMax);
+  if (!(d->ln_eps > 0.0f) || !std::isfinite(d->ln_eps))
+    return fail(HSTU_ERR_INVALID_ARG, "ln_eps must be positive and finite");
+  const int64_t H = d->num_heads;
+  const size_t es = elem_size(d->dtype);
+  struct {
+    const char* name;
+    int64_t ld;
+    int64_t need;
+  } lds[] = {{"ld_q", d->ld_q, H * d->d_qk}, {"ld_k", d->ld_k, H * d->d_qk},
+             {"ld_v", d->ld_v, H * d->d_v},  {"ld_u", d->ld_u, H * d->d_v},
+             {"ld_out", d->ld_out, H * d->d_v}};
+  for (auto& x : lds) {
+    if (x.name[3] == 'u' && d->epilogue == HSTU_EPILOGUE_NONE) continue;  // u unused
+    if (x.ld < x.need)
+      return fail(HSTU_ERR_INVALID_ARG, "%s = %lld is below H*d = %lld", x.name,
+                  (long long)x.ld, (long long)x.need);
+    if ((x.ld * (int64_t)es) % 16 != 0)
+      return fail(HSTU_ERR_INVALID_ARG, "%s * element size must be a multiple of 16 bytes",
+                  x.name);
+  }
+  const hstu::PlanLayout pl = hstu::plan_layout(d->num_seqs, d->total_tokens);
+  if (pl.pairs_max * H > 0x7fffffffLL)
+    return fail(HSTU_ERR_UNSUPPORTED, "too many work items (%lld)",
+                (long long)(pl.pairs_max * H));
+  return HSTU_OK;
+}
+
+int check_plan_args(const hstu_attn_desc* d, const int32_t* offsets, int32_t contextual_len,
+                    int32_t max_attn_len, const void* ws, size_t ws_bytes) {
+  if (d->num_seqs > 0 && !offsets) return fail(HSTU_ERR_INVALID_ARG, "offsets is NULL");
+  if (contextual_len < 0) return fail(HSTU_ERR_INVALID_ARG, "contextual_len < 0");
+  if (max_attn_len < 0) return fail(HSTU_ERR_INVALID_ARG, "max_attn_len < 0");
+  const size_t need = hstu::plan_layout(d->num_seqs, d->total_tokens).total;
+  if (!ws) return fail(HSTU_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", need);
+  if (ws_bytes < need)
+    return fail(HSTU_ERR_WORKSPACE, "workspace has %zu bytes, need %zu", ws_bytes, need);
+  if (!aligned16(ws)) return fail(HSTU_ERR_INVALID_ARG, "workspace not 16-byte aligned");
+  return HSTU_OK;
+}
+
+int check_run_args(const hstu_attn_desc* d, const void* q, const void* k, const void* v,
+                   const void* u, const int64_t* timestamps, float alpha, float n_scale,
+                   const float* pos_table, const float* time_table, const void* out) {
+  struct {
+    const char* name;
+    const void* p;
+  } ptrs[] = {{"q", q}, {"k", k}, {"v", v}, {"out", out}, {"u", u}};
+  for (auto& x : ptrs) {
+    if (x.name[0] == 'u' && d->epilogue == HSTU_EPILOGUE_NONE) continue;
+    if (!x.p) return fail(HSTU_ERR_INVALID_ARG, "%s is NULL", x.name);
+    if (!aligned16(x.p)) return fail(HSTU_ERR_INVALID_ARG, "%s is not 16-byte aligned", x.name);
+  }
+  if ((pos_table == nullptr) != (d->pos_table_len == 0))
+    return fail(HSTU_ERR_INVALID_ARG, "pos_table and pos_table_len disagree");
+  if ((time_table == nullptr) != (d->time_table_len == 0))
+    return fail(HSTU_ERR_INVALID_ARG, "time_table and time_table_len disagree");
+  if (time_table && !timestamps)
+    return fail(HSTU_ERR_INVALID_ARG, "a time bias needs timestamps");
+  if (!(n_scale > 0.0f) || !std::isfinite(n_scale))
+    return fail(HSTU_ERR_INVALID_ARG, "n_scale must be positive and finite");
+  if (!std::isfinite(alpha)) return fail(HSTU_ERR_INVALID_ARG, "alpha must be finite");
+  return HSTU_OK;
+}
+
+hstu::PlanArgs make_plan_args(const hstu_attn_desc* d, const int32_t* offsets,
+                              const int32_t* num_targets, int32_t contextual_len,
+                              int32_t max_attn_len, void* ws) {
+  const hstu::PlanLayout pl = hstu::plan_layout(d->num_seqs, d->total_tokens);
+  char* base = static_cast<char*>(ws);
+  hstu::PlanArgs a;
+  a.offsets = offsets;
+  a.num_targets = num_targets;
+  a.num_seqs = d->num_seqs;
+  a.contextual_len = contextual_len;
+  a.max_attn_len = max_attn_len;
+  a.pairs_max = (int32_t)pl.pairs_max;
+  a.count = reinterpret_cast<int32_t*>(base + pl.count_off);
+  a.pairs = reinterpret_cast<int2*>(base + pl.pairs_off);
+  a.keys = reinterpret_cast<int32_t*>(base + pl.keys_off);
+  a.seq_start = reinterpret_cast<int32_t*>(base + pl.seqstart_off);
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int hstu_jagged_attn_supported(int32_t dtype, int32_t d_qk, int32_t d_v) {
+  return hstu::attn_supported(dtype, d_qk, d_v) ? 1 : 0;
+}
+
+size_t hstu_jagged_attn_workspace_bytes(const hstu_attn_desc* desc) {
+  if (check_desc(desc) != HSTU_OK) return 0;
+  return hstu::plan_layout(desc->num_seqs, desc->total_tokens).total;
+}
+
+int hstu_jagged_attn_plan(const hstu_attn_desc* desc, const int32_t* offsets,
+                          const int32_t* num_targets, int32_t contextual_len,
+                          int32_t max_attn_len, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  int rc = check_desc(desc);
+  if (rc != HSTU_OK) return rc;
+  rc = check_plan_args(desc, offsets, contextual_len, max_attn_len, workspace, workspace_bytes);
+  if (rc != HSTU_OK) return rc;
+  if (desc->num_seqs == 0 || desc->total_tokens == 0) return HSTU_OK;
+  const hstu::PlanArgs a =
+      make_plan_args(desc, offsets, num_targets, contextual_len, max_attn_len, workspace);
+  const hipError_t e = hstu::launch_plan(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess)
+    return fail(HSTU_ERR_HIP, "scheduler launch failed: %s", hipGetErrorString(e));
+  return HSTU_OK;
+}
+
+int hstu_jagged_attn_run(const hstu_attn_desc* desc, const void* q, const void* k,
+                         const void* v, const void* u, const int32_t* offsets,
+                         const int64_t* timestamps, const int32_t* num_targets,
+                         int32_t contextual_len, int32_t max_attn_len, float alpha,
+                         float n_scale, const float* pos_table, const float* time_table,
+                         void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_desc(desc);
+  if (rc != HSTU_OK) return rc;
+  rc = check_plan_args(desc, offsets, contextual_len, max_attn_len, workspace, workspace_bytes);
+  if (rc != HSTU_OK) return rc;
+  if (desc->num_seqs == 0 || desc->total_tokens == 0) return HSTU_OK;
+  rc = check_run_args(desc, q, k, v, u, timestamps, alpha, n_scale, pos_table, time_table, out);
+  if (rc != HSTU_OK) return rc;
+
+  const hstu::PlanArgs pa =
+      make_plan_args(desc, offsets, num_targets, contextual_len, max_attn_len, workspace);
+  hstu::AttnArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.u = desc->epilogue == HSTU_EPILOGUE_NONE ? nullptr : u;
+  a.out = out;
+  a.offsets = offsets;
+  a.timestamps = time_table ? timestamps : nullptr;
+  a.num_targets = num_targets;
+  a.pos_table = pos_table;
+  a.time_table = time_table;
+  a.count = pa.count;
+  a.pairs = pa.pairs;
+  a.ld_q = desc->ld_q;
+  a.ld_k = desc->ld_k;
+  a.ld_v = desc->ld_v;
+  a.ld_u = desc->ld_u;
+  a.ld_out = desc->ld_out;
+  a.num_heads = desc->num_heads;
+  a.contextual_len = contextual_len;
+  a.max_attn_len = max_attn_len;
+  a.pos_len = desc->pos_table_len;
+  a.time_len = desc->time_table_len;
+  a.epilogue = desc->epilogue;
+  a.alpha = alpha;
+  a.inv_n_scale = (float)(1.0 / (double)n_scale);
+  a.ln_eps = desc->ln_eps;
+  const hstu::PlanLayout pl = hstu::plan_layout(desc->num_seqs, desc->total_tokens);
+  const int64_t grid = pl.pairs_max * desc->num_heads;
+  const hipError_t e = hstu::launch_attn(a, desc->dtype, desc->d_qk, desc->d_v, grid,
+                                         static_cast<hipStream_t>(stream));
+  if (e != hipSuccess)
+    return fail(HSTU_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
+  return HSTU_OK;
+}
+
+int hstu_jagged_attn_fwd(const hstu_attn_desc* desc, const void* q, const void* k,
+                         const void* v, const void* u, const int32_t* offsets,
+                         const int64_t* timestamps, const int32_t* num_targets,
+                         int32_t contextual_len, int32_t max_attn_len, float alpha,
+                         float n_scale, const float* pos_table, const float* time_table,
+                         void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  // Validate everything before the first launch so that a bad call enqueues nothing.
+  int rc = check_desc(desc);
+  if (rc != HSTU_OK) return rc;
+  rc = check_plan_args(desc, offsets, contextual_len, max_attn_len, workspace, workspace_bytes);
+  if (rc != HSTU_OK) return rc;
+  if (desc->num_seqs == 0 || desc->total_tokens == 0) return HSTU_OK;
+  rc = check_run_args(desc, q, k, v, u, timestamps, alpha, n_scale, pos_table, time_table, out);
+  if (rc != HSTU_OK) return rc;
+  rc = hstu_jagged_attn_plan(desc, offsets, num_targets, contextual_len, max_attn_len, workspace,
+                             workspace_bytes, stream);
+  if (rc != HSTU_OK) return rc;
+  return hstu_jagged_attn_run(desc, q, k, v, u, offsets, timestamps, num_targets, contextual_len,
+                              max_attn_len, alpha, n_scale, pos_table, time_table, out,
+                              workspace, workspace_bytes, stream);
+}
+
+int64_t hstu_jagged_attn_valid_pairs(int32_t num_seqs, const int32_t* offsets_host,
+                                     const int32_t* num_targets_host, int32_t contextual_len,
+                                     int32_t max_attn_len) {
+  if (num_seqs < 0) return fail(-1, "num_seqs < 0");
+  if (num_seqs > 0 && !offsets_host) return fail(-1, "offsets is NULL");
+  if (contextual_len < 0 || max_attn_len < 0) return fail(-1, "negative mask parameter");
+  int64_t n = 0;
+  for (int b = 0; b < num_seqs; ++b) {
+    const int L = offsets_host[b + 1] - offsets_host[b];
+    if (L < 0) return fail(-1, "offsets decrease at sequence %d", b);
+    const hstu::SeqGeom g = hstu::seq_geom(
+        L, num_targets_host ? num_targets_host[b] : 0, contextual_len, max_attn_len);
+    for (int i = 0; i < L; ++i) {
+      const hstu::RowBounds r = hstu::row_bounds(g, i);
+      if (r.lo != hstu::kEmptyLo) n += r.span + 1;
+      if (r.self_j >= 0) n += 1;
+    }
+  }
+  return n;
+}
+
+const char* hstu_last_error(void) { return g_err; }
+
+}  // extern "C"

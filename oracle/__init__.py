@@ -57,7 +57,7 @@ def _load():
             i32, P, i32, i32, i32,
             P, i64, P, i64, P, i64, P, i64,
             P, P, i32, i32, f64, f64,
-            P, i32, P, i32, f64, i32, P, i64, i32]
+            P, i32, P, i32, f64, i32, P, i64, P, i32]
         lib.hstu_oracle_count_allowed.restype = i64
         lib.hstu_oracle_count_allowed.argtypes = [i32, P, P, i32, i32]
         lib.hstu_oracle_time_bucket.restype = ctypes.c_int
@@ -86,8 +86,10 @@ def default_threads() -> int:
 def forward_arrays(offsets, q, k, v, u, *, timestamps=None, num_targets=None,
                    contextual_len=0, max_attn_len=0, alpha=1.0, n_scale=1.0,
                    pos_table=None, time_table=None, eps=1e-5, epilogue=EPILOGUE_LN_U,
-                   nthreads: Optional[int] = None) -> np.ndarray:
-    """fp64 forward on [N, H, d] arrays (any float dtype; upcast exactly)."""
+                   rows=None, nthreads: Optional[int] = None) -> np.ndarray:
+    """fp64 forward on [N, H, d] arrays (any float dtype; upcast exactly).
+    `rows`: optional token indices; only those output rows are computed (the
+    others are NaN)."""
     lib = _load()
     offsets = np.ascontiguousarray(offsets, dtype=np.int32)
     q = np.ascontiguousarray(q, dtype=np.float64)
@@ -100,7 +102,13 @@ def forward_arrays(offsets, q, k, v, u, *, timestamps=None, num_targets=None,
     nt = None if num_targets is None else np.ascontiguousarray(num_targets, dtype=np.int32)
     pos = None if pos_table is None else np.ascontiguousarray(pos_table, dtype=np.float64)
     tim = None if time_table is None else np.ascontiguousarray(time_table, dtype=np.float64)
-    out = np.zeros((N, H, dv), dtype=np.float64)
+    sel = None
+    if rows is not None:
+        sel = np.zeros(N, dtype=np.uint8)
+        sel[np.asarray(rows, dtype=np.int64)] = 1
+        out = np.full((N, H, dv), np.nan, dtype=np.float64)
+    else:
+        out = np.zeros((N, H, dv), dtype=np.float64)
     rc = lib.hstu_oracle_fwd(
         offsets.shape[0] - 1, _ptr(offsets), H, dqk, dv,
         _ptr(q), H * dqk, _ptr(k), H * dqk, _ptr(v), H * dv, _ptr(u), H * dv,
@@ -108,21 +116,22 @@ def forward_arrays(offsets, q, k, v, u, *, timestamps=None, num_targets=None,
         float(alpha), float(n_scale),
         _ptr(pos), 0 if pos is None else pos.shape[0],
         _ptr(tim), 0 if tim is None else tim.shape[0],
-        float(np.float32(eps)), int(epilogue), _ptr(out), H * dv,
+        float(np.float32(eps)), int(epilogue), _ptr(out), H * dv, _ptr(sel),
         int(nthreads if nthreads is not None else default_threads()))
     if rc != 0:
         raise ValueError("oracle rejected its arguments")
     return out
 
 
-def forward(inp, *, epilogue=EPILOGUE_LN_U, nthreads: Optional[int] = None) -> np.ndarray:
-    """fp64 forward of a `JaggedInputs` batch."""
+def forward(inp, *, epilogue=EPILOGUE_LN_U, rows=None,
+            nthreads: Optional[int] = None) -> np.ndarray:
+    """fp64 forward of a `JaggedInputs` batch (optionally only token `rows`)."""
     return forward_arrays(
         inp.offsets, inp.q, inp.k, inp.v, inp.u, timestamps=inp.timestamps,
         num_targets=inp.num_targets, contextual_len=inp.contextual_len,
         max_attn_len=inp.max_attn_len, alpha=inp.alpha, n_scale=inp.n_scale,
         pos_table=inp.pos_table, time_table=inp.time_table, eps=inp.eps,
-        epilogue=epilogue, nthreads=nthreads)
+        epilogue=epilogue, rows=rows, nthreads=nthreads)
 
 
 def count_allowed(offsets, num_targets=None, contextual_len=0, max_attn_len=0) -> int:

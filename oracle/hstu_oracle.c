@@ -150,7 +150,9 @@ static int cmp_item_desc(const void* a, const void* b) {
 /*
  * Full forward.  Tensors are [total_tokens, H, d] with a token stride `ld_*`
  * (in elements) and head stride d.  All floating inputs are fp64 copies of the
- * exact values the device sees.  Returns 0, or -1 on a bad argument.
+ * exact values the device sees.  If row_select is not NULL, only tokens t with
+ * row_select[t] != 0 are computed (other output rows are left untouched).
+ * Returns 0, or -1 on a bad argument.
  */
 int hstu_oracle_fwd(int num_seqs, const int32_t* offsets, int num_heads, int d_qk, int d_v,
                     const double* q, int64_t ld_q, const double* k, int64_t ld_k,
@@ -159,7 +161,7 @@ int hstu_oracle_fwd(int num_seqs, const int32_t* offsets, int num_heads, int d_q
                     int contextual_len, int max_attn_len, double alpha, double n_scale,
                     const double* pos_table, int pos_len, const double* time_table,
                     int time_len, double eps, int epilogue, double* out, int64_t ld_out,
-                    int nthreads) {
+                    const unsigned char* row_select, int nthreads) {
   if (num_seqs < 0 || num_heads <= 0 || d_qk <= 0 || d_v <= 0) return -1;
   if ((pos_table == NULL) != (pos_len == 0) || (time_table == NULL) != (time_len == 0)) return -1;
   if (time_table && !timestamps) return -1;
@@ -191,6 +193,7 @@ int hstu_oracle_fwd(int num_seqs, const int32_t* offsets, int num_heads, int d_q
       seq_geom g = geometry(offsets, num_targets, b, contextual_len, max_attn_len);
       int64_t base = offsets[b];
       for (int64_t i = 0; i < g.L; ++i) {
+        if (row_select && !row_select[base + i]) continue;
         const double* qi = q + (base + i) * ld_q + (int64_t)h * d_qk;
         for (int e = 0; e < d_v; ++e) o[e] = 0.0;
         for (int64_t j = 0; j < g.L; ++j) {

@@ -1,0 +1,195 @@
+"""The C ABI on the host: symbols, argument validation, host helpers.
+
+No compute call runs here (no GPU): every call below either fails validation
+before any HIP call, or is expected to report HSTU_ERR_HIP.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from jagged_hstu_attention_attn_amd import _lib
+from jagged_hstu_attention_attn_amd.inputs import make_inputs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from jagged_hstu_attention_attn_amd import build
+        build.build(quiet=True)
+    return _lib.load()
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "hstu_attn.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hstu_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = _declared_functions()
+    assert set(declared) == set(_lib.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(line.split()[-1] for line in out.splitlines() if " T " in line)
+    for name in declared:
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_no_oracle_linkage():
+    out = subprocess.run(["ldd", _lib.LIB_PATH], capture_output=True, text=True).stdout
+    assert "oracle" not in out
+    out = subprocess.run(["nm", "-D", _lib.LIB_PATH], capture_output=True, text=True).stdout
+    assert "oracle" not in out
+
+
+def _desc(**kw):
+    d = _lib.HstuAttnDesc()
+    base = dict(num_seqs=2, total_tokens=100, num_heads=4, d_qk=128, d_v=128,
+                dtype=_lib.HSTU_DTYPE_BF16, ld_q=512, ld_k=512, ld_v=512, ld_u=512, ld_out=512,
+                pos_table_len=0, time_table_len=0, ln_eps=1e-5, epilogue=0)
+    base.update(kw)
+    for k, v in base.items():
+        setattr(d, k, v)
+    return d
+
+
+FAKE = 0x10000  # aligned, never dereferenced by the host
+
+
+def _fwd(lib, d, ws_bytes=None, **kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, u=FAKE, offsets=FAKE, timestamps=None, num_targets=None,
+                contextual_len=0, max_attn_len=0, alpha=0.1, n_scale=10.0, pos_table=None,
+                time_table=None, out=FAKE, ws=FAKE)
+    args.update(kw)
+    if ws_bytes is None:
+        ws_bytes = lib.hstu_jagged_attn_workspace_bytes(ctypes.byref(d)) or 1 << 20
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.hstu_jagged_attn_fwd(
+        ctypes.byref(d), vp(args["q"]), vp(args["k"]), vp(args["v"]), vp(args["u"]),
+        vp(args["offsets"]), vp(args["timestamps"]), vp(args["num_targets"]),
+        args["contextual_len"], args["max_attn_len"], args["alpha"], args["n_scale"],
+        vp(args["pos_table"]), vp(args["time_table"]), vp(args["out"]), vp(args["ws"]),
+        ws_bytes, None)
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("num_seqs", -1, _lib.HSTU_ERR_INVALID_ARG),
+    ("total_tokens", -5, _lib.HSTU_ERR_INVALID_ARG),
+    ("num_heads", 0, _lib.HSTU_ERR_INVALID_ARG),
+    ("dtype", 7, _lib.HSTU_ERR_INVALID_ARG),
+    ("epilogue", 3, _lib.HSTU_ERR_INVALID_ARG),
+    ("d_qk", 96, _lib.HSTU_ERR_UNSUPPORTED),
+    ("d_v", 0, _lib.HSTU_ERR_INVALID_ARG),
+    ("ld_q", 500, _lib.HSTU_ERR_INVALID_ARG),
+    ("ld_k", 516, _lib.HSTU_ERR_INVALID_ARG),          # 1032 bytes: not a multiple of 16
+    ("ln_eps", 0.0, _lib.HSTU_ERR_INVALID_ARG),
+    ("pos_table_len", 9000, _lib.HSTU_ERR_UNSUPPORTED),
+])
+def test_bad_descriptor(lib, field, value, code):
+    d = _desc(**{field: value})
+    assert _fwd(lib, d, ws_bytes=1 << 20) == code
+    assert _lib.last_error() != ""
+    if code == _lib.HSTU_ERR_INVALID_ARG or code == _lib.HSTU_ERR_UNSUPPORTED:
+        assert lib.hstu_jagged_attn_workspace_bytes(ctypes.byref(d)) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), _lib.HSTU_ERR_INVALID_ARG),
+    (dict(out=None), _lib.HSTU_ERR_INVALID_ARG),
+    (dict(offsets=None), _lib.HSTU_ERR_INVALID_ARG),
+    (dict(v=FAKE + 8), _lib.HSTU_ERR_INVALID_ARG),       # misaligned
+    (dict(n_scale=0.0), _lib.HSTU_ERR_INVALID_ARG),
+    (dict(n_scale=float("inf")), _lib.HSTU_ERR_INVALID_ARG),
+    (dict(alpha=float("nan")), _lib.HSTU_ERR_INVALID_ARG),
+    (dict(contextual_len=-1), _lib.HSTU_ERR_INVALID_ARG),
+    (dict(max_attn_len=-2), _lib.HSTU_ERR_INVALID_ARG),
+    (dict(pos_table=FAKE), _lib.HSTU_ERR_INVALID_ARG),   # pointer without a length
+    (dict(ws=None), _lib.HSTU_ERR_WORKSPACE),
+])
+def test_bad_arguments(lib, kw, code):
+    assert _fwd(lib, _desc(), **kw) == code
+    assert _lib.last_error() != ""
+
+
+def test_time_table_needs_timestamps(lib):
+    d = _desc(time_table_len=64)
+    assert _fwd(lib, d, time_table=FAKE) == _lib.HSTU_ERR_INVALID_ARG
+    assert "timestamps" in _lib.last_error()
+
+
+def test_small_workspace(lib):
+    d = _desc()
+    need = lib.hstu_jagged_attn_workspace_bytes(ctypes.byref(d))
+    assert need > 0
+    assert _fwd(lib, d, ws_bytes=need - 1) == _lib.HSTU_ERR_WORKSPACE
+
+
+def test_empty_batch_is_a_no_op(lib):
+    assert _fwd(lib, _desc(num_seqs=0, total_tokens=0), q=None, k=None, v=None, u=None,
+                out=None, offsets=None) == _lib.HSTU_OK
+    assert _fwd(lib, _desc(num_seqs=3, total_tokens=0)) == _lib.HSTU_OK
+
+
+def test_epilogue_none_does_not_need_u(lib):
+    rc = _fwd(lib, _desc(epilogue=_lib.HSTU_EPILOGUE_NONE, ld_u=0), u=None)
+    assert rc in (_lib.HSTU_OK, _lib.HSTU_ERR_HIP)   # passes validation
+
+
+def test_valid_call_without_gpu_reports_hip_error(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    rc = _fwd(lib, _desc())
+    assert rc == _lib.HSTU_ERR_HIP
+    assert _lib.last_error() != ""
+
+
+def test_supported_set(lib):
+    assert lib.hstu_jagged_attn_supported(1, 128, 128) == 1
+    assert lib.hstu_jagged_attn_supported(0, 8, 8) == 1
+    assert lib.hstu_jagged_attn_supported(1, 8, 8) == 0
+    assert lib.hstu_jagged_attn_supported(2, 128, 128) == 0
+
+
+# The product's host pair count (used for throughput accounting) against the
+# oracle's one-pair-at-a-time count.
+@pytest.mark.parametrize("name", ["tiny", "ranking", "longtail"])
+def test_valid_pairs_matches_oracle(oracle_mod, name):
+    from jagged_hstu_attention_attn_amd.api import valid_pairs
+    inp = make_inputs(name, num_seqs=12)
+    a = valid_pairs(inp.offsets, inp.num_targets, inp.contextual_len, inp.max_attn_len)
+    b = oracle_mod.count_allowed(inp.offsets, inp.num_targets, inp.contextual_len,
+                                 inp.max_attn_len)
+    assert a == b
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_valid_pairs_random_rules(oracle_mod, seed):
+    from jagged_hstu_attention_attn_amd.api import valid_pairs
+    rng = np.random.default_rng(seed)
+    L = rng.integers(0, 300, size=6)
+    off = np.concatenate([[0], np.cumsum(L)]).astype(np.int32)
+    nt = rng.integers(-3, 60, size=6).astype(np.int32)
+    c, W = int(rng.integers(0, 40)), int(rng.integers(0, 80))
+    assert valid_pairs(off, nt, c, W) == oracle_mod.count_allowed(off, nt, c, W)
+    assert valid_pairs(off, None, c, 0) == oracle_mod.count_allowed(off, None, c, 0)
+
+
+def test_tiny_workload_pair_count():
+    from jagged_hstu_attention_attn_amd.api import valid_pairs
+    assert valid_pairs([0, 10, 110, 1110]) == 505605
+
+
+def test_loader_fails_loudly_without_library(tmp_path, monkeypatch):
+    import importlib
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(ImportError):
+        _lib.load()

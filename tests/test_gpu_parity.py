@@ -1,0 +1,359 @@
+"""HIP path against the fp64 oracle, element by element, on seeded inputs.
+
+Tolerances: max|gpu - oracle| <= 1e-5 * max|oracle| for fp32 and
+<= 1e-2 * max|oracle| for bf16, over the whole output (or over the sampled
+rows for full-size long workloads, which the oracle evaluates row by row).
+Masked / padded positions must match exactly (zero-pattern test).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from jagged_hstu_attention_attn_amd.api import JaggedAttnCall, jagged_attn_fwd
+from jagged_hstu_attention_attn_amd.device_inputs import call_kwargs, to_device
+from jagged_hstu_attention_attn_amd.inputs import JaggedInputs, make_custom, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "bf16": 1e-2}
+DEV = "cuda:0"
+
+
+def gpu_forward(inp, epilogue="ln_u", ld=None, out=None):
+    dev = to_device(inp, DEV, ld=ld)
+    o = jagged_attn_fwd(dev["q"], dev["k"], dev["v"], dev["u"], dev["offsets"],
+                        epilogue=epilogue, out=out, **call_kwargs(inp, dev))
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy().astype(np.float64)
+
+
+def assert_close(gpu, ref, dtype, rows=None):
+    if rows is not None:
+        gpu, ref = gpu[rows], ref[rows]
+    assert np.all(np.isfinite(gpu)), "non-finite GPU output"
+    scale = np.abs(ref).max()
+    err = np.abs(gpu - ref).max()
+    assert err <= TOL[dtype] * scale, f"max err {err:.3e} vs bound {TOL[dtype] * scale:.3e}"
+    return err / max(scale, 1e-300)
+
+
+def ora(inp, epilogue="ln_u", rows=None):
+    ep = oracle.EPILOGUE_LN_U if epilogue == "ln_u" else oracle.EPILOGUE_NONE
+    return oracle.forward(inp, epilogue=ep, rows=rows)
+
+
+# ---------------------------------------------------------------------------
+# Worked example of "HSTU tensor by tensor", section "SiLU aggregation
+# coefficients are not probabilities", on the device.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype,d", [("f32", 8), ("bf16", 128), ("f32", 128)])
+def test_worked_example(dtype, d):
+    inp = make_custom([2], d_qk=d, d_v=d, dtype=dtype, alpha=1.0, n_scale=1.0)
+    inp.q[:] = 0; inp.k[:] = 0; inp.v[:] = 0; inp.u[:] = 1
+    inp.q[1, 0, 0] = 1.0
+    inp.k[0, 0, 0] = -1.0; inp.k[1, 0, 0] = 1.0
+    inp.v[0, 0, 0] = 1.0; inp.v[1, 0, 1] = 1.0
+    out = gpu_forward(inp, epilogue="none")
+    tol = 1e-6 if dtype == "f32" else 4e-3
+    assert abs(out[1, 0, 0] - (-0.2689414214)) < tol
+    assert abs(out[1, 0, 1] - 0.7310585786) < tol
+    assert np.all(out[1, 0, 2:] == 0) and np.all(out[0] == 0)
+
+
+# ---------------------------------------------------------------------------
+# Named workloads.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("epilogue", ["ln_u", "none"])
+def test_tiny_workload(epilogue):
+    inp = make_inputs("tiny")
+    assert_close(gpu_forward(inp, epilogue), ora(inp, epilogue), "f32")
+
+
+@pytest.mark.parametrize("seed", [1234, 1, 2, 3, 4])
+def test_ranking_workload_full(seed):
+    inp = make_inputs("ranking", seed=seed)
+    assert_close(gpu_forward(inp), ora(inp), "bf16")
+
+
+def test_ranking_workload_epilogue_none():
+    inp = make_inputs("ranking", seed=7)
+    assert_close(gpu_forward(inp, "none"), ora(inp, "none"), "bf16")
+
+
+@pytest.mark.parametrize("name", ["ranking", "longtail", "windowed"])
+def test_fp32_shadow(name):
+    """Same geometry in fp32 separates logic errors from bf16 rounding."""
+    inp = make_inputs(name, num_seqs={"ranking": 16, "longtail": 6, "windowed": 1}[name],
+                      dtype="f32")
+    assert_close(gpu_forward(inp), ora(inp), "f32")
+
+
+@pytest.mark.parametrize("seed", [1234, 2])
+def test_longtail_reduced_full(seed):
+    inp = make_inputs("longtail", seed=seed, num_seqs=8)
+    assert_close(gpu_forward(inp), ora(inp), "bf16")
+
+
+def _sample_rows(inp, n, seed):
+    rng = np.random.default_rng(seed)
+    N = inp.total_tokens
+    rows = set(rng.choice(N, size=min(n, N), replace=False).tolist())
+    # plus the last rows of the longest sequence and the first/last token of each sequence
+    b = int(np.argmax(inp.lengths))
+    rows |= set(range(int(inp.offsets[b + 1]) - 64, int(inp.offsets[b + 1])))
+    rows |= set(int(x) for x in inp.offsets[:-1]) | set(int(x) - 1 for x in inp.offsets[1:])
+    return np.array(sorted(r for r in rows if 0 <= r < N))
+
+
+@pytest.mark.parametrize("name", ["longtail", "windowed"])
+def test_full_size_sampled_rows(name):
+    inp = make_inputs(name)
+    rows = _sample_rows(inp, 400, 5)
+    assert_close(gpu_forward(inp), ora(inp, rows=rows), "bf16", rows=rows)
+
+
+def test_windowed_one_sequence_full():
+    inp = make_inputs("windowed", num_seqs=1)
+    assert_close(gpu_forward(inp), ora(inp), "bf16")
+
+
+def test_layer_strided_views():
+    """Views with token stride 2048 (slices of a fused U|V|Q|K projection)."""
+    inp = make_inputs("layer", num_seqs=6)
+    a = gpu_forward(inp, ld=2048)
+    b = gpu_forward(inp)
+    assert np.array_equal(a, b)
+    assert_close(a, ora(inp), "bf16")
+
+
+# ---------------------------------------------------------------------------
+# Edge cases: ragged tails around the 32-key / 128-row tiles, empty
+# sequences, all-candidate sequences, prefix longer than the history, windows
+# at the tile size, large absolute timestamps and spans beyond 2^30 s.
+# ---------------------------------------------------------------------------
+EDGE_LENGTHS = [0, 1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 257, 300]
+
+
+@pytest.mark.parametrize("dtype,d", [("f32", 8), ("bf16", 128), ("bf16", 64), ("f32", 64)])
+@pytest.mark.parametrize("rules", ["causal", "targets", "prefix", "window", "all"])
+def test_edges(dtype, d, rules):
+    rng = np.random.default_rng(hash(rules) % 1000)
+    lengths = list(EDGE_LENGTHS)
+    B = len(lengths)
+    nt = None
+    c = W = 0
+    if rules in ("targets", "all"):
+        nt = [int(x) for x in rng.integers(0, 40, size=B)]
+        nt[1] = 1; nt[3] = 31; nt[7] = 64       # all-candidate / exact-tile cases
+    if rules in ("prefix", "all"):
+        c = 6 if rules == "all" else 40
+    if rules in ("window", "all"):
+        W = {"window": 32, "all": 33}[rules]
+    inp = make_custom(lengths, num_heads=2, d_qk=d, d_v=d, dtype=dtype, seed=11,
+                      num_targets=nt, contextual_len=c, max_attn_len=W, pos_len=300,
+                      pos_std=0.3, time_len=64, time_std=0.3, alpha=1.0 / math.sqrt(d),
+                      t0=(1 << 33) + 17)
+    for ep in ("ln_u", "none"):
+        assert_close(gpu_forward(inp, ep), ora(inp, ep), dtype)
+
+
+@pytest.mark.parametrize("W", [1, 31, 32, 33, 127, 128, 129])
+def test_window_sizes(W):
+    inp = make_custom([700, 129], num_heads=1, d_qk=128, d_v=128, dtype="bf16", seed=W,
+                      num_targets=[25, 3], max_attn_len=W, pos_len=1024, time_len=64,
+                      alpha=1 / math.sqrt(128))
+    assert_close(gpu_forward(inp), ora(inp), "bf16")
+
+
+def test_no_bias_tables():
+    inp = make_custom([5, 300, 77], num_heads=3, d_qk=128, d_v=128, dtype="bf16", seed=2,
+                      alpha=0.2)
+    assert_close(gpu_forward(inp), ora(inp), "bf16")
+
+
+@pytest.mark.parametrize("dtype,d", [("f32", 8), ("bf16", 128)])
+def test_wide_timestamp_span_uses_exact_buckets(dtype, d):
+    """Gaps of ~2^27 s push spans past 2^30, the 64-bit bucket path."""
+    inp = make_custom([150, 40], num_heads=2, d_qk=d, d_v=d, dtype=dtype, seed=9,
+                      time_len=64, time_std=0.5, pos_len=64, alpha=0.3)
+    rng = np.random.default_rng(1)
+    gaps = rng.integers(0, 1 << 28, size=inp.total_tokens)
+    ts = []
+    for b in range(inp.num_seqs):
+        s, e = int(inp.offsets[b]), int(inp.offsets[b + 1])
+        g = gaps[s:e].copy(); g[0] = 0
+        ts.append((1 << 40) + np.cumsum(g))
+    inp.timestamps = np.concatenate(ts).astype(np.int64)
+    assert_close(gpu_forward(inp), ora(inp), dtype)
+
+
+def test_unsorted_timestamps():
+    inp = make_custom([90, 33], num_heads=1, d_qk=8, d_v=8, dtype="f32", seed=4, time_len=40,
+                      time_std=0.5, alpha=0.5)
+    rng = np.random.default_rng(3)
+    inp.timestamps = (1_600_000_000 + rng.integers(0, 10**7, size=inp.total_tokens)).astype(np.int64)
+    assert_close(gpu_forward(inp), ora(inp), "f32")
+
+
+# ---------------------------------------------------------------------------
+# Zero pattern: with V = one-hot rows and no epilogue, out[i, j] = a_ij, so the
+# zeros of the output are exactly the masked pairs and the padding columns.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("rules", [dict(), dict(num_targets=[9, 0, 30]), dict(contextual_len=5),
+                                   dict(max_attn_len=17, num_targets=[4, 7, 2])])
+def test_zero_pattern_exact(rules):
+    lengths = [100, 57, 128]
+    inp = make_custom(lengths, num_heads=2, d_qk=128, d_v=128, dtype="bf16", seed=3,
+                      pos_len=256, pos_std=0.2, time_len=64, alpha=0.05, **rules)
+    inp.v[:] = 0
+    for b in range(inp.num_seqs):
+        s = int(inp.offsets[b])
+        for j in range(int(inp.lengths[b])):
+            inp.v[s + j, :, j] = 1.0
+    out = gpu_forward(inp, "none")
+    ref = ora(inp, "none")
+    T = rules.get("num_targets")
+    for b in range(inp.num_seqs):
+        s, L = int(inp.offsets[b]), int(inp.lengths[b])
+        t = 0 if T is None else T[b]
+        mask = np.array([[oracle.allowed(L, t, rules.get("contextual_len", 0),
+                                         rules.get("max_attn_len", 0), i, j)
+                          for j in range(L)] for i in range(L)])
+        for h in range(2):
+            blk = out[s:s + L, h, :L]
+            assert np.array_equal(blk != 0, mask)
+            assert np.all(out[s:s + L, h, L:] == 0)
+            assert np.array_equal(ref[s:s + L, h, :L] != 0, mask)
+    assert_close(out, ref, "bf16")
+
+
+# ---------------------------------------------------------------------------
+# Every row written exactly once, nothing outside `out` touched.
+# ---------------------------------------------------------------------------
+def test_write_coverage_and_guards():
+    inp = make_inputs("ranking", num_seqs=20)
+    dev = to_device(inp, DEV)
+    N, H, dv = inp.total_tokens, inp.num_heads, inp.d_v
+    big = torch.full((N + 64, H, dv), float("nan"), dtype=torch.bfloat16, device=DEV)
+    big[:32] = 7.0
+    big[32 + N:] = -3.0
+    out = big[32:32 + N]
+    jagged_attn_fwd(dev["q"], dev["k"], dev["v"], dev["u"], dev["offsets"], out=out,
+                    **call_kwargs(inp, dev))
+    torch.cuda.synchronize()
+    assert torch.all(big[:32] == 7.0) and torch.all(big[32 + N:] == -3.0)
+    assert not torch.isnan(out.float()).any()
+    assert_close(out.float().cpu().numpy().astype(np.float64), ora(inp), "bf16")
+
+
+def test_determinism_bitwise():
+    inp = make_inputs("longtail", num_seqs=10)
+    a = gpu_forward(inp)
+    b = gpu_forward(inp)
+    assert np.array_equal(a, b)
+
+
+def test_plan_reuse_across_runs():
+    inp = make_inputs("ranking", num_seqs=24)
+    dev = to_device(inp, DEV)
+    call = JaggedAttnCall(dev["q"], dev["k"], dev["v"], dev["u"], dev["offsets"],
+                          **call_kwargs(inp, dev))
+    call.plan()
+    o1 = call.run().float().cpu().numpy().astype(np.float64)
+    inp2 = JaggedInputs(**{f: getattr(inp, f) for f in inp.__dataclass_fields__})
+    inp2.q = inp.q[::-1].copy()
+    call.q.copy_(to_device(inp2, DEV)["q"])
+    o2 = call.run().float().cpu().numpy().astype(np.float64)
+    torch.cuda.synchronize()
+    assert_close(o1, ora(inp), "bf16")
+    assert_close(o2, ora(inp2), "bf16")
+
+
+# ---------------------------------------------------------------------------
+# Information flow on the device, bitwise ("Do not copy softmax masking
+# mechanically": change future inputs, earlier outputs must not move).
+# ---------------------------------------------------------------------------
+def _perturb(inp, rows, seed=5):
+    rng = np.random.default_rng(seed)
+    out = JaggedInputs(**{f: getattr(inp, f) for f in inp.__dataclass_fields__})
+    for name in ("q", "k", "v", "u"):
+        arr = getattr(inp, name).copy()
+        vals = rng.standard_normal(arr[rows].shape).astype(np.float32)
+        if inp.dtype == "bf16":
+            from jagged_hstu_attention_attn_amd.inputs import bf16_round
+            vals = bf16_round(vals)
+        arr[rows] = vals
+        setattr(out, name, arr)
+    if inp.timestamps is not None:
+        ts = inp.timestamps.copy()
+        ts[rows] += rng.integers(1, 10**6, size=len(rows))
+        out.timestamps = ts
+    return out
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 8)])
+def test_future_perturbation_bitwise(dtype, d):
+    inp = make_custom([300, 90], num_heads=2, d_qk=d, d_v=d, dtype=dtype, seed=21,
+                      num_targets=[12, 5], pos_len=512, time_len=64, alpha=0.2)
+    a = gpu_forward(inp)
+    for p in (1, 31, 32, 100, 200, 287):
+        b = gpu_forward(_perturb(inp, list(range(p, 300))))
+        assert np.array_equal(a[:p], b[:p]), p
+        assert np.array_equal(a[300:], b[300:])          # other sequence untouched
+    # candidates do not see each other
+    for cand in (288, 295, 299):
+        b = gpu_forward(_perturb(inp, [cand]))
+        others = [r for r in range(288, 300) if r != cand]
+        assert np.array_equal(a[:288], b[:288]) and np.array_equal(a[others], b[others])
+
+
+def test_window_reach_bitwise():
+    W = 40
+    inp = make_custom([400], num_heads=1, d_qk=128, d_v=128, dtype="bf16", seed=8,
+                      max_attn_len=W, pos_len=512, alpha=0.1)
+    a = gpu_forward(inp)
+    p = 150
+    b = gpu_forward(_perturb(inp, [p]))
+    changed = [i for i in range(400) if not np.array_equal(a[i], b[i])]
+    assert changed == list(range(p, p + W + 1))
+
+
+def test_batch_independence_bitwise():
+    inp = make_custom([40, 300, 0, 129], num_heads=2, d_qk=128, d_v=128, dtype="bf16", seed=2,
+                      num_targets=[3, 20, 0, 9], pos_len=512, time_len=64, alpha=0.1)
+    full = gpu_forward(inp)
+    for b in range(inp.num_seqs):
+        s, e = int(inp.offsets[b]), int(inp.offsets[b + 1])
+        if e == s:
+            continue
+        one = JaggedInputs(
+            workload="one", dtype="bf16", offsets=np.array([0, e - s], np.int32),
+            num_targets=inp.num_targets[b:b + 1], timestamps=inp.timestamps[s:e],
+            q=inp.q[s:e], k=inp.k[s:e], v=inp.v[s:e], u=inp.u[s:e], pos_table=inp.pos_table,
+            time_table=inp.time_table, contextual_len=0, max_attn_len=0, alpha=inp.alpha,
+            n_scale=inp.n_scale)
+        assert np.array_equal(gpu_forward(one), full[s:e])
+
+
+def test_overflowing_masked_scores_fp32():
+    inp = make_custom([60], num_heads=1, d_qk=8, d_v=8, dtype="f32", seed=8, alpha=1.0)
+    a = gpu_forward(inp)
+    bad = JaggedInputs(**{f: getattr(inp, f) for f in inp.__dataclass_fields__})
+    bad.k = inp.k.copy(); bad.q = inp.q.copy()
+    bad.k[40:] = 3e38
+    bad.q[40:] = -3e38
+    b = gpu_forward(bad)
+    assert np.all(np.isfinite(b[:40]))
+    assert np.array_equal(a[:40], b[:40])
+
+
+def test_empty_batch():
+    inp = make_custom([0, 0], num_heads=1, d_qk=8, d_v=8)
+    dev = to_device(inp, DEV)
+    out = jagged_attn_fwd(dev["q"], dev["k"], dev["v"], dev["u"], dev["offsets"],
+                          **call_kwargs(inp, dev))
+    torch.cuda.synchronize()
+    assert out.shape == (0, 1, 8)
