@@ -37,6 +37,8 @@ def _ptr(t: Optional[torch.Tensor]):
 def _token_stride(t: torch.Tensor, name: str) -> int:
     if t.dim() != 3:
         raise ValueError(f"{name} must be [tokens, heads, dim], got shape {tuple(t.shape)}")
+    if t.numel() == 0:
+        return int(t.shape[1] * t.shape[2])
     if t.stride(2) != 1 or t.stride(1) != t.shape[2]:
         raise ValueError(f"{name}: the head and feature dimensions must be contiguous")
     return int(t.stride(0)) if t.shape[0] > 1 else int(t.shape[1] * t.shape[2])

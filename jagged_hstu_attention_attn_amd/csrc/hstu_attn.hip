@@ -199,7 +199,7 @@ int hstu_jagged_attn_run(const hstu_attn_desc* desc, const void* q, const void* 
   a.time_len = desc->time_table_len;
   a.epilogue = desc->epilogue;
   a.alpha = alpha;
-  a.inv_n_scale = (float)(1.0 / (double)n_scale);
+  a.out_scale = (float)(0.69314718055994530942 / (double)n_scale);
   a.ln_eps = desc->ln_eps;
   const hstu::PlanLayout pl = hstu::plan_layout(desc->num_seqs, desc->total_tokens);
   const int64_t grid = pl.pairs_max * desc->num_heads;

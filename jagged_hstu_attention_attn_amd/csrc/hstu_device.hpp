@@ -21,11 +21,12 @@
 namespace hstu {
 
 constexpr int kBM = 128;        // query rows per work item: 4 waves x 32 rows
-constexpr int kBN = 32;         // keys per staged K/V tile
+constexpr int kBN = 64;         // keys per staged K/V tile (two 32-key MFMA blocks)
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kPosMax = 8192;   // longest supported position table
 constexpr int kPlanThreads = 1024;
+constexpr int kPlanLdsSeqs = 8192;  // batches up to this many sequences plan from LDS
 constexpr int kKeyBuckets = 64; // work-estimate buckets of the scheduler
 constexpr int kEmptyLo = 0x40000000;  // lower bound of an empty key interval
 
@@ -147,7 +148,7 @@ struct AttnArgs {
   int32_t time_len;
   int32_t epilogue;   // 0 = LayerNorm * U, 1 = none
   float alpha;
-  float inv_n_scale;
+  float out_scale;    // ln(2) / n_scale: SiLU values are formed in log2 units
   float ln_eps;
 };
 

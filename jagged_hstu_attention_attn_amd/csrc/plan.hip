@@ -14,8 +14,11 @@
 // sort is a stable counting sort, so pairs of equal bucket keep the natural
 // (sequence, tile) order and the result is deterministic.
 //
-// One workgroup of 1024 threads; everything stays on the device, so the
-// caller's stream never synchronises with the host.
+// One workgroup of 1024 threads.  Sequence lengths, candidate counts and the
+// first pair of every sequence live in LDS for batches of up to kPlanLdsSeqs
+// sequences (larger batches use the workspace copy), so the per-pair work is
+// LDS-only after one coalesced pass over offsets.  Everything stays on the
+// device: the caller's stream never synchronises with the host.
 #include "hstu_device.hpp"
 
 namespace hstu {
@@ -38,20 +41,6 @@ __device__ inline int find_seq(const int32_t* seq_start, int B, int p) {
   return lo;
 }
 
-__device__ inline int pair_key(const PlanArgs& a, int b, int qt) {
-  const int s0 = a.offsets[b];
-  const int L = a.offsets[b + 1] - s0;
-  const int nt = a.num_targets ? a.num_targets[b] : 0;
-  const SeqGeom g = seq_geom(L, nt, a.contextual_len, a.max_attn_len);
-  const int i0 = qt * kBM;
-  const int i1 = min(i0 + kBM, L);
-  int jlo, jhi;
-  tile_key_range(g, i0, i1, jlo, jhi);
-  const int cost = jhi / kBN - jlo / kBN + 1 + 2;
-  // descending work = ascending key
-  return kKeyBuckets - 1 - work_bucket(cost);
-}
-
 // Inclusive sum over the 1024 threads of the block; `ws` holds 16 ints.
 __device__ inline int block_inclusive_sum(int x, int* ws) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -68,23 +57,56 @@ __device__ inline int block_inclusive_sum(int x, int* ws) {
   return x + pre;
 }
 
+struct SeqView {
+  const int32_t* start;   // [B+1] first pair of each sequence (LDS or workspace)
+  const int32_t* len;     // [B] lengths (LDS), or nullptr: read offsets
+  const int32_t* nt;      // [B] candidate counts (LDS), or nullptr: read num_targets
+};
+
+__device__ inline int pair_key(const PlanArgs& a, const SeqView& sv, int b, int qt) {
+  const int L = sv.len ? sv.len[b] : a.offsets[b + 1] - a.offsets[b];
+  const int nt = sv.nt ? sv.nt[b] : (a.num_targets ? a.num_targets[b] : 0);
+  const SeqGeom g = seq_geom(L, nt, a.contextual_len, a.max_attn_len);
+  const int i0 = qt * kBM;
+  const int i1 = min(i0 + kBM, L);
+  int jlo, jhi;
+  tile_key_range(g, i0, i1, jlo, jhi);
+  const int cost = jhi / kBN - jlo / kBN + 1 + 2;
+  return kKeyBuckets - 1 - work_bucket(cost);   // descending work = ascending key
+}
+
 __global__ __launch_bounds__(kPlanThreads) void hstu_plan_kernel(PlanArgs a) {
   __shared__ int s_wsum[kPlanThreads / 64];
   __shared__ int s_total;
   __shared__ int s_hist[kKeyBuckets];
   __shared__ int s_base[kKeyBuckets];
   __shared__ int s_wcnt[kPlanThreads / 64][kKeyBuckets];
+  __shared__ int s_start[kPlanLdsSeqs + 1];
+  __shared__ int s_len[kPlanLdsSeqs];
+  __shared__ int s_nt[kPlanLdsSeqs];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int B = a.num_seqs;
+  const bool in_lds = B <= kPlanLdsSeqs;
+  int32_t* start = in_lds ? s_start : a.seq_start;
 
-  // 1. First pair of every sequence: exclusive scan of ceil(L_b / BM).
+  // 1. Lengths, candidate counts, and the first pair of every sequence
+  //    (exclusive scan of ceil(L_b / BM)).
   int carry = 0;
   for (int b0 = 0; b0 < B; b0 += kPlanThreads) {
     const int b = b0 + tid;
-    const int nq = b < B ? max(0, a.offsets[b + 1] - a.offsets[b] + kBM - 1) / kBM : 0;
+    int L = 0, nt = 0;
+    if (b < B) {
+      L = max(0, a.offsets[b + 1] - a.offsets[b]);
+      nt = a.num_targets ? a.num_targets[b] : 0;
+      if (in_lds) {
+        s_len[b] = L;
+        s_nt[b] = nt;
+      }
+    }
+    const int nq = (L + kBM - 1) / kBM;
     const int inc = block_inclusive_sum(nq, s_wsum);
-    if (b < B) a.seq_start[b] = carry + inc - nq;
+    if (b < B) start[b] = carry + inc - nq;
     if (tid == kPlanThreads - 1) s_total = inc;
     __syncthreads();
     carry += s_total;
@@ -94,18 +116,19 @@ __global__ __launch_bounds__(kPlanThreads) void hstu_plan_kernel(PlanArgs a) {
   // break the documented contract).
   const int Q = min(carry, a.pairs_max);
   if (tid == 0) {
-    a.seq_start[B] = Q;
+    start[B] = Q;
     *a.count = Q;
   }
   if (tid < kKeyBuckets) s_hist[tid] = 0;
+  for (int w = tid; w < (kPlanThreads / 64) * kKeyBuckets; w += kPlanThreads)
+    (&s_wcnt[0][0])[w] = 0;
   __syncthreads();
+  const SeqView sv{start, in_lds ? s_len : nullptr, in_lds ? s_nt : nullptr};
 
-  // 2. Work key of every pair, and the histogram of keys.
+  // 2. Histogram of work keys.
   for (int p = tid; p < Q; p += kPlanThreads) {
-    const int b = find_seq(a.seq_start, B, p);
-    const int key = pair_key(a, b, p - a.seq_start[b]);
-    a.keys[p] = key;
-    atomicAdd(&s_hist[key], 1);
+    const int b = find_seq(sv.start, B, p);
+    atomicAdd(&s_hist[pair_key(a, sv, b, p - sv.start[b])], 1);
   }
   __syncthreads();
 
@@ -120,8 +143,6 @@ __global__ __launch_bounds__(kPlanThreads) void hstu_plan_kernel(PlanArgs a) {
     }
     s_base[lane] = x - own;
   }
-  for (int w = tid; w < (kPlanThreads / 64) * kKeyBuckets; w += kPlanThreads)
-    (&s_wcnt[0][0])[w] = 0;
   __syncthreads();
 
   // 4. Stable scatter, 1024 pairs at a time: rank inside the wave from a
@@ -130,7 +151,12 @@ __global__ __launch_bounds__(kPlanThreads) void hstu_plan_kernel(PlanArgs a) {
   for (int p0 = 0; p0 < Q; p0 += kPlanThreads) {
     const int p = p0 + tid;
     const bool valid = p < Q;
-    const int key = valid ? a.keys[p] : 0;
+    int b = 0, qt = 0, key = 0;
+    if (valid) {
+      b = find_seq(sv.start, B, p);
+      qt = p - sv.start[b];
+      key = pair_key(a, sv, b, qt);
+    }
     uint64_t same = __ballot(valid);
 #pragma unroll
     for (int bit = 0; bit < 6; ++bit) {
@@ -150,10 +176,7 @@ __global__ __launch_bounds__(kPlanThreads) void hstu_plan_kernel(PlanArgs a) {
       s_base[tid] = run;
     }
     __syncthreads();
-    if (valid) {
-      const int b = find_seq(a.seq_start, B, p);
-      a.pairs[s_wcnt[wave][key] + rank] = make_int2(b, p - a.seq_start[b]);
-    }
+    if (valid) a.pairs[s_wcnt[wave][key] + rank] = make_int2(b, qt);
     __syncthreads();
     for (int w = tid; w < (kPlanThreads / 64) * kKeyBuckets; w += kPlanThreads)
       (&s_wcnt[0][0])[w] = 0;
