@@ -166,6 +166,14 @@ int64_t hstu_jagged_attn_valid_pairs(int32_t num_seqs, const int32_t* offsets_ho
                                      const int32_t* num_targets_host,
                                      int32_t contextual_len, int32_t max_attn_len);
 
+/*
+ * Launch configuration of the attention kernel for `desc` on the current
+ * device: the number of persistent workgroups (CUs x resident workgroups per
+ * CU, capped by the work-item bound).  Returns -1 and sets the message on a
+ * bad desc or a HIP error.
+ */
+int hstu_jagged_attn_grid(const hstu_attn_desc* desc);
+
 /* Thread-local message for the last failing call of this thread ("" if none). */
 const char* hstu_last_error(void);
 

@@ -30,6 +30,7 @@ EXPORTS = (
     "hstu_jagged_attn_plan",
     "hstu_jagged_attn_run",
     "hstu_jagged_attn_valid_pairs",
+    "hstu_jagged_attn_grid",
     "hstu_last_error",
 )
 
@@ -88,6 +89,8 @@ def load() -> ctypes.CDLL:
     lib.hstu_jagged_attn_plan.argtypes = [D, P, P, i32, i32, P, sz, P]
     lib.hstu_jagged_attn_valid_pairs.restype = i64
     lib.hstu_jagged_attn_valid_pairs.argtypes = [i32, P, P, i32, i32]
+    lib.hstu_jagged_attn_grid.restype = ctypes.c_int
+    lib.hstu_jagged_attn_grid.argtypes = [D]
     lib.hstu_last_error.restype = ctypes.c_char_p
     lib.hstu_last_error.argtypes = []
     _lib = lib

@@ -65,10 +65,9 @@ int check_desc(const hstu_attn_desc* d) {
       return fail(HSTU_ERR_INVALID_ARG, "%s * element size must be a multiple of 16 bytes",
                   x.name);
   }
-  const hstu::PlanLayout pl = hstu::plan_layout(d->num_seqs, d->total_tokens);
-  if (pl.pairs_max * H > 0x7fffffffLL)
-    return fail(HSTU_ERR_UNSUPPORTED, "too many work items (%lld)",
-                (long long)(pl.pairs_max * H));
+  const hstu::PlanLayout pl = hstu::plan_layout(d->num_seqs, d->total_tokens, H);
+  if (pl.items_max > 0x7fffffffLL || (int64_t)d->num_seqs * H > 0x7fffffffLL)
+    return fail(HSTU_ERR_UNSUPPORTED, "too many work items (%lld)", (long long)pl.items_max);
   return HSTU_OK;
 }
 
@@ -77,7 +76,7 @@ int check_plan_args(const hstu_attn_desc* d, const int32_t* offsets, int32_t con
   if (d->num_seqs > 0 && !offsets) return fail(HSTU_ERR_INVALID_ARG, "offsets is NULL");
   if (contextual_len < 0) return fail(HSTU_ERR_INVALID_ARG, "contextual_len < 0");
   if (max_attn_len < 0) return fail(HSTU_ERR_INVALID_ARG, "max_attn_len < 0");
-  const size_t need = hstu::plan_layout(d->num_seqs, d->total_tokens).total;
+  const size_t need = hstu::plan_layout(d->num_seqs, d->total_tokens, d->num_heads).total;
   if (!ws) return fail(HSTU_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", need);
   if (ws_bytes < need)
     return fail(HSTU_ERR_WORKSPACE, "workspace has %zu bytes, need %zu", ws_bytes, need);
@@ -109,23 +108,59 @@ int check_run_args(const hstu_attn_desc* d, const void* q, const void* k, const 
   return HSTU_OK;
 }
 
-hstu::PlanArgs make_plan_args(const hstu_attn_desc* d, const int32_t* offsets,
-                              const int32_t* num_targets, int32_t contextual_len,
-                              int32_t max_attn_len, void* ws) {
-  const hstu::PlanLayout pl = hstu::plan_layout(d->num_seqs, d->total_tokens);
+// Workgroups of the persistent attention launch: CUs x resident workgroups
+// per CU (cached per device and kernel variant), capped so that no queue gets
+// more workgroups than the work list could hold, and at least one per queue.
+// <= 0 on a HIP error.
+int persistent_grid(const hstu_attn_desc* d) {
+  struct Entry {
+    int dev, dtype, d_qk, d_v, pos_len, has_time, grid;
+  };
+  static thread_local Entry cache[16];
+  static thread_local int cache_n = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  const int has_time = d->time_table_len > 0;
+  int g = -1;
+  for (int i = 0; i < cache_n; ++i) {
+    const Entry& e = cache[i];
+    if (e.dev == dev && e.dtype == d->dtype && e.d_qk == d->d_qk && e.d_v == d->d_v &&
+        e.pos_len == d->pos_table_len && e.has_time == has_time) {
+      g = e.grid;
+      break;
+    }
+  }
+  if (g < 0) {
+    g = hstu::attn_grid(d->dtype, d->d_qk, d->d_v, d->pos_table_len, d->time_table_len);
+    if (g <= 0) return g;
+    cache[cache_n % 16] = Entry{dev, d->dtype, d->d_qk, d->d_v, d->pos_table_len, has_time, g};
+    ++cache_n;
+  }
+  const int64_t items = hstu::plan_layout(d->num_seqs, d->total_tokens, d->num_heads).items_max;
+  const int64_t cap = (int64_t)hstu::kQueues * (items > 0 ? items : 1);
+  const int64_t n = cap < g ? cap : g;
+  return (int)(n < hstu::kQueues ? hstu::kQueues : n);
+}
+
+struct PlanPtrs {
+  int32_t* queue_count;
+  int32_t* queue_start;
+  int4* items;
+  int32_t* gscan;
+  int32_t* seq;
+};
+
+PlanPtrs plan_ptrs(const hstu_attn_desc* d, void* ws) {
+  const hstu::PlanLayout pl = hstu::plan_layout(d->num_seqs, d->total_tokens, d->num_heads);
   char* base = static_cast<char*>(ws);
-  hstu::PlanArgs a;
-  a.offsets = offsets;
-  a.num_targets = num_targets;
-  a.num_seqs = d->num_seqs;
-  a.contextual_len = contextual_len;
-  a.max_attn_len = max_attn_len;
-  a.pairs_max = (int32_t)pl.pairs_max;
-  a.count = reinterpret_cast<int32_t*>(base + pl.count_off);
-  a.pairs = reinterpret_cast<int2*>(base + pl.pairs_off);
-  a.keys = reinterpret_cast<int32_t*>(base + pl.keys_off);
-  a.seq_start = reinterpret_cast<int32_t*>(base + pl.seqstart_off);
-  return a;
+  int32_t* hdr = reinterpret_cast<int32_t*>(base + pl.hdr_off);
+  PlanPtrs p;
+  p.queue_count = hdr;
+  p.queue_start = hdr + hstu::kQueues;
+  p.items = reinterpret_cast<int4*>(base + pl.items_off);
+  p.gscan = reinterpret_cast<int32_t*>(base + pl.gscan_off);
+  p.seq = reinterpret_cast<int32_t*>(base + pl.seq_off);
+  return p;
 }
 
 }  // namespace
@@ -138,7 +173,7 @@ int hstu_jagged_attn_supported(int32_t dtype, int32_t d_qk, int32_t d_v) {
 
 size_t hstu_jagged_attn_workspace_bytes(const hstu_attn_desc* desc) {
   if (check_desc(desc) != HSTU_OK) return 0;
-  return hstu::plan_layout(desc->num_seqs, desc->total_tokens).total;
+  return hstu::plan_layout(desc->num_seqs, desc->total_tokens, desc->num_heads).total;
 }
 
 int hstu_jagged_attn_plan(const hstu_attn_desc* desc, const int32_t* offsets,
@@ -150,8 +185,22 @@ int hstu_jagged_attn_plan(const hstu_attn_desc* desc, const int32_t* offsets,
   rc = check_plan_args(desc, offsets, contextual_len, max_attn_len, workspace, workspace_bytes);
   if (rc != HSTU_OK) return rc;
   if (desc->num_seqs == 0 || desc->total_tokens == 0) return HSTU_OK;
-  const hstu::PlanArgs a =
-      make_plan_args(desc, offsets, num_targets, contextual_len, max_attn_len, workspace);
+  const hstu::PlanLayout pl = hstu::plan_layout(desc->num_seqs, desc->total_tokens, desc->num_heads);
+  const PlanPtrs pp = plan_ptrs(desc, workspace);
+  hstu::PlanArgs a;
+  a.offsets = offsets;
+  a.num_targets = num_targets;
+  a.num_seqs = desc->num_seqs;
+  a.num_heads = desc->num_heads;
+  a.contextual_len = contextual_len;
+  a.max_attn_len = max_attn_len;
+  a.items_max = (int32_t)pl.items_max;
+  a.slots = (int32_t)pl.slots;
+  a.queue_count = pp.queue_count;
+  a.queue_start = pp.queue_start;
+  a.items = pp.items;
+  a.gscan = pp.gscan;
+  a.seq_scratch = pp.seq;
   const hipError_t e = hstu::launch_plan(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess)
     return fail(HSTU_ERR_HIP, "scheduler launch failed: %s", hipGetErrorString(e));
@@ -172,8 +221,9 @@ int hstu_jagged_attn_run(const hstu_attn_desc* desc, const void* q, const void* 
   rc = check_run_args(desc, q, k, v, u, timestamps, alpha, n_scale, pos_table, time_table, out);
   if (rc != HSTU_OK) return rc;
 
-  const hstu::PlanArgs pa =
-      make_plan_args(desc, offsets, num_targets, contextual_len, max_attn_len, workspace);
+  const int n_wg = persistent_grid(desc);
+  if (n_wg <= 0) return fail(HSTU_ERR_HIP, "cannot query the device for the launch size");
+  const PlanPtrs pp = plan_ptrs(desc, workspace);
   hstu::AttnArgs a;
   a.q = q;
   a.k = k;
@@ -185,8 +235,9 @@ int hstu_jagged_attn_run(const hstu_attn_desc* desc, const void* q, const void* 
   a.num_targets = num_targets;
   a.pos_table = pos_table;
   a.time_table = time_table;
-  a.count = pa.count;
-  a.pairs = pa.pairs;
+  a.queue_count = pp.queue_count;
+  a.queue_start = pp.queue_start;
+  a.items = pp.items;
   a.ld_q = desc->ld_q;
   a.ld_k = desc->ld_k;
   a.ld_v = desc->ld_v;
@@ -201,9 +252,7 @@ int hstu_jagged_attn_run(const hstu_attn_desc* desc, const void* q, const void* 
   a.alpha = alpha;
   a.out_scale = (float)(0.69314718055994530942 / (double)n_scale);
   a.ln_eps = desc->ln_eps;
-  const hstu::PlanLayout pl = hstu::plan_layout(desc->num_seqs, desc->total_tokens);
-  const int64_t grid = pl.pairs_max * desc->num_heads;
-  const hipError_t e = hstu::launch_attn(a, desc->dtype, desc->d_qk, desc->d_v, grid,
+  const hipError_t e = hstu::launch_attn(a, desc->dtype, desc->d_qk, desc->d_v, n_wg,
                                          static_cast<hipStream_t>(stream));
   if (e != hipSuccess)
     return fail(HSTU_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
@@ -251,6 +300,13 @@ int64_t hstu_jagged_attn_valid_pairs(int32_t num_seqs, const int32_t* offsets_ho
     }
   }
   return n;
+}
+
+int hstu_jagged_attn_grid(const hstu_attn_desc* desc) {
+  if (check_desc(desc) != HSTU_OK) return -1;
+  const int g = persistent_grid(desc);
+  if (g <= 0) return fail(-1, "cannot query the device for the launch size");
+  return g;
 }
 
 const char* hstu_last_error(void) { return g_err; }

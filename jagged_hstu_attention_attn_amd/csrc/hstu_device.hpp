@@ -21,12 +21,12 @@
 namespace hstu {
 
 constexpr int kBM = 128;        // query rows per work item: 4 waves x 32 rows
-constexpr int kBN = 64;         // keys per staged K/V tile (two 32-key MFMA blocks)
+constexpr int kBN = 32;         // keys per staged K/V tile (one 32-key MFMA block)
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kPosMax = 8192;   // longest supported position table
 constexpr int kPlanThreads = 1024;
-constexpr int kPlanLdsSeqs = 8192;  // batches up to this many sequences plan from LDS
+constexpr int kPlanLdsSeqs = 4096;  // batches up to this many sequences plan from LDS
 constexpr int kKeyBuckets = 64; // work-estimate buckets of the scheduler
 constexpr int kEmptyLo = 0x40000000;  // lower bound of an empty key interval
 
@@ -91,26 +91,34 @@ __host__ __device__ inline void tile_key_range(const SeqGeom& g, int i0, int i1,
 }
 
 // Work-list layout inside the caller's workspace (byte offsets, 256-aligned).
+// The scheduler fills one queue of items per XCD (the MI355X has 8 XCDs, each
+// with its own L2); items are (sequence, head, query tile).
+constexpr int kQueues = 8;
+
 struct PlanLayout {
-  size_t count_off;      // int32: number of (sequence, query-tile) pairs
-  size_t pairs_off;      // int2[pairs_max]: sorted (b, qt)
-  size_t keys_off;       // int32[pairs_max]: bucketed work estimate per pair
-  size_t seqstart_off;   // int32[B+1]: first pair of each sequence
+  size_t hdr_off;      // int32 queue_count[8], queue_start[8]
+  size_t items_off;    // int4[items_max]: (seq start, L, n_h, qt*H + h), queue by queue
+  size_t gscan_off;    // int32[8*S + 1]: item offsets of the (queue, slot) groups
+  size_t seq_off;      // int32[6*B]: per-sequence scratch of the scheduler (large batches)
   size_t total;
-  int64_t pairs_max;
+  int64_t pairs_max;   // bound on sum_b ceil(L_b / BM)
+  int64_t items_max;   // pairs_max * H
+  int64_t slots;       // S = ceil(B*H / 8)
 };
 
 __host__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-__host__ inline PlanLayout plan_layout(int64_t num_seqs, int64_t total_tokens) {
+__host__ inline PlanLayout plan_layout(int64_t num_seqs, int64_t total_tokens, int64_t heads) {
   PlanLayout p;
   // sum_b ceil(L_b / BM) <= (N + B*(BM-1)) / BM
   p.pairs_max = (total_tokens + num_seqs * (kBM - 1)) / kBM;
-  p.count_off = 0;
-  p.pairs_off = 256;
-  p.keys_off = align256(p.pairs_off + sizeof(int2) * (size_t)(p.pairs_max > 0 ? p.pairs_max : 1));
-  p.seqstart_off = align256(p.keys_off + sizeof(int32_t) * (size_t)(p.pairs_max > 0 ? p.pairs_max : 1));
-  p.total = align256(p.seqstart_off + sizeof(int32_t) * (size_t)(num_seqs + 1));
+  p.items_max = p.pairs_max * heads;
+  p.slots = (num_seqs * heads + kQueues - 1) / kQueues;
+  p.hdr_off = 0;
+  p.items_off = 256;
+  p.gscan_off = align256(p.items_off + sizeof(int4) * (size_t)(p.items_max > 0 ? p.items_max : 1));
+  p.seq_off = align256(p.gscan_off + sizeof(int32_t) * (size_t)(kQueues * p.slots + 1));
+  p.total = align256(p.seq_off + sizeof(int32_t) * (size_t)(6 * num_seqs + 6));
   return p;
 }
 
@@ -118,13 +126,16 @@ struct PlanArgs {
   const int32_t* offsets;
   const int32_t* num_targets;
   int32_t num_seqs;
+  int32_t num_heads;
   int32_t contextual_len;
   int32_t max_attn_len;
-  int32_t pairs_max;     // capacity of pairs/keys (bound from num_seqs, total_tokens)
-  int32_t* count;
-  int2* pairs;
-  int32_t* keys;
-  int32_t* seq_start;
+  int32_t items_max;     // capacity of `items`
+  int32_t slots;         // S
+  int32_t* queue_count;  // [8]
+  int32_t* queue_start;  // [8]
+  int4* items;
+  int32_t* gscan;
+  int32_t* seq_scratch;  // [6*B], used when B > kPlanLdsSeqs
 };
 
 struct AttnArgs {
@@ -138,8 +149,9 @@ struct AttnArgs {
   const int32_t* num_targets;
   const float* pos_table;
   const float* time_table;
-  const int32_t* count;
-  const int2* pairs;
+  const int32_t* queue_count;
+  const int32_t* queue_start;
+  const int4* items;
   int64_t ld_q, ld_k, ld_v, ld_u, ld_out;
   int32_t num_heads;
   int32_t contextual_len;
@@ -154,8 +166,11 @@ struct AttnArgs {
 
 // Launchers (defined in the .hip files).
 hipError_t launch_plan(const PlanArgs& a, hipStream_t stream);
-hipError_t launch_attn(const AttnArgs& a, int dtype, int d_qk, int d_v, int64_t grid,
+hipError_t launch_attn(const AttnArgs& a, int dtype, int d_qk, int d_v, int n_wg,
                        hipStream_t stream);
+// Workgroups of the persistent attention launch for this shape on the current
+// device (CUs x resident workgroups per CU), or a negative value on error.
+int attn_grid(int dtype, int d_qk, int d_v, int pos_len, int time_len);
 bool attn_supported(int dtype, int d_qk, int d_v);
 
 }  // namespace hstu
