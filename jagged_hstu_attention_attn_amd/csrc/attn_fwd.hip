@@ -5,36 +5,46 @@
 // plan.hip); the workgroups of one queue share it cyclically.  Wave w owns
 // query rows i0+32w .. i0+32w+31 of an item; lane (l % 32) owns one query row
 // and the lane half (l / 32) splits the contraction dimension, which is the
-// operand layout of the 32x32 MFMA.
+// operand layout of the 32x32 MFMA (v_mfma_f32_32x32x16_bf16; 32x32x2 for
+// fp32).  Two workgroups share a CU, so each SIMD runs two waves of different
+// workgroups whose matrix-core and vector-ALU phases overlap.
 //
-// Keys are staged 32 at a time in three LDS buffers: the stage two ahead is
-// copied from HBM straight into LDS (global_load_lds_dwordx4, no registers)
-// while the current one is computed, one barrier per stage.  Each stage:
-//   S^T = K Q^T                 32x32, bf16 MFMA with fp32 accumulation
-//   x   = alpha*S + pos[|i-j|] + time[floor(log2(1+|t_i-t_j|))]
+// Keys are staged 32 at a time in four LDS buffers, copied from HBM straight
+// into LDS (global_load_lds, no registers) three stages ahead, one barrier per
+// stage.  Per 32-key block and wave:
+//   S^T = K Q^T + C              32x32, bf16 MFMA with fp32 accumulation; the
+//                                accumulator starts at the position bias
+//   x   = alpha*S + time[bucket(|t_i - t_j|)]     (one FMA per score)
 //   a   = allowed(i,j) ? SiLU(x) : 0     a select, never a multiply by a mask
-//   O^T += V^T A^T              the SiLU values go from the first MFMA's
-//                               accumulator registers straight into the
-//                               second MFMA's B operand
+//   O^T += V^T A^T               the SiLU values go from the first MFMA's
+//                                accumulator registers straight into the
+//                                second MFMA's B operand
 // and the epilogue scales by 1/n_scale, takes LayerNorm over d_v per (token,
 // head) (the two lane halves of a row combine with one cross-lane exchange),
-// multiplies by U and stores the rows that belong to the sequence.
+// multiplies by U and stores the rows that belong to the sequence.  All LDS
+// reads of a block are issued before its arithmetic, so their latency hides
+// behind the score MFMAs and the SiLU.
 //
 // Computing S^T (keys on the MFMA's M side, queries on N) puts every query
 // row's scores in one lane, so the accumulators already have the B-operand
 // layout of the aggregation MFMA (the order of the contraction index inside
 // one MFMA is free as long as both operands agree).  V stays row-major in LDS
-// and its transposed operand comes from ds_read_b64_tr_b16.
+// and its transposed operand comes from ds_read_b64_tr_b16.  The 16-byte
+// chunks of each staged K and V row are XOR-swizzled so that the rows one LDS
+// cycle reads fall on distinct banks.
 //
-// Scores are kept in log2 units: the bias tables are staged pre-multiplied by
-// log2(e), x2 = alpha*log2(e)*S + bias2, and SiLU(x)*log2(e) = x2 / (1 +
-// 2^-x2); the factor ln(2) is folded into the epilogue's 1/n_scale.
+// Scores are kept in log2 units.  The position bias of a 128 x 32 block takes
+// only 159 distinct values, one per i - j.  Each stage gathers them from the
+// table into LDS (every lane of the copy reads the entry of its own clamped
+// |i - j|), rescales them once, and every score's accumulator starts from its
+// value: C = log2(e) pos / am and x2 = am S + log2(e) time = log2(e) x, with
+// am = alpha log2(e) (am = 1 and Q = 0 when alpha is 0).  SiLU(x) log2(e) =
+// x2 / (1 + 2^-x2); the factor ln(2) is folded into the epilogue's 1/n_scale.
 //
-// Work per 32x32 block is decided per wave from uniform bounds: blocks no
-// row of the wave may see are skipped, blocks every row sees fully skip the
-// mask, blocks wholly below the diagonal read the position bias at constant
-// offsets, and blocks whose (row, key) time gaps all fall in one bucket add
-// one constant instead of looking the time bias up per element.
+// Work per block is decided per wave from uniform bounds: blocks no row of
+// the wave may see are skipped, blocks every row sees fully skip the mask, and
+// blocks whose (row, key) time gaps all fall in one bucket add one constant
+// instead of looking the time bias up per score.
 //
 // Method: pointwise SiLU aggregation with position/time bias, zeroing after
 // the nonlinearity, Norm then U gating ("HSTU tensor by tensor: SiLU
@@ -51,47 +61,61 @@ namespace hstu {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short shortx4 __attribute__((ext_vector_type(4)));
-typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int64_t kT32Range = int64_t(1) << 30;  // |t - base| below this: 32-bit path
+constexpr int kStages = 4;                       // LDS buffers of the key/value pipeline
+constexpr int kRows = kBM / kWaves;              // query rows per wave
+constexpr int kDiag = kBM + kBN - 1;             // distinct i - j of a 128 x 32 block
+constexpr int kDiagCopies = (kDiag + 63) / 64;   // 4-byte LDS copies of 64 lanes
+static_assert(kRows == 32, "one 32x32 MFMA tile of query rows per wave");
+static_assert(kBN == 32, "a key block is one 32-key score tile");
 
 template <typename T, int DQK, int DV>
-struct Tile {
+struct Cfg {
   static constexpr bool kBf16 = std::is_same<T, __bf16>::value;
-  static constexpr int kEpc = 16 / (int)sizeof(T);             // elements per 16 B
-  static constexpr int kStep = kBf16 ? 16 : 2;                  // MFMA contraction depth
-  static constexpr int kKChunks = DQK / kEpc;                   // 16-byte chunks per K row
-  static constexpr int kVChunks = DV / kEpc;                    // 16-byte chunks per V row
-  // XOR swizzles of the 16-byte chunks of a bf16 row (fp32 rows are plain).
-  // K: the 16 lanes of a ds_read_b128 read one logical chunk of 16 consecutive
-  // rows; the swizzle spreads them over all banks.  V: the transposed reads of
-  // one lane half (4 rows x 4 chunks) hit every bank once.
+  static constexpr int kEs = (int)sizeof(T);
+  static constexpr int kStep = kBf16 ? 16 : 2;          // MFMA contraction depth
+  static constexpr int kKRow = DQK * kEs;               // staged row bytes
+  static constexpr int kVRow = DV * kEs;
+  static constexpr int kKCh = kKRow / 16;               // 16-byte chunks per row
+  static constexpr int kVCh = kVRow / 16;
+  static constexpr int kNK = kBN * kKCh / 64;           // 64-lane copies per K stage
+  static constexpr int kNV = kBN * kVCh / 64;
+  static constexpr int kNKC = DQK / kStep;              // MFMA steps of the scores
+  static constexpr int kNDB = (DV + 31) / 32;           // 32-wide d_v blocks of O^T
+  static_assert(kKRow % 16 == 0 && kVRow % 16 == 0, "rows are whole 16-byte chunks");
+  static_assert(kBN * kKCh % 64 == 0 && kBN * kVCh % 64 == 0, "stage is whole copies");
+  static_assert(DQK % kStep == 0 && DV % 4 == 0 && (!kBf16 || DV % 32 == 0), "shape");
+  // XOR swizzles of a row's 16-byte chunks (always below the number of
+  // chunks, so they permute the row).  K: one read touches the same logical
+  // chunk of 16 consecutive rows per LDS cycle.  V (bf16): a transposed read
+  // of one lane half touches 4 rows x 4 chunks; (fp32): two rows 4 apart.
   __device__ static int kswz(int row) {
-    if constexpr (!kBf16) return 0;
-    return kKChunks >= 16 ? (row & 15) : ((row >> 1) & (kKChunks - 1));
+    return kKCh >= 16 ? (row & 15) : (kKCh >= 2 ? ((row >> 1) & (kKCh - 1)) : 0);
   }
   __device__ static int vswz(int row) {
-    if constexpr (!kBf16) return 0;
-    return kVChunks >= 16 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
+    if constexpr (kBf16) return kVCh >= 16 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
+    return kVCh >= 16 ? 8 * ((row >> 2) & 1) : 0;
   }
 };
 
-constexpr int kStages = 3;   // LDS buffers of the key/value pipeline
-
 // One stage of the pipeline.  Each stage buffer is its own __shared__ object,
-// so the compiler can tell that an LDS copy into one stage does not alias
-// reads of another (and does not make those reads wait for the copy).
+// so the compiler can tell that the accesses of different stages never alias.
 template <typename T, int DQK, int DV>
 struct StageBuf {
-  T k[kBN][DQK];
-  T v[kBN][DV];
-  int64_t tj64[kBN];
-  uint32_t tj32[kBN];
-  uint32_t tjmin, tjmax;   // 32-bit key times of the stage (valid keys)
-  int tbad;                // some key needs the 64-bit time path
+  using C = Cfg<T, DQK, DV>;
+  char k[kBN * C::kKRow];        // keys: row j at byte j * kKRow, chunks swizzled
+  char v[kBN * C::kVRow];        // values
+  float diag[kDiagCopies * 64];  // position bias of i - j = i0 - j0 + 127 - f, at f
+  int64_t ts64[kBN];             // raw key timestamps
+  uint32_t ts32[kBN];            // key timestamps relative to the item's base
+  uint32_t tmin, tmax;           // range of ts32 over the valid keys
+  int tbad;                      // some key needs the 64-bit time path
+  int pad_;
 };
 
 struct TimeTables {
@@ -99,48 +123,68 @@ struct TimeTables {
   float tful[64];   // tful[b] = log2e * time[min(b, Tt - 1)]
 };
 
-typedef __attribute__((address_space(3))) void lds_void;
+// LDS byte offset of a __shared__ object's (generic) address: the LDS
+// aperture is 4 GiB aligned, so the offset is the address's low 32 bits.
+__device__ inline uint32_t lds_off(const void* p) { return (uint32_t)(uintptr_t)p; }
+// LDS pointer from an LDS byte offset.
+__device__ inline lds_shortx4* lds_ptr4(uint32_t off) { return (lds_shortx4*)(uintptr_t)off; }
 
-// LDS byte offset of a __shared__ address.
-__device__ inline uint32_t lds_off(const void* p) {
-  return (uint32_t)(uintptr_t)(const lds_void*)p;
+// A pointer that is the same in every lane, as a scalar-register value.
+__device__ inline uint64_t uni_ptr(const void* p) {
+  const uint64_t x = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
+  return ((uint64_t)hi << 32) | lo;
 }
 
-// HBM -> LDS copies (global_load_lds): lane l's bytes land at LDS offset
-// `lds` + size*l.  Issued from inline assembly on purpose: the compiler then
-// neither waits for them before unrelated LDS reads nor folds them into its
-// own vmcnt accounting; every wait on them is an explicit wait_vmem below.
-// They write no registers.  M0 is a reserved register, so clobbering it is
-// harmless; the warning about it is silenced here.
+// HBM -> LDS copies (global_load_lds): lane l reads base + voff and its bytes
+// land at LDS offset `lds` + size * l.  Issued from inline assembly on
+// purpose: the compiler then neither waits for them before unrelated LDS
+// reads nor folds them into its own vmcnt accounting; every wait on them is
+// an explicit wait_vmem below.  They write no registers.  M0 is a reserved
+// register, so clobbering it is harmless; the warning about it is silenced.
+// `base` and `lds` must be the same in every lane.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-// `lds` must be the same for every lane of the wave.
-__device__ inline void lds_copy16(const void* g, uint32_t lds) {
+__device__ inline void lds_copy16(uint64_t base, uint32_t voff, uint32_t lds) {
   const uint32_t m = __builtin_amdgcn_readfirstlane(lds);
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-               :: "s"(m), "v"(g) : "memory", "m0");
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(m), "v"(voff), "s"(base) : "memory", "m0");
 }
-__device__ inline void lds_copy4(const void* g, uint32_t lds) {
+__device__ inline void lds_copy4(uint64_t base, uint32_t voff, uint32_t lds) {
   const uint32_t m = __builtin_amdgcn_readfirstlane(lds);
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
-               :: "s"(m), "v"(g) : "memory", "m0");
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+               :: "s"(m), "v"(voff), "s"(base) : "memory", "m0");
 }
 #pragma clang diagnostic pop
 
-// s_waitcnt vmcnt(N): all but the N most recent global loads / LDS copies of
-// this wave are done (they complete in order).
+// s_waitcnt vmcnt(N): all but the N most recent global memory operations
+// (loads, stores, LDS copies) of this wave are done (they complete in order).
 template <int N>
 __device__ inline void wait_vmem() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
+// The same for a wave-uniform count below 8.
+__device__ inline void wait_vmem_n(int n) {
+  switch (n) {
+    case 0: wait_vmem<0>(); break;
+    case 1: wait_vmem<1>(); break;
+    case 2: wait_vmem<2>(); break;
+    case 3: wait_vmem<3>(); break;
+    case 4: wait_vmem<4>(); break;
+    case 5: wait_vmem<5>(); break;
+    case 6: wait_vmem<6>(); break;
+    default: wait_vmem<7>(); break;
+  }
+}
 
 // Workgroup barrier for the pipeline.  __syncthreads() carries a release
 // fence that waits for every outstanding LDS copy, which would drain the
-// copies of the stage two ahead; here the caller has already waited for the
-// copies that must have landed (vmcnt) and this waits for its own LDS writes
-// (lgkmcnt), and the empty asm statements keep the compiler from moving
-// memory accesses across the barrier.
+// copies of the stages ahead; here the caller has already waited for the
+// copies that must have landed (vmcnt) and this waits for its own LDS
+// accesses (lgkmcnt), and the empty asm statements keep the compiler from
+// moving memory accesses across the barrier.
 __device__ inline void stage_barrier() {
   __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt, expcnt untouched
   asm volatile("" ::: "memory");
@@ -148,64 +192,101 @@ __device__ inline void stage_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// LDS copies wave w issues per stage when `count` copies are spread over the
-// waves round-robin.
+// Copies wave w issues per stage when copy n goes to wave n % kWaves.
 __host__ __device__ constexpr int copies_of_wave(int count, int w) {
   return count > w ? (count - w + kWaves - 1) / kWaves : 0;
 }
+// Position-bias copy p goes to wave kWaves-1-p, the timestamp copy to the
+// wave below those.
+constexpr int kTsWave = kWaves - 1 - kDiagCopies;
+static_assert(kTsWave >= 0, "enough waves for the bias copies");
+// All LDS copies wave w issues per stage.
+template <int NK, int NV, bool POS, bool TIME>
+__host__ __device__ constexpr int stage_copies(int w) {
+  return copies_of_wave(NK, w) + copies_of_wave(NV, w) +
+         ((POS && w > kTsWave) ? 1 : 0) + ((TIME && w == kTsWave) ? 1 : 0);
+}
 
-__device__ inline uint32_t abs_diff_u32(uint32_t a, uint32_t b) { return a > b ? a - b : b - a; }
+__device__ inline int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Minimum / maximum over the 64 lanes of a wave (all lanes active), returned
+// in a scalar register.  Data-parallel-primitive (DPP) row shifts build a
+// running reduction within each 16-lane row (lane 15 ends with the row's
+// value), then row broadcasts carry rows 0..2 into lane 63: a handful of
+// register-to-register moves instead of LDS round trips.
+template <bool MAX, typename V>
+__device__ inline V wave_reduce(V x) {
+  static_assert(sizeof(V) == 4, "32-bit values");
+  auto op = [](V a, V b) { return MAX ? (a > b ? a : b) : (a < b ? a : b); };
+  auto dpp = [](V v, auto ctrl, auto rows) {
+    return __builtin_bit_cast(
+        V, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, v), __builtin_bit_cast(int, v),
+                                       decltype(ctrl)::value, decltype(rows)::value, 0xf,
+                                       false));
+  };
+  x = op(x, dpp(x, std::integral_constant<int, 0x111>{}, std::integral_constant<int, 0xf>{}));
+  x = op(x, dpp(x, std::integral_constant<int, 0x112>{}, std::integral_constant<int, 0xf>{}));
+  x = op(x, dpp(x, std::integral_constant<int, 0x114>{}, std::integral_constant<int, 0xf>{}));
+  x = op(x, dpp(x, std::integral_constant<int, 0x118>{}, std::integral_constant<int, 0xf>{}));
+  x = op(x, dpp(x, std::integral_constant<int, 0x142>{}, std::integral_constant<int, 0xa>{}));
+  x = op(x, dpp(x, std::integral_constant<int, 0x143>{}, std::integral_constant<int, 0xc>{}));
+  return __builtin_bit_cast(V, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
+}
+template <typename V>
+__device__ inline V wave_min(V v) { return wave_reduce<false>(v); }
+template <typename V>
+__device__ inline V wave_max(V v) { return wave_reduce<true>(v); }
 
 // Register r of a 32x32 accumulator (lane half hh) holds row 8(r/4) + 4hh + r%4.
 __device__ constexpr int acc_row(int r, int hh) { return 8 * (r >> 2) + 4 * hh + (r & 3); }
 
-template <typename V>
-__device__ inline V wave_min(V v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) { const V w = __shfl_xor(v, o, 64); v = w < v ? w : v; }
-  return v;
+// SiLU(x) * log2(e) = x2 / (1 + 2^-x2)
+__device__ inline float silu2(float x) {
+  return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x));
 }
-template <typename V>
-__device__ inline V wave_max(V v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) { const V w = __shfl_xor(v, o, 64); v = w > v ? w : v; }
-  return v;
-}
-__device__ inline int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 template <typename T, int DQK, int DV, bool POS, bool TIME>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void
 hstu_attn_fwd_kernel(AttnArgs a) {
-  using TL = Tile<T, DQK, DV>;
+  using C = Cfg<T, DQK, DV>;
   using SB = StageBuf<T, DQK, DV>;
-  constexpr bool BF = TL::kBf16;
-  constexpr int EPC = TL::kEpc;
-  constexpr int NKC = DQK / TL::kStep;             // MFMA steps of S^T
-  constexpr int NDB = (DV + 31) / 32;              // 32-wide d_v blocks of O^T
-  constexpr int KCPR = TL::kKChunks;               // 16-byte chunks per K row
-  constexpr int VCPR = TL::kVChunks;
-  constexpr int KRPI = 64 / KCPR;                  // K rows per wave-wide LDS copy
-  constexpr int VRPI = 64 / VCPR;
-  constexpr int KNI = kBN / KRPI;                  // LDS copies per K stage
-  constexpr int VNI = kBN / VRPI;
-  static_assert(DQK % TL::kStep == 0 && DQK % EPC == 0 && DV % EPC == 0, "shape");
-  static_assert(KCPR <= 64 && VCPR <= 64 && KRPI <= kBN && VRPI <= kBN, "stage shape");
-  static_assert(!BF || DV % 32 == 0, "bf16 needs d_v multiple of 32");
+  constexpr bool BF = C::kBf16;
+  constexpr int ES = C::kEs;
+  constexpr int NKC = C::kNKC;
+  constexpr int NDB = C::kNDB;
+  constexpr int KROW = C::kKRow, VROW = C::kVRow;
+  constexpr int KCH = C::kKCh, VCH = C::kVCh;
+  constexpr int NK = C::kNK, NV = C::kNV;
+  constexpr int SK = (NK + kWaves - 1) / kWaves;   // K copies per wave (at most)
+  constexpr int SV = (NV + kWaves - 1) / kWaves;
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  using B2 = std::integral_constant<int, 2>;
+  using B3 = std::integral_constant<int, 3>;
 
-  __shared__ __align__(16) SB st0, st1, st2;
+  __shared__ __align__(16) SB st0, st1, st2, st3;
   __shared__ TimeTables tt;
-  extern __shared__ float pos_s[];   // log2e * pos_table[0 .. n_pos)
-  auto stage = [&](auto bufc) -> SB& {
-    constexpr int b = decltype(bufc)::value;
+  auto stage = [&](auto bufc) __attribute__((always_inline)) -> SB& {
+    constexpr int b = decltype(bufc)::value % kStages;
     if constexpr (b == 0) return st0;
     else if constexpr (b == 1) return st1;
-    else return st2;
+    else if constexpr (b == 2) return st2;
+    else return st3;
   };
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  // the wave index is the same in every lane: keep it in a scalar register so
+  // that everything derived from it (rows, copy schedule, bounds) is uniform
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
   const int P = a.pos_len;
   const int H = a.num_heads;
+  const float alpha2 = a.alpha * kLog2e;
+  const bool alpha_zero = alpha2 == 0.0f;
+  const float am = alpha_zero ? 1.0f : alpha2;   // x2 = am * S + time
+  const float pscale = kLog2e / am;              // position bias in accumulator units
+  const uint32_t ldk_b = (uint32_t)(a.ld_k * ES), ldv_b = (uint32_t)(a.ld_v * ES);
+  const int my_copies = stage_copies<NK, NV, POS, TIME>(wave);
 
   if constexpr (TIME) {
     // log2(e) * time table, indexed two ways (see TimeTables)
@@ -213,7 +294,21 @@ hstu_attn_fwd_kernel(AttnArgs a) {
     if (tid < 32) tt.trev[tid] = kLog2e * a.time_table[min(31 - tid, Tt - 1)];
     if (tid < 64) tt.tful[tid] = kLog2e * a.time_table[min(tid, Tt - 1)];
   }
-  int pos_staged = 0;   // entries of pos_s already staged (uniform)
+
+  // Lane l of K copy n fills LDS chunk m = 64n + l: row m / KCH, physical
+  // chunk m % KCH, which holds the row's logical chunk (m % KCH) ^ kswz(row).
+  // Byte offsets of those chunks from the stage's first row:
+  uint32_t k_off[SK], v_off[SV];
+#pragma unroll
+  for (int s = 0; s < SK; ++s) {
+    const int m = 64 * (s * kWaves + wave) + lane, row = m / KCH;
+    k_off[s] = (uint32_t)row * ldk_b + 16u * (uint32_t)((m % KCH) ^ C::kswz(row));
+  }
+#pragma unroll
+  for (int s = 0; s < SV; ++s) {
+    const int m = 64 * (s * kWaves + wave) + lane, row = m / VCH;
+    v_off[s] = (uint32_t)row * ldv_b + 16u * (uint32_t)((m % VCH) ^ C::vswz(row));
+  }
 
   // Queue walk: workgroup k serves queue k%8 and takes its entries k/8,
   // k/8 + W, k/8 + 2W, ... where W is the number of workgroups serving that
@@ -226,227 +321,296 @@ hstu_attn_fwd_kernel(AttnArgs a) {
   const int4 it = qitems[idx];
   const int seq0 = it.x, L = it.y;
   const int qt = it.w / H, h = it.w - qt * H;
-  SeqGeom g;
-  g.L = L;
-  g.n_h = it.z;
-  g.c = clampi(a.contextual_len, 0, g.n_h);
-  g.W = a.max_attn_len;
+  SeqGeom geo;
+  geo.L = L;
+  geo.n_h = it.z;
+  geo.c = clampi(a.contextual_len, 0, geo.n_h);
+  geo.W = a.max_attn_len;
   const int i0 = qt * kBM;
   const int i1 = min(i0 + kBM, L);
   int jlo, jhi;
-  tile_key_range(g, i0, i1, jlo, jhi);
+  tile_key_range(geo, i0, i1, jlo, jhi);
   const int kt_lo = jlo / kBN, kt_hi = jhi / kBN;
 
   // ---- per-lane query row and the wave's uniform key bounds --------------
-  const int wr0 = i0 + wave * 32;
+  const int wr0 = i0 + wave * kRows;
   const int i = wr0 + l32;
   const bool row_valid = i < i1;
   const bool wave_rows = wr0 < i1;
-  const RowBounds rb = row_valid ? row_bounds(g, i) : RowBounds{kEmptyLo, 0, -1};
   // some row may see a key of [w_jmin, w_jmax]; every row sees every key of
   // [w_lomax, w_himin].
   int w_jmin, w_jmax, w_lomax, w_himin;
   {
+    const RowBounds rb = row_valid ? row_bounds(geo, i) : RowBounds{kEmptyLo, 0, -1};
     const bool nonempty = rb.lo != kEmptyLo;
     const int hi = rb.lo + rb.span;
     int jmin = nonempty ? rb.lo : (rb.self_j >= 0 ? rb.self_j : 0x7fffffff);
     int jmax = nonempty ? max(hi, rb.self_j) : rb.self_j;
     if (!row_valid) { jmin = 0x7fffffff; jmax = -1; }
-    w_jmin = uni(wave_min(jmin));
-    w_jmax = uni(wave_max(jmax));
-    w_lomax = uni(wave_max(row_valid ? rb.lo : -1));
-    w_himin = uni(wave_min(row_valid ? (nonempty ? hi : -1) : 0x7fffffff));
+    w_jmin = wave_min(jmin);
+    w_jmax = wave_max(jmax);
+    w_lomax = wave_max(row_valid ? rb.lo : -1);
+    w_himin = wave_min(row_valid ? (nonempty ? hi : -1) : 0x7fffffff);
   }
+  auto needs = [&](int kt) __attribute__((always_inline)) {
+    const int jb = kt * kBN;
+    return wave_rows && jb <= w_jmax && jb + kBN - 1 >= w_jmin;
+  };
+  auto is_full = [&](int kt) __attribute__((always_inline)) {
+    const int jb = kt * kBN;
+    return w_lomax <= jb && w_himin >= jb + kBN - 1;
+  };
 
-  // row times (set after the first stage copies are issued)
-  int64_t tbase = 0, ti64 = 0;
-  uint32_t ti32 = uint32_t(kT32Range);
-  bool w_t_ok = true;
-  uint32_t w_tmin = 0, w_tmax = 0;
-  // Q operand (B operand of S^T = K Q^T), kept in registers
-  typename std::conditional<BF, bf16x8, float>::type qf[NKC];
+  const uint64_t kseq = uni_ptr(reinterpret_cast<const char*>(a.k) +
+                                ((int64_t)seq0 * a.ld_k + (int64_t)h * DQK) * ES);
+  const uint64_t vseq = uni_ptr(reinterpret_cast<const char*>(a.v) +
+                                ((int64_t)seq0 * a.ld_v + (int64_t)h * DV) * ES);
+  const uint64_t pos_base = POS ? uni_ptr(a.pos_table) : 0;
+  const uint64_t ts_base = TIME ? uni_ptr(a.timestamps + seq0) : 0;
 
-  // ---- K/V stages: HBM -> LDS copies, 32 keys per stage --------------------
-  const char* kseq = reinterpret_cast<const char*>(a.k) +
-                     ((int64_t)seq0 * a.ld_k + (int64_t)h * DQK) * (int64_t)sizeof(T);
-  const char* vseq = reinterpret_cast<const char*>(a.v) +
-                     ((int64_t)seq0 * a.ld_v + (int64_t)h * DV) * (int64_t)sizeof(T);
-
-  // Copy key tile kt (keys, values and, with a time bias, the raw int64
-  // timestamps) into stage buffer `bufc`.  A wave-wide copy writes 64
-  // consecutive 16-byte chunks of LDS (KRPI whole rows); each lane picks the
-  // global chunk that belongs at its LDS position under the swizzle.  Rows
-  // past the end of the sequence repeat its last row (finite values whose
-  // scores are always masked and whose coefficients are therefore 0).
-  auto issue_stage = [&](auto bufc, int kt) {
+  // Copy key tile kt (keys, values, the block's position-bias values and the
+  // raw timestamps) into stage buffer `bufc`.  Rows past the end of the
+  // sequence repeat its last row (finite values whose scores are always masked
+  // and whose coefficients are therefore 0).
+  auto issue_stage = [&](auto bufc, int kt) __attribute__((always_inline)) {
     SB& sb = stage(bufc);
     const int j0 = kt * kBN;
     const bool whole = j0 + kBN <= L;
+    const uint64_t kb = kseq + (uint64_t)j0 * ldk_b, vb = vseq + (uint64_t)j0 * ldv_b;
 #pragma unroll
-    for (int s2 = 0; s2 < (KNI + kWaves - 1) / kWaves; ++s2) {
-      const int n = wave + s2 * kWaves;
-      if (n < KNI) {
-        const int row = n * KRPI + lane / KCPR;
-        const int c = (lane % KCPR) ^ TL::kswz(row);
-        const int j = whole ? j0 + row : min(j0 + row, L - 1);
-        lds_copy16(kseq + ((int64_t)j * a.ld_k + c * EPC) * (int64_t)sizeof(T),
-                   lds_off(&sb.k[n * KRPI][0]));
+    for (int s = 0; s < SK; ++s) {
+      const int n = s * kWaves + wave;   // uniform
+      if (n < NK) {
+        uint32_t off = k_off[s];
+        if (!whole) {
+          const int m = 64 * n + lane, row = m / KCH;
+          off = (uint32_t)min(row, L - 1 - j0) * ldk_b +
+                16u * (uint32_t)((m % KCH) ^ C::kswz(row));
+        }
+        lds_copy16(kb, off, lds_off(sb.k) + 1024u * (uint32_t)n);
       }
     }
 #pragma unroll
-    for (int s2 = 0; s2 < (VNI + kWaves - 1) / kWaves; ++s2) {
-      const int n = wave + s2 * kWaves;
-      if (n < VNI) {
-        const int row = n * VRPI + lane / VCPR;
-        const int c = (lane % VCPR) ^ TL::vswz(row);
-        const int j = whole ? j0 + row : min(j0 + row, L - 1);
-        lds_copy16(vseq + ((int64_t)j * a.ld_v + c * EPC) * (int64_t)sizeof(T),
-                   lds_off(&sb.v[n * VRPI][0]));
+    for (int s = 0; s < SV; ++s) {
+      const int n = s * kWaves + wave;
+      if (n < NV) {
+        uint32_t off = v_off[s];
+        if (!whole) {
+          const int m = 64 * n + lane, row = m / VCH;
+          off = (uint32_t)min(row, L - 1 - j0) * ldv_b +
+                16u * (uint32_t)((m % VCH) ^ C::vswz(row));
+        }
+        lds_copy16(vb, off, lds_off(sb.v) + 1024u * (uint32_t)n);
+      }
+    }
+    if constexpr (POS) {
+      if (wave > kTsWave) {
+        const int p = kWaves - 1 - wave;
+        const int d = i0 - j0 + (kBM - 1) - (64 * p + lane);
+        const int ix = min(d < 0 ? -d : d, P - 1);
+        lds_copy4(pos_base, 4u * (uint32_t)ix, lds_off(sb.diag) + 256u * (uint32_t)p);
       }
     }
     if constexpr (TIME) {
-      if (wave == 0) {   // 64 lanes x 4 bytes = the 32 int64 timestamps
+      if (wave == kTsWave) {
         const int j = min(j0 + (lane >> 1), L - 1);
-        lds_copy4(reinterpret_cast<const int32_t*>(a.timestamps + seq0 + j) + (lane & 1),
-                  lds_off(&sb.tj64[0]));
+        lds_copy4(ts_base, 8u * (uint32_t)j + 4u * (uint32_t)(lane & 1), lds_off(sb.ts64));
       }
     }
   };
 
-  // Key times of a landed stage (wave 0, lanes 0..31): 32-bit offsets, their
-  // range over the valid keys, and whether any key needs the 64-bit path.
-  auto finish_stage = [&](auto bufc, int kt) {
+  // row times (loaded in the prologue)
+  int64_t tbase = 0;
+  uint32_t ti32 = uint32_t(kT32Range);
+  bool w_t_ok = true;
+  uint32_t w_tmin = 0, w_tmax = 0;
+
+  // Once this wave's own copies of stage kt have landed: rescale the
+  // position-bias values it gathered and, in the wave that copied the
+  // timestamps, form the 32-bit key times, their range over the valid keys
+  // and whether any key needs the 64-bit path.
+  auto finish_stage = [&](auto bufc, int kt) __attribute__((always_inline)) {
     SB& sb = stage(bufc);
+    if constexpr (POS) {
+      if (wave > kTsWave) {
+        const int e = 64 * (kWaves - 1 - wave) + lane;
+        if (e < kDiag) sb.diag[e] *= pscale;
+      }
+    }
     if constexpr (TIME) {
-      if (tid < kBN) {
-        const int64_t tj = sb.tj64[tid];
+      if (wave == kTsWave) {   // lanes 0..31: one key each
+        int kl = lane & (kBN - 1);
+        asm volatile("" : "+v"(kl));   // addresses from here, not kept live across the loop
+        const int64_t tj = sb.ts64[kl];
         const int64_t rel = tj - tbase;
         const bool ok = rel > -kT32Range && rel < kT32Range;
         const uint32_t t32 = ok ? uint32_t(rel + kT32Range) : 0u;
-        const bool key_valid = kt * kBN + tid < L;
-        sb.tj32[tid] = t32;
-        const uint64_t bad = __ballot(!ok);
-        uint32_t mn = key_valid ? t32 : 0xffffffffu, mx = key_valid ? t32 : 0u;
-#pragma unroll
-        for (int o = 16; o > 0; o >>= 1) {
-          const uint32_t a2 = __shfl_xor(mn, o, 64), b2 = __shfl_xor(mx, o, 64);
-          mn = a2 < mn ? a2 : mn;
-          mx = b2 > mx ? b2 : mx;
-        }
-        if (tid == 0) {
-          sb.tjmin = mn;
-          sb.tjmax = mx;
-          sb.tbad = bad != 0;
+        const bool key_valid = lane < kBN && kt * kBN + kl < L;
+        if (lane < kBN) sb.ts32[kl] = t32;
+        const bool bad = __ballot(!ok) != 0;
+        const uint32_t mn = wave_min(key_valid ? t32 : 0xffffffffu);
+        const uint32_t mx = wave_max(key_valid ? t32 : 0u);
+        if (lane == 0) {
+          sb.tmin = mn;
+          sb.tmax = mx;
+          sb.tbad = bad;
         }
       }
     }
   };
 
+  // Q operand (B operand of S^T = K Q^T), kept in registers
+  typename std::conditional<BF, bf16x8, float>::type qf[NKC];
   floatx16 acc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
 
-  const float alpha2 = a.alpha * kLog2e;
+  // lane -> index into a stage's diag: f = i0 - j0 + 127 - (i - j)
+  //   = 127 - 32 wave - l32 + 4hh + 8(r/4) + r%4   (ascending in r%4)
+  const int dbase = (kBM - 1) - kRows * wave - l32 + 4 * hh;
 
-  // One 32-key stage from LDS buffer `buf` (compile-time) for this wave's rows.
-  auto compute_stage = [&](auto bufc, int kt) {
-    SB& sb = stage(bufc);
+  // Whether every (row, key) time gap of block kt for this wave falls in one
+  // bucket; then `tb` is that bucket's (log2e-scaled) bias.
+  auto time_const = [&](SB& sb, float& tb) __attribute__((always_inline)) -> bool {
+    if (!w_t_ok || uni(sb.tbad) != 0) return false;
+    const uint32_t kmin = (uint32_t)uni((int)sb.tmin), kmax = (uint32_t)uni((int)sb.tmax);
+    uint32_t dmin = 0;
+    if (w_tmin > kmax) dmin = w_tmin - kmax;
+    if (kmin > w_tmax) dmin = kmin - w_tmax;
+    const uint32_t dmax = max(w_tmax > kmin ? w_tmax - kmin : 0u,
+                              kmax > w_tmin ? kmax - w_tmin : 0u);
+    const int z0 = uni(__builtin_clz(dmin + 1u)), z1 = uni(__builtin_clz(dmax + 1u));
+    if (z0 != z1) return false;
+    tb = __builtin_bit_cast(float, uni(__builtin_bit_cast(int, tt.trev[z0])));   // scalar
+    return true;
+  };
+
+  // One 32-key block from stage buffer `sb`: scores, bias, SiLU, mask,
+  // aggregation.  Every LDS read of the block is issued first.
+  auto block = [&](SB& sb, int kt) __attribute__((always_inline)) {
     const int jb = kt * kBN;
-    // uniform block class for this wave
-    if (!wave_rows || jb > w_jmax || jb + 31 < w_jmin) return;
-    const bool full = w_lomax <= jb && w_himin >= jb + 31;
-
-    // S^T[j][i] for the 32 keys of this block and the wave's 32 rows.
+    // ---- LDS reads: score start (position bias) and K operands ----
     floatx16 s;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] = 0.0f;
-#pragma unroll
-    for (int c = 0; c < NKC; ++c) {
+    for (int r = 0; r < 16; ++r) {
+      if constexpr (POS) s[r] = sb.diag[dbase + 8 * (r >> 2) + (r & 3)];
+      else s[r] = 0.0f;
+    }
+    // K operand of MFMA step c (logical chunk 2c + hh of key row l32)
+    auto kread = [&](int c) __attribute__((always_inline)) {
       if constexpr (BF) {
-        const bf16x8 kop =
-            *reinterpret_cast<const bf16x8*>(&sb.k[l32][((2 * c + hh) ^ TL::kswz(l32)) * 8]);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qf[c], s, 0, 0, 0);
+        return *reinterpret_cast<const bf16x8*>(sb.k + l32 * KROW +
+                                                16 * ((2 * c + hh) ^ C::kswz(l32)));
       } else {
-        const float kop = sb.k[l32][c * 2 + hh];
-        s = __builtin_amdgcn_mfma_f32_32x32x2f32(kop, qf[c], s, 0, 0, 0);
+        const int d = 2 * c + hh;
+        return *reinterpret_cast<const float*>(sb.k + l32 * KROW +
+                                               16 * ((d >> 2) ^ C::kswz(l32)) + 4 * (d & 3));
       }
+    };
+    // two halves of the contraction: the second half's reads are issued once
+    // the first half's MFMAs have taken their operands
+    constexpr int NH = (NKC + 1) / 2;
+    typename std::conditional<BF, bf16x8, float>::type kop[NH];
+#pragma unroll
+    for (int c = 0; c < NH; ++c) kop[c] = kread(c);
+    __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of the arithmetic
+#pragma unroll
+    for (int c = 0; c < NH; ++c) {
+      if constexpr (BF) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[c], qf[c], s, 0, 0, 0);
+      else s = __builtin_amdgcn_mfma_f32_32x32x2f32(kop[c], qf[c], s, 0, 0, 0);
+    }
+#pragma unroll
+    for (int c = NH; c < NKC; ++c) kop[c - NH] = kread(c);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int c = NH; c < NKC; ++c) {
+      if constexpr (BF)
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[c - NH], qf[c], s, 0, 0, 0);
+      else s = __builtin_amdgcn_mfma_f32_32x32x2f32(kop[c - NH], qf[c], s, 0, 0, 0);
     }
 
-    // x2 = alpha*log2e*S + log2e*pos
-    float x[16];
-    if constexpr (POS) {
-      // constant offsets when every (i, j) of the block has 0 <= i-j < P-1
-      if (wr0 - (jb + 31) >= 0 && wr0 + 31 - jb < P - 1) {
-        const float* pb = pos_s + (i - jb - 4 * hh - 27);   // >= 0 since wr0 >= jb + 31
+    // V^T operands (bf16): ds_read_b64_tr_b16 -- in each 16-lane group, lane
+    // 4e+q loads 4 values of key row e at columns 4q..4q+3 of the group's 16
+    // columns; lane c of the group receives column c of the 4 rows.  MFMA ins
+    // (keys 16 ins ..) takes rows 16ins + 4hh + {0..3} and 16ins + 8 + 4hh +
+    // {0..3}, matching the accumulator rows of the SiLU values it multiplies.
+    bf16x8 vop[BF ? 2 * NDB : 1];
+    if constexpr (BF) {
+      const int gl = lane & 15, grp = lane >> 4;
+      const int er = gl >> 2;
+      const int rlane = 4 * hh + er;
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          x[r] = fmaf(s[r], alpha2, pb[27 - (8 * (r >> 2) + (r & 3))]);
+      for (int db = 0; db < NDB; ++db) {
+        const int col = 32 * db + 16 * (grp & 1) + 4 * (gl & 3);
+        const uint32_t base = lds_off(sb.v) + (uint32_t)(rlane * VROW) +
+                              16u * (uint32_t)((col >> 3) ^ C::vswz(rlane)) + 2u * (col & 7);
+#pragma unroll
+        for (int ins = 0; ins < 2; ++ins) {
+          const shortx4 lo =
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_ptr4(base + (16 * ins) * VROW));
+          const shortx4 hi =
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_ptr4(base + (16 * ins + 8) * VROW));
+          vop[2 * db + ins] = __builtin_bit_cast(
+              bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);   // V reads land during the SiLU
+
+
+    // ---- x2 = am * S + log2e * time ----
+    float x[16];
+    if constexpr (TIME) {
+      float tb = 0.0f;
+      if (time_const(sb, tb)) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x[r] = fmaf(s[r], am, tb);
+      } else if (w_t_ok && uni(sb.tbad) == 0) {
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const uint4 t4 = *reinterpret_cast<const uint4*>(&sb.ts32[8 * gq + 4 * hh]);
+          const uint32_t tv[4] = {t4.x, t4.y, t4.z, t4.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t d1 = (ti32 > tv[e] ? ti32 - tv[e] : tv[e] - ti32) + 1u;
+            x[4 * gq + e] = fmaf(s[4 * gq + e], am, tt.trev[__builtin_clz(d1)]);
+          }
+        }
       } else {
+        // times too far apart for 32 bits (rare): full 64-bit differences,
+        // with the row time read again
+        const int64_t t_i = row_valid ? a.timestamps[seq0 + i] : tbase;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int j = jb + acc_row(r, hh);
-          x[r] = fmaf(s[r], alpha2, pos_s[min(max(i - j, j - i), P - 1)]);
+          const int64_t tj = sb.ts64[acc_row(r, hh)];
+          const uint64_t dt = t_i >= tj ? uint64_t(t_i) - uint64_t(tj)
+                                        : uint64_t(tj) - uint64_t(t_i);
+          x[r] = fmaf(s[r], am, tt.tful[63 - __builtin_clzll(dt + 1u)]);
         }
       }
     } else {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) x[r] = s[r] * alpha2;
+      for (int r = 0; r < 16; ++r) x[r] = s[r] * am;
     }
 
-    // + log2e*time bias
-    if constexpr (TIME) {
-      if (!sb.tbad && w_t_ok) {
-        const uint32_t kmin = sb.tjmin, kmax = sb.tjmax;
-        // range of |t_i - t_j| over the block's valid rows and keys
-        uint32_t dmin = 0;
-        if (w_tmin > kmax) dmin = w_tmin - kmax;
-        if (kmin > w_tmax) dmin = kmin - w_tmax;
-        const uint32_t dmax = max(w_tmax > kmin ? w_tmax - kmin : 0u,
-                                  kmax > w_tmin ? kmax - w_tmin : 0u);
-        const int z0 = __builtin_clz(dmin + 1u), z1 = __builtin_clz(dmax + 1u);
-        if (z0 == z1) {
-          const float tb = tt.trev[z0];
-#pragma unroll
-          for (int r = 0; r < 16; ++r) x[r] += tb;
-        } else {
-#pragma unroll
-          for (int gq = 0; gq < 4; ++gq) {
-            const uint4 t4 =
-                *reinterpret_cast<const uint4*>(&sb.tj32[8 * gq + 4 * hh]);
-            const uint32_t tv[4] = {t4.x, t4.y, t4.z, t4.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              x[4 * gq + e] += tt.trev[__builtin_clz(abs_diff_u32(ti32, tv[e]) + 1u)];
-          }
-        }
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t tj = sb.tj64[acc_row(r, hh)];
-          const uint64_t dt = ti64 >= tj ? uint64_t(ti64) - uint64_t(tj)
-                                         : uint64_t(tj) - uint64_t(ti64);
-          x[r] += tt.tful[63 - __builtin_clzll(dt + 1u)];
-        }
-      }
-    }
-
-    // SiLU(x) * log2(e) = x2 / (1 + 2^-x2)
+    // ---- SiLU, then zero the illegal pairs ----
     float av[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
-      av[r] = x[r] * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x[r]));
-    if (!full) {
+    for (int r = 0; r < 16; ++r) av[r] = silu2(x[r]);
+    if (!is_full(kt)) {
+      const RowBounds rb = row_valid ? row_bounds(geo, i) : RowBounds{kEmptyLo, 0, -1};
+      const int jl = jb + 4 * hh - rb.lo, js = jb + 4 * hh - rb.self_j;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int j = jb + acc_row(r, hh);
-        const bool ok = (uint32_t)(j - rb.lo) <= (uint32_t)rb.span || j == rb.self_j;
+        const int kk = 8 * (r >> 2) + (r & 3);
+        const bool ok = (uint32_t)(jl + kk) <= (uint32_t)rb.span || js + kk == 0;
         av[r] = ok ? av[r] : 0.0f;
       }
     }
 
-    // O^T[d][i] += sum_j V[j][d] * A[i][j]
+    // ---- O^T[d][i] += sum_j V[j][d] * A[i][j] ----
     if constexpr (BF) {
       bf16x8 pa[2];
 #pragma unroll
@@ -454,97 +618,42 @@ hstu_attn_fwd_kernel(AttnArgs a) {
         pa[0][e] = (__bf16)av[e];
         pa[1][e] = (__bf16)av[8 + e];
       }
-      // ds_read_b64_tr_b16: in each 16-lane group, lane 4e+q loads 4 values of
-      // key row e at columns 4q..4q+3 of the group's 16 columns; lane c of the
-      // group receives column c of the 4 rows.
-      const int gl = lane & 15, grp = lane >> 4;
-      const int er = gl >> 2, q4 = gl & 3;
-      const char* vb = reinterpret_cast<const char*>(&sb.v[0][0]);
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const int col = 32 * db + 16 * (grp & 1) + 4 * q4;   // element column
+      for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int ins = 0; ins < 2; ++ins) {
-          shortx4 part[2];
-#pragma unroll
-          for (int half = 0; half < 2; ++half) {
-            const int row = 16 * ins + 8 * half + 4 * hh + er;
-            const int pch = (col >> 3) ^ TL::vswz(row);
-            const int off = row * (DV * 2) + pch * 16 + (col & 7) * 2;
-            part[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_shortx4*)(vb + off));
-          }
-          const shortx4 lo = part[0], hi = part[1];
-          const bf16x8 vop = __builtin_bit_cast(
-              bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pa[ins], acc[db], 0, 0, 0);
-        }
-      }
+        for (int ins = 0; ins < 2; ++ins)
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[2 * db + ins], pa[ins], acc[db],
+                                                           0, 0, 0);
     } else {
+      // 32x32x2: contraction slot hh <-> key acc_row(r, hh) for step r
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
         const int d = 32 * db + l32;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float vop = d < DV ? sb.v[acc_row(r, hh)][d] : 0.0f;
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vop, av[r], acc[db], 0, 0, 0);
+          const int row = acc_row(r, hh);
+          const float vv = d < DV ? *reinterpret_cast<const float*>(
+                                        sb.v + row * VROW + 16 * ((d >> 2) ^ C::vswz(row)) +
+                                        4 * (d & 3))
+                                  : 0.0f;
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv, av[r], acc[db], 0, 0, 0);
         }
       }
     }
   };
 
-  // Three-buffer pipeline, unrolled by three so that buffer indices are
-  // compile-time constants: stage kt is computed from buffer B while stage
-  // kt+1 (already copied) lands in buffer B+1 and stage kt+2 is copied into
-  // buffer B+2.  Before the barrier each wave waits for its own copies of
-  // stage kt+1 only -- its copies of stage kt+2 (the most recent) stay in flight.
-  auto wait_next = [&](bool ahead) {
-    constexpr int c0 = copies_of_wave(KNI, 0) + copies_of_wave(VNI, 0) + (TIME ? 1 : 0);
-    constexpr int c1 = copies_of_wave(KNI, 1) + copies_of_wave(VNI, 1);
-    constexpr int c2 = copies_of_wave(KNI, 2) + copies_of_wave(VNI, 2);
-    constexpr int c3 = copies_of_wave(KNI, 3) + copies_of_wave(VNI, 3);
-    if (!ahead) { wait_vmem<0>(); return; }
-    if (wave == 0) wait_vmem<c0>();
-    else if (wave == 1) wait_vmem<c1>();
-    else if (wave == 2) wait_vmem<c2>();
-    else wait_vmem<c3>();
-  };
-  auto step = [&](auto bufc, int kt) {
-    constexpr int buf = decltype(bufc)::value;
-    using NB1 = std::integral_constant<int, (buf + 1) % kStages>;
-    using NB2 = std::integral_constant<int, (buf + 2) % kStages>;
-    const bool more1 = kt + 1 <= kt_hi, more2 = kt + 2 <= kt_hi;
-    if (more2) issue_stage(NB2{}, kt + 2);
-    compute_stage(bufc, kt);
-    if (more1) {
-      wait_next(more2);
-      finish_stage(NB1{}, kt + 1);
-      stage_barrier();
-    }
-  };
-
-  // Item prologue.  The first two stage copies go out first; the loads the
-  // compiler tracks itself (row times, position table, Q) come after them, so
-  // its own waits for those never hold back copies issued later.
-  if constexpr (TIME) tbase = a.timestamps[seq0 + i0];   // finish_stage needs it
-  issue_stage(std::integral_constant<int, 0>{}, kt_lo);
-  if (kt_lo + 1 <= kt_hi) issue_stage(std::integral_constant<int, 1>{}, kt_lo + 1);
-
+  // ---- item prologue -------------------------------------------------------
+  // The first two stages go out first; then the loads the compiler tracks
+  // itself (row times, Q), whose completion it waits for right here (the
+  // empty asm statements make the registers plain values afterwards, so no
+  // wait on them is placed in the stage loop, where it would also drain the
+  // copies ahead); then the third stage.
+  issue_stage(B0{}, kt_lo);
+  if (kt_lo + 1 <= kt_hi) issue_stage(B1{}, kt_lo + 1);
+  int64_t ti64 = 0;   // this lane's row time (prologue only)
   if constexpr (TIME) {
+    tbase = a.timestamps[seq0 + i0];
     ti64 = row_valid ? a.timestamps[seq0 + i] : tbase;
-    const int64_t rel = ti64 - tbase;
-    const bool ok = rel > -kT32Range && rel < kT32Range;
-    ti32 = ok ? uint32_t(rel + kT32Range) : 0u;
-    w_t_ok = __all(ok);
-    w_tmin = (uint32_t)uni((int)wave_min(row_valid ? ti32 : 0xffffffffu));
-    w_tmax = (uint32_t)uni((int)wave_max(row_valid ? ti32 : 0u));
-  }
-  // position table into LDS (log2 units), grown as items need it
-  if constexpr (POS) {
-    const int maxrel = max(i0 + kBM - 1 - kt_lo * kBN, kt_hi * kBN + kBN - 1 - i0);
-    const int n_pos = min(P, maxrel + 1);
-    for (int x = pos_staged + tid; x < n_pos; x += kThreads) pos_s[x] = kLog2e * a.pos_table[x];
-    pos_staged = max(pos_staged, n_pos);
   }
   {
     const T* qrow = reinterpret_cast<const T*>(a.q) +
@@ -553,28 +662,54 @@ hstu_attn_fwd_kernel(AttnArgs a) {
     for (int c = 0; c < NKC; ++c) {
       if constexpr (BF) {
         bf16x8 z = {};
-        qf[c] = row_valid ? *reinterpret_cast<const bf16x8*>(qrow + c * 16 + hh * 8) : z;
+        qf[c] = (row_valid && !alpha_zero)
+                    ? *reinterpret_cast<const bf16x8*>(qrow + c * 16 + hh * 8) : z;
       } else {
-        qf[c] = row_valid ? qrow[c * 2 + hh] : 0.0f;
+        qf[c] = (row_valid && !alpha_zero) ? qrow[c * 2 + hh] : 0.0f;
       }
     }
   }
-  // The compiler waits for the Q loads here (in the prologue, where every
-  // copy is in flight anyway); afterwards the empty asm makes the registers
-  // plain values, so no wait on them is placed inside the stage loop, where it
-  // would also drain the copies of the stage two ahead.
+  wait_vmem<0>();
 #pragma unroll
   for (int c = 0; c < NKC; ++c) asm volatile("" : "+v"(qf[c]));
-  wait_next(kt_lo + 1 <= kt_hi);
-  finish_stage(std::integral_constant<int, 0>{}, kt_lo);
-  stage_barrier();   // also publishes the bias tables
+  if constexpr (TIME) {
+    asm volatile("" : "+v"(ti64));
+    const int64_t rel = ti64 - tbase;
+    const bool ok = rel > -kT32Range && rel < kT32Range;
+    ti32 = ok ? uint32_t(rel + kT32Range) : 0u;
+    w_t_ok = __all(ok);
+    w_tmin = wave_min(row_valid ? ti32 : 0xffffffffu);
+    w_tmax = wave_max(row_valid ? ti32 : 0u);
+  }
+  if (kt_lo + 2 <= kt_hi) issue_stage(B2{}, kt_lo + 2);
+  finish_stage(B0{}, kt_lo);   // stage kt_lo+1 is finished by the first step
+  stage_barrier();             // also publishes the time tables
+
+  // One pipeline step on key block kt held in buffer `bufc`: copy block kt+3
+  // into the buffer freed by the previous barrier, compute block kt, then
+  // (own copies of block kt+1 landed) finish block kt+1 and synchronise.
+  auto step = [&](auto bufc, int kt) __attribute__((always_inline)) {
+    constexpr int b = decltype(bufc)::value;
+    using N1 = std::integral_constant<int, (b + 1) % kStages>;
+    using N3 = std::integral_constant<int, (b + 3) % kStages>;
+    const bool more3 = kt + 3 <= kt_hi, more2 = kt + 2 <= kt_hi;
+    if (more3) issue_stage(N3{}, kt + 3);
+    if (needs(kt)) block(stage(bufc), kt);
+    if (kt + 1 <= kt_hi) {
+      wait_vmem_n(more3 ? 2 * my_copies : (more2 ? my_copies : 0));
+      finish_stage(N1{}, kt + 1);
+      stage_barrier();
+    }
+  };
   for (int kt = kt_lo;; kt += kStages) {
-    step(std::integral_constant<int, 0>{}, kt);
+    step(B0{}, kt);
     if (kt + 1 > kt_hi) break;
-    step(std::integral_constant<int, 1>{}, kt + 1);
+    step(B1{}, kt + 1);
     if (kt + 2 > kt_hi) break;
-    step(std::integral_constant<int, 2>{}, kt + 2);
+    step(B2{}, kt + 2);
     if (kt + 3 > kt_hi) break;
+    step(B3{}, kt + 3);
+    if (kt + 4 > kt_hi) break;
   }
 
   // ---- epilogue: ln(2)/n_scale, LayerNorm over d_v, * U, store ------------
@@ -652,26 +787,16 @@ hstu_attn_fwd_kernel(AttnArgs a) {
 template <typename T, int DQK, int DV, bool POS, bool TIME>
 static hipError_t launch_one(const AttnArgs& a, int n_wg, hipStream_t stream) {
   auto kern = hstu_attn_fwd_kernel<T, DQK, DV, POS, TIME>;
-  const size_t dyn = (size_t)(a.pos_len > 0 ? a.pos_len : 1) * sizeof(float);
-  hipLaunchKernelGGL(kern, dim3((unsigned)n_wg), dim3(kThreads), dyn, stream, a);
+  hipLaunchKernelGGL(kern, dim3((unsigned)n_wg), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
-// Resident workgroups per CU for one instantiation and dynamic LDS size.
+// Resident workgroups per CU for one instantiation.
 template <typename T, int DQK, int DV, bool POS, bool TIME>
-static int blocks_per_cu(int pos_len) {
+static int blocks_per_cu() {
   auto kern = hstu_attn_fwd_kernel<T, DQK, DV, POS, TIME>;
-  static bool attr_done = false;
-  if (!attr_done) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                            hipFuncAttributeMaxDynamicSharedMemorySize,
-                            kPosMax * (int)sizeof(float)) != hipSuccess)
-      return -1;
-    attr_done = true;
-  }
-  const size_t dyn = (size_t)(pos_len > 0 ? pos_len : 1) * sizeof(float);
   int nb = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, kThreads, dyn) != hipSuccess)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, kThreads, 0) != hipSuccess)
     return -1;
   return nb;
 }
@@ -688,10 +813,10 @@ static hipError_t launch_bias(const AttnArgs& a, int n_wg, hipStream_t stream) {
 template <typename T, int DQK, int DV>
 static int bpc_bias(int pos_len, int time_len) {
   const bool pos = pos_len > 0, tim = time_len > 0;
-  if (pos && tim) return blocks_per_cu<T, DQK, DV, true, true>(pos_len);
-  if (pos) return blocks_per_cu<T, DQK, DV, true, false>(pos_len);
-  if (tim) return blocks_per_cu<T, DQK, DV, false, true>(pos_len);
-  return blocks_per_cu<T, DQK, DV, false, false>(pos_len);
+  if (pos && tim) return blocks_per_cu<T, DQK, DV, true, true>();
+  if (pos) return blocks_per_cu<T, DQK, DV, true, false>();
+  if (tim) return blocks_per_cu<T, DQK, DV, false, true>();
+  return blocks_per_cu<T, DQK, DV, false, false>();
 }
 
 int attn_grid(int dtype, int d_qk, int d_v, int pos_len, int time_len) {
