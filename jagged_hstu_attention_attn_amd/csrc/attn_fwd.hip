@@ -445,14 +445,21 @@ hstu_attn_fwd_kernel(AttnArgs a) {
         const int64_t rel = tj - tbase;
         const bool ok = rel > -kT32Range && rel < kT32Range;
         const uint32_t t32 = ok ? uint32_t(rel + kT32Range) : 0u;
-        const bool key_valid = lane < kBN && kt * kBN + kl < L;
+        const int nvalid = min(kBN, L - kt * kBN);   // valid keys of the block (>= 1)
         if (lane < kBN) sb.ts32[kl] = t32;
         const bool bad = __ballot(!ok) != 0;
-        const uint32_t mn = wave_min(key_valid ? t32 : 0xffffffffu);
-        const uint32_t mx = wave_max(key_valid ? t32 : 0u);
+        // Range of the valid keys' times.  Keys are normally in time order:
+        // then it is (first, last), checked with one lane shift; otherwise
+        // the block is marked as spanning every bucket (exact per-score path).
+        const uint32_t nxt = (uint32_t)__builtin_amdgcn_update_dpp(
+            (int)t32, (int)t32, 0x130, 0xf, 0xf, false);   // lane l gets lane l+1
+        const bool desc = lane + 1 < nvalid && nxt < t32;
+        const bool sorted = __ballot(desc) == 0;
+        const uint32_t first = (uint32_t)__builtin_amdgcn_readlane((int)t32, 0);
+        const uint32_t last = (uint32_t)__builtin_amdgcn_readlane((int)t32, nvalid - 1);
         if (lane == 0) {
-          sb.tmin = mn;
-          sb.tmax = mx;
+          sb.tmin = sorted ? first : 0u;
+          sb.tmax = sorted ? last : 0xffffffffu;
           sb.tbad = bad;
         }
       }
@@ -694,12 +701,12 @@ hstu_attn_fwd_kernel(AttnArgs a) {
     using N3 = std::integral_constant<int, (b + 3) % kStages>;
     const bool more3 = kt + 3 <= kt_hi, more2 = kt + 2 <= kt_hi;
     if (more3) issue_stage(N3{}, kt + 3);
-    if (needs(kt)) block(stage(bufc), kt);
     if (kt + 1 <= kt_hi) {
       wait_vmem_n(more3 ? 2 * my_copies : (more2 ? my_copies : 0));
-      finish_stage(N1{}, kt + 1);
-      stage_barrier();
+      finish_stage(N1{}, kt + 1);   // its LDS traffic overlaps block kt
     }
+    if (needs(kt)) block(stage(bufc), kt);
+    if (kt + 1 <= kt_hi) stage_barrier();
   };
   for (int kt = kt_lo;; kt += kStages) {
     step(B0{}, kt);
@@ -780,7 +787,9 @@ hstu_attn_fwd_kernel(AttnArgs a) {
       }
   }
 
-  __syncthreads();   // the LDS of this item is free again
+  // The LDS of this item is free again once every wave is here; the output
+  // stores need not have completed (the next item's first wait covers them).
+  stage_barrier();
   }  // queue walk
 }
 
