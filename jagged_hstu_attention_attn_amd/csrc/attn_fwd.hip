@@ -752,39 +752,53 @@ hstu_attn_fwd_kernel(AttnArgs a) {
     const int64_t tok = seq0 + i;
     T* orow = reinterpret_cast<T*>(a.out) + tok * a.ld_out + (int64_t)h * DV;
     const T* urow = reinterpret_cast<const T*>(a.u) + tok * a.ld_u + (int64_t)h * DV;
+    // The U loads of a group of columns go out before its first store (a
+    // store may alias a later load, so interleaving them would serialise one
+    // memory round trip per four columns); two groups keep the registers the
+    // loads land in within what the epilogue has free.
+    using U4 = std::conditional_t<BF, bf16x4, floatx4>;
+    constexpr int kGroups = NDB >= 2 ? 2 : 1, kDbPer = (NDB + kGroups - 1) / kGroups;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+    for (int g = 0; g < kGroups; ++g) {
+      U4 uu[kDbPer][4];
+      if (ln) {
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const int d0 = 32 * db + 8 * gq + 4 * hh;
-        if (d0 < DV) {
-          float y[4];
+        for (int x = 0; x < kDbPer; ++x)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) y[e] = acc[db][4 * gq + e];
-          if (ln) {
+          for (int gq = 0; gq < 4; ++gq) {
+            const int d0 = 32 * (g * kDbPer + x) + 8 * gq + 4 * hh;
+            if (g * kDbPer + x < NDB && d0 < DV)
+              uu[x][gq] = *reinterpret_cast<const U4*>(urow + d0);
+          }
+      }
+#pragma unroll
+      for (int x = 0; x < kDbPer; ++x)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int db = g * kDbPer + x;
+          const int d0 = 32 * db + 8 * gq + 4 * hh;
+          if (db < NDB && d0 < DV) {
+            float y[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) y[e] = acc[db][4 * gq + e];
+            if (ln) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) y[e] = (y[e] - mean) * rstd * (float)uu[x][gq][e];
+            }
             if constexpr (BF) {
-              const bf16x4 uu = *reinterpret_cast<const bf16x4*>(urow + d0);
+              bf16x4 o;
 #pragma unroll
-              for (int e = 0; e < 4; ++e) y[e] = (y[e] - mean) * rstd * (float)uu[e];
+              for (int e = 0; e < 4; ++e) o[e] = (__bf16)y[e];
+              *reinterpret_cast<bf16x4*>(orow + d0) = o;
             } else {
-              const floatx4 uu = *reinterpret_cast<const floatx4*>(urow + d0);
+              floatx4 o;
 #pragma unroll
-              for (int e = 0; e < 4; ++e) y[e] = (y[e] - mean) * rstd * uu[e];
+              for (int e = 0; e < 4; ++e) o[e] = y[e];
+              *reinterpret_cast<floatx4*>(orow + d0) = o;
             }
           }
-          if constexpr (BF) {
-            bf16x4 o;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] = (__bf16)y[e];
-            *reinterpret_cast<bf16x4*>(orow + d0) = o;
-          } else {
-            floatx4 o;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] = y[e];
-            *reinterpret_cast<floatx4*>(orow + d0) = o;
-          }
         }
-      }
+    }
   }
 
   // The LDS of this item is free again once every wave is here; the output
