@@ -266,6 +266,7 @@ hstu_attn_fwd_kernel(AttnArgs a) {
 
   __shared__ __align__(16) SB st0, st1, st2, st3;
   __shared__ TimeTables tt;
+  __shared__ int s_ticket;   // arrival order of a split item's chunk
   auto stage = [&](auto bufc) __attribute__((always_inline)) -> SB& {
     constexpr int b = decltype(bufc)::value % kStages;
     if constexpr (b == 0) return st0;
@@ -310,15 +311,15 @@ hstu_attn_fwd_kernel(AttnArgs a) {
     v_off[s] = (uint32_t)row * ldv_b + 16u * (uint32_t)((m % VCH) ^ C::vswz(row));
   }
 
-  // Queue walk: workgroup k serves queue k%8 and takes its entries k/8,
-  // k/8 + W, k/8 + 2W, ... where W is the number of workgroups serving that
-  // queue (at least 8 workgroups are launched, so every queue is served).
-  const int qx = blockIdx.x & (kQueues - 1);
-  const int qstride = ((int)gridDim.x + kQueues - 1 - qx) / kQueues;
-  const int qcount = a.queue_count[qx];
-  const int4* qitems = a.items + a.queue_start[qx];
-  for (int idx = blockIdx.x >> 3; idx < qcount; idx += qstride) {
-  const int4 it = qitems[idx];
+  // Work walk: planned workgroup v processes units [wg[2v], wg[2v] + wg[2v+1])
+  // in order; a launch of another size than the plan's maps the planned
+  // workgroups onto its own cyclically.
+  const int n_plan = a.hdr[0];
+  for (int v = blockIdx.x; v < n_plan; v += gridDim.x) {
+  const int u_begin = a.wg[2 * v], u_end = u_begin + a.wg[2 * v + 1];
+  for (int u = u_begin; u < u_end; ++u) {
+  const int4 it = a.units[2 * u];
+  const int4 ch = a.units[2 * u + 1];   // key tiles [ch.x, ch.y]; split slot, chunk
   const int seq0 = it.x, L = it.y;
   const int qt = it.w / H, h = it.w - qt * H;
   SeqGeom geo;
@@ -330,7 +331,7 @@ hstu_attn_fwd_kernel(AttnArgs a) {
   const int i1 = min(i0 + kBM, L);
   int jlo, jhi;
   tile_key_range(geo, i0, i1, jlo, jhi);
-  const int kt_lo = jlo / kBN, kt_hi = jhi / kBN;
+  const int kt_lo = max(jlo / kBN, ch.x), kt_hi = min(jhi / kBN, ch.y);
 
   // ---- per-lane query row and the wave's uniform key bounds --------------
   const int wr0 = i0 + wave * kRows;
@@ -719,6 +720,71 @@ hstu_attn_fwd_kernel(AttnArgs a) {
     if (kt + 4 > kt_hi) break;
   }
 
+  // ---- chunk of a split item: publish the partial output; the chunk that
+  // arrives last adds all partials in chunk order and runs the epilogue ----
+  // The partials are written and read only with device-scope (agent) atomic
+  // stores and loads, which go to and come from the device's coherence point
+  // (global_store/global_load with sc1) on whatever XCD the chunks run: a
+  // chunk's stores have completed (vmcnt 0) before its workgroup bumps the
+  // item's arrival counter, and the last chunk issues its loads only after
+  // its own bump has returned the count of the others.  No cache-wide
+  // write-back or invalidation is needed.
+  const int n_chunks = ch.w & 0xffff;
+  if (n_chunks > 1) {
+    // slot layout: [wave][db][r/4][lane] x 4 floats (two 8-byte words)
+    auto slot = [&](int c) __attribute__((always_inline)) {
+      return reinterpret_cast<uint64_t*>(a.partials + (int64_t)(ch.z + c) * a.slot_floats) +
+             2 * (wave * NDB * 4 * 64 + lane);
+    };
+    uint64_t* own = slot(ch.w >> 16);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+        for (int hw = 0; hw < 2; ++hw) {
+          // (__float_as_uint, not __builtin_bit_cast: this compiler turns a
+          // bit cast of a vector element into a cast of element 0)
+          const uint64_t w2 = (uint64_t)__float_as_uint(acc[db][4 * q4 + 2 * hw]) |
+                              ((uint64_t)__float_as_uint(acc[db][4 * q4 + 2 * hw + 1]) << 32);
+          __hip_atomic_store(own + 2 * (db * 4 + q4) * 64 + hw, w2, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+        }
+    wait_vmem<0>();    // this wave's partial has reached the coherence point
+    __syncthreads();
+    if (tid == 0)
+      s_ticket = __hip_atomic_fetch_add(a.counters + ch.z, 1, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (s_ticket != n_chunks - 1) continue;   // another chunk finishes the item
+    if (tid == 0) a.counters[ch.z] = 0;       // ready for the next run of this plan
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
+    for (int c = 0; c < n_chunks; ++c) {
+      const uint64_t* src = slot(c);
+      uint64_t p[NDB][4][2];
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+          for (int hw = 0; hw < 2; ++hw)
+            p[db][q4][hw] = __hip_atomic_load(src + 2 * (db * 4 + q4) * 64 + hw,
+                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+          for (int hw = 0; hw < 2; ++hw) {
+            acc[db][4 * q4 + 2 * hw] += __uint_as_float((uint32_t)p[db][q4][hw]);
+            acc[db][4 * q4 + 2 * hw + 1] += __uint_as_float((uint32_t)(p[db][q4][hw] >> 32));
+          }
+    }
+  }
+
   // ---- epilogue: ln(2)/n_scale, LayerNorm over d_v, * U, store ------------
   // acc[db][r] holds d = 32db + 8(r/4) + 4hh + r%4 of row i.
   const float osc = a.out_scale;
@@ -804,7 +870,8 @@ hstu_attn_fwd_kernel(AttnArgs a) {
   // The LDS of this item is free again once every wave is here; the output
   // stores need not have completed (the next item's first wait covers them).
   stage_barrier();
-  }  // queue walk
+  }  // units
+  }  // planned workgroups
 }
 
 template <typename T, int DQK, int DV, bool POS, bool TIME>

@@ -65,8 +65,8 @@ int check_desc(const hstu_attn_desc* d) {
       return fail(HSTU_ERR_INVALID_ARG, "%s * element size must be a multiple of 16 bytes",
                   x.name);
   }
-  const hstu::PlanLayout pl = hstu::plan_layout(d->num_seqs, d->total_tokens, H);
-  if (pl.items_max > 0x7fffffffLL || (int64_t)d->num_seqs * H > 0x7fffffffLL)
+  const hstu::PlanLayout pl = hstu::plan_layout(d->num_seqs, d->total_tokens, H, d->d_v);
+  if (2 * pl.units_max > 0x7fffffffLL || (int64_t)d->num_seqs * H > 0x7fffffffLL)
     return fail(HSTU_ERR_UNSUPPORTED, "too many work items (%lld)", (long long)pl.items_max);
   return HSTU_OK;
 }
@@ -76,7 +76,7 @@ int check_plan_args(const hstu_attn_desc* d, const int32_t* offsets, int32_t con
   if (d->num_seqs > 0 && !offsets) return fail(HSTU_ERR_INVALID_ARG, "offsets is NULL");
   if (contextual_len < 0) return fail(HSTU_ERR_INVALID_ARG, "contextual_len < 0");
   if (max_attn_len < 0) return fail(HSTU_ERR_INVALID_ARG, "max_attn_len < 0");
-  const size_t need = hstu::plan_layout(d->num_seqs, d->total_tokens, d->num_heads).total;
+  const size_t need = hstu::plan_layout(d->num_seqs, d->total_tokens, d->num_heads, d->d_v).total;
   if (!ws) return fail(HSTU_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", need);
   if (ws_bytes < need)
     return fail(HSTU_ERR_WORKSPACE, "workspace has %zu bytes, need %zu", ws_bytes, need);
@@ -109,9 +109,8 @@ int check_run_args(const hstu_attn_desc* d, const void* q, const void* k, const 
 }
 
 // Workgroups of the persistent attention launch: CUs x resident workgroups
-// per CU (cached per device and kernel variant), capped so that no queue gets
-// more workgroups than the work list could hold, and at least one per queue.
-// <= 0 on a HIP error.
+// per CU (cached per device and kernel variant), between 8 (one per XCD) and
+// kMaxGrid (the most a plan serves).  <= 0 on a HIP error.
 int persistent_grid(const hstu_attn_desc* d) {
   struct Entry {
     int dev, dtype, d_qk, d_v, pos_len, has_time, grid;
@@ -122,7 +121,7 @@ int persistent_grid(const hstu_attn_desc* d) {
   if (hipGetDevice(&dev) != hipSuccess) return -1;
   const int has_time = d->time_table_len > 0;
   int g = -1;
-  for (int i = 0; i < cache_n; ++i) {
+  for (int i = 0; i < cache_n && i < 16; ++i) {
     const Entry& e = cache[i];
     if (e.dev == dev && e.dtype == d->dtype && e.d_qk == d->d_qk && e.d_v == d->d_v &&
         e.pos_len == d->pos_table_len && e.has_time == has_time) {
@@ -136,30 +135,33 @@ int persistent_grid(const hstu_attn_desc* d) {
     cache[cache_n % 16] = Entry{dev, d->dtype, d->d_qk, d->d_v, d->pos_table_len, has_time, g};
     ++cache_n;
   }
-  const int64_t items = hstu::plan_layout(d->num_seqs, d->total_tokens, d->num_heads).items_max;
-  const int64_t cap = (int64_t)hstu::kQueues * (items > 0 ? items : 1);
-  const int64_t n = cap < g ? cap : g;
-  return (int)(n < hstu::kQueues ? hstu::kQueues : n);
+  // at least one workgroup per XCD, at most what a plan serves
+  return g < hstu::kXcds ? hstu::kXcds : (g < hstu::kMaxGrid ? g : hstu::kMaxGrid);
 }
 
 struct PlanPtrs {
-  int32_t* queue_count;
-  int32_t* queue_start;
-  int4* items;
-  int32_t* gscan;
+  int32_t* hdr;
+  int4* units;
+  int32_t* wg;
+  int32_t* counters;
+  float* partials;
   int32_t* seq;
+  char* items;
+  int64_t slot_floats;
 };
 
 PlanPtrs plan_ptrs(const hstu_attn_desc* d, void* ws) {
-  const hstu::PlanLayout pl = hstu::plan_layout(d->num_seqs, d->total_tokens, d->num_heads);
+  const hstu::PlanLayout pl = hstu::plan_layout(d->num_seqs, d->total_tokens, d->num_heads, d->d_v);
   char* base = static_cast<char*>(ws);
-  int32_t* hdr = reinterpret_cast<int32_t*>(base + pl.hdr_off);
   PlanPtrs p;
-  p.queue_count = hdr;
-  p.queue_start = hdr + hstu::kQueues;
-  p.items = reinterpret_cast<int4*>(base + pl.items_off);
-  p.gscan = reinterpret_cast<int32_t*>(base + pl.gscan_off);
+  p.hdr = reinterpret_cast<int32_t*>(base + pl.hdr_off);
+  p.units = reinterpret_cast<int4*>(base + pl.units_off);
+  p.wg = reinterpret_cast<int32_t*>(base + pl.wg_off);
+  p.counters = reinterpret_cast<int32_t*>(base + pl.ctr_off);
+  p.partials = reinterpret_cast<float*>(base + pl.part_off);
   p.seq = reinterpret_cast<int32_t*>(base + pl.seq_off);
+  p.items = base + pl.item_off;
+  p.slot_floats = pl.slot_floats;
   return p;
 }
 
@@ -173,7 +175,7 @@ int hstu_jagged_attn_supported(int32_t dtype, int32_t d_qk, int32_t d_v) {
 
 size_t hstu_jagged_attn_workspace_bytes(const hstu_attn_desc* desc) {
   if (check_desc(desc) != HSTU_OK) return 0;
-  return hstu::plan_layout(desc->num_seqs, desc->total_tokens, desc->num_heads).total;
+  return hstu::plan_layout(desc->num_seqs, desc->total_tokens, desc->num_heads, desc->d_v).total;
 }
 
 int hstu_jagged_attn_plan(const hstu_attn_desc* desc, const int32_t* offsets,
@@ -185,8 +187,10 @@ int hstu_jagged_attn_plan(const hstu_attn_desc* desc, const int32_t* offsets,
   rc = check_plan_args(desc, offsets, contextual_len, max_attn_len, workspace, workspace_bytes);
   if (rc != HSTU_OK) return rc;
   if (desc->num_seqs == 0 || desc->total_tokens == 0) return HSTU_OK;
-  const hstu::PlanLayout pl = hstu::plan_layout(desc->num_seqs, desc->total_tokens, desc->num_heads);
+  const hstu::PlanLayout pl = hstu::plan_layout(desc->num_seqs, desc->total_tokens, desc->num_heads, desc->d_v);
   const PlanPtrs pp = plan_ptrs(desc, workspace);
+  const int n_wg = persistent_grid(desc);
+  if (n_wg <= 0) return fail(HSTU_ERR_HIP, "cannot query the device for the launch size");
   hstu::PlanArgs a;
   a.offsets = offsets;
   a.num_targets = num_targets;
@@ -195,13 +199,15 @@ int hstu_jagged_attn_plan(const hstu_attn_desc* desc, const int32_t* offsets,
   a.contextual_len = contextual_len;
   a.max_attn_len = max_attn_len;
   a.items_max = (int32_t)pl.items_max;
-  a.slots = (int32_t)pl.slots;
-  a.queue_count = pp.queue_count;
-  a.queue_start = pp.queue_start;
-  a.items = pp.items;
-  a.gscan = pp.gscan;
+  a.n_wg = n_wg;
+  a.hdr = pp.hdr;
+  a.units = pp.units;
+  a.wg = pp.wg;
+  a.counters = pp.counters;
   a.seq_scratch = pp.seq;
-  const hipError_t e = hstu::launch_plan(a, static_cast<hipStream_t>(stream));
+  a.item_scratch = pp.items;
+  const bool compact = hstu::plan_is_compact(pl.items_max, desc->total_tokens);
+  const hipError_t e = hstu::launch_plan(a, compact, static_cast<hipStream_t>(stream));
   if (e != hipSuccess)
     return fail(HSTU_ERR_HIP, "scheduler launch failed: %s", hipGetErrorString(e));
   return HSTU_OK;
@@ -235,9 +241,12 @@ int hstu_jagged_attn_run(const hstu_attn_desc* desc, const void* q, const void* 
   a.num_targets = num_targets;
   a.pos_table = pos_table;
   a.time_table = time_table;
-  a.queue_count = pp.queue_count;
-  a.queue_start = pp.queue_start;
-  a.items = pp.items;
+  a.hdr = pp.hdr;
+  a.units = pp.units;
+  a.wg = pp.wg;
+  a.counters = pp.counters;
+  a.partials = pp.partials;
+  a.slot_floats = pp.slot_floats;
   a.ld_q = desc->ld_q;
   a.ld_k = desc->ld_k;
   a.ld_v = desc->ld_v;

@@ -26,8 +26,7 @@ constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kPosMax = 8192;   // longest supported position table
 constexpr int kPlanThreads = 1024;
-constexpr int kPlanLdsSeqs = 4096;  // batches up to this many sequences plan from LDS
-constexpr int kKeyBuckets = 64; // work-estimate buckets of the scheduler
+constexpr int kPlanLdsSeqs = 2048;  // batches up to this many sequences plan from LDS
 constexpr int kEmptyLo = 0x40000000;  // lower bound of an empty key interval
 
 struct SeqGeom {
@@ -90,35 +89,71 @@ __host__ __device__ inline void tile_key_range(const SeqGeom& g, int i0, int i1,
   if (i0 < g.c && g.c - 1 > jhi) jhi = g.c - 1;
 }
 
-// Work-list layout inside the caller's workspace (byte offsets, 256-aligned).
-// The scheduler fills one queue of items per XCD (the MI355X has 8 XCDs, each
-// with its own L2); items are (sequence, head, query tile).
-constexpr int kQueues = 8;
+// Work list.  The scheduler lists the (sequence, head, query tile) items
+// sequence by sequence, the tiles of one (sequence, head) together, and
+// balances their cost (key tiles plus a fixed per-item term) over the
+// workgroups of the persistent attention launch.  The MI355X dispatches
+// workgroup g to XCD g % 8 and each XCD has its own L2, so the items are cut
+// into 8 consecutive, equally expensive portions, one per XCD; inside a
+// portion they are dealt round-robin to the XCD's workgroups, so that the
+// workgroups running side by side work on neighbouring query tiles, which
+// share most of their keys and values.  The dealt order is then cut into
+// equal shares, one per workgroup; an item a share boundary cuts is split
+// along its key tiles into chunks.  The aggregation is a plain sum over
+// keys, so every chunk writes its fp32 partial output and the chunk that
+// finishes last adds them in chunk order and runs the epilogue.
+constexpr int kXcds = 8;
+constexpr int kMaxGrid = 1024;      // most workgroups one plan serves
+constexpr int kCostOverhead = 6;    // fixed cost of an item, in key tiles
+constexpr int kMinChunk = 8;        // fewest key tiles of a chunk of a split item
+constexpr int kPlanLdsItems = 4096; // plans of up to this many items stay in LDS
 
 struct PlanLayout {
-  size_t hdr_off;      // int32 queue_count[8], queue_start[8]
-  size_t items_off;    // int4[items_max]: (seq start, L, n_h, qt*H + h), queue by queue
-  size_t gscan_off;    // int32[8*S + 1]: item offsets of the (queue, slot) groups
-  size_t seq_off;      // int32[6*B]: per-sequence scratch of the scheduler (large batches)
+  size_t hdr_off;      // int32[64]: [0] workgroups the plan was made for
+  size_t units_off;    // int4[2 * units_max]: (seq start, L, n_h, qt*H + h),
+                       //   (kt_begin, kt_end, split slot or -1, chunk << 16 | chunks)
+  size_t wg_off;       // int32[2 * kMaxGrid]: (first unit, units) per workgroup
+  size_t ctr_off;      // int32[slots_max]: arrival counter of each split item
+  size_t part_off;     // float[slots_max * slot_floats]: partial outputs of chunks
+  size_t seq_off;      // int32[4 * (B + 1)]: per-sequence scratch of large batches
+  size_t item_off;     // per-item scratch of large plans: int32 cost[items_max + 1],
+                       //   int32 order[items_max], int64 line[items_max + 1],
+                       //   int64 ubase[items_max + 1]
   size_t total;
-  int64_t pairs_max;   // bound on sum_b ceil(L_b / BM)
-  int64_t items_max;   // pairs_max * H
-  int64_t slots;       // S = ceil(B*H / 8)
+  int64_t items_max;   // bound on sum_b ceil(L_b / BM) * H
+  int64_t units_max;   // items_max + kMaxGrid
+  int64_t slots_max;   // 2 * kMaxGrid: chunks of split items
+  int64_t slot_floats; // kBM rows x d_v rounded up to 32
 };
 
 __host__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-__host__ inline PlanLayout plan_layout(int64_t num_seqs, int64_t total_tokens, int64_t heads) {
+// The scheduler's compact variant (32-bit cost sums, per-item arrays in LDS)
+// serves plans of at most kPlanLdsItems items over fewer than 2^21 tokens:
+// then every item costs below 2^16 and every cost sum stays below 2^28.
+__host__ inline bool plan_is_compact(int64_t items_max, int64_t total_tokens) {
+  return items_max <= kPlanLdsItems && total_tokens < (int64_t(1) << 21);
+}
+
+__host__ inline PlanLayout plan_layout(int64_t num_seqs, int64_t total_tokens, int64_t heads,
+                                       int64_t d_v) {
   PlanLayout p;
   // sum_b ceil(L_b / BM) <= (N + B*(BM-1)) / BM
-  p.pairs_max = (total_tokens + num_seqs * (kBM - 1)) / kBM;
-  p.items_max = p.pairs_max * heads;
-  p.slots = (num_seqs * heads + kQueues - 1) / kQueues;
+  p.items_max = (total_tokens + num_seqs * (kBM - 1)) / kBM * heads;
+  p.units_max = p.items_max + kMaxGrid;
+  p.slots_max = 2 * kMaxGrid;
+  p.slot_floats = (int64_t)kBM * 32 * ((d_v + 31) / 32);
+  const size_t im = (size_t)(p.items_max > 0 ? p.items_max : 1);
+  const bool big_b = num_seqs > kPlanLdsSeqs, big_i = !plan_is_compact(p.items_max, total_tokens);
   p.hdr_off = 0;
-  p.items_off = 256;
-  p.gscan_off = align256(p.items_off + sizeof(int4) * (size_t)(p.items_max > 0 ? p.items_max : 1));
-  p.seq_off = align256(p.gscan_off + sizeof(int32_t) * (size_t)(kQueues * p.slots + 1));
-  p.total = align256(p.seq_off + sizeof(int32_t) * (size_t)(6 * num_seqs + 6));
+  p.units_off = 256;
+  p.wg_off = align256(p.units_off + 2 * sizeof(int4) * (size_t)p.units_max);
+  p.ctr_off = align256(p.wg_off + sizeof(int32_t) * 2 * kMaxGrid);
+  p.part_off = align256(p.ctr_off + sizeof(int32_t) * (size_t)p.slots_max);
+  p.seq_off = align256(p.part_off + sizeof(float) * (size_t)(p.slots_max * p.slot_floats));
+  p.item_off = align256(p.seq_off + (big_b ? sizeof(int32_t) * 4 * (size_t)(num_seqs + 1) : 0));
+  p.total = align256(p.item_off +
+                     (big_i ? (2 * sizeof(int32_t) + 2 * sizeof(int64_t)) * (im + 1) + 16 : 0));
   return p;
 }
 
@@ -129,13 +164,14 @@ struct PlanArgs {
   int32_t num_heads;
   int32_t contextual_len;
   int32_t max_attn_len;
-  int32_t items_max;     // capacity of `items`
-  int32_t slots;         // S
-  int32_t* queue_count;  // [8]
-  int32_t* queue_start;  // [8]
-  int4* items;
-  int32_t* gscan;
-  int32_t* seq_scratch;  // [6*B], used when B > kPlanLdsSeqs
+  int32_t items_max;     // capacity of the item scratch
+  int32_t n_wg;          // workgroups of the attention launch (<= kMaxGrid)
+  int32_t* hdr;
+  int4* units;
+  int32_t* wg;
+  int32_t* counters;
+  int32_t* seq_scratch;  // used when B > kPlanLdsSeqs
+  char* item_scratch;    // used when the items exceed kPlanLdsItems
 };
 
 struct AttnArgs {
@@ -149,9 +185,12 @@ struct AttnArgs {
   const int32_t* num_targets;
   const float* pos_table;
   const float* time_table;
-  const int32_t* queue_count;
-  const int32_t* queue_start;
-  const int4* items;
+  const int32_t* hdr;        // [0]: workgroups the plan was made for
+  const int4* units;
+  const int32_t* wg;         // (first unit, units) per planned workgroup
+  int32_t* counters;         // arrival counters of split items
+  float* partials;           // fp32 partial outputs of split chunks
+  int64_t slot_floats;
   int64_t ld_q, ld_k, ld_v, ld_u, ld_out;
   int32_t num_heads;
   int32_t contextual_len;
@@ -165,7 +204,7 @@ struct AttnArgs {
 };
 
 // Launchers (defined in the .hip files).
-hipError_t launch_plan(const PlanArgs& a, hipStream_t stream);
+hipError_t launch_plan(const PlanArgs& a, bool compact, hipStream_t stream);
 hipError_t launch_attn(const AttnArgs& a, int dtype, int d_qk, int d_v, int n_wg,
                        hipStream_t stream);
 // Workgroups of the persistent attention launch for this shape on the current

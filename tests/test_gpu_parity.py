@@ -272,6 +272,41 @@ def test_plan_reuse_across_runs():
     assert_close(o2, ora(inp2), "bf16")
 
 
+def test_split_items_plan_reuse():
+    """One long causal sequence: its last query tiles reach far more key tiles
+    than a workgroup's share, so the scheduler splits them along the keys and
+    the chunks' partial outputs are summed by the chunk that finishes last.
+    Two runs of one plan (the arrival counters must rearm) and a third call
+    with a fresh plan all match the oracle and each other bitwise."""
+    inp = make_custom([4096, 700, 33], num_heads=2, d_qk=128, d_v=128, dtype="bf16", seed=8,
+                      contextual_len=6, pos_len=4096, time_len=64, alpha=0.0884)
+    dev = to_device(inp, DEV)
+    call = JaggedAttnCall(dev["q"], dev["k"], dev["v"], dev["u"], dev["offsets"],
+                          **call_kwargs(inp, dev))
+    call.plan()
+    o1 = call.run().float().cpu().numpy().astype(np.float64)
+    o2 = call.run().float().cpu().numpy().astype(np.float64)
+    o3 = gpu_forward(inp)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(3968, 4096), np.arange(0, 4096, 97),
+                                     np.arange(4096, 4829, 41)]))
+    assert_close(o1, ora(inp, rows=rows), "bf16", rows=rows)
+    assert np.array_equal(o1, o2) and np.array_equal(o1, o3)
+
+
+@pytest.mark.parametrize("dtype,d", [("f32", 8), ("bf16", 64)])
+def test_large_batch_plan(dtype, d):
+    """More sequences than the scheduler keeps in LDS (2048) and more items
+    than its compact variant takes (4096): the workspace-backed path."""
+    rng = np.random.default_rng(17)
+    lengths = rng.integers(0, 160, size=3000)
+    lengths[::7] = 0
+    inp = make_custom(lengths.tolist(), num_heads=2, d_qk=d, d_v=d, dtype=dtype, seed=3,
+                      num_targets=rng.integers(0, 12, size=3000).tolist(), pos_len=512,
+                      time_len=64, alpha=0.3)
+    assert_close(gpu_forward(inp), ora(inp), dtype)
+
+
 # ---------------------------------------------------------------------------
 # Information flow on the device, bitwise ("Do not copy softmax masking
 # mechanically": change future inputs, earlier outputs must not move).
