@@ -62,6 +62,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef unsigned int uintx4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
 
@@ -73,6 +74,13 @@ constexpr int kDiag = kBM + kBN - 1;             // distinct i - j of a 128 x 32
 constexpr int kDiagCopies = (kDiag + 63) / 64;   // 4-byte LDS copies of 64 lanes
 static_assert(kRows == 32, "one 32x32 MFMA tile of query rows per wave");
 static_assert(kBN == 32, "a key block is one 32-key score tile");
+
+// XOR swizzle of the 16-byte chunks of a staged row of CH chunks: the rows a
+// wave touches at one chunk position fall on distinct LDS banks.
+template <int CH>
+__device__ inline int row_swz(int row) {
+  return CH >= 16 ? (row & 15) : (CH >= 2 ? ((row >> 1) & (CH - 1)) : 0);
+}
 
 template <typename T, int DQK, int DV>
 struct Cfg {
@@ -90,6 +98,9 @@ struct Cfg {
   static_assert(kKRow % 16 == 0 && kVRow % 16 == 0, "rows are whole 16-byte chunks");
   static_assert(kBN * kKCh % 64 == 0 && kBN * kVCh % 64 == 0, "stage is whole copies");
   static_assert(DQK % kStep == 0 && DV % 4 == 0 && (!kBf16 || DV % 32 == 0), "shape");
+  // the Q tile and the epilogue stage 32 rows per wave in half of the K+V
+  // space of a stage buffer
+  static_assert(DQK == DV, "staging layout assumes d_qk == d_v");
   // XOR swizzles of a row's 16-byte chunks (always below the number of
   // chunks, so they permute the row).  K: one read touches the same logical
   // chunk of 16 consecutive rows per LDS cycle.  V (bf16): a transposed read
@@ -128,6 +139,15 @@ struct TimeTables {
 __device__ inline uint32_t lds_off(const void* p) { return (uint32_t)(uintptr_t)p; }
 // LDS pointer from an LDS byte offset.
 __device__ inline lds_shortx4* lds_ptr4(uint32_t off) { return (lds_shortx4*)(uintptr_t)off; }
+// Typed LDS access by byte offset.
+template <typename V>
+__device__ inline V lds_ld(uint32_t off) {
+  return *(__attribute__((address_space(3))) const V*)(uintptr_t)off;
+}
+template <typename V>
+__device__ inline void lds_st(uint32_t off, V v) {
+  *(__attribute__((address_space(3))) V*)(uintptr_t)off = v;
+}
 
 // A pointer that is the same in every lane, as a scalar-register value.
 __device__ inline uint64_t uni_ptr(const void* p) {
@@ -663,23 +683,40 @@ hstu_attn_fwd_kernel(AttnArgs a) {
     tbase = a.timestamps[seq0 + i0];
     ti64 = row_valid ? a.timestamps[seq0 + i] : tbase;
   }
-  {
-    const T* qrow = reinterpret_cast<const T*>(a.q) +
-                    (int64_t)(seq0 + (row_valid ? i : i0)) * a.ld_q + (int64_t)h * DQK;
+  // Q tile: every wave copies its 32 rows into LDS with whole-row copies (1 KB
+  // per copy; stage buffers 2 and 3 are not in use yet), then reads its MFMA
+  // operands from there.  Rows past the tile repeat its last row.
+  const uint32_t q_lds = lds_off(wave < 2 ? st2.k : st3.k) + (uint32_t)((wave & 1) * kRows * KROW);
+  if (wave_rows && !alpha_zero) {
+    int ql = lane;   // recomputed per item: kept out of the registers live across items
+    asm volatile("" : "+v"(ql));
+    const uint64_t qb = uni_ptr(reinterpret_cast<const char*>(a.q) +
+                                ((int64_t)(seq0 + i0) * a.ld_q + (int64_t)h * DQK) * ES);
+    const uint32_t ldq_b = (uint32_t)(a.ld_q * ES);
 #pragma unroll
-    for (int c = 0; c < NKC; ++c) {
-      if constexpr (BF) {
-        bf16x8 z = {};
-        qf[c] = (row_valid && !alpha_zero)
-                    ? *reinterpret_cast<const bf16x8*>(qrow + c * 16 + hh * 8) : z;
-      } else {
-        qf[c] = (row_valid && !alpha_zero) ? qrow[c * 2 + hh] : 0.0f;
-      }
+    for (int n = 0; n < kRows * KCH / 64; ++n) {
+      const int m = 64 * n + ql, r = m / KCH;
+      const int row = min(wr0 + r, i1 - 1) - i0;
+      lds_copy16(qb, (uint32_t)row * ldq_b + 16u * (uint32_t)((m % KCH) ^ C::kswz(r)),
+                 q_lds + 1024u * (uint32_t)n);
     }
   }
   wait_vmem<0>();
 #pragma unroll
-  for (int c = 0; c < NKC; ++c) asm volatile("" : "+v"(qf[c]));
+  for (int c = 0; c < NKC; ++c) {
+    if constexpr (BF) {
+      const bf16x8 z = {};
+      qf[c] = (row_valid && !alpha_zero)
+                  ? lds_ld<bf16x8>(q_lds + l32 * KROW + 16 * ((2 * c + hh) ^ C::kswz(l32)))
+                  : z;
+    } else {
+      const int d = 2 * c + hh;
+      qf[c] = (row_valid && !alpha_zero)
+                  ? lds_ld<float>(q_lds + l32 * KROW + 16 * ((d >> 2) ^ C::kswz(l32)) +
+                                  4 * (d & 3))
+                  : 0.0f;
+    }
+  }
   if constexpr (TIME) {
     asm volatile("" : "+v"(ti64));
     const int64_t rel = ti64 - tbase;
@@ -689,9 +726,9 @@ hstu_attn_fwd_kernel(AttnArgs a) {
     w_tmin = wave_min(row_valid ? ti32 : 0xffffffffu);
     w_tmax = wave_max(row_valid ? ti32 : 0u);
   }
-  if (kt_lo + 2 <= kt_hi) issue_stage(B2{}, kt_lo + 2);
   finish_stage(B0{}, kt_lo);   // stage kt_lo+1 is finished by the first step
-  stage_barrier();             // also publishes the time tables
+  stage_barrier();             // also publishes the time tables; Q reads are done
+  if (kt_lo + 2 <= kt_hi) issue_stage(B2{}, kt_lo + 2);
 
   // One pipeline step on key block kt held in buffer `bufc`: copy block kt+3
   // into the buffer freed by the previous barrier, compute block kt, then
@@ -786,10 +823,32 @@ hstu_attn_fwd_kernel(AttnArgs a) {
   }
 
   // ---- epilogue: ln(2)/n_scale, LayerNorm over d_v, * U, store ------------
-  // acc[db][r] holds d = 32db + 8(r/4) + 4hh + r%4 of row i.
+  // acc[db][r] holds d = 32db + 8(r/4) + 4hh + r%4 of row i.  U comes in and
+  // the output goes out through LDS with whole-row copies and stores (8 full
+  // 128-byte lines per instruction); each wave uses 32 rows of a stage buffer
+  // that the last block does not read (the other waves may still be in it).
   const float osc = a.out_scale;
   float mean = 0.0f, rstd = 1.0f;
   const bool ln = a.epilogue == 0;
+  int el = lane;   // recomputed per item: kept out of the registers live across items
+  asm volatile("" : "+v"(el));
+  const int b_ep = ((kt_hi - kt_lo) + 1 + (wave >> 1)) & (kStages - 1);
+  const uint32_t e_lds =
+      (b_ep == 0 ? lds_off(st0.k) : b_ep == 1 ? lds_off(st1.k) : b_ep == 2 ? lds_off(st2.k)
+                                                                          : lds_off(st3.k)) +
+      (uint32_t)((wave & 1) * kRows * VROW);
+  if (ln && wave_rows) {
+    const uint64_t ub = uni_ptr(reinterpret_cast<const char*>(a.u) +
+                                ((int64_t)(seq0 + i0) * a.ld_u + (int64_t)h * DV) * ES);
+    const uint32_t ldu_b = (uint32_t)(a.ld_u * ES);
+#pragma unroll
+    for (int n = 0; n < kRows * VCH / 64; ++n) {
+      const int m = 64 * n + el, r = m / VCH;
+      const int row = min(wr0 + r, i1 - 1) - i0;
+      lds_copy16(ub, (uint32_t)row * ldu_b + 16u * (uint32_t)((m % VCH) ^ row_swz<VCH>(r)),
+                 e_lds + 1024u * (uint32_t)n);
+    }
+  }
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -814,56 +873,57 @@ hstu_attn_fwd_kernel(AttnArgs a) {
     sq += __shfl_xor(sq, 32, 64);
     rstd = rsqrtf(sq * (1.0f / DV) + a.ln_eps);
   }
-  if (row_valid) {
-    const int64_t tok = seq0 + i;
-    T* orow = reinterpret_cast<T*>(a.out) + tok * a.ld_out + (int64_t)h * DV;
-    const T* urow = reinterpret_cast<const T*>(a.u) + tok * a.ld_u + (int64_t)h * DV;
-    // The U loads of a group of columns go out before its first store (a
-    // store may alias a later load, so interleaving them would serialise one
-    // memory round trip per four columns); two groups keep the registers the
-    // loads land in within what the epilogue has free.
-    using U4 = std::conditional_t<BF, bf16x4, floatx4>;
-    constexpr int kGroups = NDB >= 2 ? 2 : 1, kDbPer = (NDB + kGroups - 1) / kGroups;
+  if (wave_rows) {
+    wait_vmem<0>();   // this wave's U rows have landed
+    // y = (O - mean) * rstd * U in place of U, as the output's element type
 #pragma unroll
-    for (int g = 0; g < kGroups; ++g) {
-      U4 uu[kDbPer][4];
-      if (ln) {
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int x = 0; x < kDbPer; ++x)
+      for (int gq = 0; gq < 4; ++gq) {
+        const int d0 = 32 * db + 8 * gq + 4 * hh;
+        if (d0 < DV) {
+          const int byte = d0 * ES;
+          const uint32_t off = e_lds + (uint32_t)(l32 * VROW) +
+                               16u * (uint32_t)((byte >> 4) ^ row_swz<VCH>(l32)) +
+                               (uint32_t)(byte & 15);
+          float y[4];
 #pragma unroll
-          for (int gq = 0; gq < 4; ++gq) {
-            const int d0 = 32 * (g * kDbPer + x) + 8 * gq + 4 * hh;
-            if (g * kDbPer + x < NDB && d0 < DV)
-              uu[x][gq] = *reinterpret_cast<const U4*>(urow + d0);
-          }
-      }
-#pragma unroll
-      for (int x = 0; x < kDbPer; ++x)
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const int db = g * kDbPer + x;
-          const int d0 = 32 * db + 8 * gq + 4 * hh;
-          if (db < NDB && d0 < DV) {
-            float y[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) y[e] = acc[db][4 * gq + e];
+          for (int e = 0; e < 4; ++e) y[e] = acc[db][4 * gq + e];
+          if constexpr (BF) {
             if (ln) {
+              const bf16x4 uu = lds_ld<bf16x4>(off);
 #pragma unroll
-              for (int e = 0; e < 4; ++e) y[e] = (y[e] - mean) * rstd * (float)uu[x][gq][e];
+              for (int e = 0; e < 4; ++e) y[e] = (y[e] - mean) * rstd * (float)uu[e];
             }
-            if constexpr (BF) {
-              bf16x4 o;
+            bf16x4 o;
 #pragma unroll
-              for (int e = 0; e < 4; ++e) o[e] = (__bf16)y[e];
-              *reinterpret_cast<bf16x4*>(orow + d0) = o;
-            } else {
-              floatx4 o;
+            for (int e = 0; e < 4; ++e) o[e] = (__bf16)y[e];
+            lds_st<bf16x4>(off, o);
+          } else {
+            if (ln) {
+              const floatx4 uu = lds_ld<floatx4>(off);
 #pragma unroll
-              for (int e = 0; e < 4; ++e) o[e] = y[e];
-              *reinterpret_cast<floatx4*>(orow + d0) = o;
+              for (int e = 0; e < 4; ++e) y[e] = (y[e] - mean) * rstd * uu[e];
             }
+            floatx4 o;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = y[e];
+            lds_st<floatx4>(off, o);
           }
         }
+      }
+    // whole rows out: lane l of store n writes physical chunk (64n + l) % VCH
+    // of row (64n + l) / VCH, i.e. logical chunk ^ swizzle, rows of the tile only
+    char* obase = reinterpret_cast<char*>(uni_ptr(
+        reinterpret_cast<char*>(a.out) + ((int64_t)(seq0 + wr0) * a.ld_out + (int64_t)h * DV) * ES));
+    const uint32_t ldo_b = (uint32_t)(a.ld_out * ES);
+#pragma unroll
+    for (int n = 0; n < kRows * VCH / 64; ++n) {
+      const int m = 64 * n + el, r = m / VCH;
+      const uintx4 w4 = lds_ld<uintx4>(e_lds + 16u * (uint32_t)m);
+      if (wr0 + r < i1)
+        *reinterpret_cast<uintx4*>(obase + ((uint32_t)r * ldo_b +
+                                           16u * (uint32_t)((m % VCH) ^ row_swz<VCH>(r)))) = w4;
     }
   }
 
