@@ -105,8 +105,10 @@ typedef struct {
 int hstu_jagged_attn_supported(int32_t dtype, int32_t d_qk, int32_t d_v);
 
 /*
- * Workspace bytes the call needs for `desc` (the work list of the scheduler).
- * Depends on num_seqs, total_tokens and num_heads only.  Returns 0 and sets
+ * Workspace bytes the call needs for `desc`: the scheduler's work list, the
+ * arrival counters and the fp32 partial outputs of items split along keys.
+ * Depends on num_seqs, total_tokens, num_heads and d_v only (no device
+ * query).  Returns 0 and sets
  * the error message if desc is invalid.
  */
 size_t hstu_jagged_attn_workspace_bytes(const hstu_attn_desc* desc);
@@ -156,6 +158,37 @@ int hstu_jagged_attn_run(const hstu_attn_desc* desc,
                          int32_t max_attn_len, float alpha, float n_scale,
                          const float* pos_table, const float* time_table, void* out,
                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Candidate rows only (candidate micro-batching with history reuse, "Scaling
+ * HSTU: ragged execution, candidate amortization and content features",
+ * section "Many candidates make reuse valuable").  The candidates of a
+ * sequence attend to its history keys and to themselves only, and with the
+ * candidate position clamped to the history end (the mask rules of
+ * hstu_attn_desc's header comment) every candidate sees the same history, so
+ * a candidate's output depends on the history and on itself, never on the
+ * other candidates.  These calls compute exactly the candidate rows
+ * [n_h, L) of every sequence, tiled from n_h (128 candidates of a sequence
+ * per work item, all reading the same cached history keys and values), and
+ * write only those rows of `out`: history rows are not touched, so a history
+ * computed once (its K/V, and its rows' outputs from a previous call) can
+ * serve any number of candidate micro-batches laid out after it.  Arguments,
+ * layouts, ownership and errors are those of hstu_jagged_attn_plan and
+ * hstu_jagged_attn_fwd; a candidates-only plan is run with
+ * hstu_jagged_attn_run.  Sequences without candidates contribute no work.
+ */
+int hstu_jagged_attn_plan_candidates(const hstu_attn_desc* desc, const int32_t* offsets,
+                                     const int32_t* num_targets, int32_t contextual_len,
+                                     int32_t max_attn_len, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
+int hstu_jagged_attn_fwd_candidates(const hstu_attn_desc* desc,
+                                    const void* q, const void* k, const void* v, const void* u,
+                                    const int32_t* offsets, const int64_t* timestamps,
+                                    const int32_t* num_targets, int32_t contextual_len,
+                                    int32_t max_attn_len, float alpha, float n_scale,
+                                    const float* pos_table, const float* time_table, void* out,
+                                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Host helper for throughput accounting: the exact number of allowed (i, j)

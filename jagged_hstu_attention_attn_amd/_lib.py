@@ -29,6 +29,8 @@ EXPORTS = (
     "hstu_jagged_attn_fwd",
     "hstu_jagged_attn_plan",
     "hstu_jagged_attn_run",
+    "hstu_jagged_attn_plan_candidates",
+    "hstu_jagged_attn_fwd_candidates",
     "hstu_jagged_attn_valid_pairs",
     "hstu_jagged_attn_grid",
     "hstu_last_error",
@@ -81,12 +83,15 @@ def load() -> ctypes.CDLL:
     lib.hstu_jagged_attn_workspace_bytes.restype = sz
     lib.hstu_jagged_attn_workspace_bytes.argtypes = [D]
     run_args = [D, P, P, P, P, P, P, P, i32, i32, f32, f32, P, P, P, P, sz, P]
-    for name in ("hstu_jagged_attn_fwd", "hstu_jagged_attn_run"):
+    for name in ("hstu_jagged_attn_fwd", "hstu_jagged_attn_run",
+                 "hstu_jagged_attn_fwd_candidates"):
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
         fn.argtypes = run_args
-    lib.hstu_jagged_attn_plan.restype = ctypes.c_int
-    lib.hstu_jagged_attn_plan.argtypes = [D, P, P, i32, i32, P, sz, P]
+    for name in ("hstu_jagged_attn_plan", "hstu_jagged_attn_plan_candidates"):
+        fn = getattr(lib, name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = [D, P, P, i32, i32, P, sz, P]
     lib.hstu_jagged_attn_valid_pairs.restype = i64
     lib.hstu_jagged_attn_valid_pairs.argtypes = [i32, P, P, i32, i32]
     lib.hstu_jagged_attn_grid.restype = ctypes.c_int

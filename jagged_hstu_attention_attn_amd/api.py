@@ -81,9 +81,13 @@ def _stream(device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def plan(desc, offsets, num_targets, contextual_len, max_attn_len, workspace) -> None:
-    """Enqueue the scheduler kernel (writes the work list into `workspace`)."""
-    _lib.check(_lib.load().hstu_jagged_attn_plan(
+def plan(desc, offsets, num_targets, contextual_len, max_attn_len, workspace,
+         candidates_only: bool = False) -> None:
+    """Enqueue the scheduler kernel (writes the work list into `workspace`).
+    With `candidates_only`, the work list covers only the candidate rows."""
+    fn = (_lib.load().hstu_jagged_attn_plan_candidates if candidates_only
+          else _lib.load().hstu_jagged_attn_plan)
+    _lib.check(fn(
         ctypes.byref(desc), _ptr(offsets), _ptr(num_targets), int(contextual_len),
         int(max_attn_len), _ptr(workspace), int(workspace.numel()), _stream(workspace.device)))
 
@@ -126,7 +130,8 @@ class JaggedAttnCall:
 
     def __init__(self, q, k, v, u, offsets, *, timestamps=None, num_targets=None,
                  contextual_len=0, max_attn_len=0, alpha, n_scale, pos_table=None,
-                 time_table=None, eps=1e-5, epilogue="ln_u", out=None):
+                 time_table=None, eps=1e-5, epilogue="ln_u", out=None,
+                 candidates_only: bool = False):
         if not q.is_cuda:
             raise ValueError("tensors must be on a GPU")
         _check_aux(offsets, timestamps, num_targets, pos_table, time_table, q.device)
@@ -135,6 +140,7 @@ class JaggedAttnCall:
         self.contextual_len, self.max_attn_len = int(contextual_len), int(max_attn_len)
         self.alpha, self.n_scale = float(alpha), float(n_scale)
         self.pos_table, self.time_table = pos_table, time_table
+        self.candidates_only = bool(candidates_only)
         if out is None:
             out = torch.empty((q.shape[0], q.shape[1], v.shape[2]), dtype=q.dtype,
                               device=q.device)
@@ -146,7 +152,7 @@ class JaggedAttnCall:
 
     def plan(self) -> None:
         plan(self.desc, self.offsets, self.num_targets, self.contextual_len, self.max_attn_len,
-             self.workspace)
+             self.workspace, self.candidates_only)
 
     def run(self) -> torch.Tensor:
         run(self.desc, self.q, self.k, self.v, self.u, self.offsets, self.timestamps,
@@ -155,7 +161,8 @@ class JaggedAttnCall:
         return self.out
 
     def __call__(self) -> torch.Tensor:
-        _run_like("hstu_jagged_attn_fwd", self.desc, self.q, self.k, self.v, self.u,
+        _run_like("hstu_jagged_attn_fwd_candidates" if self.candidates_only
+                  else "hstu_jagged_attn_fwd", self.desc, self.q, self.k, self.v, self.u,
                   self.offsets, self.timestamps, self.num_targets, self.contextual_len,
                   self.max_attn_len, self.alpha, self.n_scale, self.pos_table, self.time_table,
                   self.out, self.workspace)
@@ -165,12 +172,16 @@ class JaggedAttnCall:
 def jagged_attn_fwd(q, k, v, u, offsets, *, timestamps=None, num_targets=None,
                     contextual_len: int = 0, max_attn_len: int = 0, alpha: float,
                     n_scale: float, pos_table=None, time_table=None, eps: float = 1e-5,
-                    epilogue: str = "ln_u", out=None) -> torch.Tensor:
-    """One full forward (scheduler + attention) on the current stream."""
+                    epilogue: str = "ln_u", out=None,
+                    candidates_only: bool = False) -> torch.Tensor:
+    """One full forward (scheduler + attention) on the current stream.  With
+    `candidates_only`, only the candidate rows of `out` are computed and
+    written (history rows keep their contents)."""
     call = JaggedAttnCall(q, k, v, u, offsets, timestamps=timestamps, num_targets=num_targets,
                           contextual_len=contextual_len, max_attn_len=max_attn_len,
                           alpha=alpha, n_scale=n_scale, pos_table=pos_table,
-                          time_table=time_table, eps=eps, epilogue=epilogue, out=out)
+                          time_table=time_table, eps=eps, epilogue=epilogue, out=out,
+                          candidates_only=candidates_only)
     return call()
 
 

@@ -347,7 +347,7 @@ hstu_attn_fwd_kernel(AttnArgs a) {
   geo.n_h = it.z;
   geo.c = clampi(a.contextual_len, 0, geo.n_h);
   geo.W = a.max_attn_len;
-  const int i0 = qt * kBM;
+  const int i0 = ((ch.w & kUnitCandRows) ? geo.n_h : 0) + qt * kBM;
   const int i1 = min(i0 + kBM, L);
   int jlo, jhi;
   tile_key_range(geo, i0, i1, jlo, jhi);
@@ -766,14 +766,14 @@ hstu_attn_fwd_kernel(AttnArgs a) {
   // item's arrival counter, and the last chunk issues its loads only after
   // its own bump has returned the count of the others.  No cache-wide
   // write-back or invalidation is needed.
-  const int n_chunks = ch.w & 0xffff;
+  const int n_chunks = ch.w & 0x7fff;
   if (n_chunks > 1) {
     // slot layout: [wave][db][r/4][lane] x 4 floats (two 8-byte words)
     auto slot = [&](int c) __attribute__((always_inline)) {
       return reinterpret_cast<uint64_t*>(a.partials + (int64_t)(ch.z + c) * a.slot_floats) +
              2 * (wave * NDB * 4 * 64 + lane);
     };
-    uint64_t* own = slot(ch.w >> 16);
+    uint64_t* own = slot((ch.w >> 16) & 0x7fff);
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll

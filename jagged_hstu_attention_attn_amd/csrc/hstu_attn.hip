@@ -178,10 +178,9 @@ size_t hstu_jagged_attn_workspace_bytes(const hstu_attn_desc* desc) {
   return hstu::plan_layout(desc->num_seqs, desc->total_tokens, desc->num_heads, desc->d_v).total;
 }
 
-int hstu_jagged_attn_plan(const hstu_attn_desc* desc, const int32_t* offsets,
-                          const int32_t* num_targets, int32_t contextual_len,
-                          int32_t max_attn_len, void* workspace, size_t workspace_bytes,
-                          void* stream) {
+static int plan_impl(const hstu_attn_desc* desc, const int32_t* offsets,
+                     const int32_t* num_targets, int32_t contextual_len, int32_t max_attn_len,
+                     void* workspace, size_t workspace_bytes, void* stream, bool cand_only) {
   int rc = check_desc(desc);
   if (rc != HSTU_OK) return rc;
   rc = check_plan_args(desc, offsets, contextual_len, max_attn_len, workspace, workspace_bytes);
@@ -200,6 +199,7 @@ int hstu_jagged_attn_plan(const hstu_attn_desc* desc, const int32_t* offsets,
   a.max_attn_len = max_attn_len;
   a.items_max = (int32_t)pl.items_max;
   a.n_wg = n_wg;
+  a.cand_only = cand_only ? 1 : 0;
   a.hdr = pp.hdr;
   a.units = pp.units;
   a.wg = pp.wg;
@@ -211,6 +211,22 @@ int hstu_jagged_attn_plan(const hstu_attn_desc* desc, const int32_t* offsets,
   if (e != hipSuccess)
     return fail(HSTU_ERR_HIP, "scheduler launch failed: %s", hipGetErrorString(e));
   return HSTU_OK;
+}
+
+int hstu_jagged_attn_plan(const hstu_attn_desc* desc, const int32_t* offsets,
+                          const int32_t* num_targets, int32_t contextual_len,
+                          int32_t max_attn_len, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  return plan_impl(desc, offsets, num_targets, contextual_len, max_attn_len, workspace,
+                   workspace_bytes, stream, false);
+}
+
+int hstu_jagged_attn_plan_candidates(const hstu_attn_desc* desc, const int32_t* offsets,
+                                     const int32_t* num_targets, int32_t contextual_len,
+                                     int32_t max_attn_len, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  return plan_impl(desc, offsets, num_targets, contextual_len, max_attn_len, workspace,
+                   workspace_bytes, stream, true);
 }
 
 int hstu_jagged_attn_run(const hstu_attn_desc* desc, const void* q, const void* k,
@@ -284,6 +300,28 @@ int hstu_jagged_attn_fwd(const hstu_attn_desc* desc, const void* q, const void* 
   if (rc != HSTU_OK) return rc;
   rc = hstu_jagged_attn_plan(desc, offsets, num_targets, contextual_len, max_attn_len, workspace,
                              workspace_bytes, stream);
+  if (rc != HSTU_OK) return rc;
+  return hstu_jagged_attn_run(desc, q, k, v, u, offsets, timestamps, num_targets, contextual_len,
+                              max_attn_len, alpha, n_scale, pos_table, time_table, out,
+                              workspace, workspace_bytes, stream);
+}
+
+int hstu_jagged_attn_fwd_candidates(const hstu_attn_desc* desc, const void* q, const void* k,
+                         const void* v, const void* u, const int32_t* offsets,
+                         const int64_t* timestamps, const int32_t* num_targets,
+                         int32_t contextual_len, int32_t max_attn_len, float alpha,
+                         float n_scale, const float* pos_table, const float* time_table,
+                         void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  // Validate everything before the first launch so that a bad call enqueues nothing.
+  int rc = check_desc(desc);
+  if (rc != HSTU_OK) return rc;
+  rc = check_plan_args(desc, offsets, contextual_len, max_attn_len, workspace, workspace_bytes);
+  if (rc != HSTU_OK) return rc;
+  if (desc->num_seqs == 0 || desc->total_tokens == 0) return HSTU_OK;
+  rc = check_run_args(desc, q, k, v, u, timestamps, alpha, n_scale, pos_table, time_table, out);
+  if (rc != HSTU_OK) return rc;
+  rc = hstu_jagged_attn_plan_candidates(desc, offsets, num_targets, contextual_len,
+                                        max_attn_len, workspace, workspace_bytes, stream);
   if (rc != HSTU_OK) return rc;
   return hstu_jagged_attn_run(desc, q, k, v, u, offsets, timestamps, num_targets, contextual_len,
                               max_attn_len, alpha, n_scale, pos_table, time_table, out,

@@ -90,16 +90,14 @@ __host__ __device__ inline void tile_key_range(const SeqGeom& g, int i0, int i1,
 }
 
 // Work list.  The scheduler lists the (sequence, head, query tile) items
-// sequence by sequence, the tiles of one (sequence, head) together, and
-// balances their cost (key tiles plus a fixed per-item term) over the
-// workgroups of the persistent attention launch.  The MI355X dispatches
-// workgroup g to XCD g % 8 and each XCD has its own L2, so the items are cut
-// into 8 consecutive, equally expensive portions, one per XCD; inside a
-// portion they are dealt round-robin to the XCD's workgroups, so that the
+// sequence by sequence, the tiles of one (sequence, head) together, deals them
+// round-robin to the workgroups of the persistent attention launch and cuts
+// the dealt order into equal-cost shares (cost = key tiles plus a fixed
+// per-item term), placing consecutive shares on one XCD (the MI355X
+// dispatches workgroup g to XCD g % 8; each XCD has its own L2) so that the
 // workgroups running side by side work on neighbouring query tiles, which
-// share most of their keys and values.  The dealt order is then cut into
-// equal shares, one per workgroup; an item a share boundary cuts is split
-// along its key tiles into chunks.  The aggregation is a plain sum over
+// share most of their keys and values.  An item a share boundary cuts is
+// split along its key tiles into chunks.  The aggregation is a plain sum over
 // keys, so every chunk writes its fp32 partial output and the chunk that
 // finishes last adds them in chunk order and runs the epilogue.
 constexpr int kXcds = 8;
@@ -107,6 +105,9 @@ constexpr int kMaxGrid = 1024;      // most workgroups one plan serves
 constexpr int kCostOverhead = 6;    // fixed cost of an item, in key tiles
 constexpr int kMinChunk = 8;        // fewest key tiles of a chunk of a split item
 constexpr int kPlanLdsItems = 4096; // plans of up to this many items stay in LDS
+// Unit flag (bit 31 of the chunk word): the unit's query tiles start at the
+// history end n_h instead of row 0 (candidates-only plans).
+constexpr int kUnitCandRows = int(0x80000000u);
 
 struct PlanLayout {
   size_t hdr_off;      // int32[64]: [0] workgroups the plan was made for
@@ -117,7 +118,7 @@ struct PlanLayout {
   size_t part_off;     // float[slots_max * slot_floats]: partial outputs of chunks
   size_t seq_off;      // int32[4 * (B + 1)]: per-sequence scratch of large batches
   size_t item_off;     // per-item scratch of large plans: int32 cost[items_max + 1],
-                       //   int32 order[items_max], int64 line[items_max + 1],
+                       //   int32 seq[items_max + 1], int64 line[items_max + 1],
                        //   int64 ubase[items_max + 1]
   size_t total;
   int64_t items_max;   // bound on sum_b ceil(L_b / BM) * H
@@ -166,6 +167,7 @@ struct PlanArgs {
   int32_t max_attn_len;
   int32_t items_max;     // capacity of the item scratch
   int32_t n_wg;          // workgroups of the attention launch (<= kMaxGrid)
+  int32_t cand_only;     // 1: only the candidate rows [n_h, L), tiled from n_h
   int32_t* hdr;
   int4* units;
   int32_t* wg;

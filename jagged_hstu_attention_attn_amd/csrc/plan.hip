@@ -9,23 +9,24 @@
 //   1. items are the (sequence, head, 128-row query tile) triples, sequence
 //      by sequence, the tiles of one (sequence, head) together with the last
 //      (most expensive) tile first; an item costs the key tiles its mask lets
-//      it reach (tile_key_range) plus a fixed term;
-//   2. the items are cut into 8 consecutive portions of about equal cost,
-//      one per XCD (an item goes to the portion holding its midpoint);
-//   3. inside the portion of XCD x the items are dealt round-robin to the
-//      W_x workgroups of that XCD, and the dealt order (workgroup 0's items,
-//      then workgroup 1's, ...) is cut into W_x shares of equal cost
-//      T_x = ceil(C_x / W_x).  With items of equal cost the shares are the
-//      dealt columns, so workgroups running side by side process neighbouring
-//      query tiles, whose key/value rows their XCD's L2 then serves once;
+//      it reach (tile_key_range) plus a fixed term.  A candidates-only plan
+//      tiles just the candidate rows [n_h, L) of each sequence, from n_h;
+//   2. items are dealt round-robin to n_wg columns (item t * n_wg + c goes to
+//      column c in round t) and the columns are laid end to end on one line
+//      (the dealt order), which is cut into n_wg shares of equal cost;
+//   3. share r runs on workgroup x + 8w with x = r / (n_wg / 8): consecutive
+//      shares share an XCD (the MI355X dispatches workgroup g to XCD g % 8
+//      and each XCD has its own L2).  With items of equal cost the shares are
+//      the columns, so in every round the 64 workgroups of an XCD process 64
+//      neighbouring query tiles, whose key/value rows that L2 serves once;
 //   4. an item that a share boundary cuts is split there along its key tiles
 //      (proportionally, never into chunks under kMinChunk tiles): the
 //      pointwise aggregation is a sum over keys, so the chunks' partial
 //      outputs add up exactly to the item's output.
 //
-// One workgroup of 1024 threads; the per-item arrays stay in LDS up to
-// kPlanLdsItems items.  Everything stays on the device, so the caller's
-// stream never synchronises with the host.
+// One workgroup of 1024 threads, five phases; the per-item arrays stay in LDS
+// up to kPlanLdsItems items.  Everything stays on the device, so the
+// caller's stream never synchronises with the host.
 #include <type_traits>
 
 #include "hstu_device.hpp"
@@ -76,7 +77,9 @@ __device__ inline V block_excl_scan(V x, V* ws, V& total) {
 }
 
 // Chunks of an item spanning cost units [P, P + cost) of a line cut into
-// shares of T units.  Each multiple rT strictly inside the span is a candidate
+// shares of T units.  An item under 2 * kMinChunk tiles stays whole and goes
+// to the share holding its midpoint.  Otherwise each multiple rT strictly
+// inside the span is a candidate
 // cut at tile offset t = floor((rT - P) * tiles / cost).  A cut that would
 // close a chunk of fewer than kMinChunk tiles instead hands the open chunk to
 // share r; a cut that would leave fewer than kMinChunk tiles after it is
@@ -86,6 +89,10 @@ __device__ inline V block_excl_scan(V x, V* ws, V& total) {
 template <typename I, typename F>
 __device__ inline int item_chunks(I P, int cost, int tiles, I T, F&& f) {
   using U = typename std::make_unsigned<I>::type;   // products stay below 2^(bits of I)
+  if (tiles < 2 * kMinChunk) {   // never split: the share holding its midpoint takes it
+    f(0, 0, tiles, (int)((P + cost / 2) / T));
+    return 1;
+  }
   const I r0 = P / T, r1 = (P + cost - 1) / T;
   int j = 0, tb = 0;
   I owner = r0;
@@ -122,13 +129,18 @@ struct ItemGeo {
   int b, h, qt, kt_lo, kt_hi, n_h;
 };
 
+// First query row of a sequence's tiles: 0, or the history end when only the
+// candidate rows are computed.
+__device__ inline int row_base(int n_h, bool cand_only) { return cand_only ? n_h : 0; }
+
 // Item k of sequence b (head-major, last query tile first).
 __device__ inline ItemGeo item_geo_of(int k, int b, const int32_t* base, const int32_t* slen,
                                       const int32_t* hist, int contextual_len,
-                                      int max_attn_len) {
+                                      int max_attn_len, bool cand_only) {
   ItemGeo r;
   r.b = b;
-  const int L = slen[b], nq = (L + kBM - 1) / kBM;
+  const int L = slen[b], i_b = row_base(hist[b], cand_only);
+  const int nq = (L - i_b + kBM - 1) / kBM;
   const int t = k - base[b];
   r.h = t / nq;
   r.qt = nq - 1 - (t - r.h * nq);
@@ -137,7 +149,7 @@ __device__ inline ItemGeo item_geo_of(int k, int b, const int32_t* base, const i
   g.n_h = hist[b];
   g.c = clampi(contextual_len, 0, g.n_h);
   g.W = max_attn_len;
-  const int i0 = r.qt * kBM, i1 = min(i0 + kBM, L);
+  const int i0 = i_b + r.qt * kBM, i1 = min(i0 + kBM, L);
   int jlo, jhi;
   tile_key_range(g, i0, i1, jlo, jhi);
   r.kt_lo = jlo / kBN;
@@ -159,6 +171,26 @@ __device__ inline int seq_of(int k, const int32_t* base, int B) {
 // I: type of the cost prefix sums (int when they fit, else int64_t).  LDS:
 // the per-item arrays live in LDS (at most kPlanLdsItems items) instead of
 // the workspace.
+// Dealt order: item i = t * n_wg + c (round t, column c) sits at position
+// start(c) + t of the line, columns one after another, where column c holds
+// `full` + (c < extra) items.  Returns the item at line position j.
+__device__ inline int dealt_item(int j, int n, int n_wg) {
+  const int full = n / n_wg, extra = n - full * n_wg;
+  const int big = extra * (full + 1);   // positions held by the longer columns
+  int c, t;
+  if (j < big) {
+    c = j / (full + 1);
+    t = j - c * (full + 1);
+  } else {
+    c = extra + (j - big) / full;
+    t = j - big - (c - extra) * full;
+  }
+  return t * n_wg + c;
+}
+
+// I: type of the cost prefix sums (int when they fit, else int64_t).  LDS:
+// the per-item arrays live in LDS (at most kPlanLdsItems items) instead of
+// the workspace.
 template <typename I, bool LDS>
 __global__ __launch_bounds__(kPlanThreads) void hstu_plan_kernel(PlanArgs a) {
   constexpr int kItems = LDS ? kPlanLdsItems : 1;
@@ -167,16 +199,15 @@ __global__ __launch_bounds__(kPlanThreads) void hstu_plan_kernel(PlanArgs a) {
   __shared__ I s_ws[kPlanThreads / 64];
   __shared__ int s_ws32[kPlanThreads / 64];
   __shared__ int s_cnt[kMaxGrid];
-  __shared__ int s_xa[kXcds + 1];                 // first item of each XCD's portion
   __shared__ int s_seq[4 * (kPlanLdsSeqs + 1)];
   __shared__ int s_cost[kItems + 1];
-  __shared__ int s_order[kItems];
   __shared__ int s_iseq[kItems];
   __shared__ I s_line[kItems + 1];
   __shared__ I s_ub[kItems + 1];
 
   const int tid = threadIdx.x;
   const int B = a.num_seqs, H = a.num_heads, n_wg = a.n_wg;
+  const bool cand = a.cand_only != 0;
   int32_t* seq = B <= kPlanLdsSeqs ? s_seq : a.seq_scratch;
   const int LD = B <= kPlanLdsSeqs ? kPlanLdsSeqs + 1 : B + 1;
   int32_t* base = seq;            // [B + 1] first item of each sequence
@@ -198,7 +229,7 @@ __global__ __launch_bounds__(kPlanThreads) void hstu_plan_kernel(PlanArgs a) {
       start[b] = s0;
       slen[b] = L;
       hist[b] = L - clampi(nt, 0, L);
-      cnt = (L + kBM - 1) / kBM * H;
+      cnt = (L - row_base(hist[b], cand) + kBM - 1) / kBM * H;
     }
     int tot;
     const int ex = block_excl_scan(cnt, s_ws32, tot);
@@ -206,97 +237,50 @@ __global__ __launch_bounds__(kPlanThreads) void hstu_plan_kernel(PlanArgs a) {
     carry += tot;
   }
   const int n = min(carry, a.items_max);   // never beyond the scratch's capacity
-  if (tid <= kXcds) s_xa[tid] = n;
 
   int* cost = s_cost;
-  int* order = s_order;
+  int* iseq = s_iseq;
   I* line = s_line;
   I* ub = s_ub;
   if constexpr (!LDS) {
     const size_t im = (size_t)a.items_max + 1;
     cost = reinterpret_cast<int*>(a.item_scratch);
-    order = cost + im;
+    iseq = cost + im;
     line = reinterpret_cast<I*>(a.item_scratch + ((2 * sizeof(int) * im + 15) & ~size_t(15)));
     ub = line + im;
   }
   __syncthreads();
 
-  // 2. Item costs and their prefix sums in list order.
+  // 2. Costs in dealt order and their prefix sums (the line).
   I ccarry = 0;
-  for (int k0 = 0; k0 < n; k0 += kPlanThreads) {
-    const int k = k0 + tid;
-    int c = 0;
-    if (k < n) {
-      const int b = seq_of(k, base, B);
-      const ItemGeo g = item_geo_of(k, b, base, slen, hist, a.contextual_len, a.max_attn_len);
-      c = g.kt_hi - g.kt_lo + 1 + kCostOverhead;
-      cost[k] = c;
-      if constexpr (LDS) s_iseq[k] = b;
-    }
-    I tot;
-    const I ex = block_excl_scan((I)c, s_ws, tot);
-    if (k < n) line[k] = ccarry + ex;
-    ccarry += tot;
-  }
-  const I C = ccarry;
-  __syncthreads();
-
-  // 3. XCD portions: item k goes to XCD floor(8 * midpoint / C).
-  using U = typename std::make_unsigned<I>::type;
-  for (int k = tid; k < n; k += kPlanThreads) {
-    auto xcd_of = [&](int i) {
-      const U m = (U)(2 * line[i] + cost[i]) * (U)(kXcds / 2) / (U)C;
-      return (int)(m < (U)kXcds ? m : (U)(kXcds - 1));
-    };
-    const int xk = xcd_of(k), xp = k > 0 ? xcd_of(k - 1) : -1;
-    for (int x = xp + 1; x <= xk; ++x) s_xa[x] = k;
-  }
-  __syncthreads();
-
-  // 4. Dealt order inside each portion (column-major over the XCD's workgroups).
-  for (int k = tid; k < n; k += kPlanThreads) {
-    int x = 0;
-    while (x < kXcds - 1 && s_xa[x + 1] <= k) ++x;
-    const int a0 = s_xa[x], nx = s_xa[x + 1] - a0, W = xcd_wgs(n_wg, x);
-    const int i = k - a0, col = i % W, row = i / W;
-    const int full = nx / W, extra = nx % W;
-    order[a0 + col * full + min(col, extra) + row] = k;
-  }
-  __syncthreads();
-
-  // 5. Cost prefix sums in dealt order (portions stay where they were).
-  ccarry = 0;
   for (int j0 = 0; j0 < n; j0 += kPlanThreads) {
     const int j = j0 + tid;
-    const int c = j < n ? cost[order[j]] : 0;
+    int c = 0;
+    if (j < n) {
+      const int k = dealt_item(j, n, n_wg);
+      const int b = seq_of(k, base, B);
+      const ItemGeo g = item_geo_of(k, b, base, slen, hist, a.contextual_len, a.max_attn_len, cand);
+      c = g.kt_hi - g.kt_lo + 1 + kCostOverhead;
+      cost[j] = c;
+      iseq[j] = b;
+    }
     I tot;
     const I ex = block_excl_scan((I)c, s_ws, tot);
     if (j < n) line[j] = ccarry + ex;
     ccarry += tot;
   }
-  if (tid == 0) line[n] = ccarry;
+  const I C = ccarry;
+  const I T = C > 0 ? (C + n_wg - 1) / n_wg : 1;   // cost of one share
   __syncthreads();
 
-  // 6. Chunks per dealt item; prefix sums of the units and of the split chunks.
-  auto share_of = [&](int j, int& x, I& P, I& T) {
-    x = 0;
-    while (x < kXcds - 1 && s_xa[x + 1] <= j) ++x;
-    const I p0 = line[s_xa[x]];
-    const I Cx = line[s_xa[x + 1]] - p0;
-    const int W = xcd_wgs(n_wg, x);
-    P = line[j] - p0;
-    T = Cx > 0 ? (Cx + W - 1) / W : 1;
-  };
+  // 3. Chunks per item; prefix sums of the units and of the split chunks.
   I ucarry = 0;
   for (int j0 = 0; j0 < n; j0 += kPlanThreads) {
     const int j = j0 + tid;
     I packed = 0;
     if (j < n) {
-      int x;
-      I P, T;
-      share_of(j, x, P, T);
-      const int c = cost[order[j]];
-      const int nc = item_chunks(P, c, c - kCostOverhead, T, [](int, int, int, int) {});
+      const int c = cost[j];
+      const int nc = item_chunks(line[j], c, c - kCostOverhead, T, [](int, int, int, int) {});
       packed = (I)nc | ((I)(nc > 1 ? nc : 0) << kShift);
     }
     I tot;
@@ -307,31 +291,24 @@ __global__ __launch_bounds__(kPlanThreads) void hstu_plan_kernel(PlanArgs a) {
   if (tid == 0) ub[n] = ucarry;
   __syncthreads();
 
-  // 7. Units, one per chunk in dealt order; count the units of every workgroup.
+  // 4. Units, one per chunk in line order; count the units of every workgroup.
   for (int j = tid; j < n; j += kPlanThreads) {
-    int x;
-    I P, T;
-    share_of(j, x, P, T);
-    const int k = order[j];
-    int b;
-    if constexpr (LDS) b = s_iseq[k];
-    else b = seq_of(k, base, B);
-    const ItemGeo g = item_geo_of(k, b, base, slen, hist, a.contextual_len, a.max_attn_len);
+    const int k = dealt_item(j, n, n_wg), b = iseq[j];
+    const ItemGeo g = item_geo_of(k, b, base, slen, hist, a.contextual_len, a.max_attn_len, cand);
     const int4 it = make_int4(start[b], slen[b], g.n_h, g.qt * H + g.h);
     const int u0 = (int)(ub[j] & kLow), slot0 = (int)(ub[j] >> kShift);
     const int nc = (int)(ub[j + 1] & kLow) - u0;
-    item_chunks(P, cost[k], g.kt_hi - g.kt_lo + 1, T, [&](int c, int tb, int te, int r) {
+    item_chunks(line[j], cost[j], g.kt_hi - g.kt_lo + 1, T, [&](int c, int tb, int te, int r) {
       a.units[2 * (u0 + c)] = it;
-      a.units[2 * (u0 + c) + 1] =
-          make_int4(g.kt_lo + tb, g.kt_lo + te - 1, nc > 1 ? slot0 : -1, (c << 16) | nc);
-      atomicAdd(&s_cnt[x + kXcds * r], 1);
+      a.units[2 * (u0 + c) + 1] = make_int4(g.kt_lo + tb, g.kt_lo + te - 1, nc > 1 ? slot0 : -1,
+                                            (cand ? kUnitCandRows : 0) | (c << 16) | nc);
+      atomicAdd(&s_cnt[share_wg(r, n_wg)], 1);
     });
     if (nc > 1) a.counters[slot0] = 0;
   }
   __syncthreads();
 
-  // 8. First unit and unit count of every workgroup (shares XCD-major, in
-  //    the order their units were written).
+  // 5. First unit and unit count of every workgroup (shares in line order).
   int rcarry = 0;
   for (int f0 = 0; f0 < n_wg; f0 += kPlanThreads) {
     const int f = f0 + tid;

@@ -308,6 +308,102 @@ def test_large_batch_plan(dtype, d):
 
 
 # ---------------------------------------------------------------------------
+# Candidate rows only ("Scaling HSTU", section "Many candidates make reuse
+# valuable"): the candidates of a sequence see its history and themselves, so
+# their outputs can be computed apart from the history rows and in micro-batches.
+# ---------------------------------------------------------------------------
+def _candidates_forward(inp, sentinel=-5.0):
+    dev = to_device(inp, DEV)
+    N, H, dv = inp.total_tokens, inp.num_heads, inp.d_v
+    out = torch.full((N, H, dv), sentinel, dtype=dev["q"].dtype, device=DEV)
+    jagged_attn_fwd(dev["q"], dev["k"], dev["v"], dev["u"], dev["offsets"], out=out,
+                    candidates_only=True, **call_kwargs(inp, dev))
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64)
+
+
+def _candidate_rows(inp):
+    rows = []
+    for b in range(inp.num_seqs):
+        s0, s1 = int(inp.offsets[b]), int(inp.offsets[b + 1])
+        nt = 0 if inp.num_targets is None else int(inp.num_targets[b])
+        rows.extend(range(s1 - min(max(nt, 0), s1 - s0), s1))
+    return np.array(rows, dtype=np.int64)
+
+
+@pytest.mark.parametrize("name,kw", [("ranking", dict(num_seqs=24)),
+                                     ("windowed", dict(num_seqs=2))])
+def test_candidates_only(name, kw):
+    inp = make_inputs(name, **kw)
+    got = _candidates_forward(inp)
+    rows = _candidate_rows(inp)
+    hist = np.setdiff1d(np.arange(inp.total_tokens), rows)
+    assert np.all(got[hist] == -5.0), "history rows were written"
+    assert_close(got, ora(inp, rows=rows), "bf16", rows=rows)
+
+
+def _subset(inp, keep_rows, offsets, num_targets):
+    out = JaggedInputs(**{f: getattr(inp, f) for f in inp.__dataclass_fields__})
+    for name in ("q", "k", "v", "u"):
+        setattr(out, name, getattr(inp, name)[keep_rows].copy())
+    if inp.timestamps is not None:
+        out.timestamps = inp.timestamps[keep_rows].copy()
+    out.offsets = np.asarray(offsets, dtype=np.int32)
+    out.num_targets = np.asarray(num_targets, dtype=np.int32)
+    return out
+
+
+def test_candidate_independence_bitwise():
+    """A candidate's output does not depend on the other candidates: changing
+    their q, k, v, u and timestamps leaves its row bitwise unchanged."""
+    inp = make_custom([300, 45, 129], num_heads=2, d_qk=128, d_v=128, dtype="bf16", seed=33,
+                      num_targets=[60, 60, 60], contextual_len=4, pos_len=512, time_len=64,
+                      alpha=0.2, n_scale=400.0)
+    keep = []   # candidates 20..39 of each sequence stay, the others change
+    others = []
+    for b in range(3):
+        s1 = int(inp.offsets[b + 1])
+        keep.extend(range(s1 - 40, s1 - 20))
+        others.extend(list(range(s1 - 60, s1 - 40)) + list(range(s1 - 20, s1)))
+    a = _candidates_forward(inp)
+    b = _candidates_forward(_perturb(inp, np.array(others)))
+    assert np.array_equal(a[keep], b[keep])
+
+
+@pytest.mark.parametrize("dtype,d,tol", [("f32", 64, 1e-6), ("bf16", 128, 1e-2)])
+def test_candidate_microbatches(dtype, d, tol):
+    """Three users, each with a history and 60 candidates.  Computing the
+    candidates in micro-batches of 20 (each laid out after its user's
+    history) gives the rows of the all-at-once computation.  The position
+    bias uses the raw i - j, and a micro-batch moves its candidates to other
+    positions, so this holds exactly with the time bias alone (timestamps
+    travel with their tokens)."""
+    hist = [300, 45, 129]
+    lengths = [h + 60 for h in hist]
+    inp = make_custom(lengths, num_heads=2, d_qk=d, d_v=d, dtype=dtype, seed=31,
+                      num_targets=[60, 60, 60], contextual_len=4, time_len=64,
+                      alpha=0.2, n_scale=400.0)
+    full = _candidates_forward(inp)
+    for m in range(3):
+        keep, offs, nts = [], [0], []
+        for b, h in enumerate(hist):
+            s0 = int(inp.offsets[b])
+            keep.extend(range(s0, s0 + h))
+            keep.extend(range(s0 + h + 20 * m, s0 + h + 20 * m + 20))
+            offs.append(offs[-1] + h + 20)
+            nts.append(20)
+        mb = _subset(inp, np.array(keep), offs, nts)
+        got = _candidates_forward(mb)
+        for b, h in enumerate(hist):
+            g = got[offs[b] + h: offs[b] + h + 20]
+            f = full[int(inp.offsets[b]) + h + 20 * m: int(inp.offsets[b]) + h + 20 * m + 20]
+            scale = np.abs(f).max()
+            assert np.abs(g - f).max() <= tol * scale
+        rows = _candidate_rows(mb)
+        assert_close(got, ora(mb, rows=rows), dtype, rows=rows)
+
+
+# ---------------------------------------------------------------------------
 # Information flow on the device, bitwise ("Do not copy softmax masking
 # mechanically": change future inputs, earlier outputs must not move).
 # ---------------------------------------------------------------------------
