@@ -79,8 +79,8 @@ __device__ inline V block_excl_scan(V x, V* ws, V& total) {
 // Chunks of an item spanning cost units [P, P + cost) of a line cut into
 // shares of T units.  An item under 2 * kMinChunk tiles stays whole and goes
 // to the share holding its midpoint.  Otherwise each multiple rT strictly
-// inside the span is a candidate
-// cut at tile offset t = floor((rT - P) * tiles / cost).  A cut that would
+// inside the span is a candidate cut at tile offset
+// t = floor((rT - P) * tiles / cost).  A cut that would
 // close a chunk of fewer than kMinChunk tiles instead hands the open chunk to
 // share r; a cut that would leave fewer than kMinChunk tiles after it is
 // dropped.  f(j, tb, te, r): chunk j covers tile offsets [tb, te) and belongs
@@ -168,9 +168,6 @@ __device__ inline int seq_of(int k, const int32_t* base, int B) {
   return lo;
 }
 
-// I: type of the cost prefix sums (int when they fit, else int64_t).  LDS:
-// the per-item arrays live in LDS (at most kPlanLdsItems items) instead of
-// the workspace.
 // Dealt order: item i = t * n_wg + c (round t, column c) sits at position
 // start(c) + t of the line, columns one after another, where column c holds
 // `full` + (c < extra) items.  Returns the item at line position j.
