@@ -30,6 +30,7 @@ _LIB = os.path.join(_HERE, "libhstu_oracle.so")
 
 EPILOGUE_LN_U = 0
 EPILOGUE_NONE = 1
+EPILOGUE_LN_ALL_U = 2   # LayerNorm over all heads' d_v of a token, then * u
 
 _lib = None
 
@@ -230,6 +231,12 @@ def dense_forward(inp, *, epilogue=EPILOGUE_LN_U) -> np.ndarray:
         mu = O.mean(-1, keepdims=True)
         var = ((O - mu) ** 2).mean(-1, keepdims=True)
         O = (O - mu) / np.sqrt(var + float(np.float32(inp.eps))) * Up
+    elif epilogue == EPILOGUE_LN_ALL_U:
+        Ot = np.swapaxes(O, 1, 2).reshape(B, Lpad, H * dv)    # a token's heads side by side
+        mu = Ot.mean(-1, keepdims=True)
+        var = ((Ot - mu) ** 2).mean(-1, keepdims=True)
+        Ot = (Ot - mu) / np.sqrt(var + float(np.float32(inp.eps)))
+        O = np.swapaxes(Ot.reshape(B, Lpad, H, dv), 1, 2) * Up
     for b in range(B):
         s, e = int(inp.offsets[b]), int(inp.offsets[b + 1])
         out[s:e] = O[b, :, : e - s].transpose(1, 0, 2)

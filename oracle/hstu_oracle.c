@@ -24,6 +24,9 @@
  *       are simply never evaluated, which is the same value and cannot make NaN.
  *   o_i  = sum_j a_ij v_j
  *   out_i = LayerNorm(o_i) * u_i   (or o_i itself with epilogue NONE)
+ * With epilogue LN_ALL_U the LayerNorm runs over the concatenation of all
+ * heads' o_i of a token (H * d_v values) instead of each head's d_v values;
+ * the gate by u_i is the same.
  *       The norm-then-gate step U_i (.) Norm(sum_j A_ij V_j) of the teaching
  *       equation ("Similar shape, different aggregation"; "Follow the U, V, Q
  *       and K branches").
@@ -55,6 +58,7 @@
 
 #define ORACLE_EPILOGUE_LN_U 0
 #define ORACLE_EPILOGUE_NONE 1
+#define ORACLE_EPILOGUE_LN_ALL_U 2
 
 static int64_t clamp64(int64_t x, int64_t lo, int64_t hi) {
   return x < lo ? lo : (x > hi ? hi : x);
@@ -215,7 +219,7 @@ int hstu_oracle_fwd(int num_seqs, const int32_t* offsets, int num_heads, int d_q
           for (int e = 0; e < d_v; ++e) o[e] += a * vj[e];
         }
         double* dst = out + (base + i) * ld_out + (int64_t)h * d_v;
-        if (epilogue == ORACLE_EPILOGUE_NONE) {
+        if (epilogue == ORACLE_EPILOGUE_NONE || epilogue == ORACLE_EPILOGUE_LN_ALL_U) {
           for (int e = 0; e < d_v; ++e) dst[e] = o[e];
         } else {
           double mean = 0.0;
@@ -233,6 +237,30 @@ int hstu_oracle_fwd(int num_seqs, const int32_t* offsets, int num_heads, int d_q
     free(o);
   }
   free(items);
+  if (epilogue == ORACLE_EPILOGUE_LN_ALL_U) {
+    /* second pass: each token's H * d_v raw outputs, normalised together */
+    int64_t n_tok = num_seqs > 0 ? (int64_t)offsets[num_seqs] : 0;
+    int64_t width = (int64_t)num_heads * d_v;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < n_tok; ++t) {
+      if (row_select && !row_select[t]) continue;
+      double* row = out + t * ld_out;   /* heads are consecutive d_v blocks */
+      double mean = 0.0;
+      for (int64_t e = 0; e < width; ++e) mean += row[e];
+      mean /= (double)width;
+      double var = 0.0;
+      for (int64_t e = 0; e < width; ++e) var += (row[e] - mean) * (row[e] - mean);
+      var /= (double)width;
+      double rstd = 1.0 / sqrt(var + eps);
+      for (int h = 0; h < num_heads; ++h) {
+        const double* ui = u + t * ld_u + (int64_t)h * d_v;
+        for (int e = 0; e < d_v; ++e) {
+          double* x = row + (int64_t)h * d_v + e;
+          *x = (*x - mean) * rstd * ui[e];
+        }
+      }
+    }
+  }
   return 0;
 }
 

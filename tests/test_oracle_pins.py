@@ -155,7 +155,7 @@ def _random_case(seed):
 @pytest.mark.parametrize("seed", range(40))
 def test_oracle_equals_dense_bruteforce(oracle_mod, seed):
     inp = _random_case(seed)
-    for ep in (oracle_mod.EPILOGUE_NONE, oracle_mod.EPILOGUE_LN_U):
+    for ep in (oracle_mod.EPILOGUE_NONE, oracle_mod.EPILOGUE_LN_U, oracle_mod.EPILOGUE_LN_ALL_U):
         a = oracle_mod.forward(inp, epilogue=ep)
         b = oracle_mod.dense_forward(inp, epilogue=ep)
         scale = max(1.0, np.abs(b).max())
@@ -374,3 +374,36 @@ def test_padding_arithmetic_tiny_workload(oracle_mod):
     assert round(len(L) * L.max() ** 2 / float((L ** 2).sum()), 3) == 2.970
     assert oracle_mod.count_allowed(inp.offsets) == 505605
     assert inp.n_scale == 1000.0
+
+
+# ---------------------------------------------------------------------------
+# LayerNorm over all heads of a token (the variant that normalises the
+# concatenated H * d_v outputs instead of each head's d_v; "HSTU tensor by
+# tensor", section "Similar shape, different aggregation", norm then U gate).
+# ---------------------------------------------------------------------------
+def test_ln_all_heads_reduces_to_per_head_for_one_head(oracle_mod):
+    inp = make_custom([9, 40, 3], num_heads=1, d_qk=8, d_v=8, seed=41, num_targets=[2, 5, 0],
+                      pos_len=32, time_len=16, alpha=0.5)
+    a = oracle_mod.forward(inp, epilogue=oracle_mod.EPILOGUE_LN_ALL_U)
+    b = oracle_mod.forward(inp, epilogue=oracle_mod.EPILOGUE_LN_U)
+    assert np.array_equal(a, b)
+
+
+def test_ln_all_heads_moments_and_scale_invariance(oracle_mod):
+    """With u = 1 every token's H * d_v outputs have mean 0 and a mean square
+    of at most 1 (exactly var / (var + eps)); scaling v by 1000 leaves them
+    unchanged up to the epsilon's share; per-head normalisation does not give
+    zero-mean heads' concatenation a unit second moment per head."""
+    inp = make_custom([30, 17], num_heads=3, d_qk=8, d_v=8, seed=42, pos_len=64, alpha=0.7,
+                      eps=1e-12)
+    inp.u = np.ones_like(inp.u)
+    a = oracle_mod.forward(inp, epilogue=oracle_mod.EPILOGUE_LN_ALL_U).reshape(inp.total_tokens, -1)
+    assert np.abs(a.mean(-1)).max() < 1e-12
+    ms = (a ** 2).mean(-1)
+    assert np.all(ms <= 1.0 + 1e-12) and np.all(ms > 1.0 - 1e-6)
+    inp.v = inp.v * 1000.0
+    b = oracle_mod.forward(inp, epilogue=oracle_mod.EPILOGUE_LN_ALL_U).reshape(inp.total_tokens, -1)
+    assert np.abs(a - b).max() < 1e-6
+    per_head = oracle_mod.forward(inp, epilogue=oracle_mod.EPILOGUE_LN_U).reshape(
+        inp.total_tokens, 3, 8)
+    assert not np.allclose(per_head.reshape(inp.total_tokens, -1), b, atol=1e-3)
