@@ -152,6 +152,8 @@ def main() -> int:
     ap.add_argument("--no-flush", action="store_true", help="keep inputs cache-resident")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
+    ap.add_argument("--epilogue", default="ln_u", choices=["ln_u", "none", "ln_all_u"],
+                    help="per-head LayerNorm * U (default), none, or one LayerNorm over all heads")
     ap.add_argument("--candidates-only", action="store_true",
                     help="compute only the candidate rows (history reused; no CPU baseline)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -183,7 +185,8 @@ def main() -> int:
     inp = make_inputs(args.workload, seed=args.seed)
     dev = to_device(inp, "cuda")
     call = JaggedAttnCall(dev["q"], dev["k"], dev["v"], dev["u"], dev["offsets"],
-                          candidates_only=args.candidates_only, **call_kwargs(inp, dev))
+                          candidates_only=args.candidates_only, epilogue=args.epilogue,
+                          **call_kwargs(inp, dev))
     if args.candidates_only:
         pairs, flops, byts = candidate_rows_work(inp)
         args.no_cpu_baseline = True
@@ -236,7 +239,8 @@ def main() -> int:
         achieved = flops / (attn * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                 "frac": achieved / peak}
-    roof["traffic"] = None if args.candidates_only else traffic_from_profile(args.workload)
+    roof["traffic"] = (None if args.candidates_only or args.epilogue != "ln_u"
+                       else traffic_from_profile(args.workload))
     roof["kernel"] = "hstu_attn_fwd_kernel"
     roof["kernel_us"] = attn * 1e3
     roof["algorithmic_bytes"] = byts
@@ -258,6 +262,7 @@ def main() -> int:
         "config": {
             "workload": args.workload,
             "rows": "candidates" if args.candidates_only else "all",
+            "epilogue": args.epilogue,
             "num_seqs": inp.num_seqs,
             "total_tokens": inp.total_tokens,
             "num_heads": inp.num_heads,

@@ -13,6 +13,7 @@
  *   o_i   = sum_j a_ij * v_j
  *   out_i = LayerNorm(o_i) * u_i        (HSTU_EPILOGUE_LN_U)
  *         = o_i                         (HSTU_EPILOGUE_NONE)
+ *         = LayerNorm over all heads of the token, * u_i   (HSTU_EPILOGUE_LN_ALL_U)
  *
  * This is the pointwise SiLU aggregation with relative position / time bias
  * and the norm-then-U gating of "HSTU tensor by tensor: SiLU aggregation,
@@ -79,7 +80,18 @@ typedef enum {
 
 typedef enum { HSTU_DTYPE_F32 = 0, HSTU_DTYPE_BF16 = 1 } hstu_dtype;
 
-typedef enum { HSTU_EPILOGUE_LN_U = 0, HSTU_EPILOGUE_NONE = 1 } hstu_epilogue;
+/*
+ * HSTU_EPILOGUE_LN_ALL_U: the same gate with one LayerNorm over all H * d_v
+ * values of a token (all heads together) instead of one per (token, head);
+ * the attention writes O / n_scale and a second pass normalises each token in
+ * place (for bf16 the raw outputs are rounded to bf16 in between).  Requires
+ * H * d_v <= 4096 (bf16) or 2048 (fp32).
+ */
+typedef enum {
+  HSTU_EPILOGUE_LN_U = 0,
+  HSTU_EPILOGUE_NONE = 1,
+  HSTU_EPILOGUE_LN_ALL_U = 2
+} hstu_epilogue;
 
 /* Shapes, element type and strides of one call. */
 typedef struct {

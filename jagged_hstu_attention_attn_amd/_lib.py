@@ -21,6 +21,7 @@ HSTU_DTYPE_F32 = 0
 HSTU_DTYPE_BF16 = 1
 HSTU_EPILOGUE_LN_U = 0
 HSTU_EPILOGUE_NONE = 1
+HSTU_EPILOGUE_LN_ALL_U = 2
 
 # every function the header declares
 EXPORTS = (

@@ -27,7 +27,8 @@ __all__ = ["jagged_attn_fwd", "plan", "run", "make_desc", "workspace_bytes", "va
            "JaggedAttnCall"]
 
 _DTYPES = {torch.float32: _lib.HSTU_DTYPE_F32, torch.bfloat16: _lib.HSTU_DTYPE_BF16}
-_EPILOGUES = {"ln_u": _lib.HSTU_EPILOGUE_LN_U, "none": _lib.HSTU_EPILOGUE_NONE}
+_EPILOGUES = {"ln_u": _lib.HSTU_EPILOGUE_LN_U, "none": _lib.HSTU_EPILOGUE_NONE,
+              "ln_all_u": _lib.HSTU_EPILOGUE_LN_ALL_U}
 
 
 def _ptr(t: Optional[torch.Tensor]):

@@ -33,7 +33,8 @@ int check_desc(const hstu_attn_desc* d) {
   if (d->num_heads < 1) return fail(HSTU_ERR_INVALID_ARG, "num_heads < 1 (%d)", d->num_heads);
   if (d->dtype != HSTU_DTYPE_F32 && d->dtype != HSTU_DTYPE_BF16)
     return fail(HSTU_ERR_INVALID_ARG, "unknown dtype %d", d->dtype);
-  if (d->epilogue != HSTU_EPILOGUE_LN_U && d->epilogue != HSTU_EPILOGUE_NONE)
+  if (d->epilogue != HSTU_EPILOGUE_LN_U && d->epilogue != HSTU_EPILOGUE_NONE &&
+      d->epilogue != HSTU_EPILOGUE_LN_ALL_U)
     return fail(HSTU_ERR_INVALID_ARG, "unknown epilogue %d", d->epilogue);
   if (d->d_qk <= 0 || d->d_v <= 0)
     return fail(HSTU_ERR_INVALID_ARG, "d_qk and d_v must be positive (%d, %d)", d->d_qk, d->d_v);
@@ -47,6 +48,10 @@ int check_desc(const hstu_attn_desc* d) {
                 hstu::kPosMax);
   if (!(d->ln_eps > 0.0f) || !std::isfinite(d->ln_eps))
     return fail(HSTU_ERR_INVALID_ARG, "ln_eps must be positive and finite");
+  if (d->epilogue == HSTU_EPILOGUE_LN_ALL_U &&
+      (int64_t)d->num_heads * d->d_v > hstu::ln_all_heads_max_width(d->dtype))
+    return fail(HSTU_ERR_UNSUPPORTED, "LayerNorm over all heads supports H*d_v <= %d",
+                hstu::ln_all_heads_max_width(d->dtype));
   const int64_t H = d->num_heads;
   const size_t es = elem_size(d->dtype);
   struct {
@@ -250,7 +255,10 @@ int hstu_jagged_attn_run(const hstu_attn_desc* desc, const void* q, const void* 
   a.q = q;
   a.k = k;
   a.v = v;
-  a.u = desc->epilogue == HSTU_EPILOGUE_NONE ? nullptr : u;
+  // LayerNorm over all heads: the attention writes O / n_scale, a second pass
+  // normalises every token's heads together
+  const bool ln_all = desc->epilogue == HSTU_EPILOGUE_LN_ALL_U;
+  a.u = (desc->epilogue == HSTU_EPILOGUE_NONE || ln_all) ? nullptr : u;
   a.out = out;
   a.offsets = offsets;
   a.timestamps = time_table ? timestamps : nullptr;
@@ -273,7 +281,7 @@ int hstu_jagged_attn_run(const hstu_attn_desc* desc, const void* q, const void* 
   a.max_attn_len = max_attn_len;
   a.pos_len = desc->pos_table_len;
   a.time_len = desc->time_table_len;
-  a.epilogue = desc->epilogue;
+  a.epilogue = ln_all ? HSTU_EPILOGUE_NONE : desc->epilogue;
   a.alpha = alpha;
   a.out_scale = (float)(0.69314718055994530942 / (double)n_scale);
   a.ln_eps = desc->ln_eps;
@@ -281,6 +289,24 @@ int hstu_jagged_attn_run(const hstu_attn_desc* desc, const void* q, const void* 
                                          static_cast<hipStream_t>(stream));
   if (e != hipSuccess)
     return fail(HSTU_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
+  if (ln_all) {
+    hstu::LnArgs la;
+    la.out = out;
+    la.u = u;
+    la.ld_out = desc->ld_out;
+    la.ld_u = desc->ld_u;
+    la.offsets = offsets;
+    la.num_targets = num_targets;
+    la.hdr = pp.hdr;
+    la.num_seqs = desc->num_seqs;
+    la.n_tok = desc->total_tokens;
+    la.width = desc->num_heads * desc->d_v;
+    la.eps = desc->ln_eps;
+    const hipError_t e2 = hstu::launch_ln_all_heads(la, desc->dtype,
+                                                    static_cast<hipStream_t>(stream));
+    if (e2 != hipSuccess)
+      return fail(HSTU_ERR_HIP, "LayerNorm launch failed: %s", hipGetErrorString(e2));
+  }
   return HSTU_OK;
 }
 

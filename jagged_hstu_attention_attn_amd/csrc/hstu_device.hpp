@@ -110,7 +110,8 @@ constexpr int kPlanLdsItems = 4096; // plans of up to this many items stay in LD
 constexpr int kUnitCandRows = int(0x80000000u);
 
 struct PlanLayout {
-  size_t hdr_off;      // int32[64]: [0] workgroups the plan was made for
+  size_t hdr_off;      // int32[64]: [0] workgroups the plan was made for,
+                       //   [1] 1 for a candidates-only plan
   size_t units_off;    // int4[2 * units_max]: (seq start, L, n_h, qt*H + h),
                        //   (kt_begin, kt_end, split slot or -1, chunk << 16 | chunks)
   size_t wg_off;       // int32[2 * kMaxGrid]: (first unit, units) per workgroup
@@ -205,6 +206,20 @@ struct AttnArgs {
   float ln_eps;
 };
 
+// Epilogue variant: LayerNorm over all heads of a token, in place on `out`.
+struct LnArgs {
+  void* out;
+  const void* u;
+  int64_t ld_out, ld_u;
+  const int32_t* offsets;
+  const int32_t* num_targets;
+  const int32_t* hdr;    // plan header: [1] != 0 for a candidates-only plan
+  int32_t num_seqs;
+  int32_t n_tok;
+  int32_t width;         // H * d_v
+  float eps;
+};
+
 // Launchers (defined in the .hip files).
 hipError_t launch_plan(const PlanArgs& a, bool compact, hipStream_t stream);
 hipError_t launch_attn(const AttnArgs& a, int dtype, int d_qk, int d_v, int n_wg,
@@ -213,5 +228,7 @@ hipError_t launch_attn(const AttnArgs& a, int dtype, int d_qk, int d_v, int n_wg
 // device (CUs x resident workgroups per CU), or a negative value on error.
 int attn_grid(int dtype, int d_qk, int d_v, int pos_len, int time_len);
 bool attn_supported(int dtype, int d_qk, int d_v);
+int ln_all_heads_max_width(int dtype);
+hipError_t launch_ln_all_heads(const LnArgs& a, int dtype, hipStream_t stream);
 
 }  // namespace hstu

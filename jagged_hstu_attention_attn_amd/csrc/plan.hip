@@ -319,7 +319,10 @@ __global__ __launch_bounds__(kPlanThreads) void hstu_plan_kernel(PlanArgs a) {
     }
     rcarry += tot;
   }
-  if (tid == 0) a.hdr[0] = n_wg;
+  if (tid == 0) {
+    a.hdr[0] = n_wg;
+    a.hdr[1] = cand ? 1 : 0;
+  }
 }
 
 hipError_t launch_plan(const PlanArgs& a, bool compact, hipStream_t stream) {

@@ -41,7 +41,8 @@ def assert_close(gpu, ref, dtype, rows=None):
 
 
 def ora(inp, epilogue="ln_u", rows=None):
-    ep = oracle.EPILOGUE_LN_U if epilogue == "ln_u" else oracle.EPILOGUE_NONE
+    ep = {"ln_u": oracle.EPILOGUE_LN_U, "none": oracle.EPILOGUE_NONE,
+          "ln_all_u": oracle.EPILOGUE_LN_ALL_U}[epilogue]
     return oracle.forward(inp, epilogue=ep, rows=rows)
 
 
@@ -401,6 +402,34 @@ def test_candidate_microbatches(dtype, d, tol):
             assert np.abs(g - f).max() <= tol * scale
         rows = _candidate_rows(mb)
         assert_close(got, ora(mb, rows=rows), dtype, rows=rows)
+
+
+# ---------------------------------------------------------------------------
+# Epilogue variant: LayerNorm over all heads of a token.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name,kw,dtype", [("ranking", dict(num_seqs=24), "bf16"),
+                                           ("longtail", dict(num_seqs=6), "f32"),
+                                           ("tiny", dict(), "f32")])
+def test_ln_all_heads(name, kw, dtype):
+    inp = make_inputs(name, dtype=dtype, **kw)
+    assert_close(gpu_forward(inp, epilogue="ln_all_u"), ora(inp, "ln_all_u"), dtype)
+
+
+def test_ln_all_heads_strided_and_candidates():
+    inp = make_inputs("layer", num_seqs=5)
+    assert_close(gpu_forward(inp, epilogue="ln_all_u", ld=2048), ora(inp, "ln_all_u"), "bf16")
+    inp = make_inputs("ranking", num_seqs=12)
+    dev = to_device(inp, DEV)
+    out = torch.full((inp.total_tokens, inp.num_heads, inp.d_v), -5.0, dtype=torch.bfloat16,
+                     device=DEV)
+    jagged_attn_fwd(dev["q"], dev["k"], dev["v"], dev["u"], dev["offsets"], out=out,
+                    epilogue="ln_all_u", candidates_only=True, **call_kwargs(inp, dev))
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().astype(np.float64)
+    rows = _candidate_rows(inp)
+    hist = np.setdiff1d(np.arange(inp.total_tokens), rows)
+    assert np.all(got[hist] == -5.0)
+    assert_close(got, ora(inp, "ln_all_u", rows=rows), "bf16", rows=rows)
 
 
 # ---------------------------------------------------------------------------
