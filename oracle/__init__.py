@@ -135,6 +135,48 @@ def forward(inp, *, epilogue=EPILOGUE_LN_U, rows=None,
         epilogue=epilogue, rows=rows, nthreads=nthreads)
 
 
+def layer_forward(inp, *, rows=None, nthreads: Optional[int] = None) -> np.ndarray:
+    """fp64 forward of the full HSTU layer on a batch with `inp.layer` weights
+    ("HSTU tensor by tensor: SiLU aggregation, temporal bias and gating":
+    "Trace four projections" -- normalised inputs give U/V/Q/K through one
+    projection; the teaching equation of "Similar shape, different
+    aggregation" -- o_i = W_o[U_i * Norm(sum_j A_ij V_j)] + x_i):
+        xn = LayerNorm(x) (no affine), uvqk = SiLU(xn W_uvqk^T + b),
+        U, V, Q, K = column blocks of uvqk (widths H d_v, H d_v, H d_qk, H d_qk),
+        a = attention with the per-(token, head) LayerNorm * U gate,
+        y = a W_o^T + x.
+    `rows`: optional token indices; only those rows of y are meaningful."""
+    L = inp.layer
+    f64 = np.float64
+    x = L["x"].astype(f64)
+    N, D = x.shape
+    H, dqk, dv = inp.num_heads, inp.d_qk, inp.d_v
+    eps = float(np.float32(inp.eps))
+    mu = x.mean(axis=1, keepdims=True)
+    var = ((x - mu) ** 2).mean(axis=1, keepdims=True)
+    xn = (x - mu) / np.sqrt(var + eps)
+    z = xn @ L["w_uvqk"].astype(f64).T + L["b_uvqk"].astype(f64)
+    with np.errstate(over="ignore"):
+        uvqk = z / (1.0 + np.exp(-z))
+    c0, c1, c2 = H * dv, 2 * H * dv, 2 * H * dv + H * dqk
+    U = uvqk[:, :c0].reshape(N, H, dv)
+    V = uvqk[:, c0:c1].reshape(N, H, dv)
+    Q = uvqk[:, c1:c2].reshape(N, H, dqk)
+    K = uvqk[:, c2:].reshape(N, H, dqk)
+    a = forward_arrays(inp.offsets, Q, K, V, U, timestamps=inp.timestamps,
+                       num_targets=inp.num_targets, contextual_len=inp.contextual_len,
+                       max_attn_len=inp.max_attn_len, alpha=inp.alpha, n_scale=inp.n_scale,
+                       pos_table=inp.pos_table, time_table=inp.time_table, eps=inp.eps,
+                       epilogue=EPILOGUE_LN_U, rows=rows, nthreads=nthreads)
+    a = a.reshape(N, H * dv)
+    if rows is not None:
+        y = np.full((N, D), np.nan)
+        r = np.asarray(rows, dtype=np.int64)
+        y[r] = a[r] @ L["w_o"].astype(f64).T + x[r]
+        return y
+    return a @ L["w_o"].astype(f64).T + x
+
+
 def count_allowed(offsets, num_targets=None, contextual_len=0, max_attn_len=0) -> int:
     lib = _load()
     offsets = np.ascontiguousarray(offsets, dtype=np.int32)

@@ -407,3 +407,61 @@ def test_ln_all_heads_moments_and_scale_invariance(oracle_mod):
     per_head = oracle_mod.forward(inp, epilogue=oracle_mod.EPILOGUE_LN_U).reshape(
         inp.total_tokens, 3, 8)
     assert not np.allclose(per_head.reshape(inp.total_tokens, -1), b, atol=1e-3)
+
+
+# ---------------------------------------------------------------------------
+# Full layer (o_i = W_o[U_i * Norm(sum_j A_ij V_j)] + x_i, "HSTU tensor by
+# tensor", teaching equation of "Similar shape, different aggregation").
+# ---------------------------------------------------------------------------
+def _small_layer(seed, lengths, targets=None, alpha=0.2, pos=True):
+    rng = np.random.default_rng(seed)
+    H, d, D = 2, 16, 64
+    inp = make_custom(lengths, num_heads=H, d_qk=d, d_v=d, seed=seed, num_targets=targets,
+                      pos_len=64 if pos else 0, time_len=16, alpha=alpha)
+    N = inp.total_tokens
+    inp.layer = {"x": rng.standard_normal((N, D)),
+                 "w_uvqk": 0.3 * rng.standard_normal((4 * H * d, D)),
+                 "b_uvqk": 0.3 * rng.standard_normal(4 * H * d),
+                 "w_o": 0.3 * rng.standard_normal((D, H * d))}
+    return inp
+
+
+def test_layer_zero_scores_is_identity(oracle_mod):
+    """alpha = 0 and no bias tables: every score is 0, SiLU(0) = 0, the
+    aggregate and its normalisation are 0, so y = x exactly."""
+    inp = _small_layer(50, [7, 20, 1], targets=[2, 3, 0], alpha=0.0, pos=False)
+    inp.time_table = None
+    inp.timestamps = None
+    y = oracle_mod.layer_forward(inp)
+    assert np.array_equal(y, inp.layer["x"])
+
+
+def test_layer_single_token_closed_form(oracle_mod):
+    """One-token sequences: o = SiLU(s)/n * v with s = alpha q.k + pos[0] +
+    time[0], and LayerNorm(c v) = sign(c) LayerNorm(v) (eps negligible), so
+    y = W_o (u * sign(SiLU(s)) * LN(v)) + x, computed here from the projected
+    branches without the attention loop."""
+    inp = _small_layer(51, [1, 1, 1, 1], alpha=0.7)
+    inp.eps = 1e-12
+    y = oracle_mod.layer_forward(inp)
+    L = inp.layer
+    x = L["x"]
+    xn = (x - x.mean(1, keepdims=True)) / np.sqrt(x.var(1, keepdims=True) + float(np.float32(1e-12)))
+    z = xn @ L["w_uvqk"].T + L["b_uvqk"]
+    br = z / (1 + np.exp(-z))
+    H, d = 2, 16
+    U, V = br[:, :H * d].reshape(-1, H, d), br[:, H * d:2 * H * d].reshape(-1, H, d)
+    Q, K = br[:, 2 * H * d:3 * H * d].reshape(-1, H, d), br[:, 3 * H * d:].reshape(-1, H, d)
+    s = inp.alpha * (Q * K).sum(-1) + inp.pos_table[0] + inp.time_table[0]
+    sgn = np.sign(s / (1 + np.exp(-s)))[..., None]
+    lnv = (V - V.mean(-1, keepdims=True)) / V.std(-1, keepdims=True)
+    want = (U * sgn * lnv).reshape(-1, H * d) @ L["w_o"].T + x
+    assert np.abs(y - want).max() < 1e-6 * np.abs(want).max()
+
+
+def test_layer_rows_subset(oracle_mod):
+    inp = _small_layer(52, [30, 9, 40], targets=[3, 0, 5])
+    full = oracle_mod.layer_forward(inp)
+    rows = np.array([0, 5, 29, 33, 77, 78])
+    part = oracle_mod.layer_forward(inp, rows=rows)
+    assert np.abs(full[rows] - part[rows]).max() <= 1e-12 * np.abs(full).max()
