@@ -21,6 +21,8 @@ import re
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -80,6 +82,64 @@ def candidate_rows_work(inp):
     if inp.timestamps is not None:
         byts += 8 * (keys + rows)
     return pairs, flops, byts
+
+
+def bench_layer(args, inp) -> int:
+    """Whole-layer timing: one step = LayerNorm + projection GEMM + scheduler +
+    attention + output GEMM on one batch already in HBM."""
+    import torch
+    from jagged_hstu_attention_attn_amd.api import HstuLayer, valid_pairs
+    from jagged_hstu_attention_attn_amd.device_inputs import call_kwargs, to_device
+    from jagged_hstu_attention_attn_amd.inputs import WORKLOADS
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda().to(
+        torch.bfloat16)
+    L = inp.layer
+    dev = to_device(inp, "cuda")
+    kw = call_kwargs(inp, dev)
+    lay = HstuLayer(t(L["x"]), t(L["w_uvqk"]), t(L["b_uvqk"]), t(L["w_o"]), dev["offsets"],
+                    num_heads=inp.num_heads, d_qk=inp.d_qk, d_v=inp.d_v, **kw)
+    N, D = L["x"].shape
+    H, dqk, dv = inp.num_heads, inp.d_qk, inp.d_v
+    W = H * (2 * dv + 2 * dqk)
+    pairs = valid_pairs(inp.offsets, inp.num_targets, inp.contextual_len, inp.max_attn_len)
+    f_proj, f_out = 2.0 * N * D * W, 2.0 * N * H * dv * D
+    f_attn = 2.0 * (dqk + dv) * H * pairs
+    flops = f_proj + f_attn + f_out
+    flush = None if args.no_flush else torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    for _ in range(args.warmup):
+        lay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    wall0 = time.perf_counter()
+    for s, (e0, e1) in enumerate(evs):
+        if flush is not None:
+            flush.fill_(s & 0xFF)
+        e0.record(stream)
+        lay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = sum(a.elapsed_time(b) for a, b in evs) / len(evs)
+    tflops = flops / (ms * 1e-3) / 1e12
+    result = {
+        "metric": "HSTU layer forward TFLOP/s (projections + valid-pair attention)",
+        "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "layer (full HSTU layer)", "num_seqs": inp.num_seqs,
+                   "total_tokens": N, "hidden": D, "num_heads": H, "d_qk": dqk, "d_v": dv,
+                   "valid_pairs_per_head": pairs,
+                   "seed": args.seed if args.seed is not None else WORKLOADS["layer"].seed,
+                   "cache_flushed": flush is not None, "parallelism": "single GPU"},
+        "flops": {"projection": f_proj, "attention": f_attn, "output": f_out},
+        "tokens_per_s": N / (ms * 1e-3),
+        "pct_bf16_mfma_peak": 100.0 * tflops / PEAK_TFLOPS["bf16"],
+        "wall_s": wall,
+    }
+    print(json.dumps(result), flush=True)
+    return 0
 
 
 def traffic_from_profile(workload: str):
@@ -154,6 +214,9 @@ def main() -> int:
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
     ap.add_argument("--epilogue", default="ln_u", choices=["ln_u", "none", "ln_all_u"],
                     help="per-head LayerNorm * U (default), none, or one LayerNorm over all heads")
+    ap.add_argument("--full-layer", action="store_true",
+                    help="layer workload only: time the whole HSTU layer (LayerNorm, "
+                         "projection GEMM, attention, output GEMM)")
     ap.add_argument("--candidates-only", action="store_true",
                     help="compute only the candidate rows (history reused; no CPU baseline)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -183,6 +246,11 @@ def main() -> int:
 
     log(f"workload {args.workload}: generating inputs")
     inp = make_inputs(args.workload, seed=args.seed)
+    if args.full_layer:
+        if inp.layer is None:
+            print("--full-layer needs the layer workload", file=sys.stderr)
+            return 2
+        return bench_layer(args, inp)
     dev = to_device(inp, "cuda")
     call = JaggedAttnCall(dev["q"], dev["k"], dev["v"], dev["u"], dev["offsets"],
                           candidates_only=args.candidates_only, epilogue=args.epilogue,

@@ -219,6 +219,49 @@ int64_t hstu_jagged_attn_valid_pairs(int32_t num_seqs, const int32_t* offsets_ho
  */
 int hstu_jagged_attn_grid(const hstu_attn_desc* desc);
 
+/*
+ * Full HSTU layer forward, bf16 (the block of "HSTU tensor by tensor: SiLU
+ * aggregation, temporal bias and gating": sections "Follow the U, V, Q and K
+ * branches", "Trace four projections" and the teaching equation of "Similar
+ * shape, different aggregation", o_i = W_o[U_i * Norm(sum_j A_ij V_j)] + x_i):
+ *
+ *   xn   = LayerNorm(x)                       per token over `hidden`, no affine
+ *   uvqk = SiLU(xn W_uvqk^T + b_uvqk)         one fused projection
+ *   U, V, Q, K = column blocks of uvqk        widths H d_v, H d_v, H d_qk, H d_qk
+ *   a    = jagged attention with the per-(token, head) LayerNorm * U gate
+ *   y    = a W_o^T + x                        output projection, residual
+ *
+ * x, y: [total_tokens, hidden]; w_uvqk: [H (2 d_v + 2 d_qk), hidden] and
+ * b_uvqk: [H (2 d_v + 2 d_qk)]; w_o: [hidden, H d_v] (weights in the [out, in]
+ * layout), all bf16, rows contiguous, 16-byte aligned.  The intermediates (xn,
+ * uvqk, a) are bf16 in the workspace (hstu_layer_workspace_bytes, which also
+ * holds the attention's work list).  Requires hidden % 128 == 0 and <= 4096,
+ * H (2 d_v + 2 d_qk) % 128 == 0, H d_v % 64 == 0 and a supported bf16
+ * attention shape.  The attention arguments and errors are those of
+ * hstu_jagged_attn_fwd; ln_eps serves both LayerNorms.  Enqueues five kernels
+ * on `stream` (LayerNorm, projection GEMM, scheduler, attention, output GEMM).
+ */
+typedef struct {
+  int32_t num_seqs;
+  int32_t total_tokens;
+  int32_t num_heads;
+  int32_t d_qk;
+  int32_t d_v;
+  int32_t hidden;          /* width of x and y                                    */
+  int32_t pos_table_len;
+  int32_t time_table_len;
+  float ln_eps;
+} hstu_layer_desc;
+
+size_t hstu_layer_workspace_bytes(const hstu_layer_desc* desc);
+
+int hstu_layer_fwd(const hstu_layer_desc* desc, const void* x, const void* w_uvqk,
+                   const void* b_uvqk, const void* w_o, const int32_t* offsets,
+                   const int64_t* timestamps, const int32_t* num_targets,
+                   int32_t contextual_len, int32_t max_attn_len, float alpha, float n_scale,
+                   const float* pos_table, const float* time_table, void* y, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
 /* Thread-local message for the last failing call of this thread ("" if none). */
 const char* hstu_last_error(void);
 

@@ -32,6 +32,8 @@ EXPORTS = (
     "hstu_jagged_attn_run",
     "hstu_jagged_attn_plan_candidates",
     "hstu_jagged_attn_fwd_candidates",
+    "hstu_layer_workspace_bytes",
+    "hstu_layer_fwd",
     "hstu_jagged_attn_valid_pairs",
     "hstu_jagged_attn_grid",
     "hstu_last_error",
@@ -55,6 +57,20 @@ class HstuAttnDesc(ctypes.Structure):
         ("time_table_len", ctypes.c_int32),
         ("ln_eps", ctypes.c_float),
         ("epilogue", ctypes.c_int32),
+    ]
+
+
+class HstuLayerDesc(ctypes.Structure):
+    _fields_ = [
+        ("num_seqs", ctypes.c_int32),
+        ("total_tokens", ctypes.c_int32),
+        ("num_heads", ctypes.c_int32),
+        ("d_qk", ctypes.c_int32),
+        ("d_v", ctypes.c_int32),
+        ("hidden", ctypes.c_int32),
+        ("pos_table_len", ctypes.c_int32),
+        ("time_table_len", ctypes.c_int32),
+        ("ln_eps", ctypes.c_float),
     ]
 
 
@@ -93,6 +109,12 @@ def load() -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
         fn.argtypes = [D, P, P, i32, i32, P, sz, P]
+    LD = ctypes.POINTER(HstuLayerDesc)
+    lib.hstu_layer_workspace_bytes.restype = sz
+    lib.hstu_layer_workspace_bytes.argtypes = [LD]
+    lib.hstu_layer_fwd.restype = ctypes.c_int
+    lib.hstu_layer_fwd.argtypes = [LD, P, P, P, P, P, P, P, i32, i32, f32, f32, P, P, P, P, sz,
+                                   P]
     lib.hstu_jagged_attn_valid_pairs.restype = i64
     lib.hstu_jagged_attn_valid_pairs.argtypes = [i32, P, P, i32, i32]
     lib.hstu_jagged_attn_grid.restype = ctypes.c_int

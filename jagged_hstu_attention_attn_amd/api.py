@@ -23,7 +23,8 @@ import torch
 
 from . import _lib
 
-__all__ = ["jagged_attn_fwd", "plan", "run", "make_desc", "workspace_bytes", "valid_pairs",
+__all__ = ["jagged_attn_fwd", "layer_fwd", "HstuLayer", "plan", "run", "make_desc",
+           "workspace_bytes", "valid_pairs",
            "JaggedAttnCall"]
 
 _DTYPES = {torch.float32: _lib.HSTU_DTYPE_F32, torch.bfloat16: _lib.HSTU_DTYPE_BF16}
@@ -198,3 +199,51 @@ def valid_pairs(offsets, num_targets=None, contextual_len: int = 0, max_attn_len
     if n < 0:
         raise _lib.HstuError(_lib.HSTU_ERR_INVALID_ARG, _lib.last_error())
     return int(n)
+
+
+class HstuLayer:
+    """The full layer forward on one batch: owns its descriptor, workspace and
+    output; x [N, hidden], w_uvqk [H (2 d_v + 2 d_qk), hidden], b_uvqk [..],
+    w_o [hidden, H d_v], all bf16 on one GPU."""
+
+    def __init__(self, x, w_uvqk, b_uvqk, w_o, offsets, *, num_heads, d_qk, d_v,
+                 timestamps=None, num_targets=None, contextual_len=0, max_attn_len=0, alpha,
+                 n_scale, pos_table=None, time_table=None, eps=1e-5):
+        if not x.is_cuda:
+            raise ValueError("tensors must be on a GPU")
+        for name, t in (("x", x), ("w_uvqk", w_uvqk), ("b_uvqk", b_uvqk), ("w_o", w_o)):
+            if t.dtype != torch.bfloat16 or not t.is_contiguous():
+                raise TypeError(f"{name} must be a contiguous bfloat16 tensor")
+        _check_aux(offsets, timestamps, num_targets, pos_table, time_table, x.device)
+        self.args = (x, w_uvqk, b_uvqk, w_o, offsets, timestamps, num_targets)
+        self.contextual_len, self.max_attn_len = int(contextual_len), int(max_attn_len)
+        self.alpha, self.n_scale = float(alpha), float(n_scale)
+        self.pos_table, self.time_table = pos_table, time_table
+        d = _lib.HstuLayerDesc()
+        d.num_seqs = offsets.numel() - 1
+        d.total_tokens = x.shape[0]
+        d.num_heads, d.d_qk, d.d_v, d.hidden = int(num_heads), int(d_qk), int(d_v), x.shape[1]
+        d.pos_table_len = 0 if pos_table is None else pos_table.numel()
+        d.time_table_len = 0 if time_table is None else time_table.numel()
+        d.ln_eps = float(eps)
+        self.desc = d
+        n = _lib.load().hstu_layer_workspace_bytes(ctypes.byref(d))
+        if n == 0:
+            raise _lib.HstuError(_lib.HSTU_ERR_INVALID_ARG, _lib.last_error())
+        self.workspace = torch.empty(n, dtype=torch.uint8, device=x.device)
+        self.y = torch.empty_like(x)
+
+    def __call__(self) -> torch.Tensor:
+        x, w_uvqk, b_uvqk, w_o, offsets, timestamps, num_targets = self.args
+        _lib.check(_lib.load().hstu_layer_fwd(
+            ctypes.byref(self.desc), _ptr(x), _ptr(w_uvqk), _ptr(b_uvqk), _ptr(w_o),
+            _ptr(offsets), _ptr(timestamps), _ptr(num_targets), self.contextual_len,
+            self.max_attn_len, self.alpha, self.n_scale, _ptr(self.pos_table),
+            _ptr(self.time_table), _ptr(self.y), _ptr(self.workspace),
+            int(self.workspace.numel()), _stream(x.device)))
+        return self.y
+
+
+def layer_fwd(x, w_uvqk, b_uvqk, w_o, offsets, **kw) -> torch.Tensor:
+    """One full layer forward on the current stream (see HstuLayer)."""
+    return HstuLayer(x, w_uvqk, b_uvqk, w_o, offsets, **kw)()

@@ -7,6 +7,7 @@
 #include <cstring>
 
 #include "hstu_attn.h"
+#include "gemm.hpp"
 #include "hstu_device.hpp"
 
 namespace {
@@ -385,3 +386,156 @@ int hstu_jagged_attn_grid(const hstu_attn_desc* desc) {
 const char* hstu_last_error(void) { return g_err; }
 
 }  // extern "C"
+
+// ---- full HSTU layer ------------------------------------------------------
+
+namespace {
+
+struct LayerLayout {
+  size_t xn_off, uvqk_off, attn_off, attn_ws_off, total;
+  int64_t uvqk_w;   // H * (2 d_v + 2 d_qk)
+};
+
+hstu_attn_desc layer_attn_desc(const hstu_layer_desc* d) {
+  hstu_attn_desc a;
+  a.num_seqs = d->num_seqs;
+  a.total_tokens = d->total_tokens;
+  a.num_heads = d->num_heads;
+  a.d_qk = d->d_qk;
+  a.d_v = d->d_v;
+  a.dtype = HSTU_DTYPE_BF16;
+  const int64_t w = (int64_t)d->num_heads * (2 * d->d_v + 2 * d->d_qk);
+  a.ld_q = a.ld_k = a.ld_v = a.ld_u = w;
+  a.ld_out = (int64_t)d->num_heads * d->d_v;
+  a.pos_table_len = d->pos_table_len;
+  a.time_table_len = d->time_table_len;
+  a.ln_eps = d->ln_eps;
+  a.epilogue = HSTU_EPILOGUE_LN_U;
+  return a;
+}
+
+LayerLayout layer_layout(const hstu_layer_desc* d) {
+  LayerLayout l;
+  const int64_t N = d->total_tokens, H = d->num_heads;
+  l.uvqk_w = H * (2 * d->d_v + 2 * d->d_qk);
+  l.xn_off = 0;
+  l.uvqk_off = hstu::align256(l.xn_off + (size_t)N * d->hidden * 2);
+  l.attn_off = hstu::align256(l.uvqk_off + (size_t)N * l.uvqk_w * 2);
+  l.attn_ws_off = hstu::align256(l.attn_off + (size_t)N * H * d->d_v * 2);
+  l.total = l.attn_ws_off +
+            hstu::plan_layout(d->num_seqs, d->total_tokens, d->num_heads, d->d_v).total;
+  return l;
+}
+
+int check_layer_desc(const hstu_layer_desc* d) {
+  if (!d) return fail(HSTU_ERR_INVALID_ARG, "desc is NULL");
+  if (d->hidden <= 0) return fail(HSTU_ERR_INVALID_ARG, "hidden must be positive");
+  if (d->hidden % 128 != 0 || d->hidden > hstu::layernorm_rows_max_width())
+    return fail(HSTU_ERR_UNSUPPORTED, "hidden must be a multiple of 128 up to %d",
+                hstu::layernorm_rows_max_width());
+  const hstu_attn_desc a = layer_attn_desc(d);
+  int rc = check_desc(&a);
+  if (rc != HSTU_OK) return rc;
+  const int64_t w = (int64_t)d->num_heads * (2 * d->d_v + 2 * d->d_qk);
+  if (w % 128 != 0 || ((int64_t)d->num_heads * d->d_v) % 64 != 0)
+    return fail(HSTU_ERR_UNSUPPORTED, "H*(2 d_v + 2 d_qk) must be a multiple of 128 and "
+                "H*d_v of 64");
+  return HSTU_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t hstu_layer_workspace_bytes(const hstu_layer_desc* desc) {
+  if (check_layer_desc(desc) != HSTU_OK) return 0;
+  return layer_layout(desc).total;
+}
+
+int hstu_layer_fwd(const hstu_layer_desc* desc, const void* x, const void* w_uvqk,
+                   const void* b_uvqk, const void* w_o, const int32_t* offsets,
+                   const int64_t* timestamps, const int32_t* num_targets, int32_t contextual_len,
+                   int32_t max_attn_len, float alpha, float n_scale, const float* pos_table,
+                   const float* time_table, void* y, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+  int rc = check_layer_desc(desc);
+  if (rc != HSTU_OK) return rc;
+  struct {
+    const char* name;
+    const void* p;
+  } ptrs[] = {{"x", x}, {"w_uvqk", w_uvqk}, {"b_uvqk", b_uvqk}, {"w_o", w_o}, {"y", y}};
+  for (auto& e : ptrs) {
+    if (!e.p) return fail(HSTU_ERR_INVALID_ARG, "%s is NULL", e.name);
+    if (!aligned16(e.p)) return fail(HSTU_ERR_INVALID_ARG, "%s is not 16-byte aligned", e.name);
+  }
+  const LayerLayout l = layer_layout(desc);
+  if (!workspace) return fail(HSTU_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", l.total);
+  if (workspace_bytes < l.total)
+    return fail(HSTU_ERR_WORKSPACE, "workspace has %zu bytes, need %zu", workspace_bytes, l.total);
+  if (!aligned16(workspace)) return fail(HSTU_ERR_INVALID_ARG, "workspace not 16-byte aligned");
+  const hstu_attn_desc ad = layer_attn_desc(desc);
+  char* ws = static_cast<char*>(workspace);
+  __bf16* xn = reinterpret_cast<__bf16*>(ws + l.xn_off);
+  __bf16* uvqk = reinterpret_cast<__bf16*>(ws + l.uvqk_off);
+  __bf16* attn = reinterpret_cast<__bf16*>(ws + l.attn_off);
+  const size_t attn_ws_bytes = l.total - l.attn_ws_off;
+  // the attention's arguments are checked before anything is enqueued
+  rc = check_plan_args(&ad, offsets, contextual_len, max_attn_len, ws + l.attn_ws_off,
+                       attn_ws_bytes);
+  if (rc != HSTU_OK) return rc;
+  const int64_t H = desc->num_heads, dv = desc->d_v, dqk = desc->d_qk;
+  const __bf16* u_view = uvqk;
+  const __bf16* v_view = uvqk + H * dv;
+  const __bf16* q_view = uvqk + 2 * H * dv;
+  const __bf16* k_view = uvqk + 2 * H * dv + H * dqk;
+  rc = check_run_args(&ad, q_view, k_view, v_view, u_view, timestamps, alpha, n_scale,
+                      pos_table, time_table, attn);
+  if (rc != HSTU_OK) return rc;
+  if (desc->num_seqs == 0 || desc->total_tokens == 0) return HSTU_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int N = desc->total_tokens, D = desc->hidden;
+
+  hipError_t e = hstu::launch_layernorm_rows(static_cast<const __bf16*>(x), D, xn, D, N, D,
+                                             desc->ln_eps, st);
+  if (e != hipSuccess) return fail(HSTU_ERR_HIP, "LayerNorm launch failed: %s", hipGetErrorString(e));
+  hstu::GemmArgs g1;
+  g1.A = xn;
+  g1.B = static_cast<const __bf16*>(w_uvqk);
+  g1.bias = static_cast<const __bf16*>(b_uvqk);
+  g1.residual = nullptr;
+  g1.C = uvqk;
+  g1.lda = D;
+  g1.ldb = D;
+  g1.ldc = l.uvqk_w;
+  g1.ldr = 0;
+  g1.M = N;
+  g1.N = (int32_t)l.uvqk_w;
+  g1.K = D;
+  g1.act_silu = 1;
+  e = hstu::launch_gemm_bt(g1, st);
+  if (e != hipSuccess) return fail(HSTU_ERR_HIP, "projection launch failed: %s", hipGetErrorString(e));
+  rc = hstu_jagged_attn_fwd(&ad, q_view, k_view, v_view, u_view, offsets, timestamps, num_targets,
+                            contextual_len, max_attn_len, alpha, n_scale, pos_table, time_table,
+                            attn, ws + l.attn_ws_off, attn_ws_bytes, stream);
+  if (rc != HSTU_OK) return rc;
+  hstu::GemmArgs g2;
+  g2.A = attn;
+  g2.B = static_cast<const __bf16*>(w_o);
+  g2.bias = nullptr;
+  g2.residual = static_cast<const __bf16*>(x);
+  g2.C = static_cast<__bf16*>(y);
+  g2.lda = H * dv;
+  g2.ldb = H * dv;
+  g2.ldc = D;
+  g2.ldr = D;
+  g2.M = N;
+  g2.N = D;
+  g2.K = (int32_t)(H * dv);
+  g2.act_silu = 0;
+  e = hstu::launch_gemm_bt(g2, st);
+  if (e != hipSuccess) return fail(HSTU_ERR_HIP, "output projection launch failed: %s", hipGetErrorString(e));
+  return HSTU_OK;
+}
+
+}  // extern "C"
+

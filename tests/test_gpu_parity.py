@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import oracle
-from jagged_hstu_attention_attn_amd.api import JaggedAttnCall, jagged_attn_fwd
+from jagged_hstu_attention_attn_amd.api import HstuLayer, JaggedAttnCall, jagged_attn_fwd
 from jagged_hstu_attention_attn_amd.device_inputs import call_kwargs, to_device
 from jagged_hstu_attention_attn_amd.inputs import JaggedInputs, make_custom, make_inputs
 
@@ -430,6 +430,39 @@ def test_ln_all_heads_strided_and_candidates():
     hist = np.setdiff1d(np.arange(inp.total_tokens), rows)
     assert np.all(got[hist] == -5.0)
     assert_close(got, ora(inp, "ln_all_u", rows=rows), "bf16", rows=rows)
+
+
+# ---------------------------------------------------------------------------
+# Full HSTU layer: LayerNorm, fused U/V/Q/K projection + SiLU (MFMA GEMM),
+# attention on the strided branches, output projection + residual.
+# ---------------------------------------------------------------------------
+def gpu_layer(inp):
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(
+        DEV).to(torch.bfloat16)
+    L = inp.layer
+    dev = to_device(inp, DEV)
+    kw = call_kwargs(inp, dev)
+    lay = HstuLayer(t(L["x"]), t(L["w_uvqk"]), t(L["b_uvqk"]), t(L["w_o"]), dev["offsets"],
+                    num_heads=inp.num_heads, d_qk=inp.d_qk, d_v=inp.d_v,
+                    timestamps=kw["timestamps"], num_targets=kw["num_targets"],
+                    contextual_len=kw["contextual_len"], max_attn_len=kw["max_attn_len"],
+                    alpha=kw["alpha"], n_scale=kw["n_scale"], pos_table=kw["pos_table"],
+                    time_table=kw["time_table"], eps=kw["eps"])
+    y = lay()
+    torch.cuda.synchronize()
+    return y.float().cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("num_seqs,seed", [(8, 1234), (3, 7)])
+def test_layer_forward(num_seqs, seed):
+    inp = make_inputs("layer", num_seqs=num_seqs, seed=seed)
+    assert_close(gpu_layer(inp), oracle.layer_forward(inp), "bf16")
+
+
+def test_layer_forward_full_size_sampled_rows():
+    inp = make_inputs("layer")
+    rows = _sample_rows(inp, 300, 9)
+    assert_close(gpu_layer(inp), oracle.layer_forward(inp, rows=rows), "bf16", rows=rows)
 
 
 # ---------------------------------------------------------------------------
