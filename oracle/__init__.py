@@ -5,7 +5,10 @@ this package.  The product path (the HIP library and its Python binding) never
 touches it, and it shares no code with them: the only common module is the
 seeded input generator, which holds none of the method's arithmetic.
 
-Two independent formulations live here:
+The backward (`backward`) is the chain rule through the same steps, one
+allowed pair at a time, in the same C file.
+
+Two independent formulations of the forward live here:
   * `forward`  -- the fp64 C loop in hstu_oracle.c (one pair at a time, only
     allowed pairs evaluated), built by `build()` with gcc -O2 -fopenmp.
   * `dense_forward` -- the padded dense form of the teaching snippet on the
@@ -59,6 +62,13 @@ def _load():
             P, i64, P, i64, P, i64, P, i64,
             P, P, i32, i32, f64, f64,
             P, i32, P, i32, f64, i32, P, i64, P, i32]
+        lib.hstu_oracle_bwd.restype = ctypes.c_int
+        lib.hstu_oracle_bwd.argtypes = [
+            i32, P, i32, i32, i32,
+            P, i64, P, i64, P, i64, P, i64,
+            P, P, i32, i32, f64, f64,
+            P, i32, P, i32, f64, i32, P, i64,
+            P, P, P, P, P, P, i32]
         lib.hstu_oracle_count_allowed.restype = i64
         lib.hstu_oracle_count_allowed.argtypes = [i32, P, P, i32, i32]
         lib.hstu_oracle_time_bucket.restype = ctypes.c_int
@@ -175,6 +185,57 @@ def layer_forward(inp, *, rows=None, nthreads: Optional[int] = None) -> np.ndarr
         y[r] = a[r] @ L["w_o"].astype(f64).T + x[r]
         return y
     return a @ L["w_o"].astype(f64).T + x
+
+
+def backward_arrays(offsets, q, k, v, u, dout, *, timestamps=None, num_targets=None,
+                    contextual_len=0, max_attn_len=0, alpha=1.0, n_scale=1.0,
+                    pos_table=None, time_table=None, eps=1e-5, epilogue=EPILOGUE_LN_U,
+                    nthreads: Optional[int] = None) -> dict:
+    """fp64 gradients of sum(dout * forward(...)) with respect to q, k, v, u,
+    pos_table and time_table (the C oracle's chain rule; [N, H, d] arrays).
+    Returns a dict with keys dq, dk, dv, du, dpos (or None), dtime (or None)."""
+    lib = _load()
+    offsets = np.ascontiguousarray(offsets, dtype=np.int32)
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    k = np.ascontiguousarray(k, dtype=np.float64)
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    u = np.ascontiguousarray(u, dtype=np.float64)
+    dout = np.ascontiguousarray(dout, dtype=np.float64)
+    N, H, dqk = q.shape
+    dv = v.shape[2]
+    assert dout.shape == (N, H, dv)
+    ts = None if timestamps is None else np.ascontiguousarray(timestamps, dtype=np.int64)
+    nt = None if num_targets is None else np.ascontiguousarray(num_targets, dtype=np.int32)
+    pos = None if pos_table is None else np.ascontiguousarray(pos_table, dtype=np.float64)
+    tim = None if time_table is None else np.ascontiguousarray(time_table, dtype=np.float64)
+    g = {"dq": np.empty_like(q), "dk": np.empty_like(k), "dv": np.empty_like(v),
+         "du": np.empty_like(u),
+         "dpos": None if pos is None else np.empty_like(pos),
+         "dtime": None if tim is None else np.empty_like(tim)}
+    rc = lib.hstu_oracle_bwd(
+        offsets.shape[0] - 1, _ptr(offsets), H, dqk, dv,
+        _ptr(q), H * dqk, _ptr(k), H * dqk, _ptr(v), H * dv, _ptr(u), H * dv,
+        _ptr(ts), _ptr(nt), int(contextual_len), int(max_attn_len),
+        float(alpha), float(n_scale),
+        _ptr(pos), 0 if pos is None else pos.shape[0],
+        _ptr(tim), 0 if tim is None else tim.shape[0],
+        float(np.float32(eps)), int(epilogue), _ptr(dout), H * dv,
+        _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["du"]),
+        _ptr(g["dpos"]), _ptr(g["dtime"]),
+        int(nthreads if nthreads is not None else default_threads()))
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments")
+    return g
+
+
+def backward(inp, dout, *, epilogue=EPILOGUE_LN_U, nthreads: Optional[int] = None) -> dict:
+    """fp64 gradients for a `JaggedInputs` batch and output gradient `dout`."""
+    return backward_arrays(
+        inp.offsets, inp.q, inp.k, inp.v, inp.u, dout, timestamps=inp.timestamps,
+        num_targets=inp.num_targets, contextual_len=inp.contextual_len,
+        max_attn_len=inp.max_attn_len, alpha=inp.alpha, n_scale=inp.n_scale,
+        pos_table=inp.pos_table, time_table=inp.time_table, eps=inp.eps,
+        epilogue=epilogue, nthreads=nthreads)
 
 
 def count_allowed(offsets, num_targets=None, contextual_len=0, max_attn_len=0) -> int:

@@ -1,5 +1,6 @@
 /*
- * hstu_oracle.c -- plain fp64 CPU oracle for jagged HSTU attention (forward).
+ * hstu_oracle.c -- plain fp64 CPU oracle for jagged HSTU attention (forward,
+ * and its backward further down).
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may call, link or
  * load this file or the library built from it; it exists so that the tests,
@@ -261,6 +262,196 @@ int hstu_oracle_fwd(int num_seqs, const int32_t* offsets, int num_heads, int d_q
       }
     }
   }
+  return 0;
+}
+
+/*
+ * Backward of hstu_oracle_fwd (the same arguments, plus dout = dLoss/dout):
+ * the gradients of a scalar loss with respect to q, k, v, u and both bias
+ * tables, by the chain rule taken through the forward's steps in reverse.
+ * Training needs them ("Scaling HSTU: ragged execution, candidate
+ * amortization and content features", where the model is trained end to
+ * end); the pages give no backward, so every step below is the derivative of
+ * the forward step named beside it.
+ *
+ *   gate  out_i = xhat_i * u_i, xhat_i = (o_i - mean) * rstd  (no affine):
+ *         du_i = dout_i * xhat_i;  g = dout_i * u_i;
+ *         do_i = rstd * (g - mean(g) - xhat_i * mean(g * xhat_i))
+ *         (means over the d_v values of the head, or over all H * d_v values
+ *         of the token for LN_ALL_U; epilogue NONE: do_i = dout_i, du_i = 0)
+ *   sum   o_i = sum_j a_ij v_j:      dv_j += a_ij do_i;  da_ij = <do_i, v_j>
+ *   gate  a_ij = SiLU(s_ij)/n_scale on allowed pairs (0 elsewhere):
+ *         ds_ij = da_ij * SiLU'(s_ij) / n_scale,
+ *         SiLU'(s) = sig(s) * (1 + s * (1 - sig(s))), sig(s) = 1/(1 + e^-s)
+ *   score s_ij = alpha <q_i, k_j> + pos[..] + time[..]:
+ *         dq_i += alpha ds_ij k_j;  dk_j += alpha ds_ij q_i;
+ *         dpos[min(|i-j|, P-1)] += ds_ij;  dtime[bucket_ij] += ds_ij
+ *
+ * dq, dk, dv, du use the token strides of q, k, v, u; dout uses ld_out.  All
+ * outputs are overwritten (every token row, whole tables).  dpos / dtime may
+ * be NULL only when the matching table is.  Returns 0, or -1 on a bad
+ * argument or allocation failure.
+ */
+int hstu_oracle_bwd(int num_seqs, const int32_t* offsets, int num_heads, int d_qk, int d_v,
+                    const double* q, int64_t ld_q, const double* k, int64_t ld_k,
+                    const double* v, int64_t ld_v, const double* u, int64_t ld_u,
+                    const int64_t* timestamps, const int32_t* num_targets,
+                    int contextual_len, int max_attn_len, double alpha, double n_scale,
+                    const double* pos_table, int pos_len, const double* time_table,
+                    int time_len, double eps, int epilogue, const double* dout,
+                    int64_t ld_out, double* dq, double* dk, double* dv, double* du,
+                    double* dpos, double* dtime, int nthreads) {
+  if (num_seqs < 0 || num_heads <= 0 || d_qk <= 0 || d_v <= 0) return -1;
+  if ((pos_table != NULL && dpos == NULL) || (time_table != NULL && dtime == NULL)) return -1;
+  int64_t n_tok = num_seqs > 0 ? (int64_t)offsets[num_seqs] : 0;
+  int64_t width = (int64_t)num_heads * d_v;
+  for (int64_t t = 0; t < n_tok; ++t) {
+    for (int64_t e = 0; e < (int64_t)num_heads * d_qk; ++e) {
+      dq[t * ld_q + e] = 0.0;
+      dk[t * ld_k + e] = 0.0;
+    }
+    for (int64_t e = 0; e < width; ++e) {
+      dv[t * ld_v + e] = 0.0;
+      du[t * ld_u + e] = 0.0;
+    }
+  }
+  if (dpos) memset(dpos, 0, sizeof(double) * (size_t)pos_len);
+  if (dtime) memset(dtime, 0, sizeof(double) * (size_t)time_len);
+  if (n_tok == 0) return 0;
+
+  /* forward again, stopping before the gate: o_i for every token and head */
+  double* o = (double*)malloc(sizeof(double) * (size_t)(n_tok * width));
+  double* dO = (double*)malloc(sizeof(double) * (size_t)(n_tok * width));
+  if (!o || !dO) {
+    free(o);
+    free(dO);
+    return -1;
+  }
+  int rc = hstu_oracle_fwd(num_seqs, offsets, num_heads, d_qk, d_v, q, ld_q, k, ld_k, v, ld_v,
+                           u, ld_u, timestamps, num_targets, contextual_len, max_attn_len,
+                           alpha, n_scale, pos_table, pos_len, time_table, time_len, eps,
+                           ORACLE_EPILOGUE_NONE, o, width, NULL, nthreads);
+  if (rc != 0) {
+    free(o);
+    free(dO);
+    return rc;
+  }
+
+  /* gate backward: groups of `gw` consecutive values normalised together */
+  int64_t gw = epilogue == ORACLE_EPILOGUE_LN_ALL_U ? width : d_v;
+  int64_t groups_per_tok = width / gw;
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < n_tok; ++t) {
+    for (int64_t gi = 0; gi < groups_per_tok; ++gi) {
+      const double* x = o + t * width + gi * gw;
+      const double* dy = dout + t * ld_out + gi * gw;
+      const double* ug = u + t * ld_u + gi * gw;
+      double* dx = dO + t * width + gi * gw;
+      double* dug = du + t * ld_u + gi * gw;
+      if (epilogue == ORACLE_EPILOGUE_NONE) {
+        for (int64_t e = 0; e < gw; ++e) dx[e] = dy[e];
+        continue;
+      }
+      double mean = 0.0, var = 0.0;
+      for (int64_t e = 0; e < gw; ++e) mean += x[e];
+      mean /= (double)gw;
+      for (int64_t e = 0; e < gw; ++e) var += (x[e] - mean) * (x[e] - mean);
+      var /= (double)gw;
+      double rstd = 1.0 / sqrt(var + eps);
+      double mg = 0.0, mgx = 0.0;
+      for (int64_t e = 0; e < gw; ++e) {
+        double xh = (x[e] - mean) * rstd;
+        double g = dy[e] * ug[e];
+        dug[e] = dy[e] * xh;
+        mg += g;
+        mgx += g * xh;
+      }
+      mg /= (double)gw;
+      mgx /= (double)gw;
+      for (int64_t e = 0; e < gw; ++e) {
+        double xh = (x[e] - mean) * rstd;
+        dx[e] = rstd * (dy[e] * ug[e] - mg - xh * mgx);
+      }
+    }
+  }
+
+  /* pair pass: one (sequence, head) at a time; table gradients per thread */
+  int n_items = num_seqs * num_heads;
+  int nt = 1;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+  nt = omp_get_max_threads();
+#else
+  (void)nthreads;
+#endif
+  size_t tab = (size_t)pos_len + (size_t)time_len;
+  double* part = (double*)calloc((size_t)nt * (tab > 0 ? tab : 1), sizeof(double));
+  if (!part) {
+    free(o);
+    free(dO);
+    return -1;
+  }
+#pragma omp parallel
+  {
+    int tid = 0;
+#ifdef _OPENMP
+    tid = omp_get_thread_num();
+#endif
+    double* tp = part + (size_t)tid * (tab > 0 ? tab : 1);
+#pragma omp for schedule(dynamic, 1)
+    for (int it = 0; it < n_items; ++it) {
+      int b = it / num_heads, h = it % num_heads;
+      seq_geom g = geometry(offsets, num_targets, b, contextual_len, max_attn_len);
+      int64_t base = offsets[b];
+      for (int64_t i = 0; i < g.L; ++i) {
+        const double* qi = q + (base + i) * ld_q + (int64_t)h * d_qk;
+        const double* doi = dO + (base + i) * width + (int64_t)h * d_v;
+        double* dqi = dq + (base + i) * ld_q + (int64_t)h * d_qk;
+        for (int64_t j = 0; j < g.L; ++j) {
+          if (!allowed(&g, i, j)) continue;
+          const double* kj = k + (base + j) * ld_k + (int64_t)h * d_qk;
+          const double* vj = v + (base + j) * ld_v + (int64_t)h * d_v;
+          double dot = 0.0;
+          for (int e = 0; e < d_qk; ++e) dot += qi[e] * kj[e];
+          double s = alpha * dot;
+          int64_t pidx = 0;
+          int bidx = 0;
+          if (pos_table) {
+            int64_t rel = i >= j ? i - j : j - i;
+            pidx = rel < pos_len - 1 ? rel : pos_len - 1;
+            s += pos_table[pidx];
+          }
+          if (time_table) {
+            int bucket = hstu_oracle_time_bucket(timestamps[base + i], timestamps[base + j]);
+            bidx = bucket < time_len - 1 ? bucket : time_len - 1;
+            s += time_table[bidx];
+          }
+          double sig = 1.0 / (1.0 + exp(-s));
+          double a = s * sig / n_scale;
+          double da = 0.0;
+          for (int e = 0; e < d_v; ++e) da += doi[e] * vj[e];
+          double ds = da * sig * (1.0 + s * (1.0 - sig)) / n_scale;
+          double* dvj = dv + (base + j) * ld_v + (int64_t)h * d_v;
+          for (int e = 0; e < d_v; ++e) dvj[e] += a * doi[e];
+          double* dkj = dk + (base + j) * ld_k + (int64_t)h * d_qk;
+          for (int e = 0; e < d_qk; ++e) {
+            dqi[e] += alpha * ds * kj[e];
+            dkj[e] += alpha * ds * qi[e];
+          }
+          if (pos_table) tp[pidx] += ds;
+          if (time_table) tp[pos_len + bidx] += ds;
+        }
+      }
+    }
+  }
+  for (int t = 0; t < nt; ++t) {
+    const double* tp = part + (size_t)t * (tab > 0 ? tab : 1);
+    for (int e = 0; e < pos_len; ++e) dpos[e] += tp[e];
+    for (int e = 0; e < time_len; ++e) dtime[e] += tp[pos_len + e];
+  }
+  free(part);
+  free(o);
+  free(dO);
   return 0;
 }
 
