@@ -1,9 +1,9 @@
 /*
  * hstu_attn.h -- C ABI of the MI355X (gfx950) jagged HSTU attention library.
  *
- * Operation (forward only).  Sequences are stored jagged: the tokens of all
- * sequences are concatenated and an int32 offsets array marks where each
- * sequence starts ("Scaling HSTU: ragged execution, candidate amortization and
+ * Operation (forward; its backward is declared near the end).  Sequences
+ * are stored jagged: the tokens of all sequences are concatenated and an
+ * int32 offsets array marks where each sequence starts ("Scaling HSTU: ragged execution, candidate amortization and
  * content features", section "Variable length is a central systems issue").
  * For every sequence b, head h and query row i of the sequence:
  *
@@ -263,6 +263,55 @@ int hstu_layer_fwd(const hstu_layer_desc* desc, const void* x, const void* w_uvq
                    size_t workspace_bytes, void* stream);
 
 /* Thread-local message for the last failing call of this thread ("" if none). */
+/*
+ * Backward of the attention (dtype, shapes, strides, rules and epilogue of
+ * `desc`, the same inputs as the forward).  Given dout = dLoss/d(out) it
+ * writes the gradients of the loss with respect to q, k, v, u and both bias
+ * tables, by the chain rule through the forward's steps (the pages give the
+ * forward only; training the model end to end, "Scaling HSTU: ragged
+ * execution, candidate amortization and content features", needs these):
+ *
+ *   gate   xhat_i = (o_i - mean) * rstd,  out_i = xhat_i * u_i:
+ *          du_i = dout_i * xhat_i,  g = dout_i * u_i,
+ *          do_i = rstd * (g - mean(g) - xhat_i * mean(g * xhat_i))
+ *          (per (token, head) over d_v, or over all H * d_v values of the
+ *          token for LN_ALL_U; epilogue NONE: do_i = dout_i)
+ *   da_ij = <do_i, v_j>,  ds_ij = da_ij * SiLU'(s_ij) / n_scale on allowed
+ *          pairs (0 elsewhere), SiLU'(x) = sig(x) (1 + x (1 - sig(x)))
+ *   dq_i = alpha sum_j ds_ij k_j,  dk_j = alpha sum_i ds_ij q_i,
+ *   dv_j = sum_i a_ij do_i,
+ *   dpos_table[min(|i-j|, P-1)] += ds_ij,  dtime_table[bucket_ij] += ds_ij.
+ *
+ * Layouts: dq, dk, dv, du have the layouts (token strides ld_q, ld_k, ld_v,
+ * ld_u) and dtype of q, k, v, u; dout has those of out (ld_out).
+ * dpos_table / dtime_table: float32 [P] / [Tt], NULL exactly when the table
+ * is.  Every token row of dq, dk, dv (and du unless the epilogue is NONE, in
+ * which case du may be NULL and is not touched) and both tables are
+ * overwritten.  The raw aggregation o that the gate needs is recomputed (one
+ * forward pass with epilogue NONE, rounded to dtype) inside the call.
+ *
+ * Execution: a scheduler kernel, then for bf16 (d = 64, 128) a dQ pass over
+ * query tiles and a dK/dV pass over key tiles (bf16 MFMA, fp32 accumulation;
+ * each token gradient written by one workgroup, so those are deterministic)
+ * and a reduction of the table gradients (fp32 sums whose order depends on
+ * the schedule only through LDS atomics within a workgroup); for fp32 two
+ * plain kernels with fp32 atomics on the tables.  Ownership, streams, error
+ * behaviour and trusted device data as for the forward.  Workspace:
+ * hstu_jagged_attn_bwd_workspace_bytes(desc) bytes, 16-byte aligned; B == 0
+ * or total_tokens == 0 only zeroes the tables.
+ */
+size_t hstu_jagged_attn_bwd_workspace_bytes(const hstu_attn_desc* desc);
+
+int hstu_jagged_attn_bwd(const hstu_attn_desc* desc,
+                         const void* q, const void* k, const void* v, const void* u,
+                         const int32_t* offsets, const int64_t* timestamps,
+                         const int32_t* num_targets, int32_t contextual_len,
+                         int32_t max_attn_len, float alpha, float n_scale,
+                         const float* pos_table, const float* time_table,
+                         const void* dout, void* dq, void* dk, void* dv, void* du,
+                         float* dpos_table, float* dtime_table,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
 const char* hstu_last_error(void);
 
 #ifdef __cplusplus

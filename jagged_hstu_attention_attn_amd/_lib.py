@@ -36,6 +36,8 @@ EXPORTS = (
     "hstu_layer_fwd",
     "hstu_jagged_attn_valid_pairs",
     "hstu_jagged_attn_grid",
+    "hstu_jagged_attn_bwd_workspace_bytes",
+    "hstu_jagged_attn_bwd",
     "hstu_last_error",
 )
 
@@ -119,6 +121,11 @@ def load() -> ctypes.CDLL:
     lib.hstu_jagged_attn_valid_pairs.argtypes = [i32, P, P, i32, i32]
     lib.hstu_jagged_attn_grid.restype = ctypes.c_int
     lib.hstu_jagged_attn_grid.argtypes = [D]
+    lib.hstu_jagged_attn_bwd_workspace_bytes.restype = sz
+    lib.hstu_jagged_attn_bwd_workspace_bytes.argtypes = [D]
+    lib.hstu_jagged_attn_bwd.restype = ctypes.c_int
+    lib.hstu_jagged_attn_bwd.argtypes = [D, P, P, P, P, P, P, P, i32, i32, f32, f32, P, P, P,
+                                         P, P, P, P, P, P, P, sz, P]
     lib.hstu_last_error.restype = ctypes.c_char_p
     lib.hstu_last_error.argtypes = []
     _lib = lib

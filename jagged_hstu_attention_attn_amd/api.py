@@ -187,6 +187,72 @@ def jagged_attn_fwd(q, k, v, u, offsets, *, timestamps=None, num_targets=None,
     return call()
 
 
+class JaggedAttnBwdCall:
+    """A reusable backward call (owns its descriptor, workspace and gradient
+    buffers).  `__call__(dout)` enqueues the whole backward on the current
+    stream and returns (dq, dk, dv, du, dpos, dtime); du is None for epilogue
+    "none", dpos / dtime are None when the table is."""
+
+    def __init__(self, q, k, v, u, offsets, *, timestamps=None, num_targets=None,
+                 contextual_len=0, max_attn_len=0, alpha, n_scale, pos_table=None,
+                 time_table=None, eps=1e-5, epilogue="ln_u"):
+        if not q.is_cuda:
+            raise ValueError("tensors must be on a GPU")
+        _check_aux(offsets, timestamps, num_targets, pos_table, time_table, q.device)
+        self.q, self.k, self.v, self.u = q, k, v, u
+        self.offsets, self.timestamps, self.num_targets = offsets, timestamps, num_targets
+        self.contextual_len, self.max_attn_len = int(contextual_len), int(max_attn_len)
+        self.alpha, self.n_scale = float(alpha), float(n_scale)
+        self.pos_table, self.time_table = pos_table, time_table
+        self.epilogue = epilogue
+        shape_o = (q.shape[0], q.shape[1], v.shape[2])
+        out_like = torch.empty(shape_o, dtype=q.dtype, device=q.device)
+        self.desc = make_desc(q, k, v, u, out_like, offsets.numel() - 1, pos_table=pos_table,
+                              time_table=time_table, eps=eps, epilogue=epilogue)
+        n = _lib.load().hstu_jagged_attn_bwd_workspace_bytes(ctypes.byref(self.desc))
+        if n == 0:
+            raise _lib.HstuError(_lib.HSTU_ERR_INVALID_ARG, _lib.last_error())
+        self.workspace = torch.empty(int(n), dtype=torch.uint8, device=q.device)
+        # gradients share the layouts of their inputs (token strides included)
+        self.dq = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
+        self.dk = torch.empty_strided(k.shape, k.stride(), dtype=k.dtype, device=k.device)
+        self.dv = torch.empty_strided(v.shape, v.stride(), dtype=v.dtype, device=v.device)
+        self.du = (None if epilogue == "none" else
+                   torch.empty_strided(u.shape, u.stride(), dtype=u.dtype, device=u.device))
+        self.dpos = None if pos_table is None else torch.empty_like(pos_table)
+        self.dtime = None if time_table is None else torch.empty_like(time_table)
+
+    def __call__(self, dout):
+        if dout.shape != (self.q.shape[0], self.q.shape[1], self.v.shape[2]):
+            raise ValueError(f"dout has shape {tuple(dout.shape)}")
+        if dout.dtype != self.q.dtype:
+            raise TypeError(f"dout has dtype {dout.dtype}, q has {self.q.dtype}")
+        if _token_stride(dout, "dout") != self.desc.ld_out:
+            raise ValueError("dout must be contiguous in its token dimension")
+        _lib.check(_lib.load().hstu_jagged_attn_bwd(
+            ctypes.byref(self.desc), _ptr(self.q), _ptr(self.k), _ptr(self.v), _ptr(self.u),
+            _ptr(self.offsets), _ptr(self.timestamps), _ptr(self.num_targets),
+            self.contextual_len, self.max_attn_len, self.alpha, self.n_scale,
+            _ptr(self.pos_table), _ptr(self.time_table), _ptr(dout), _ptr(self.dq),
+            _ptr(self.dk), _ptr(self.dv), _ptr(self.du), _ptr(self.dpos), _ptr(self.dtime),
+            _ptr(self.workspace), int(self.workspace.numel()), _stream(self.q.device)))
+        return self.dq, self.dk, self.dv, self.du, self.dpos, self.dtime
+
+
+def jagged_attn_bwd(q, k, v, u, offsets, dout, *, timestamps=None, num_targets=None,
+                    contextual_len: int = 0, max_attn_len: int = 0, alpha: float,
+                    n_scale: float, pos_table=None, time_table=None, eps: float = 1e-5,
+                    epilogue: str = "ln_u"):
+    """Gradients (dq, dk, dv, du, dpos, dtime) of sum(dout * forward(...)),
+    computed on the GPU on the current stream."""
+    call = JaggedAttnBwdCall(q, k, v, u, offsets, timestamps=timestamps,
+                             num_targets=num_targets, contextual_len=contextual_len,
+                             max_attn_len=max_attn_len, alpha=alpha, n_scale=n_scale,
+                             pos_table=pos_table, time_table=time_table, eps=eps,
+                             epilogue=epilogue)
+    return call(dout)
+
+
 def valid_pairs(offsets, num_targets=None, contextual_len: int = 0, max_attn_len: int = 0) -> int:
     """Exact allowed-pair count per head, from host copies of the metadata."""
     off = np.ascontiguousarray(np.asarray(offsets), dtype=np.int32)

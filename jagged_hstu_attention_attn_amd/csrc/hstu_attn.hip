@@ -539,3 +539,239 @@ int hstu_layer_fwd(const hstu_layer_desc* desc, const void* x, const void* w_uvq
 
 }  // extern "C"
 
+
+// ---- backward ---------------------------------------------------------------
+
+namespace {
+
+struct BwdLayout {
+  size_t o_off, do_off, hdr_off, gstart_off, lq_off, lkv_off, part_off, total;
+  bool gate;
+};
+
+BwdLayout bwd_layout(const hstu_attn_desc* d) {
+  BwdLayout l;
+  l.gate = d->epilogue != HSTU_EPILOGUE_NONE;
+  const int64_t N = d->total_tokens, H = d->num_heads;
+  const size_t es = elem_size(d->dtype);
+  const size_t rows = (size_t)(N * H * d->d_v) * es;
+  const int64_t G = hstu::bwd_groups_max(d->num_seqs, N);
+  size_t off = l.gate ? hstu::plan_layout(d->num_seqs, N, H, d->d_v).total : 0;
+  l.o_off = hstu::align256(off);
+  off = l.o_off + (l.gate ? rows : 0);
+  l.do_off = hstu::align256(off);
+  off = l.do_off + (l.gate ? rows : 0);
+  l.hdr_off = hstu::align256(off);
+  off = l.hdr_off + 256;
+  l.gstart_off = hstu::align256(off);
+  off = l.gstart_off + sizeof(int32_t) * (size_t)(d->num_seqs + 1);
+  l.lq_off = hstu::align256(off);
+  off = l.lq_off + sizeof(int2) * (size_t)(G > 0 ? G : 1);
+  l.lkv_off = hstu::align256(off);
+  off = l.lkv_off + sizeof(int2) * (size_t)(G > 0 ? G : 1);
+  l.part_off = hstu::align256(off);
+  const bool tables = d->pos_table_len > 0 || d->time_table_len > 0;
+  if (d->dtype == HSTU_DTYPE_BF16 && tables)
+    off = l.part_off + sizeof(float) * (size_t)hstu::kMaxGrid * (size_t)(d->pos_table_len + 64);
+  l.total = hstu::align256(off);
+  return l;
+}
+
+// Workgroups of a persistent backward pass (cached per device and variant).
+int bwd_pass_grid(const hstu_attn_desc* d, bool kv) {
+  struct Entry {
+    int dev, d, pos_len, has_time, kv, grid;
+  };
+  static thread_local Entry cache[16];
+  static thread_local int cache_n = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  const int has_time = d->time_table_len > 0 ? 1 : 0;
+  for (int e = 0; e < cache_n && e < 16; ++e) {
+    const Entry& c = cache[e];
+    if (c.dev == dev && c.d == d->d_v && c.pos_len == d->pos_table_len &&
+        c.has_time == has_time && c.kv == (kv ? 1 : 0))
+      return c.grid;
+  }
+  const int g = hstu::bwd_grid(d->dtype, d->d_v, d->pos_table_len, d->time_table_len, kv);
+  if (g > 0) cache[cache_n++ % 16] = Entry{dev, d->d_v, d->pos_table_len, has_time, kv ? 1 : 0, g};
+  return g;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t hstu_jagged_attn_bwd_workspace_bytes(const hstu_attn_desc* desc) {
+  if (check_desc(desc) != HSTU_OK) return 0;
+  return bwd_layout(desc).total;
+}
+
+int hstu_jagged_attn_bwd(const hstu_attn_desc* desc, const void* q, const void* k,
+                         const void* v, const void* u, const int32_t* offsets,
+                         const int64_t* timestamps, const int32_t* num_targets,
+                         int32_t contextual_len, int32_t max_attn_len, float alpha,
+                         float n_scale, const float* pos_table, const float* time_table,
+                         const void* dout, void* dq, void* dk, void* dv, void* du,
+                         float* dpos_table, float* dtime_table, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  int rc = check_desc(desc);
+  if (rc != HSTU_OK) return rc;
+  if (desc->num_seqs > 0 && !offsets) return fail(HSTU_ERR_INVALID_ARG, "offsets is NULL");
+  if (contextual_len < 0) return fail(HSTU_ERR_INVALID_ARG, "contextual_len < 0");
+  if (max_attn_len < 0) return fail(HSTU_ERR_INVALID_ARG, "max_attn_len < 0");
+  const BwdLayout bl = bwd_layout(desc);
+  if (!workspace)
+    return fail(HSTU_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", bl.total);
+  if (workspace_bytes < bl.total)
+    return fail(HSTU_ERR_WORKSPACE, "workspace has %zu bytes, need %zu", workspace_bytes,
+                bl.total);
+  if (!aligned16(workspace)) return fail(HSTU_ERR_INVALID_ARG, "workspace not 16-byte aligned");
+  if ((dpos_table == nullptr) != (desc->pos_table_len == 0))
+    return fail(HSTU_ERR_INVALID_ARG, "dpos_table and pos_table_len disagree");
+  if ((dtime_table == nullptr) != (desc->time_table_len == 0))
+    return fail(HSTU_ERR_INVALID_ARG, "dtime_table and time_table_len disagree");
+  const bool empty = desc->num_seqs == 0 || desc->total_tokens == 0;
+  if (!empty) {
+    rc = check_run_args(desc, q, k, v, u, timestamps, alpha, n_scale, pos_table, time_table,
+                        dout);
+    if (rc != HSTU_OK) return rc;
+    struct {
+      const char* name;
+      const void* p;
+    } g[] = {{"dq", dq}, {"dk", dk}, {"dv", dv}, {"du", du}};
+    for (auto& x : g) {
+      if (x.name[1] == 'u' && desc->epilogue == HSTU_EPILOGUE_NONE) continue;
+      if (!x.p) return fail(HSTU_ERR_INVALID_ARG, "%s is NULL", x.name);
+      if (!aligned16(x.p)) return fail(HSTU_ERR_INVALID_ARG, "%s is not 16-byte aligned", x.name);
+    }
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  const bool bf16 = desc->dtype == HSTU_DTYPE_BF16;
+  // the table gradients are sums: zero them where no pass writes them whole
+  if (empty || !bf16) {
+    if (dpos_table) e = hstu::launch_fill_zero(dpos_table, desc->pos_table_len, s);
+    if (e == hipSuccess && dtime_table)
+      e = hstu::launch_fill_zero(dtime_table, desc->time_table_len, s);
+    if (e != hipSuccess) return fail(HSTU_ERR_HIP, "fill launch failed: %s", hipGetErrorString(e));
+  }
+  if (empty) return HSTU_OK;
+
+  int n_q = 0, n_kv = 0;
+  if (bf16) {
+    n_q = bwd_pass_grid(desc, false);
+    n_kv = bwd_pass_grid(desc, true);
+    if (n_q <= 0 || n_kv <= 0)
+      return fail(HSTU_ERR_HIP, "cannot query the device for the launch size");
+  }
+  char* ws = static_cast<char*>(workspace);
+  const int64_t H = desc->num_heads;
+  const void* d_o = dout;
+  int64_t ld_do = desc->ld_out;
+  if (bl.gate) {
+    // the gate needs the raw aggregation o: the forward again with epilogue none
+    hstu_attn_desc fd = *desc;
+    fd.epilogue = HSTU_EPILOGUE_NONE;
+    fd.ld_out = H * desc->d_v;
+    void* o = ws + bl.o_off;
+    rc = hstu_jagged_attn_fwd(&fd, q, k, v, nullptr, offsets, timestamps, num_targets,
+                              contextual_len, max_attn_len, alpha, n_scale, pos_table, time_table,
+                              o, ws, bl.o_off, stream);
+    if (rc != HSTU_OK) return rc;
+    hstu::GateBwdArgs ga;
+    ga.o = o;
+    ga.u = u;
+    ga.dy = dout;
+    ga.du = du;
+    ga.d_o = ws + bl.do_off;
+    ga.ld_o = H * desc->d_v;
+    ga.ld_u = desc->ld_u;
+    ga.ld_dy = desc->ld_out;
+    ga.n_tok = desc->total_tokens;
+    const bool all = desc->epilogue == HSTU_EPILOGUE_LN_ALL_U;
+    ga.groups = all ? 1 : desc->num_heads;
+    ga.width = all ? desc->num_heads * desc->d_v : desc->d_v;
+    ga.eps = desc->ln_eps;
+    e = hstu::launch_gate_bwd(ga, desc->dtype, s);
+    if (e != hipSuccess)
+      return fail(HSTU_ERR_HIP, "gate backward launch failed: %s", hipGetErrorString(e));
+    d_o = ws + bl.do_off;
+    ld_do = H * desc->d_v;
+  }
+
+  hstu::BwdArgs ba;
+  ba.q = q;
+  ba.k = k;
+  ba.v = v;
+  ba.dout = d_o;
+  ba.dq = dq;
+  ba.dk = dk;
+  ba.dv = dv;
+  ba.offsets = offsets;
+  ba.timestamps = time_table ? timestamps : nullptr;
+  ba.num_targets = num_targets;
+  ba.pos_table = pos_table;
+  ba.time_table = time_table;
+  ba.dpos = dpos_table;
+  ba.dtime = dtime_table;
+  ba.tab_part = reinterpret_cast<float*>(ws + bl.part_off);
+  ba.hdr = reinterpret_cast<int32_t*>(ws + bl.hdr_off);
+  ba.list = nullptr;
+  ba.ld_q = desc->ld_q;
+  ba.ld_k = desc->ld_k;
+  ba.ld_v = desc->ld_v;
+  ba.ld_do = ld_do;
+  ba.num_heads = desc->num_heads;
+  ba.contextual_len = contextual_len;
+  ba.max_attn_len = max_attn_len;
+  ba.pos_len = desc->pos_table_len;
+  ba.time_len = desc->time_table_len;
+  ba.n_tok = desc->total_tokens;
+  ba.alpha = alpha;
+  ba.inv_scale = (float)(1.0 / (double)n_scale);
+  if (!bf16) {
+    e = hstu::launch_bwd_dq(ba, desc->dtype, desc->d_v, desc->num_seqs, s);
+    if (e == hipSuccess) e = hstu::launch_bwd_dkv(ba, desc->dtype, desc->d_v, desc->num_seqs, s);
+    if (e != hipSuccess)
+      return fail(HSTU_ERR_HIP, "backward launch failed: %s", hipGetErrorString(e));
+    return HSTU_OK;
+  }
+
+  hstu::BwdPlanArgs pa;
+  pa.offsets = offsets;
+  pa.num_targets = num_targets;
+  pa.num_seqs = desc->num_seqs;
+  pa.contextual_len = contextual_len;
+  pa.max_attn_len = max_attn_len;
+  pa.hdr = reinterpret_cast<int32_t*>(ws + bl.hdr_off);
+  pa.gstart = reinterpret_cast<int32_t*>(ws + bl.gstart_off);
+  pa.list_q = reinterpret_cast<int2*>(ws + bl.lq_off);
+  pa.list_kv = reinterpret_cast<int2*>(ws + bl.lkv_off);
+  e = hstu::launch_bwd_plan(pa, s);
+  if (e != hipSuccess)
+    return fail(HSTU_ERR_HIP, "backward scheduler launch failed: %s", hipGetErrorString(e));
+  ba.list = pa.list_q;
+  e = hstu::launch_bwd_dq(ba, desc->dtype, desc->d_v, n_q, s);
+  if (e != hipSuccess) return fail(HSTU_ERR_HIP, "dQ launch failed: %s", hipGetErrorString(e));
+  ba.list = pa.list_kv;
+  e = hstu::launch_bwd_dkv(ba, desc->dtype, desc->d_v, n_kv, s);
+  if (e != hipSuccess) return fail(HSTU_ERR_HIP, "dK/dV launch failed: %s", hipGetErrorString(e));
+  if (desc->pos_table_len > 0 || desc->time_table_len > 0) {
+    hstu::TabReduceArgs ra;
+    ra.part = ba.tab_part;
+    ra.dpos = dpos_table;
+    ra.dtime = dtime_table;
+    ra.n_part = n_kv;
+    ra.stride = desc->pos_table_len + 64;
+    ra.pos_len = desc->pos_table_len;
+    ra.time_len = desc->time_table_len;
+    ra.scale = ba.inv_scale;
+    e = hstu::launch_tab_reduce(ra, s);
+    if (e != hipSuccess)
+      return fail(HSTU_ERR_HIP, "table reduction launch failed: %s", hipGetErrorString(e));
+  }
+  return HSTU_OK;
+}
+
+}  // extern "C"

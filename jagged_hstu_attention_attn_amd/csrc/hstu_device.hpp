@@ -220,6 +220,103 @@ struct LnArgs {
   float eps;
 };
 
+// Allowed query rows of key j -- the same rules read by column: a candidate
+// key (j >= n_h) is seen by its own row only; any other key by the rows
+// [j < c ? 0 : j, hi_j], where hi_j = L - 1 when the key is within the window
+// of the history end (W == 0 or j + W >= n_h: the candidates see it, and so
+// does every later history row), else j + W.  Same encoding as RowBounds:
+// (unsigned)(i - lo) <= span, or i == self_j.
+__host__ __device__ inline RowBounds col_bounds(const SeqGeom& g, int j) {
+  RowBounds r;
+  if (j >= g.n_h) {
+    r.lo = kEmptyLo;
+    r.span = 0;
+    r.self_j = j;
+    return r;
+  }
+  const int lo = j < g.c ? 0 : j;
+  const int hi = (g.W == 0 || j + g.W >= g.n_h) ? g.L - 1 : j + g.W;
+  r.lo = lo;
+  r.span = hi - lo;
+  r.self_j = -1;
+  return r;
+}
+
+// Backward.  Work is listed as (sequence, 128-token tile) groups, sorted by
+// decreasing cost twice: once for the dQ pass (query tiles, cost = key
+// steps) and once for the dK/dV pass (key tiles, cost = query steps); item
+// v of a pass is group list[v / H], head v % H.
+constexpr int kBwdCostBins = 1024;
+
+__host__ inline int64_t bwd_groups_max(int64_t num_seqs, int64_t total_tokens) {
+  return (total_tokens + num_seqs * (kBM - 1)) / kBM;
+}
+
+struct BwdPlanArgs {
+  const int32_t* offsets;
+  const int32_t* num_targets;
+  int32_t num_seqs;
+  int32_t contextual_len;
+  int32_t max_attn_len;
+  int32_t* hdr;       // [0]: groups
+  int32_t* gstart;    // int32[B + 1]: first group of each sequence
+  int2* list_q;       // groups by decreasing dQ cost: (sequence, tile)
+  int2* list_kv;      // groups by decreasing dK/dV cost
+};
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dout;          // dLoss / dO (the gate's input gradient)
+  void* dq;
+  void* dk;
+  void* dv;
+  const int32_t* offsets;
+  const int64_t* timestamps;
+  const int32_t* num_targets;
+  const float* pos_table;
+  const float* time_table;
+  float* dpos;               // fp32 kernels: table gradients, accumulated
+  float* dtime;
+  float* tab_part;           // MFMA kernels: per-workgroup table sums
+  const int32_t* hdr;
+  const int2* list;
+  int64_t ld_q, ld_k, ld_v, ld_do;
+  int32_t num_heads;
+  int32_t contextual_len;
+  int32_t max_attn_len;
+  int32_t pos_len;
+  int32_t time_len;
+  int32_t n_tok;
+  float alpha;
+  float inv_scale;           // 1 / n_scale
+};
+
+struct GateBwdArgs {
+  const void* o;             // raw aggregated output (epilogue NONE), ld = ld_o
+  const void* u;
+  const void* dy;            // dLoss / d(out)
+  void* du;
+  void* d_o;                 // dLoss / dO, ld = ld_o
+  int64_t ld_o, ld_u, ld_dy;
+  int32_t n_tok;
+  int32_t groups;            // LayerNorm groups per token
+  int32_t width;             // values per group
+  float eps;
+};
+
+struct TabReduceArgs {
+  const float* part;         // [n_part][stride]
+  float* dpos;
+  float* dtime;
+  int32_t n_part;
+  int32_t stride;            // pos_len + 64
+  int32_t pos_len;
+  int32_t time_len;
+  float scale;
+};
+
 // Launchers (defined in the .hip files).
 hipError_t launch_plan(const PlanArgs& a, bool compact, hipStream_t stream);
 hipError_t launch_attn(const AttnArgs& a, int dtype, int d_qk, int d_v, int n_wg,
@@ -230,5 +327,14 @@ int attn_grid(int dtype, int d_qk, int d_v, int pos_len, int time_len);
 bool attn_supported(int dtype, int d_qk, int d_v);
 int ln_all_heads_max_width(int dtype);
 hipError_t launch_ln_all_heads(const LnArgs& a, int dtype, hipStream_t stream);
+hipError_t launch_bwd_plan(const BwdPlanArgs& a, hipStream_t stream);
+hipError_t launch_gate_bwd(const GateBwdArgs& a, int dtype, hipStream_t stream);
+// Workgroups of the persistent dQ / dK-dV launches for this shape (CUs x
+// resident workgroups per CU), or a negative value on error.
+int bwd_grid(int dtype, int d, int pos_len, int time_len, bool kv);
+hipError_t launch_bwd_dq(const BwdArgs& a, int dtype, int d, int n_wg, hipStream_t stream);
+hipError_t launch_bwd_dkv(const BwdArgs& a, int dtype, int d, int n_wg, hipStream_t stream);
+hipError_t launch_tab_reduce(const TabReduceArgs& a, hipStream_t stream);
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream);
 
 }  // namespace hstu
