@@ -142,6 +142,68 @@ def bench_layer(args, inp) -> int:
     return 0
 
 
+def bench_backward(args, inp) -> int:
+    """Backward timing: one step = the whole backward call (o recomputed by
+    the forward kernel when the epilogue needs it, gate backward, scheduler,
+    dQ pass, dK/dV pass, table reduction) on one batch already in HBM, with
+    dout given.  Flops counted: 2 (3 d_qk + 2 d_v) per valid pair and head
+    (S, dA, dV, dK, dQ contractions; the recomputation is not counted)."""
+    import torch
+    from jagged_hstu_attention_attn_amd.api import JaggedAttnBwdCall, valid_pairs
+    from jagged_hstu_attention_attn_amd.device_inputs import call_kwargs, to_device
+    from jagged_hstu_attention_attn_amd.inputs import WORKLOADS
+    dev = to_device(inp, "cuda")
+    call = JaggedAttnBwdCall(dev["q"], dev["k"], dev["v"], dev["u"], dev["offsets"],
+                             epilogue=args.epilogue, **call_kwargs(inp, dev))
+    dt = dev["q"].dtype
+    g = torch.Generator(device="cuda").manual_seed(0)
+    dout = torch.randn(dev["v"].shape, generator=g, device="cuda", dtype=torch.float32).to(dt)
+    pairs = valid_pairs(inp.offsets, inp.num_targets, inp.contextual_len, inp.max_attn_len)
+    H, dqk, dv = inp.num_heads, inp.d_qk, inp.d_v
+    fpp = 2.0 * (3 * dqk + 2 * dv)
+    flops = fpp * H * pairs
+    flush = None if args.no_flush else torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    log(f"backward: {inp.num_seqs} sequences, {inp.total_tokens} tokens, {pairs} valid "
+        f"pairs/head; warmup {args.warmup}")
+    for _ in range(args.warmup):
+        call(dout)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    wall0 = time.perf_counter()
+    for s, (e0, e1) in enumerate(evs):
+        if flush is not None:
+            flush.fill_(s & 0xFF)
+        e0.record(stream)
+        call(dout)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = sum(a.elapsed_time(b) for a, b in evs) / len(evs)
+    tflops = flops / (ms * 1e-3) / 1e12
+    log(f"backward step {ms * 1e3:.1f} us, {tflops:.1f} TFLOP/s")
+    result = {
+        "metric": "jagged HSTU attn bwd TFLOP/s (valid pairs, 5 contractions)",
+        "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": inp.dtype, "data": "synthetic",
+        "config": {"workload": args.workload, "pass": "backward", "epilogue": args.epilogue,
+                   "num_seqs": inp.num_seqs, "total_tokens": inp.total_tokens,
+                   "num_heads": H, "d_qk": dqk, "d_v": dv, "valid_pairs_per_head": pairs,
+                   "seed": args.seed if args.seed is not None else WORKLOADS[args.workload].seed,
+                   "cache_flushed": flush is not None, "parallelism": "single GPU"},
+        "tokens_per_s": inp.total_tokens / (ms * 1e-3),
+        "pct_bf16_mfma_peak": 100.0 * tflops / PEAK_TFLOPS["bf16"],
+        "wall_s": wall,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the fp64 CPU oracle backward")
+        result["cpu_baseline"] = cpu_baseline(inp, fpp, args.cpu_budget, backward=True)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def traffic_from_profile(workload: str):
     """HBM bytes per attention launch from the committed counter summary, if
     it was taken on the current kernel source; else None."""
@@ -156,18 +218,28 @@ def traffic_from_profile(workload: str):
     return float(m_bytes.group(1))
 
 
-def cpu_baseline(inp, flops_per_pair_head: float, budget_s: float):
+def cpu_baseline(inp, flops_per_pair_head: float, budget_s: float, backward: bool = False):
     """The fp64 oracle, as it stands, on this host's cores over a bounded
     prefix of the batch (whole sequences), in the metric's unit."""
     import numpy as np
     import oracle
     oracle.build(force=False)
     from jagged_hstu_attention_attn_amd.inputs import make_inputs
-    # estimate from a small prefix, then take the largest prefix within budget
     nthreads = oracle.default_threads()
+
+    def timed(x):
+        if not backward:
+            return oracle.timed_forward(x, nthreads=nthreads)[1]
+        dout = np.random.default_rng(0).standard_normal(
+            (x.total_tokens, x.num_heads, x.d_v))
+        t0 = time.perf_counter()
+        oracle.backward(x, dout, nthreads=nthreads)
+        return time.perf_counter() - t0
+
+    # estimate from a small prefix, then take the largest prefix within budget
     B = inp.num_seqs
     probe = make_inputs(inp.workload, num_seqs=max(1, min(B, 4)), dtype=inp.dtype)
-    _, t_probe, _ = oracle.timed_forward(probe, nthreads=nthreads)
+    t_probe = timed(probe)
     pairs_probe = oracle.count_allowed(probe.offsets, probe.num_targets, probe.contextual_len,
                                        probe.max_attn_len)
     rate = pairs_probe / max(t_probe, 1e-6)
@@ -190,12 +262,14 @@ def cpu_baseline(inp, flops_per_pair_head: float, budget_s: float):
     sample = make_inputs(inp.workload, num_seqs=nb, dtype=inp.dtype) if nb < B else inp
     pairs = oracle.count_allowed(sample.offsets, sample.num_targets, sample.contextual_len,
                                  sample.max_attn_len)
-    _, secs, used = oracle.timed_forward(sample, nthreads=nthreads)
+    secs = timed(sample)
+    used = nthreads
     tflops = flops_per_pair_head * sample.num_heads * pairs / secs / 1e12
     return {
         "value": tflops, "unit": "TFLOP/s", "cores": used, "kind": "oracle",
         "sample": (f"{nb} of {B} sequences of the {inp.workload} batch "
-                   f"({sample.total_tokens} tokens, {sample.num_heads} heads, fp64 C loop, "
+                   f"({sample.total_tokens} tokens, {sample.num_heads} heads, "
+                   f"{'backward, ' if backward else ''}fp64 C loop, "
                    f"OpenMP over (sequence, head)), {secs:.2f} s"),
         "seconds": secs, "tokens_per_s": sample.total_tokens / secs,
     }
@@ -219,6 +293,8 @@ def main() -> int:
                          "projection GEMM, attention, output GEMM)")
     ap.add_argument("--candidates-only", action="store_true",
                     help="compute only the candidate rows (history reused; no CPU baseline)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward (gradients of q, k, v, u and the bias tables)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 256 MiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -251,6 +327,8 @@ def main() -> int:
             print("--full-layer needs the layer workload", file=sys.stderr)
             return 2
         return bench_layer(args, inp)
+    if args.backward:
+        return bench_backward(args, inp)
     dev = to_device(inp, "cuda")
     call = JaggedAttnCall(dev["q"], dev["k"], dev["v"], dev["u"], dev["offsets"],
                           candidates_only=args.candidates_only, epilogue=args.epilogue,

@@ -164,6 +164,15 @@ __device__ inline float wave_sum_f(float x) {
 // Register r of a 32x32 accumulator (lane half hh) holds row 8(r/4) + 4hh + r%4.
 __device__ constexpr int acc_row(int r, int hh) { return 8 * (r >> 2) + 4 * hh + (r & 3); }
 
+// The lane index as a value the compiler cannot see through: offsets derived
+// from it inside the step loop are recomputed there (a few VALU operations)
+// instead of being hoisted and kept live in registers for every stage buffer.
+__device__ inline int opaque_lane() {
+  int l = (int)(threadIdx.x & 63);
+  asm volatile("" : "+v"(l));
+  return l;
+}
+
 // Query rows [rlo, rhi] that keys [j0, j1) can be seen by (col_bounds is
 // nondecreasing in both ends over the history keys; candidate keys are seen
 // by their own rows only).
@@ -317,53 +326,71 @@ __device__ inline void st_chunk(T* p, const float* x) {
   }
 }
 
-template <typename T, int EPC>
+// G lanes share one group (G a power of two, G * CPL * EPC >= width); a wave
+// holds 64 / G groups.  The values stay in registers between the passes.
+template <typename T, int EPC, int G, int CPL>
 __global__ __launch_bounds__(256) void hstu_gate_bwd_kernel(GateBwdArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (w >= (int64_t)a.n_tok * a.groups) return;   // whole waves leave together
-  const int64_t t = w / a.groups;
-  const int64_t col = (w - t * a.groups) * (int64_t)a.width;
+  const int lane = threadIdx.x & 63, sub = lane & (G - 1);
+  const int64_t w = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * (64 / G) + lane / G;
+  const bool live = w < (int64_t)a.n_tok * a.groups;
+  const int64_t ww = live ? w : 0;   // dead groups compute on group 0 and store nothing
+  const int64_t t = ww / a.groups;
+  const int64_t col = (ww - t * a.groups) * (int64_t)a.width;
   const T* o = static_cast<const T*>(a.o) + t * a.ld_o + col;
   const T* u = static_cast<const T*>(a.u) + t * a.ld_u + col;
   const T* dy = static_cast<const T*>(a.dy) + t * a.ld_dy + col;
-  T* du = static_cast<T*>(a.du) + t * a.ld_u + col;
-  T* d_o = static_cast<T*>(a.d_o) + t * a.ld_o + col;
   const int chunks = a.width / EPC;
   const float inv_w = 1.0f / (float)a.width;
-  float x[EPC], uu[EPC], yy[EPC], r0[EPC], r1[EPC];
-  float sum = 0.0f;
-  for (int c = lane; c < chunks; c += 64) {
-    ld_chunk<T, EPC>(o + EPC * c, x);
+  auto gsum = [](float x) {
 #pragma unroll
-    for (int e = 0; e < EPC; ++e) sum += x[e];
+    for (int m = G / 2; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
+    return x;
+  };
+  float x[CPL][EPC], uu[CPL][EPC], yy[CPL][EPC];
+  float sum = 0.0f;
+#pragma unroll
+  for (int k = 0; k < CPL; ++k) {
+    const int c = sub + G * k;
+    if (c < chunks) {
+      ld_chunk<T, EPC>(o + EPC * c, x[k]);
+      ld_chunk<T, EPC>(u + EPC * c, uu[k]);
+      ld_chunk<T, EPC>(dy + EPC * c, yy[k]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) x[k][e] = uu[k][e] = yy[k][e] = 0.0f;
+    }
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) sum += x[k][e];
   }
-  const float mean = wave_sum_f(sum) * inv_w;
+  const float mean = gsum(sum) * inv_w;
   float sq = 0.0f, sg = 0.0f, sgx = 0.0f;
-  for (int c = lane; c < chunks; c += 64) {
-    ld_chunk<T, EPC>(o + EPC * c, x);
-    ld_chunk<T, EPC>(u + EPC * c, uu);
-    ld_chunk<T, EPC>(dy + EPC * c, yy);
+#pragma unroll
+  for (int k = 0; k < CPL; ++k) {
+    if (sub + G * k >= chunks) continue;
 #pragma unroll
     for (int e = 0; e < EPC; ++e) {
-      const float xc = x[e] - mean, g = yy[e] * uu[e];
+      const float xc = x[k][e] - mean, g = yy[k][e] * uu[k][e];
       sq += xc * xc;
       sg += g;
       sgx += g * xc;
     }
   }
-  const float rstd = rsqrtf(wave_sum_f(sq) * inv_w + a.eps);
-  const float mg = wave_sum_f(sg) * inv_w;
-  const float mgx = wave_sum_f(sgx) * inv_w * rstd;   // mean(g * xhat)
-  for (int c = lane; c < chunks; c += 64) {
-    ld_chunk<T, EPC>(o + EPC * c, x);
-    ld_chunk<T, EPC>(u + EPC * c, uu);
-    ld_chunk<T, EPC>(dy + EPC * c, yy);
+  const float rstd = rsqrtf(gsum(sq) * inv_w + a.eps);
+  const float mg = gsum(sg) * inv_w;
+  const float mgx = gsum(sgx) * inv_w * rstd;   // mean(g * xhat)
+  if (!live) return;
+  T* du = static_cast<T*>(a.du) + t * a.ld_u + col;
+  T* d_o = static_cast<T*>(a.d_o) + t * a.ld_o + col;
+#pragma unroll
+  for (int k = 0; k < CPL; ++k) {
+    const int c = sub + G * k;
+    if (c >= chunks) continue;
+    float r0[EPC], r1[EPC];
 #pragma unroll
     for (int e = 0; e < EPC; ++e) {
-      const float xh = (x[e] - mean) * rstd;
-      r0[e] = yy[e] * xh;
-      r1[e] = rstd * (yy[e] * uu[e] - mg - xh * mgx);
+      const float xh = (x[k][e] - mean) * rstd;
+      r0[e] = yy[k][e] * xh;
+      r1[e] = rstd * (yy[k][e] * uu[k][e] - mg - xh * mgx);
     }
     st_chunk<T, EPC>(du + EPC * c, r0);
     st_chunk<T, EPC>(d_o + EPC * c, r1);
@@ -769,11 +796,12 @@ hstu_bwd_dq_kernel(BwdArgs a) {
       if (wave_rows && jb <= w_jmax && jb + kStep - 1 >= w_jmin) {
         const SB& sb = st[b];
         const uint32_t xt = lds_off(sb.x), yt = lds_off(sb.y);
-        floatx16 s = pp.diag_init(sb, dbase);
-        s = PP::contract(xt, l32, hh, qf, s);
+        const int ol = opaque_lane(), ol32 = ol & 31, ohh = ol >> 5;
+        floatx16 s = pp.diag_init(sb, (kBM - 1) - 32 * wave - ol32 + 4 * ohh);
+        s = PP::contract(xt, ol32, ohh, qf, s);
         __builtin_amdgcn_sched_barrier(0);
         floatx16 da = {};
-        da = PP::contract(yt, l32, hh, dof, da);
+        da = PP::contract(yt, ol32, ohh, dof, da);
         __builtin_amdgcn_sched_barrier(0);
 
         // dS^T = dA^T SiLU'(x), zero on illegal pairs (time bias, SiLU'
@@ -826,7 +854,7 @@ hstu_bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
           for (int u2 = 0; u2 < 2; ++u2)
 #pragma unroll
-            for (int ins = 0; ins < 2; ++ins) kt4[2 * u2 + ins] = PP::tr_op(xt, lane, db + u2, ins);
+            for (int ins = 0; ins < 2; ++ins) kt4[2 * u2 + ins] = PP::tr_op(xt, ol, db + u2, ins);
 #pragma unroll
           for (int u2 = 0; u2 < 2; ++u2)
 #pragma unroll
@@ -857,17 +885,22 @@ hstu_bwd_dq_kernel(BwdArgs a) {
   }
 }
 
-template <int D, bool POS, bool TIME>
+// M: 0 = dK, dV and the table sums in one pass; 1 = dK and the table sums;
+// 2 = dV only.  At d = 128 the fused pass would need more registers than two
+// waves per SIMD leave (K and V operands plus two 32 x 128 fp32
+// accumulators), so it runs as passes 1 and 2, which recompute S.
+template <int D, bool POS, bool TIME, int M>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void
 hstu_bwd_dkv_kernel(BwdArgs a) {
+  constexpr bool DK = M != 2, DV = M != 1, TABS = DK;
   using C = BCfg<D>;
   using SB = BStage<D>;
   using PP = Pipe<D, POS, TIME>;
   constexpr int NC = C::kNC, NDB = C::kNDB;
   __shared__ __align__(16) SB st[kStages];
   __shared__ float trev[32], tful[64];
-  __shared__ float htime[TIME ? kTimeBins * 32 : 1];   // [bin][lane % 32]
-  extern __shared__ float hpos[];                      // [pos_len] (POS only)
+  __shared__ float htime[(TIME && TABS) ? kTimeBins * 32 : 1];   // [bin][lane % 32]
+  extern __shared__ float hpos[];                      // [pos_len] (POS && TABS only)
 
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
   const int wave = uni(tid >> 6);
@@ -878,9 +911,10 @@ hstu_bwd_dkv_kernel(BwdArgs a) {
     const int Tt = a.time_len;
     if (tid < 32) trev[tid] = a.time_table[min(31 - tid, Tt - 1)];
     if (tid < 64) tful[tid] = a.time_table[min(tid, Tt - 1)];
-    for (int e = tid; e < kTimeBins * 32; e += kThreads) htime[e] = 0.0f;
+    if constexpr (TABS)
+      for (int e = tid; e < kTimeBins * 32; e += kThreads) htime[e] = 0.0f;
   }
-  if constexpr (POS)
+  if constexpr (POS && TABS)
     for (int e = tid; e < P; e += kThreads) hpos[e] = 0.0f;
   PP pp;
   pp.init(st, trev, tful, wave, lane, P, 1.0f / am, a.ld_q, a.ld_do);
@@ -933,7 +967,7 @@ hstu_bwd_dkv_kernel(BwdArgs a) {
     issue(0, st_lo);
     if (st_lo + 1 <= st_hi) issue(1, st_lo + 1);
     // K and V rows of this lane's key (B operands), key times
-    bf16x8 kf[NC], vf[NC];
+    bf16x8 kf[NC], vf[DK ? NC : 1];
     {
       const int jr = min(j, j1 - 1);
       const char* krow = reinterpret_cast<const char*>(a.k) +
@@ -944,9 +978,9 @@ hstu_bwd_dkv_kernel(BwdArgs a) {
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         const bf16x8 kv = *reinterpret_cast<const bf16x8*>(krow + 16 * (2 * c + hh));
-        const bf16x8 vv = *reinterpret_cast<const bf16x8*>(vrow + 16 * (2 * c + hh));
+        const bf16x8 vv = DK ? *reinterpret_cast<const bf16x8*>(vrow + 16 * (2 * c + hh)) : z;
         kf[c] = (key_valid && !alpha_zero) ? kv : z;
-        vf[c] = key_valid ? vv : z;
+        if constexpr (DK) vf[c] = key_valid ? vv : z;
       }
     }
     int64_t tj64 = 0;
@@ -960,13 +994,13 @@ hstu_bwd_dkv_kernel(BwdArgs a) {
     pp.finish(0, st_lo * kStep, L);
     stage_barrier();
 
-    floatx16 acck[NDB], accv[NDB];
+    floatx16 acck[DK ? NDB : 1], accv[DV ? NDB : 1];
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        acck[db][r] = 0.0f;
-        accv[db][r] = 0.0f;
+        if constexpr (DK) acck[db][r] = 0.0f;
+        if constexpr (DV) accv[db][r] = 0.0f;
       }
 
     int b = 0;
@@ -982,30 +1016,66 @@ hstu_bwd_dkv_kernel(BwdArgs a) {
       if (wave_keys && ib <= w_rmax && ib + kStep - 1 >= w_rmin) {
         const SB& sb = st[b];
         const uint32_t xt = lds_off(sb.x), yt = lds_off(sb.y);
+        const int ol = opaque_lane(), ol32 = ol & 31, ohh = ol >> 5;
         // S[i][j] (rows in registers, this lane's key in the column)
-        floatx16 s = pp.diag_init(sb, dbase);
-        s = PP::contract(xt, l32, hh, kf, s);
+        floatx16 s = pp.diag_init(sb, (kBM - 1) - 32 * wave - ol32 + 4 * ohh);
+        s = PP::contract(xt, ol32, ohh, kf, s);
         __builtin_amdgcn_sched_barrier(0);
         floatx16 da = {};
-        da = PP::contract(yt, l32, hh, vf, da);
-        __builtin_amdgcn_sched_barrier(0);
-        // A and dS (time bias, SiLU, SiLU', mask and the table sums fused
-        // per register)
-        float av[16], ds[16];
+        if constexpr (DK) {
+          da = PP::contract(yt, ol32, ohh, vf, da);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        // A and dS (time bias, SiLU, SiLU', mask, bf16 packing and the table
+        // sums fused per register group)
+        bf16x8 pa[2], pd[2];
         {
           float tb;
           int cbin;
           const int mode = pp.time_mode(sb, tb, cbin);
           const bool full = w_lomax <= ib && w_himin >= ib + kStep - 1;
           const int il = ib + 4 * hh - cb.lo, is = ib + 4 * hh - cb.self_j;
-          const int rel0 = ib + 4 * hh - j;
+          const int R0 = ib - wk0;   // i - j of register r: R0 + acc_row(r, hh) - l32
+          // Time-bin sums: a lane's registers run over rows in increasing
+          // order, along which the bin of |t_i - t_j| changes only a few
+          // times when times grow with position, so each lane adds up runs
+          // of equal bins and touches the LDS sums only where a run ends.
+          auto tflush = [&](int bin, float v) __attribute__((always_inline)) {
+            if (v != 0.0f)
+              __hip_atomic_fetch_add(&htime[bin * 32 + ol32], v, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_WORKGROUP);
+          };
+          // Position-bin sums of register group g (rows 8g + 4hh + e): lane c
+          // gathers register 4g+e of lane c+e (same lane half), so that its
+          // four terms share i - j = R0 + 8g + 4hh - c; terms that wrap
+          // around the 32 keys (key c + e - 32, i - j 32 higher) go to a
+          // second sum.
+          auto pflush = [&](int g, const float* dg) __attribute__((always_inline)) {
+            float A = dg[0], Bw = 0.0f;
+#pragma unroll
+            for (int e = 1; e < 4; ++e) {
+              const int src = ((ol32 + e) & 31) + 32 * ohh;
+              const float v = __builtin_bit_cast(
+                  float, __builtin_amdgcn_ds_bpermute(4 * src, __builtin_bit_cast(int, dg[e])));
+              if (ol32 + e >= 32) Bw += v; else A += v;
+            }
+            const int ra = R0 + 8 * g + 4 * ohh - ol32, rb = ra + 32;
+            if (A != 0.0f)
+              __hip_atomic_fetch_add(&hpos[min(ra < 0 ? -ra : ra, P - 1)], A, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_WORKGROUP);
+            if (Bw != 0.0f)
+              __hip_atomic_fetch_add(&hpos[min(rb < 0 ? -rb : rb, P - 1)], Bw, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_WORKGROUP);
+          };
           auto elem = [&](auto mc) __attribute__((always_inline)) {
             constexpr int MODE = decltype(mc)::value;
-            float tsum = 0.0f;
+            float run = 0.0f;
+            int prev = cbin;
 #pragma unroll
             for (int gq = 0; gq < 4; ++gq) {
               uint4 t4 = {};
               if constexpr (MODE == 1) t4 = *reinterpret_cast<const uint4*>(&sb.ts32[8 * gq + 4 * hh]);
+              float dg[4];
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
                 const int r = 4 * gq + e, kk = 8 * gq + e;
@@ -1013,45 +1083,35 @@ hstu_bwd_dkv_kernel(BwdArgs a) {
                 const float t = MODE == 0 ? tb : pp.template pair_time<MODE>(sb, t4, r, hh, tj64, bin);
                 const float x = fmaf(s[r], am, t);
                 const float sg = sigm(x);
-                float aa = x * sg, d = da[r] * (sg * fmaf(x, 1.0f - sg, 1.0f));
+                float aa = x * sg, d = DK ? da[r] * (sg * fmaf(x, 1.0f - sg, 1.0f)) : 0.0f;
                 if (!full) {
                   const bool ok = (uint32_t)(il + kk) <= (uint32_t)cb.span || is + kk == 0;
                   aa = ok ? aa : 0.0f;
                   d = ok ? d : 0.0f;
                 }
-                av[r] = aa;
-                ds[r] = d;
-                if constexpr (POS) {
-                  const int dd = rel0 + kk;
-                  const int ix = min(dd < 0 ? -dd : dd, P - 1);
-                  __hip_atomic_fetch_add(&hpos[ix], d, __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_WORKGROUP);
-                }
-                if constexpr (TIME) {
-                  if constexpr (MODE == 0) {
-                    tsum += d;
-                  } else {
-                    __hip_atomic_fetch_add(&htime[bin * 32 + l32], d, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_WORKGROUP);
+                if constexpr (DV) pa[gq >> 1][4 * (gq & 1) + e] = (__bf16)aa;
+                if constexpr (DK) pd[gq >> 1][4 * (gq & 1) + e] = (__bf16)d;
+                dg[e] = d;
+                if constexpr (TIME && TABS) {
+                  if constexpr (MODE != 0) {
+                    if (r == 0) {
+                      prev = bin;
+                    } else if (bin != prev) {
+                      tflush(prev, run);
+                      run = 0.0f;
+                      prev = bin;
+                    }
                   }
+                  run += d;
                 }
               }
+              if constexpr (POS && TABS) pflush(gq, dg);
             }
-            if constexpr (TIME && MODE == 0)
-              __hip_atomic_fetch_add(&htime[cbin * 32 + l32], tsum, __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_WORKGROUP);
+            if constexpr (TIME && TABS) tflush(prev, run);
           };
           if (mode == 0) elem(std::integral_constant<int, 0>{});
           else if (mode == 1) elem(std::integral_constant<int, 1>{});
           else elem(std::integral_constant<int, 2>{});
-        }
-        bf16x8 pa[2], pd[2];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          pa[0][e] = (__bf16)av[e];
-          pa[1][e] = (__bf16)av[8 + e];
-          pd[0][e] = (__bf16)ds[e];
-          pd[1][e] = (__bf16)ds[8 + e];
         }
         __builtin_amdgcn_sched_barrier(0);
         // dV^T += dO^T A and dK^T += Q^T dS, one d-block of operands at a time
@@ -1060,15 +1120,17 @@ hstu_bwd_dkv_kernel(BwdArgs a) {
           bf16x8 t4[4];
 #pragma unroll
           for (int ins = 0; ins < 2; ++ins) {
-            t4[ins] = PP::tr_op(yt, lane, db, ins);
-            t4[2 + ins] = PP::tr_op(xt, lane, db, ins);
+            if constexpr (DV) t4[ins] = PP::tr_op(yt, ol, db, ins);
+            if constexpr (DK) t4[2 + ins] = PP::tr_op(xt, ol, db, ins);
           }
 #pragma unroll
           for (int ins = 0; ins < 2; ++ins) {
-            accv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t4[ins], pa[ins], accv[db], 0, 0,
-                                                              0);
-            acck[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t4[2 + ins], pd[ins], acck[db], 0,
-                                                              0, 0);
+            if constexpr (DV)
+              accv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t4[ins], pa[ins], accv[db], 0,
+                                                                0, 0);
+            if constexpr (DK)
+              acck[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t4[2 + ins], pd[ins], acck[db],
+                                                                0, 0, 0);
           }
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -1084,15 +1146,19 @@ hstu_bwd_dkv_kernel(BwdArgs a) {
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          bf16x4 ok4, ov4;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            ok4[e] = (__bf16)(acck[db][4 * g + e] * k_scale);
-            ov4[e] = (__bf16)(accv[db][4 * g + e] * v_scale);
-          }
           const int off = 2 * (32 * db + 8 * g + 4 * hh);
-          *reinterpret_cast<bf16x4*>(dk + off) = ok4;
-          *reinterpret_cast<bf16x4*>(dv + off) = ov4;
+          if constexpr (DK) {
+            bf16x4 ok4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ok4[e] = (__bf16)(acck[db][4 * g + e] * k_scale);
+            *reinterpret_cast<bf16x4*>(dk + off) = ok4;
+          }
+          if constexpr (DV) {
+            bf16x4 ov4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ov4[e] = (__bf16)(accv[db][4 * g + e] * v_scale);
+            *reinterpret_cast<bf16x4*>(dv + off) = ov4;
+          }
         }
     }
     stage_barrier();
@@ -1100,7 +1166,7 @@ hstu_bwd_dkv_kernel(BwdArgs a) {
 
   // this workgroup's table sums
   __syncthreads();
-  if constexpr (POS || TIME) {
+  if constexpr (TABS && (POS || TIME)) {
     float* part = a.tab_part + (size_t)blockIdx.x * (size_t)(P + kTabExtra);
     if constexpr (POS)
       for (int e = tid; e < P; e += kThreads) part[e] = hpos[e];
@@ -1114,25 +1180,41 @@ hstu_bwd_dkv_kernel(BwdArgs a) {
   }
 }
 
-// Table gradients: entry e = scale * sum over workgroups (fixed order);
-// time bins past Tt - 1 fold into the last table entry.
-__global__ __launch_bounds__(256) void hstu_tab_reduce_kernel(TabReduceArgs a) {
+// Table gradients: entry e = scale * sum over the workgroups' rows, in a
+// fixed order.  Stage 1: workgroup (x, y) sums rows [64y, 64y + 64) of
+// entries [64x, 64x + 64) (4 row slices of 16, combined in order); stage 2
+// sums the row blocks and folds time bins past Tt - 1 into the last entry.
+__global__ __launch_bounds__(256) void hstu_tab_reduce1_kernel(TabReduceArgs a) {
+  __shared__ float red[4][64];
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  const int e = blockIdx.x * 64 + tx;
+  const int r0 = blockIdx.y * 64 + ty * 16;
+  float t = 0.0f;
+  if (e < a.stride) {
+#pragma unroll 4
+    for (int r = r0; r < min(r0 + 16, a.n_part); ++r) t += a.part[(size_t)r * a.stride + e];
+  }
+  red[ty][tx] = t;
+  __syncthreads();
+  if (ty == 0 && e < a.stride)
+    a.part2[(size_t)blockIdx.y * a.stride + e] = ((red[0][tx] + red[1][tx]) + red[2][tx]) + red[3][tx];
+}
+
+__global__ __launch_bounds__(256) void hstu_tab_reduce2_kernel(TabReduceArgs a) {
   const int e = blockIdx.x * 256 + threadIdx.x;
-  if (e < a.pos_len) {
+  const int nb = (a.n_part + 63) / 64;
+  auto col = [&](int c) {
     float t = 0.0f;
-    for (int w = 0; w < a.n_part; ++w) t += a.part[(size_t)w * a.stride + e];
-    a.dpos[e] = t * a.scale;
+    for (int b = 0; b < nb; ++b) t += a.part2[(size_t)b * a.stride + c];
+    return t;
+  };
+  if (e < a.pos_len) {
+    a.dpos[e] = col(e) * a.scale;
   } else if (e < a.pos_len + a.time_len) {
     const int tb = e - a.pos_len;
-    float t = 0.0f;
-    for (int w = 0; w < a.n_part; ++w) {
-      const float* p = a.part + (size_t)w * a.stride + a.pos_len;
-      if (tb < a.time_len - 1) {
-        t += p[tb];
-      } else {
-        for (int bb = tb; bb < kTimeBins; ++bb) t += p[bb];
-      }
-    }
+    float t = col(a.pos_len + tb);
+    if (tb == a.time_len - 1)
+      for (int bb = tb + 1; bb < kTimeBins; ++bb) t += col(a.pos_len + bb);
     a.dtime[tb] = t * a.scale;
   }
 }
@@ -1302,18 +1384,27 @@ __global__ __launch_bounds__(256) void hstu_bwd_dkv_f32_kernel(BwdArgs a, int nu
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
+// Which backward kernel: 0 = dQ, 1 = the pass that sums the tables (dK, or
+// dK and dV fused), 2 = the dV-only pass (d = 128).
+template <int D>
+constexpr int kv_mode_tab() { return D == 128 ? 1 : 0; }
+
 template <int D, bool POS, bool TIME>
-size_t dkv_dyn_lds(int pos_len) {
-  return POS ? sizeof(float) * (size_t)pos_len : 0;
+size_t dkv_dyn_lds(int which, int pos_len) {
+  return (POS && which == 1) ? sizeof(float) * (size_t)pos_len : 0;
 }
 
 template <int D, bool POS, bool TIME>
-int bpc_one(bool kv, int pos_len) {
+int bpc_one(int which, int pos_len) {
   int nb = 0;
   hipError_t e;
-  if (kv)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, hstu_bwd_dkv_kernel<D, POS, TIME>,
-                                                     kThreads, dkv_dyn_lds<D, POS, TIME>(pos_len));
+  const size_t dyn = dkv_dyn_lds<D, POS, TIME>(which, pos_len);
+  if (which == 1)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &nb, hstu_bwd_dkv_kernel<D, POS, TIME, kv_mode_tab<D>()>, kThreads, dyn);
+  else if (which == 2)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, hstu_bwd_dkv_kernel<D, POS, TIME, 2>,
+                                                     kThreads, 0);
   else
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, hstu_bwd_dq_kernel<D, POS, TIME>,
                                                      kThreads, 0);
@@ -1321,20 +1412,23 @@ int bpc_one(bool kv, int pos_len) {
 }
 
 template <int D>
-int bpc_d(bool kv, int pos_len, int time_len) {
+int bpc_d(int which, int pos_len, int time_len) {
   const bool pos = pos_len > 0, tim = time_len > 0;
-  if (pos && tim) return bpc_one<D, true, true>(kv, pos_len);
-  if (pos) return bpc_one<D, true, false>(kv, pos_len);
-  if (tim) return bpc_one<D, false, true>(kv, pos_len);
-  return bpc_one<D, false, false>(kv, pos_len);
+  if (pos && tim) return bpc_one<D, true, true>(which, pos_len);
+  if (pos) return bpc_one<D, true, false>(which, pos_len);
+  if (tim) return bpc_one<D, false, true>(which, pos_len);
+  return bpc_one<D, false, false>(which, pos_len);
 }
 
 template <int D, bool POS, bool TIME>
-hipError_t launch_mfma_one(const BwdArgs& a, bool kv, int n_wg, hipStream_t stream) {
-  const size_t dyn = dkv_dyn_lds<D, POS, TIME>(a.pos_len);
-  if (kv)
-    hipLaunchKernelGGL((hstu_bwd_dkv_kernel<D, POS, TIME>), dim3((unsigned)n_wg), dim3(kThreads),
-                       dyn, stream, a);
+hipError_t launch_mfma_one(const BwdArgs& a, int which, int n_wg, hipStream_t stream) {
+  const size_t dyn = dkv_dyn_lds<D, POS, TIME>(which, a.pos_len);
+  if (which == 1)
+    hipLaunchKernelGGL((hstu_bwd_dkv_kernel<D, POS, TIME, kv_mode_tab<D>()>),
+                       dim3((unsigned)n_wg), dim3(kThreads), dyn, stream, a);
+  else if (which == 2)
+    hipLaunchKernelGGL((hstu_bwd_dkv_kernel<D, POS, TIME, 2>), dim3((unsigned)n_wg),
+                       dim3(kThreads), 0, stream, a);
   else
     hipLaunchKernelGGL((hstu_bwd_dq_kernel<D, POS, TIME>), dim3((unsigned)n_wg), dim3(kThreads),
                        0, stream, a);
@@ -1342,12 +1436,12 @@ hipError_t launch_mfma_one(const BwdArgs& a, bool kv, int n_wg, hipStream_t stre
 }
 
 template <int D>
-hipError_t launch_mfma_d(const BwdArgs& a, bool kv, int n_wg, hipStream_t stream) {
+hipError_t launch_mfma_d(const BwdArgs& a, int which, int n_wg, hipStream_t stream) {
   const bool pos = a.pos_len > 0, tim = a.time_len > 0;
-  if (pos && tim) return launch_mfma_one<D, true, true>(a, kv, n_wg, stream);
-  if (pos) return launch_mfma_one<D, true, false>(a, kv, n_wg, stream);
-  if (tim) return launch_mfma_one<D, false, true>(a, kv, n_wg, stream);
-  return launch_mfma_one<D, false, false>(a, kv, n_wg, stream);
+  if (pos && tim) return launch_mfma_one<D, true, true>(a, which, n_wg, stream);
+  if (pos) return launch_mfma_one<D, true, false>(a, which, n_wg, stream);
+  if (tim) return launch_mfma_one<D, false, true>(a, which, n_wg, stream);
+  return launch_mfma_one<D, false, false>(a, which, n_wg, stream);
 }
 
 template <int D>
@@ -1368,22 +1462,41 @@ hipError_t launch_bwd_plan(const BwdPlanArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_gate_bwd(const GateBwdArgs& a, int dtype, hipStream_t stream) {
-  const int64_t waves = (int64_t)a.n_tok * a.groups;
-  if (waves <= 0) return hipSuccess;
-  const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
-  if (dtype == 1)
-    hipLaunchKernelGGL((hstu_gate_bwd_kernel<__bf16, 8>), grid, block, 0, stream, a);
-  else
-    hipLaunchKernelGGL((hstu_gate_bwd_kernel<float, 4>), grid, block, 0, stream, a);
+template <typename T, int EPC, int G, int CPL>
+static hipError_t launch_gate_one(const GateBwdArgs& a, hipStream_t stream) {
+  const int64_t groups = (int64_t)a.n_tok * a.groups;
+  const int64_t waves = (groups + 64 / G - 1) / (64 / G);
+  hipLaunchKernelGGL((hstu_gate_bwd_kernel<T, EPC, G, CPL>), dim3((unsigned)((waves + 3) / 4)),
+                     dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
-int bwd_grid(int dtype, int d, int pos_len, int time_len, bool kv) {
+template <typename T, int EPC>
+static hipError_t launch_gate_t(const GateBwdArgs& a, hipStream_t stream) {
+  const int chunks = a.width / EPC;
+  if (chunks <= 2) return launch_gate_one<T, EPC, 2, 1>(a, stream);
+  if (chunks <= 4) return launch_gate_one<T, EPC, 4, 1>(a, stream);
+  if (chunks <= 8) return launch_gate_one<T, EPC, 8, 1>(a, stream);
+  if (chunks <= 16) return launch_gate_one<T, EPC, 16, 1>(a, stream);
+  if (chunks <= 32) return launch_gate_one<T, EPC, 32, 1>(a, stream);
+  if (chunks <= 64) return launch_gate_one<T, EPC, 64, 1>(a, stream);
+  if (chunks <= 128) return launch_gate_one<T, EPC, 64, 2>(a, stream);
+  if (chunks <= 256) return launch_gate_one<T, EPC, 64, 4>(a, stream);
+  if (chunks <= 512) return launch_gate_one<T, EPC, 64, 8>(a, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_gate_bwd(const GateBwdArgs& a, int dtype, hipStream_t stream) {
+  if ((int64_t)a.n_tok * a.groups <= 0) return hipSuccess;
+  return dtype == 1 ? launch_gate_t<__bf16, 8>(a, stream) : launch_gate_t<float, 4>(a, stream);
+}
+
+int bwd_grid(int dtype, int d, int pos_len, int time_len, int which) {
   if (dtype != 1) return 1;   // fp32 kernels are not persistent
+  if (which == 2 && d != 128) return 0;   // no separate dV pass
   int bpc = -1;
-  if (d == 128) bpc = bpc_d<128>(kv, pos_len, time_len);
-  if (d == 64) bpc = bpc_d<64>(kv, pos_len, time_len);
+  if (d == 128) bpc = bpc_d<128>(which, pos_len, time_len);
+  if (d == 64) bpc = bpc_d<64>(which, pos_len, time_len);
   if (bpc <= 0) return -1;
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess) return -1;
@@ -1393,32 +1506,30 @@ int bwd_grid(int dtype, int d, int pos_len, int time_len, bool kv) {
   return g < kMaxGrid ? g : kMaxGrid;
 }
 
-static hipError_t launch_bwd_pass(const BwdArgs& a, int dtype, int d, int n_wg, bool kv,
-                                  hipStream_t stream) {
+hipError_t launch_bwd(const BwdArgs& a, int dtype, int d, int which, int n_wg,
+                      hipStream_t stream) {
   if (dtype == 1) {
-    if (d == 128) return launch_mfma_d<128>(a, kv, n_wg, stream);
-    if (d == 64) return launch_mfma_d<64>(a, kv, n_wg, stream);
+    if (which == 2 && d != 128) return hipSuccess;
+    if (d == 128) return launch_mfma_d<128>(a, which, n_wg, stream);
+    if (d == 64) return launch_mfma_d<64>(a, which, n_wg, stream);
     return hipErrorInvalidValue;
   }
-  // fp32: n_wg carries the number of sequences
+  // fp32: one kernel per side; n_wg carries the number of sequences
+  if (which == 2) return hipSuccess;
+  const bool kv = which == 1;
   if (d == 128) return launch_f32_d<128>(a, kv, n_wg, stream);
   if (d == 64) return launch_f32_d<64>(a, kv, n_wg, stream);
   if (d == 8) return launch_f32_d<8>(a, kv, n_wg, stream);
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_bwd_dq(const BwdArgs& a, int dtype, int d, int n_wg, hipStream_t stream) {
-  return launch_bwd_pass(a, dtype, d, n_wg, false, stream);
-}
-
-hipError_t launch_bwd_dkv(const BwdArgs& a, int dtype, int d, int n_wg, hipStream_t stream) {
-  return launch_bwd_pass(a, dtype, d, n_wg, true, stream);
-}
-
 hipError_t launch_tab_reduce(const TabReduceArgs& a, hipStream_t stream) {
   const int n = a.pos_len + a.time_len;
-  if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(hstu_tab_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+  if (n <= 0 || a.n_part <= 0) return hipSuccess;
+  hipLaunchKernelGGL(hstu_tab_reduce1_kernel,
+                     dim3((unsigned)((a.stride + 63) / 64), (unsigned)((a.n_part + 63) / 64)),
+                     dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(hstu_tab_reduce2_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
                      stream, a);
   return hipGetLastError();
 }

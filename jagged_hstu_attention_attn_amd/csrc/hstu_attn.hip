@@ -545,7 +545,7 @@ int hstu_layer_fwd(const hstu_layer_desc* desc, const void* x, const void* w_uvq
 namespace {
 
 struct BwdLayout {
-  size_t o_off, do_off, hdr_off, gstart_off, lq_off, lkv_off, part_off, total;
+  size_t o_off, do_off, hdr_off, gstart_off, lq_off, lkv_off, part_off, part2_off, total;
   bool gate;
 };
 
@@ -571,16 +571,20 @@ BwdLayout bwd_layout(const hstu_attn_desc* d) {
   off = l.lkv_off + sizeof(int2) * (size_t)(G > 0 ? G : 1);
   l.part_off = hstu::align256(off);
   const bool tables = d->pos_table_len > 0 || d->time_table_len > 0;
-  if (d->dtype == HSTU_DTYPE_BF16 && tables)
-    off = l.part_off + sizeof(float) * (size_t)hstu::kMaxGrid * (size_t)(d->pos_table_len + 64);
+  const size_t stride = (size_t)(d->pos_table_len + 64);
+  l.part2_off = l.part_off;
+  if (d->dtype == HSTU_DTYPE_BF16 && tables) {
+    l.part2_off = hstu::align256(l.part_off + sizeof(float) * (size_t)hstu::kMaxGrid * stride);
+    off = l.part2_off + sizeof(float) * (size_t)((hstu::kMaxGrid + 63) / 64) * stride;
+  }
   l.total = hstu::align256(off);
   return l;
 }
 
 // Workgroups of a persistent backward pass (cached per device and variant).
-int bwd_pass_grid(const hstu_attn_desc* d, bool kv) {
+int bwd_pass_grid(const hstu_attn_desc* d, int which) {
   struct Entry {
-    int dev, d, pos_len, has_time, kv, grid;
+    int dev, d, pos_len, has_time, which, grid;
   };
   static thread_local Entry cache[16];
   static thread_local int cache_n = 0;
@@ -590,11 +594,11 @@ int bwd_pass_grid(const hstu_attn_desc* d, bool kv) {
   for (int e = 0; e < cache_n && e < 16; ++e) {
     const Entry& c = cache[e];
     if (c.dev == dev && c.d == d->d_v && c.pos_len == d->pos_table_len &&
-        c.has_time == has_time && c.kv == (kv ? 1 : 0))
+        c.has_time == has_time && c.which == which)
       return c.grid;
   }
-  const int g = hstu::bwd_grid(d->dtype, d->d_v, d->pos_table_len, d->time_table_len, kv);
-  if (g > 0) cache[cache_n++ % 16] = Entry{dev, d->d_v, d->pos_table_len, has_time, kv ? 1 : 0, g};
+  const int g = hstu::bwd_grid(d->dtype, d->d_v, d->pos_table_len, d->time_table_len, which);
+  if (g >= 0) cache[cache_n++ % 16] = Entry{dev, d->d_v, d->pos_table_len, has_time, which, g};
   return g;
 }
 
@@ -658,11 +662,12 @@ int hstu_jagged_attn_bwd(const hstu_attn_desc* desc, const void* q, const void* 
   }
   if (empty) return HSTU_OK;
 
-  int n_q = 0, n_kv = 0;
+  int n_q = 0, n_kv = 0, n_v = 0;
   if (bf16) {
-    n_q = bwd_pass_grid(desc, false);
-    n_kv = bwd_pass_grid(desc, true);
-    if (n_q <= 0 || n_kv <= 0)
+    n_q = bwd_pass_grid(desc, 0);
+    n_kv = bwd_pass_grid(desc, 1);
+    n_v = bwd_pass_grid(desc, 2);
+    if (n_q <= 0 || n_kv <= 0 || n_v < 0)
       return fail(HSTU_ERR_HIP, "cannot query the device for the launch size");
   }
   char* ws = static_cast<char*>(workspace);
@@ -731,8 +736,8 @@ int hstu_jagged_attn_bwd(const hstu_attn_desc* desc, const void* q, const void* 
   ba.alpha = alpha;
   ba.inv_scale = (float)(1.0 / (double)n_scale);
   if (!bf16) {
-    e = hstu::launch_bwd_dq(ba, desc->dtype, desc->d_v, desc->num_seqs, s);
-    if (e == hipSuccess) e = hstu::launch_bwd_dkv(ba, desc->dtype, desc->d_v, desc->num_seqs, s);
+    e = hstu::launch_bwd(ba, desc->dtype, desc->d_v, 0, desc->num_seqs, s);
+    if (e == hipSuccess) e = hstu::launch_bwd(ba, desc->dtype, desc->d_v, 1, desc->num_seqs, s);
     if (e != hipSuccess)
       return fail(HSTU_ERR_HIP, "backward launch failed: %s", hipGetErrorString(e));
     return HSTU_OK;
@@ -752,14 +757,16 @@ int hstu_jagged_attn_bwd(const hstu_attn_desc* desc, const void* q, const void* 
   if (e != hipSuccess)
     return fail(HSTU_ERR_HIP, "backward scheduler launch failed: %s", hipGetErrorString(e));
   ba.list = pa.list_q;
-  e = hstu::launch_bwd_dq(ba, desc->dtype, desc->d_v, n_q, s);
+  e = hstu::launch_bwd(ba, desc->dtype, desc->d_v, 0, n_q, s);
   if (e != hipSuccess) return fail(HSTU_ERR_HIP, "dQ launch failed: %s", hipGetErrorString(e));
   ba.list = pa.list_kv;
-  e = hstu::launch_bwd_dkv(ba, desc->dtype, desc->d_v, n_kv, s);
+  e = hstu::launch_bwd(ba, desc->dtype, desc->d_v, 1, n_kv, s);
+  if (e == hipSuccess && n_v > 0) e = hstu::launch_bwd(ba, desc->dtype, desc->d_v, 2, n_v, s);
   if (e != hipSuccess) return fail(HSTU_ERR_HIP, "dK/dV launch failed: %s", hipGetErrorString(e));
   if (desc->pos_table_len > 0 || desc->time_table_len > 0) {
     hstu::TabReduceArgs ra;
     ra.part = ba.tab_part;
+    ra.part2 = reinterpret_cast<float*>(ws + bl.part2_off);
     ra.dpos = dpos_table;
     ra.dtime = dtime_table;
     ra.n_part = n_kv;

@@ -308,6 +308,7 @@ struct GateBwdArgs {
 
 struct TabReduceArgs {
   const float* part;         // [n_part][stride]
+  float* part2;              // [ceil(n_part / 64)][stride]: row-block sums
   float* dpos;
   float* dtime;
   int32_t n_part;
@@ -329,11 +330,14 @@ int ln_all_heads_max_width(int dtype);
 hipError_t launch_ln_all_heads(const LnArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_bwd_plan(const BwdPlanArgs& a, hipStream_t stream);
 hipError_t launch_gate_bwd(const GateBwdArgs& a, int dtype, hipStream_t stream);
-// Workgroups of the persistent dQ / dK-dV launches for this shape (CUs x
-// resident workgroups per CU), or a negative value on error.
-int bwd_grid(int dtype, int d, int pos_len, int time_len, bool kv);
-hipError_t launch_bwd_dq(const BwdArgs& a, int dtype, int d, int n_wg, hipStream_t stream);
-hipError_t launch_bwd_dkv(const BwdArgs& a, int dtype, int d, int n_wg, hipStream_t stream);
+// Backward passes: which = 0 (dQ), 1 (dK with the table sums; also dV for
+// d = 64), 2 (dV alone, d = 128 only; a no-op otherwise).  bwd_grid gives the
+// persistent launch size (CUs x resident workgroups per CU), 0 for a pass
+// that does not exist, or a negative value on error; for fp32 n_wg of
+// launch_bwd is the number of sequences instead.
+int bwd_grid(int dtype, int d, int pos_len, int time_len, int which);
+hipError_t launch_bwd(const BwdArgs& a, int dtype, int d, int which, int n_wg,
+                      hipStream_t stream);
 hipError_t launch_tab_reduce(const TabReduceArgs& a, hipStream_t stream);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream);
 
