@@ -1045,27 +1045,42 @@ hstu_bwd_dkv_kernel(BwdArgs a) {
               __hip_atomic_fetch_add(&htime[bin * 32 + ol32], v, __ATOMIC_RELAXED,
                                      __HIP_MEMORY_SCOPE_WORKGROUP);
           };
-          // Position-bin sums of register group g (rows 8g + 4hh + e): lane c
-          // gathers register 4g+e of lane c+e (same lane half), so that its
-          // four terms share i - j = R0 + 8g + 4hh - c; terms that wrap
-          // around the 32 keys (key c + e - 32, i - j 32 higher) go to a
-          // second sum.
-          auto pflush = [&](int g, const float* dg) __attribute__((always_inline)) {
+          // Position-bin sums: the step's 32 x 32 block has 63 distinct
+          // i - j = R0 + delta, delta = row - key in [-31, 31]; register 4g+e
+          // of lane (c, hh) holds delta = 8g + 4hh + e - c.  Three rounds of
+          // lane exchanges (ds_bpermute) gather the block into one value per
+          // lane -- lane (c, 0) ends with delta = -c, lane (c, 1) with
+          // delta = 32 - c -- so one LDS atomic per lane and step is left.
+          // Round 1 (per group g): lane c adds register 4g+e of lane c+e, all
+          // of delta 8g + 4hh - c (lo); past the wrap the key is c + e - 32
+          // and delta 32 higher (hi).  Round 2: lane c adds group g's lo and
+          // hi of lane c + 8g (delta 4hh - c, or 32 higher past the wrap).
+          // Round 3 (after the groups) merges the two lane halves.
+          float lo2 = 0.0f, hi2 = 0.0f;
+          auto bperm = [](int src_lane, float v) __attribute__((always_inline)) {
+            return __builtin_bit_cast(
+                float, __builtin_amdgcn_ds_bpermute(4 * src_lane, __builtin_bit_cast(int, v)));
+          };
+          auto pgroup = [&](int g, const float* dg) __attribute__((always_inline)) {
             float A = dg[0], Bw = 0.0f;
 #pragma unroll
             for (int e = 1; e < 4; ++e) {
-              const int src = ((ol32 + e) & 31) + 32 * ohh;
-              const float v = __builtin_bit_cast(
-                  float, __builtin_amdgcn_ds_bpermute(4 * src, __builtin_bit_cast(int, dg[e])));
+              const float v = bperm(((ol32 + e) & 31) + 32 * ohh, dg[e]);
               if (ol32 + e >= 32) Bw += v; else A += v;
             }
-            const int ra = R0 + 8 * g + 4 * ohh - ol32, rb = ra + 32;
-            if (A != 0.0f)
-              __hip_atomic_fetch_add(&hpos[min(ra < 0 ? -ra : ra, P - 1)], A, __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_WORKGROUP);
-            if (Bw != 0.0f)
-              __hip_atomic_fetch_add(&hpos[min(rb < 0 ? -rb : rb, P - 1)], Bw, __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_WORKGROUP);
+            if (g == 0) {
+              lo2 += A;
+              hi2 += Bw;
+            } else {
+              const int src = ((ol32 + 8 * g) & 31) + 32 * ohh;
+              const float a2 = bperm(src, A), b2 = bperm(src, Bw);
+              if (ol32 + 8 * g >= 32) {
+                hi2 += a2;
+              } else {
+                lo2 += a2;
+                hi2 += b2;
+              }
+            }
           };
           auto elem = [&](auto mc) __attribute__((always_inline)) {
             constexpr int MODE = decltype(mc)::value;
@@ -1105,13 +1120,27 @@ hstu_bwd_dkv_kernel(BwdArgs a) {
                   run += d;
                 }
               }
-              if constexpr (POS && TABS) pflush(gq, dg);
+              if constexpr (POS && TABS) pgroup(gq, dg);
             }
             if constexpr (TIME && TABS) tflush(prev, run);
           };
           if (mode == 0) elem(std::integral_constant<int, 0>{});
           else if (mode == 1) elem(std::integral_constant<int, 1>{});
           else elem(std::integral_constant<int, 2>{});
+          if constexpr (POS && TABS) {
+            // round 3: lane (c, 0) adds lane (c + 4, 1)'s lo (delta -c);
+            // lane (c, 1) takes lane (c, 0)'s hi and, from lane (c + 4, 1),
+            // its hi -- or past the wrap (c >= 28) the lo of lane c - 28
+            const int s4 = ((ol32 + 4) & 31) + 32;
+            const float x = bperm(s4, lo2);
+            const float y = bperm(ol32, hi2);
+            const float z = bperm(s4, ol32 < 4 ? lo2 : hi2);
+            const float pacc = ohh ? y + z : lo2 + (ol32 < 28 ? x : 0.0f);
+            const int rel = R0 + (ohh ? 32 - ol32 : -ol32);
+            if (pacc != 0.0f)
+              __hip_atomic_fetch_add(&hpos[min(rel < 0 ? -rel : rel, P - 1)], pacc,
+                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
         // dV^T += dO^T A and dK^T += Q^T dS, one d-block of operands at a time
@@ -1219,6 +1248,13 @@ __global__ __launch_bounds__(256) void hstu_tab_reduce2_kernel(TabReduceArgs a) 
   }
 }
 
+__global__ __launch_bounds__(256) void hstu_tab64_finish_kernel(const double* t, float* dpos,
+                                                                float* dtime, int P, int Tt) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e < P) dpos[e] = (float)t[e];
+  else if (e < P + Tt) dtime[e - P] = (float)t[e];
+}
+
 __global__ __launch_bounds__(256) void hstu_fill_zero_kernel(float* p, int64_t n) {
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (e < n) p[e] = 0.0f;
@@ -1305,8 +1341,9 @@ __global__ __launch_bounds__(256) void hstu_bwd_dq_f32_kernel(BwdArgs a, int num
 #pragma unroll
     for (int m = 0; m < E; ++m) acc[m] += a.alpha * ds * kj[m];
     if (lane == 0) {
-      if (a.pos_len > 0) atomicAdd(&a.dpos[pidx], ds);
-      if (a.time_len > 0) atomicAdd(&a.dtime[tidx], ds);
+      // fp64 sums: their rounding does not depend on the order of arrival
+      if (a.pos_len > 0) atomicAdd(&a.tab64[pidx], (double)ds);
+      if (a.time_len > 0) atomicAdd(&a.tab64[a.pos_len + tidx], (double)ds);
     }
   }
   float* dq = static_cast<float*>(a.dq);
@@ -1531,6 +1568,15 @@ hipError_t launch_tab_reduce(const TabReduceArgs& a, hipStream_t stream) {
                      dim3(256), 0, stream, a);
   hipLaunchKernelGGL(hstu_tab_reduce2_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
                      stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_tab64_finish(const double* tab64, float* dpos, float* dtime, int pos_len,
+                               int time_len, hipStream_t stream) {
+  const int n = pos_len + time_len;
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(hstu_tab64_finish_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                     stream, tab64, dpos, dtime, pos_len, time_len);
   return hipGetLastError();
 }
 

@@ -576,6 +576,8 @@ BwdLayout bwd_layout(const hstu_attn_desc* d) {
   if (d->dtype == HSTU_DTYPE_BF16 && tables) {
     l.part2_off = hstu::align256(l.part_off + sizeof(float) * (size_t)hstu::kMaxGrid * stride);
     off = l.part2_off + sizeof(float) * (size_t)((hstu::kMaxGrid + 63) / 64) * stride;
+  } else if (tables) {   // fp32: the fp64 table sums
+    off = l.part_off + sizeof(double) * (size_t)(d->pos_table_len + d->time_table_len);
   }
   l.total = hstu::align256(off);
   return l;
@@ -654,7 +656,14 @@ int hstu_jagged_attn_bwd(const hstu_attn_desc* desc, const void* q, const void* 
   hipError_t e = hipSuccess;
   const bool bf16 = desc->dtype == HSTU_DTYPE_BF16;
   // the table gradients are sums: zero them where no pass writes them whole
-  if (empty || !bf16) {
+  const bool tables = desc->pos_table_len > 0 || desc->time_table_len > 0;
+  double* tab64 = reinterpret_cast<double*>(static_cast<char*>(workspace) + bl.part_off);
+  if (!empty && !bf16 && tables) {
+    e = hstu::launch_fill_zero(reinterpret_cast<float*>(tab64),
+                               2 * (int64_t)(desc->pos_table_len + desc->time_table_len), s);
+    if (e != hipSuccess) return fail(HSTU_ERR_HIP, "fill launch failed: %s", hipGetErrorString(e));
+  }
+  if (empty) {
     if (dpos_table) e = hstu::launch_fill_zero(dpos_table, desc->pos_table_len, s);
     if (e == hipSuccess && dtime_table)
       e = hstu::launch_fill_zero(dtime_table, desc->time_table_len, s);
@@ -718,8 +727,7 @@ int hstu_jagged_attn_bwd(const hstu_attn_desc* desc, const void* q, const void* 
   ba.num_targets = num_targets;
   ba.pos_table = pos_table;
   ba.time_table = time_table;
-  ba.dpos = dpos_table;
-  ba.dtime = dtime_table;
+  ba.tab64 = tab64;
   ba.tab_part = reinterpret_cast<float*>(ws + bl.part_off);
   ba.hdr = reinterpret_cast<int32_t*>(ws + bl.hdr_off);
   ba.list = nullptr;
@@ -738,6 +746,9 @@ int hstu_jagged_attn_bwd(const hstu_attn_desc* desc, const void* q, const void* 
   if (!bf16) {
     e = hstu::launch_bwd(ba, desc->dtype, desc->d_v, 0, desc->num_seqs, s);
     if (e == hipSuccess) e = hstu::launch_bwd(ba, desc->dtype, desc->d_v, 1, desc->num_seqs, s);
+    if (e == hipSuccess && tables)
+      e = hstu::launch_tab64_finish(tab64, dpos_table, dtime_table, desc->pos_table_len,
+                                    desc->time_table_len, s);
     if (e != hipSuccess)
       return fail(HSTU_ERR_HIP, "backward launch failed: %s", hipGetErrorString(e));
     return HSTU_OK;

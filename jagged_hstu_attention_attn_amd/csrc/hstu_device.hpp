@@ -277,8 +277,7 @@ struct BwdArgs {
   const int32_t* num_targets;
   const float* pos_table;
   const float* time_table;
-  float* dpos;               // fp32 kernels: table gradients, accumulated
-  float* dtime;
+  double* tab64;             // fp32 kernels: [pos_len + time_len] fp64 table sums
   float* tab_part;           // MFMA kernels: per-workgroup table sums
   const int32_t* hdr;
   const int2* list;
@@ -340,5 +339,8 @@ hipError_t launch_bwd(const BwdArgs& a, int dtype, int d, int which, int n_wg,
                       hipStream_t stream);
 hipError_t launch_tab_reduce(const TabReduceArgs& a, hipStream_t stream);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream);
+// dpos[e] = tab64[e], dtime[e] = tab64[pos_len + e], rounded to float.
+hipError_t launch_tab64_finish(const double* tab64, float* dpos, float* dtime, int pos_len,
+                               int time_len, hipStream_t stream);
 
 }  // namespace hstu
