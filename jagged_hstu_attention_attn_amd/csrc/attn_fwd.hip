@@ -730,6 +730,35 @@ hstu_attn_fwd_kernel(AttnArgs a) {
   stage_barrier();             // also publishes the time tables; Q reads are done
   if (kt_lo + 2 <= kt_hi) issue_stage(B2{}, kt_lo + 2);
 
+  // Epilogue staging: each wave uses 32 rows of a stage buffer that neither
+  // the last block nor any copy still in flight touches (the buffers after
+  // the last block's, last read two or more barriers before the last step).
+  const bool ln = a.epilogue == 0;
+  auto ep_lds = [&]() __attribute__((always_inline)) -> uint32_t {
+    const int b_ep = ((kt_hi - kt_lo) + 1 + (wave >> 1)) & (kStages - 1);
+    return (b_ep == 0 ? lds_off(st0.k) : b_ep == 1 ? lds_off(st1.k) : b_ep == 2 ? lds_off(st2.k)
+                                                                               : lds_off(st3.k)) +
+           (uint32_t)((wave & 1) * kRows * VROW);
+  };
+  // U rows of this wave into the epilogue buffer; issued at the start of the
+  // last step so that their latency hides behind the last block.
+  auto issue_u = [&]() __attribute__((always_inline)) {
+    if (!(ln && wave_rows)) return;
+    int ul = lane;
+    asm volatile("" : "+v"(ul));
+    const uint32_t e_lds = ep_lds();
+    const uint64_t ub = uni_ptr(reinterpret_cast<const char*>(a.u) +
+                                ((int64_t)(seq0 + i0) * a.ld_u + (int64_t)h * DV) * ES);
+    const uint32_t ldu_b = (uint32_t)(a.ld_u * ES);
+#pragma unroll
+    for (int n = 0; n < kRows * VCH / 64; ++n) {
+      const int m = 64 * n + ul, r = m / VCH;
+      const int row = min(wr0 + r, i1 - 1) - i0;
+      lds_copy16(ub, (uint32_t)row * ldu_b + 16u * (uint32_t)((m % VCH) ^ row_swz<VCH>(r)),
+                 e_lds + 1024u * (uint32_t)n);
+    }
+  };
+
   // One pipeline step on key block kt held in buffer `bufc`: copy block kt+3
   // into the buffer freed by the previous barrier, compute block kt, then
   // (own copies of block kt+1 landed) finish block kt+1 and synchronise.
@@ -742,6 +771,8 @@ hstu_attn_fwd_kernel(AttnArgs a) {
     if (kt + 1 <= kt_hi) {
       wait_vmem_n(more3 ? 2 * my_copies : (more2 ? my_copies : 0));
       finish_stage(N1{}, kt + 1);   // its LDS traffic overlaps block kt
+    } else {
+      issue_u();
     }
     if (needs(kt)) block(stage(bufc), kt);
     if (kt + 1 <= kt_hi) stage_barrier();
@@ -829,26 +860,9 @@ hstu_attn_fwd_kernel(AttnArgs a) {
   // that the last block does not read (the other waves may still be in it).
   const float osc = a.out_scale;
   float mean = 0.0f, rstd = 1.0f;
-  const bool ln = a.epilogue == 0;
   int el = lane;   // recomputed per item: kept out of the registers live across items
   asm volatile("" : "+v"(el));
-  const int b_ep = ((kt_hi - kt_lo) + 1 + (wave >> 1)) & (kStages - 1);
-  const uint32_t e_lds =
-      (b_ep == 0 ? lds_off(st0.k) : b_ep == 1 ? lds_off(st1.k) : b_ep == 2 ? lds_off(st2.k)
-                                                                          : lds_off(st3.k)) +
-      (uint32_t)((wave & 1) * kRows * VROW);
-  if (ln && wave_rows) {
-    const uint64_t ub = uni_ptr(reinterpret_cast<const char*>(a.u) +
-                                ((int64_t)(seq0 + i0) * a.ld_u + (int64_t)h * DV) * ES);
-    const uint32_t ldu_b = (uint32_t)(a.ld_u * ES);
-#pragma unroll
-    for (int n = 0; n < kRows * VCH / 64; ++n) {
-      const int m = 64 * n + el, r = m / VCH;
-      const int row = min(wr0 + r, i1 - 1) - i0;
-      lds_copy16(ub, (uint32_t)row * ldu_b + 16u * (uint32_t)((m % VCH) ^ row_swz<VCH>(r)),
-                 e_lds + 1024u * (uint32_t)n);
-    }
-  }
+  const uint32_t e_lds = ep_lds();
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
