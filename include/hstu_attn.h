@@ -109,8 +109,9 @@ typedef struct {
 } hstu_attn_desc;
 
 /*
- * Supported (dtype, d_qk, d_v): (BF16,128,128), (BF16,64,64), (F32,128,128),
- * (F32,64,64), (F32,8,8).  Alignment: q, k, v, u, out 16-byte aligned and
+ * Supported (dtype, d_qk, d_v): (BF16,128,128), (BF16,64,64), (BF16,64,128),
+ * (BF16,128,64), (F32,128,128), (F32,64,64), (F32,8,8); the backward needs
+ * d_qk == d_v.  Alignment: q, k, v, u, out 16-byte aligned and
  * ld_x * sizeof(element) a multiple of 16 bytes with ld_x >= H * d.
  * Returns 1 if supported, 0 if not (no message is set).
  */

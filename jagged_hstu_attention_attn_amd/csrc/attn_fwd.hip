@@ -98,9 +98,13 @@ struct Cfg {
   static_assert(kKRow % 16 == 0 && kVRow % 16 == 0, "rows are whole 16-byte chunks");
   static_assert(kBN * kKCh % 64 == 0 && kBN * kVCh % 64 == 0, "stage is whole copies");
   static_assert(DQK % kStep == 0 && DV % 4 == 0 && (!kBf16 || DV % 32 == 0), "shape");
-  // the Q tile and the epilogue stage 32 rows per wave in half of the K+V
-  // space of a stage buffer
-  static_assert(DQK == DV, "staging layout assumes d_qk == d_v");
+  // The Q tile and the epilogue stage 32 rows per wave in half of the K+V
+  // space of a stage buffer, which holds 64 rows of d_qk when d_qk <= d_v and
+  // 64 rows of d_v when d_v <= d_qk; otherwise that side goes directly
+  // between HBM and registers (Q operands loaded per lane; U loaded and the
+  // output stored 4 values per lane).
+  static constexpr bool kQLds = kKRow <= kVRow;
+  static constexpr bool kEpLds = kVRow <= kKRow;
   // XOR swizzles of a row's 16-byte chunks (always below the number of
   // chunks, so they permute the row).  K: one read touches the same logical
   // chunk of 16 consecutive rows per LDS cycle.  V (bf16): a transposed read
@@ -687,7 +691,7 @@ hstu_attn_fwd_kernel(AttnArgs a) {
   // per copy; stage buffers 2 and 3 are not in use yet), then reads its MFMA
   // operands from there.  Rows past the tile repeat its last row.
   const uint32_t q_lds = lds_off(wave < 2 ? st2.k : st3.k) + (uint32_t)((wave & 1) * kRows * KROW);
-  if (wave_rows && !alpha_zero) {
+  if (C::kQLds && wave_rows && !alpha_zero) {
     int ql = lane;   // recomputed per item: kept out of the registers live across items
     asm volatile("" : "+v"(ql));
     const uint64_t qb = uni_ptr(reinterpret_cast<const char*>(a.q) +
@@ -701,9 +705,26 @@ hstu_attn_fwd_kernel(AttnArgs a) {
                  q_lds + 1024u * (uint32_t)n);
     }
   }
+  if constexpr (!C::kQLds) {
+    // Q operands straight from HBM: lane (row i, half hh) takes 16 bytes of
+    // its row per MFMA step
+    const char* qrow = reinterpret_cast<const char*>(a.q) +
+                       ((int64_t)(seq0 + min(i, i1 - 1)) * a.ld_q + (int64_t)h * DQK) * ES;
+#pragma unroll
+    for (int c = 0; c < NKC; ++c) {
+      if constexpr (BF) {
+        const bf16x8 z = {};
+        const bf16x8 v = *reinterpret_cast<const bf16x8*>(qrow + 16 * (2 * c + hh));
+        qf[c] = (row_valid && !alpha_zero) ? v : z;
+      } else {
+        const float v = *reinterpret_cast<const float*>(qrow + 4 * (2 * c + hh));
+        qf[c] = (row_valid && !alpha_zero) ? v : 0.0f;
+      }
+    }
+  }
   wait_vmem<0>();
 #pragma unroll
-  for (int c = 0; c < NKC; ++c) {
+  for (int c = 0; C::kQLds && c < NKC; ++c) {
     if constexpr (BF) {
       const bf16x8 z = {};
       qf[c] = (row_valid && !alpha_zero)
@@ -743,7 +764,7 @@ hstu_attn_fwd_kernel(AttnArgs a) {
   // U rows of this wave into the epilogue buffer; issued at the start of the
   // last step so that their latency hides behind the last block.
   auto issue_u = [&]() __attribute__((always_inline)) {
-    if (!(ln && wave_rows)) return;
+    if (!C::kEpLds || !(ln && wave_rows)) return;
     int ul = lane;
     asm volatile("" : "+v"(ul));
     const uint32_t e_lds = ep_lds();
@@ -887,7 +908,46 @@ hstu_attn_fwd_kernel(AttnArgs a) {
     sq += __shfl_xor(sq, 32, 64);
     rstd = rsqrtf(sq * (1.0f / DV) + a.ln_eps);
   }
-  if (wave_rows) {
+  if (!C::kEpLds && row_valid) {
+    // y = (O - mean) * rstd * U straight between registers and HBM
+    const char* urow = reinterpret_cast<const char*>(a.u) +
+                       ((int64_t)(seq0 + i) * a.ld_u + (int64_t)h * DV) * ES;
+    char* orow = reinterpret_cast<char*>(a.out) +
+                 ((int64_t)(seq0 + i) * a.ld_out + (int64_t)h * DV) * ES;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int d0 = 32 * db + 8 * gq + 4 * hh;
+        if (d0 < DV) {
+          float y[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) y[e] = acc[db][4 * gq + e];
+          if constexpr (BF) {
+            if (ln) {
+              const bf16x4 uu = *reinterpret_cast<const bf16x4*>(urow + 2 * d0);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) y[e] = (y[e] - mean) * rstd * (float)uu[e];
+            }
+            bf16x4 o;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = (__bf16)y[e];
+            *reinterpret_cast<bf16x4*>(orow + 2 * d0) = o;
+          } else {
+            if (ln) {
+              const floatx4 uu = *reinterpret_cast<const floatx4*>(urow + 4 * d0);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) y[e] = (y[e] - mean) * rstd * uu[e];
+            }
+            floatx4 o;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = y[e];
+            *reinterpret_cast<floatx4*>(orow + 4 * d0) = o;
+          }
+        }
+      }
+  }
+  if (C::kEpLds && wave_rows) {
     wait_vmem<0>();   // this wave's U rows have landed
     // y = (O - mean) * rstd * U in place of U, as the output's element type
 #pragma unroll
@@ -988,6 +1048,8 @@ int attn_grid(int dtype, int d_qk, int d_v, int pos_len, int time_len) {
   if (dtype == 1) {
     if (d_qk == 128 && d_v == 128) bpc = bpc_bias<__bf16, 128, 128>(pos_len, time_len);
     if (d_qk == 64 && d_v == 64) bpc = bpc_bias<__bf16, 64, 64>(pos_len, time_len);
+    if (d_qk == 64 && d_v == 128) bpc = bpc_bias<__bf16, 64, 128>(pos_len, time_len);
+    if (d_qk == 128 && d_v == 64) bpc = bpc_bias<__bf16, 128, 64>(pos_len, time_len);
   } else if (dtype == 0) {
     if (d_qk == 128 && d_v == 128) bpc = bpc_bias<float, 128, 128>(pos_len, time_len);
     if (d_qk == 64 && d_v == 64) bpc = bpc_bias<float, 64, 64>(pos_len, time_len);
@@ -1002,7 +1064,9 @@ int attn_grid(int dtype, int d_qk, int d_v, int pos_len, int time_len) {
 }
 
 bool attn_supported(int dtype, int d_qk, int d_v) {
-  if (dtype == 1) return (d_qk == 128 && d_v == 128) || (d_qk == 64 && d_v == 64);
+  if (dtype == 1)
+    return (d_qk == 128 && d_v == 128) || (d_qk == 64 && d_v == 64) ||
+           (d_qk == 64 && d_v == 128) || (d_qk == 128 && d_v == 64);
   if (dtype == 0) return (d_qk == 128 && d_v == 128) || (d_qk == 64 && d_v == 64) ||
                          (d_qk == 8 && d_v == 8);
   return false;
@@ -1013,6 +1077,8 @@ hipError_t launch_attn(const AttnArgs& a, int dtype, int d_qk, int d_v, int n_wg
   if (dtype == 1) {
     if (d_qk == 128 && d_v == 128) return launch_bias<__bf16, 128, 128>(a, n_wg, stream);
     if (d_qk == 64 && d_v == 64) return launch_bias<__bf16, 64, 64>(a, n_wg, stream);
+    if (d_qk == 64 && d_v == 128) return launch_bias<__bf16, 64, 128>(a, n_wg, stream);
+    if (d_qk == 128 && d_v == 64) return launch_bias<__bf16, 128, 64>(a, n_wg, stream);
   } else if (dtype == 0) {
     if (d_qk == 128 && d_v == 128) return launch_bias<float, 128, 128>(a, n_wg, stream);
     if (d_qk == 64 && d_v == 64) return launch_bias<float, 64, 64>(a, n_wg, stream);

@@ -623,6 +623,9 @@ int hstu_jagged_attn_bwd(const hstu_attn_desc* desc, const void* q, const void* 
                          size_t workspace_bytes, void* stream) {
   int rc = check_desc(desc);
   if (rc != HSTU_OK) return rc;
+  if (desc->d_qk != desc->d_v)
+    return fail(HSTU_ERR_UNSUPPORTED, "the backward needs d_qk == d_v (%d, %d)", desc->d_qk,
+                desc->d_v);
   if (desc->num_seqs > 0 && !offsets) return fail(HSTU_ERR_INVALID_ARG, "offsets is NULL");
   if (contextual_len < 0) return fail(HSTU_ERR_INVALID_ARG, "contextual_len < 0");
   if (max_attn_len < 0) return fail(HSTU_ERR_INVALID_ARG, "max_attn_len < 0");

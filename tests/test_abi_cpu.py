@@ -153,9 +153,45 @@ def test_valid_call_without_gpu_reports_hip_error(lib):
 
 def test_supported_set(lib):
     assert lib.hstu_jagged_attn_supported(1, 128, 128) == 1
+    assert lib.hstu_jagged_attn_supported(1, 64, 128) == 1
+    assert lib.hstu_jagged_attn_supported(1, 128, 64) == 1
     assert lib.hstu_jagged_attn_supported(0, 8, 8) == 1
     assert lib.hstu_jagged_attn_supported(1, 8, 8) == 0
+    assert lib.hstu_jagged_attn_supported(0, 64, 128) == 0
     assert lib.hstu_jagged_attn_supported(2, 128, 128) == 0
+
+
+def _bwd(lib, d, **kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, u=FAKE, offsets=FAKE, dout=FAKE, dq=FAKE, dk=FAKE,
+                dv=FAKE, du=FAKE, ws=FAKE)
+    args.update(kw)
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    ws_bytes = lib.hstu_jagged_attn_bwd_workspace_bytes(ctypes.byref(d)) or 1 << 20
+    return lib.hstu_jagged_attn_bwd(
+        ctypes.byref(d), vp(args["q"]), vp(args["k"]), vp(args["v"]), vp(args["u"]),
+        vp(args["offsets"]), None, None, 0, 0, 0.1, 10.0, None, None, vp(args["dout"]),
+        vp(args["dq"]), vp(args["dk"]), vp(args["dv"]), vp(args["du"]), None, None,
+        vp(args["ws"]), ws_bytes, None)
+
+
+def test_backward_validation(lib):
+    # unequal head dims: the forward supports them, the backward does not
+    d = _desc(d_qk=64, d_v=128, ld_q=256, ld_k=256)
+    assert lib.hstu_jagged_attn_workspace_bytes(ctypes.byref(d)) > 0
+    assert _bwd(lib, d) == _lib.HSTU_ERR_UNSUPPORTED
+    assert "d_qk == d_v" in _lib.last_error()
+    assert _bwd(lib, _desc(), dq=None) == _lib.HSTU_ERR_INVALID_ARG
+    assert _bwd(lib, _desc(), du=None) == _lib.HSTU_ERR_INVALID_ARG
+    assert _bwd(lib, _desc(), ws=None) == _lib.HSTU_ERR_WORKSPACE
+    # du is not needed without the gate
+    rc = _bwd(lib, _desc(epilogue=_lib.HSTU_EPILOGUE_NONE), du=None)
+    assert rc in (_lib.HSTU_OK, _lib.HSTU_ERR_HIP)
+    # a table gradient pointer must come with its table
+    d = _desc(pos_table_len=16)
+    assert lib.hstu_jagged_attn_bwd(
+        ctypes.byref(d), *[ctypes.c_void_p(FAKE)] * 5, None, None, 0, 0, 0.1, 10.0,
+        ctypes.c_void_p(FAKE), None, *[ctypes.c_void_p(FAKE)] * 5, None, None,
+        ctypes.c_void_p(FAKE), 1 << 30, None) == _lib.HSTU_ERR_INVALID_ARG
 
 
 # The product's host pair count (used for throughput accounting) against the

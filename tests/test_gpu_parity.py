@@ -550,3 +550,42 @@ def test_empty_batch():
                           **call_kwargs(inp, dev))
     torch.cuda.synchronize()
     assert out.shape == (0, 1, 8)
+
+
+# ---------------------------------------------------------------------------
+# d_qk != d_v ("HSTU tensor by tensor", section "Trace four projections":
+# the Q/K and U/V branches have their own widths).  One side of the staging
+# then goes directly between HBM and registers.
+# ---------------------------------------------------------------------------
+def _unequal(dqk, dv, W=0, seed=61, H=2):
+    return make_custom([1, 37, 129, 300, 260, 5], num_heads=H, d_qk=dqk, d_v=dv, dtype="bf16",
+                       seed=seed, num_targets=[0, 5, 20, 50, 3, 5], contextual_len=3,
+                       max_attn_len=W, pos_len=64, pos_std=0.3, time_len=16, time_std=0.3,
+                       alpha=1.0 / math.sqrt(dqk))
+
+
+@pytest.mark.parametrize("dqk,dv", [(64, 128), (128, 64)])
+@pytest.mark.parametrize("epilogue", ["ln_u", "none", "ln_all_u"])
+@pytest.mark.parametrize("W", [0, 100])
+def test_unequal_head_dims(dqk, dv, epilogue, W):
+    inp = _unequal(dqk, dv, W=W)
+    assert_close(gpu_forward(inp, epilogue), ora(inp, epilogue), "bf16")
+
+
+@pytest.mark.parametrize("dqk,dv", [(64, 128), (128, 64)])
+def test_unequal_head_dims_ranking_shape(dqk, dv):
+    """Ranking-like batch (128 users, histories U[20, 200] + 20 candidates, 4 heads)."""
+    rng = np.random.default_rng(77)
+    hist = rng.integers(20, 201, size=128)
+    inp = make_custom((hist + 20).tolist(), num_heads=4, d_qk=dqk, d_v=dv, dtype="bf16",
+                      seed=78, num_targets=[20] * 128, pos_len=4096, time_len=64,
+                      alpha=1.0 / math.sqrt(dqk))
+    assert_close(gpu_forward(inp), ora(inp), "bf16")
+
+
+@pytest.mark.parametrize("dqk,dv", [(64, 128), (128, 64)])
+def test_unequal_head_dims_candidates_only(dqk, dv):
+    inp = _unequal(dqk, dv, W=40)
+    got = _candidates_forward(inp)
+    rows = _candidate_rows(inp)
+    assert_close(got, ora(inp, rows=rows), "bf16", rows=rows)
