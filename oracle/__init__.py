@@ -61,7 +61,7 @@ def _load():
             i32, P, i32, i32, i32,
             P, i64, P, i64, P, i64, P, i64,
             P, P, i32, i32, f64, f64,
-            P, i32, P, i32, f64, i32, P, i64, P, i32]
+            P, i32, P, i32, f64, i32, P, i64, P, i32, i32]
         lib.hstu_oracle_bwd.restype = ctypes.c_int
         lib.hstu_oracle_bwd.argtypes = [
             i32, P, i32, i32, i32,
@@ -97,10 +97,11 @@ def default_threads() -> int:
 def forward_arrays(offsets, q, k, v, u, *, timestamps=None, num_targets=None,
                    contextual_len=0, max_attn_len=0, alpha=1.0, n_scale=1.0,
                    pos_table=None, time_table=None, eps=1e-5, epilogue=EPILOGUE_LN_U,
-                   rows=None, nthreads: Optional[int] = None) -> np.ndarray:
+                   rows=None, nthreads: Optional[int] = None, pos_clamp=False) -> np.ndarray:
     """fp64 forward on [N, H, d] arrays (any float dtype; upcast exactly).
     `rows`: optional token indices; only those output rows are computed (the
-    others are NaN)."""
+    others are NaN).  `pos_clamp`: position bias at clamped positions
+    min(position, n_h) (the alternative reading of the candidate clamp)."""
     lib = _load()
     offsets = np.ascontiguousarray(offsets, dtype=np.int32)
     q = np.ascontiguousarray(q, dtype=np.float64)
@@ -128,21 +129,21 @@ def forward_arrays(offsets, q, k, v, u, *, timestamps=None, num_targets=None,
         _ptr(pos), 0 if pos is None else pos.shape[0],
         _ptr(tim), 0 if tim is None else tim.shape[0],
         float(np.float32(eps)), int(epilogue), _ptr(out), H * dv, _ptr(sel),
-        int(nthreads if nthreads is not None else default_threads()))
+        int(nthreads if nthreads is not None else default_threads()), int(bool(pos_clamp)))
     if rc != 0:
         raise ValueError("oracle rejected its arguments")
     return out
 
 
 def forward(inp, *, epilogue=EPILOGUE_LN_U, rows=None,
-            nthreads: Optional[int] = None) -> np.ndarray:
+            nthreads: Optional[int] = None, pos_clamp=False) -> np.ndarray:
     """fp64 forward of a `JaggedInputs` batch (optionally only token `rows`)."""
     return forward_arrays(
         inp.offsets, inp.q, inp.k, inp.v, inp.u, timestamps=inp.timestamps,
         num_targets=inp.num_targets, contextual_len=inp.contextual_len,
         max_attn_len=inp.max_attn_len, alpha=inp.alpha, n_scale=inp.n_scale,
         pos_table=inp.pos_table, time_table=inp.time_table, eps=inp.eps,
-        epilogue=epilogue, rows=rows, nthreads=nthreads)
+        epilogue=epilogue, rows=rows, nthreads=nthreads, pos_clamp=pos_clamp)
 
 
 def layer_forward(inp, *, rows=None, nthreads: Optional[int] = None) -> np.ndarray:
@@ -286,9 +287,11 @@ def _dense_mask(L: int, T: int, c: int, W: int, Lpad: int) -> np.ndarray:
     return m & valid
 
 
-def dense_forward(inp, *, epilogue=EPILOGUE_LN_U) -> np.ndarray:
+def dense_forward(inp, *, epilogue=EPILOGUE_LN_U, pos_clamp=False) -> np.ndarray:
     """Padded dense evaluation: SiLU on every padded entry, then zero the
-    illegal ones, then aggregate.  numpy fp64; tiny inputs only."""
+    illegal ones, then aggregate.  numpy fp64; tiny inputs only.  With
+    `pos_clamp` the position-bias matrix of each sequence is built from the
+    clamped position vector p = min(arange(L), n_h)."""
     B = inp.num_seqs
     L = inp.lengths
     Lpad = int(L.max()) if B else 0
@@ -315,8 +318,16 @@ def dense_forward(inp, *, epilogue=EPILOGUE_LN_U) -> np.ndarray:
     jj = np.arange(Lpad)[None, :]
     if inp.pos_table is not None:
         P = inp.pos_table.shape[0]
-        rel = np.minimum(np.abs(ii - jj), P - 1)
-        S = S + inp.pos_table.astype(f64)[rel][None, None]
+        if pos_clamp:
+            for b in range(B):
+                T = 0 if inp.num_targets is None else int(inp.num_targets[b])
+                n_h = int(L[b]) - min(max(T, 0), int(L[b]))
+                p = np.minimum(np.arange(Lpad), n_h)
+                rel = np.minimum(np.abs(p[:, None] - p[None, :]), P - 1)
+                S[b] = S[b] + inp.pos_table.astype(f64)[rel][None]
+        else:
+            rel = np.minimum(np.abs(ii - jj), P - 1)
+            S = S + inp.pos_table.astype(f64)[rel][None, None]
     if inp.time_table is not None:
         Tt = inp.time_table.shape[0]
         dt = np.abs(Tp[:, :, None] - Tp[:, None, :]).astype(np.uint64)

@@ -44,7 +44,10 @@
  *     candidate rows i >= n_h see every history token j < n_h, plus j == i.
  *   - window W > 0: additionally p_i - j <= W, where p_i = min(i, n_h) is the
  *     clamped candidate position (candidates all sit at the history end).
- *   - the bias uses the raw |i-j| and |t_i - t_j| (symmetric inside the prefix).
+ *   - the bias uses the raw |i-j| and |t_i - t_j| (symmetric inside the prefix);
+ *     with pos_clamp != 0 the position bias uses |p_i - p_j| instead, p = min(
+ *     position, n_h): the candidate clamp of the mask applied to the bias too
+ *     (the alternative reading; the backward takes the raw reading only).
  *   - floor(log2(1+dt)) is taken in exact integer arithmetic.
  *   - LayerNorm per (token, head) over d_v, no affine weights, biased
  *     variance, epsilon given by the caller.
@@ -166,7 +169,7 @@ int hstu_oracle_fwd(int num_seqs, const int32_t* offsets, int num_heads, int d_q
                     int contextual_len, int max_attn_len, double alpha, double n_scale,
                     const double* pos_table, int pos_len, const double* time_table,
                     int time_len, double eps, int epilogue, double* out, int64_t ld_out,
-                    const unsigned char* row_select, int nthreads) {
+                    const unsigned char* row_select, int nthreads, int pos_clamp) {
   if (num_seqs < 0 || num_heads <= 0 || d_qk <= 0 || d_v <= 0) return -1;
   if ((pos_table == NULL) != (pos_len == 0) || (time_table == NULL) != (time_len == 0)) return -1;
   if (time_table && !timestamps) return -1;
@@ -208,7 +211,11 @@ int hstu_oracle_fwd(int num_seqs, const int32_t* offsets, int num_heads, int d_q
           for (int e = 0; e < d_qk; ++e) dot += qi[e] * kj[e];
           double s = alpha * dot;
           if (pos_table) {
-            int64_t rel = i >= j ? i - j : j - i;
+            /* pos_clamp: positions taken as p = min(position, n_h), the
+               candidate clamp applied to the bias as well */
+            int64_t pi = pos_clamp && i > g.n_h ? g.n_h : i;
+            int64_t pj = pos_clamp && j > g.n_h ? g.n_h : j;
+            int64_t rel = pi >= pj ? pi - pj : pj - pi;
             s += pos_table[rel < pos_len - 1 ? rel : pos_len - 1];
           }
           if (time_table) {
@@ -330,7 +337,7 @@ int hstu_oracle_bwd(int num_seqs, const int32_t* offsets, int num_heads, int d_q
   int rc = hstu_oracle_fwd(num_seqs, offsets, num_heads, d_qk, d_v, q, ld_q, k, ld_k, v, ld_v,
                            u, ld_u, timestamps, num_targets, contextual_len, max_attn_len,
                            alpha, n_scale, pos_table, pos_len, time_table, time_len, eps,
-                           ORACLE_EPILOGUE_NONE, o, width, NULL, nthreads);
+                           ORACLE_EPILOGUE_NONE, o, width, NULL, nthreads, 0);
   if (rc != 0) {
     free(o);
     free(dO);

@@ -4,6 +4,7 @@ Each test names the passage it follows.  None of these retypes the oracle's
 formula: they use printed values, hand-worked masks, closed forms written as
 prefix sums, library routines (scipy, torch, Python integers) and invariants.
 """
+import dataclasses
 import math
 
 import numpy as np
@@ -465,3 +466,67 @@ def test_layer_rows_subset(oracle_mod):
     rows = np.array([0, 5, 29, 33, 77, 78])
     part = oracle_mod.layer_forward(inp, rows=rows)
     assert np.abs(full[rows] - part[rows]).max() <= 1e-12 * np.abs(full).max()
+
+
+# ---------------------------------------------------------------------------
+# Position bias at clamped positions (alternative reading of the candidate
+# clamp, "HSTU-MUSA", section "Mathematical Equivalence": every candidate sits
+# at the history end).  Pinned by what the clamp is for -- candidates become
+# interchangeable ("Scaling HSTU", section "Many candidates make reuse
+# valuable") -- and by the dense form built from a clamped position vector.
+# ---------------------------------------------------------------------------
+def _clamp_case(seed, T=6, L=40, W=0, c=0):
+    return make_custom([L, 23, L + 5], num_heads=2, d_qk=8, d_v=8, seed=seed,
+                       num_targets=[T, 3, T], contextual_len=c, max_attn_len=W, pos_len=64,
+                       pos_std=0.5, time_len=16, time_std=0.5, alpha=0.5)
+
+
+def test_pos_clamp_without_candidates_changes_nothing(oracle_mod):
+    inp = make_custom([30, 17], num_heads=2, d_qk=8, d_v=8, seed=3, pos_len=64, pos_std=0.5,
+                      time_len=16, alpha=0.5)
+    a = oracle_mod.forward(inp)
+    b = oracle_mod.forward(inp, pos_clamp=True)
+    assert np.array_equal(a, b)
+
+
+def test_pos_clamp_leaves_history_rows(oracle_mod):
+    inp = _clamp_case(5, W=9, c=3)
+    a = oracle_mod.forward(inp)
+    b = oracle_mod.forward(inp, pos_clamp=True)
+    hist = []
+    for bq in range(inp.num_seqs):
+        s0, s1 = int(inp.offsets[bq]), int(inp.offsets[bq + 1])
+        hist.extend(range(s0, s1 - int(inp.num_targets[bq])))
+    assert np.array_equal(a[hist], b[hist])
+    assert not np.allclose(a, b)        # the candidates' rows do change
+
+
+@pytest.mark.parametrize("W", [0, 7])
+def test_pos_clamp_makes_candidates_interchangeable(oracle_mod, W):
+    """Permuting the candidates of a sequence (all their inputs, timestamps
+    included) permutes their outputs when the bias is clamped -- and not with
+    the raw bias, which tells candidates apart by position."""
+    inp = _clamp_case(7, W=W)
+    s0, s1 = int(inp.offsets[0]), int(inp.offsets[1])
+    cand = np.arange(s1 - 6, s1)
+    perm = cand[np.random.default_rng(1).permutation(6)]
+    order = np.arange(inp.total_tokens)
+    order[cand] = perm
+    shuffled = dataclasses.replace(
+        inp, q=inp.q[order], k=inp.k[order], v=inp.v[order], u=inp.u[order],
+        timestamps=inp.timestamps[order])
+    a = oracle_mod.forward(inp, pos_clamp=True)
+    b = oracle_mod.forward(shuffled, pos_clamp=True)
+    assert np.allclose(b[cand], a[perm], rtol=0, atol=1e-12)
+    raw_a = oracle_mod.forward(inp)
+    raw_b = oracle_mod.forward(shuffled)
+    assert not np.allclose(raw_b[cand], raw_a[perm], rtol=0, atol=1e-9)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_pos_clamp_equals_dense_bruteforce(oracle_mod, seed):
+    inp = _random_case(100 + seed)
+    for ep in (oracle_mod.EPILOGUE_NONE, oracle_mod.EPILOGUE_LN_U):
+        a = oracle_mod.forward(inp, epilogue=ep, pos_clamp=True)
+        b = oracle_mod.dense_forward(inp, epilogue=ep, pos_clamp=True)
+        assert np.allclose(a, b, rtol=1e-12, atol=1e-12)
