@@ -32,7 +32,11 @@
  *   candidate rows i >= n_h      : j < n_h, or j == i   (target group)
  *   if max_attn_len W > 0, also p_i - j <= W with p_i = min(i, n_h)
  *   (candidate position clamping: every candidate sits at the history end).
- * The bias always uses the raw |i-j| and |t_i - t_j|.  LayerNorm is taken per
+ * The bias uses the raw |i-j| and |t_i - t_j|; with desc->pos_clamp = 1 the
+ * position bias uses |p_i - p_j| instead, the clamp p = min(position, n_h) of
+ * the candidate rule applied to the bias too (so candidates, all at the
+ * history end, become interchangeable; "Scaling HSTU", section "Many
+ * candidates make reuse valuable").  The backward takes pos_clamp = 0 only.  LayerNorm is taken per
  * (token, head) over d_v, without affine weights, with biased variance and
  * epsilon desc->ln_eps.
  *
@@ -106,6 +110,8 @@ typedef struct {
   int32_t time_table_len; /* Tt; 0 iff time_table is NULL (then no timestamps)    */
   float ln_eps;           /* LayerNorm epsilon (> 0 and finite)                   */
   int32_t epilogue;       /* hstu_epilogue                                        */
+  int32_t pos_clamp;      /* 0: position bias of |i-j| (default); 1: of |p_i-p_j|  */
+                          /* with p = min(position, n_h) (forward only, see above) */
 } hstu_attn_desc;
 
 /*

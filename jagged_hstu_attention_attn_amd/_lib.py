@@ -59,6 +59,7 @@ class HstuAttnDesc(ctypes.Structure):
         ("time_table_len", ctypes.c_int32),
         ("ln_eps", ctypes.c_float),
         ("epilogue", ctypes.c_int32),
+        ("pos_clamp", ctypes.c_int32),
     ]
 
 

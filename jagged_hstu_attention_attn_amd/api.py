@@ -47,7 +47,8 @@ def _token_stride(t: torch.Tensor, name: str) -> int:
 
 
 def make_desc(q, k, v, u, out, num_seqs: int, *, pos_table=None, time_table=None,
-              eps: float = 1e-5, epilogue: str = "ln_u") -> _lib.HstuAttnDesc:
+              eps: float = 1e-5, epilogue: str = "ln_u",
+              pos_clamp: bool = False) -> _lib.HstuAttnDesc:
     if q.dtype not in _DTYPES:
         raise TypeError(f"unsupported dtype {q.dtype}")
     for name, t in (("k", k), ("v", v), ("out", out)) + ((("u", u),) if u is not None else ()):
@@ -69,6 +70,7 @@ def make_desc(q, k, v, u, out, num_seqs: int, *, pos_table=None, time_table=None
     d.time_table_len = 0 if time_table is None else int(time_table.numel())
     d.ln_eps = float(eps)
     d.epilogue = _EPILOGUES[epilogue]
+    d.pos_clamp = 1 if pos_clamp else 0
     return d
 
 
@@ -133,7 +135,7 @@ class JaggedAttnCall:
     def __init__(self, q, k, v, u, offsets, *, timestamps=None, num_targets=None,
                  contextual_len=0, max_attn_len=0, alpha, n_scale, pos_table=None,
                  time_table=None, eps=1e-5, epilogue="ln_u", out=None,
-                 candidates_only: bool = False):
+                 candidates_only: bool = False, pos_clamp: bool = False):
         if not q.is_cuda:
             raise ValueError("tensors must be on a GPU")
         _check_aux(offsets, timestamps, num_targets, pos_table, time_table, q.device)
@@ -148,7 +150,8 @@ class JaggedAttnCall:
                               device=q.device)
         self.out = out
         self.desc = make_desc(q, k, v, u, out, offsets.numel() - 1, pos_table=pos_table,
-                              time_table=time_table, eps=eps, epilogue=epilogue)
+                              time_table=time_table, eps=eps, epilogue=epilogue,
+                              pos_clamp=pos_clamp)
         self.workspace = torch.empty(workspace_bytes(self.desc), dtype=torch.uint8,
                                      device=q.device)
 
@@ -175,7 +178,7 @@ def jagged_attn_fwd(q, k, v, u, offsets, *, timestamps=None, num_targets=None,
                     contextual_len: int = 0, max_attn_len: int = 0, alpha: float,
                     n_scale: float, pos_table=None, time_table=None, eps: float = 1e-5,
                     epilogue: str = "ln_u", out=None,
-                    candidates_only: bool = False) -> torch.Tensor:
+                    candidates_only: bool = False, pos_clamp: bool = False) -> torch.Tensor:
     """One full forward (scheduler + attention) on the current stream.  With
     `candidates_only`, only the candidate rows of `out` are computed and
     written (history rows keep their contents)."""
@@ -183,7 +186,7 @@ def jagged_attn_fwd(q, k, v, u, offsets, *, timestamps=None, num_targets=None,
                           contextual_len=contextual_len, max_attn_len=max_attn_len,
                           alpha=alpha, n_scale=n_scale, pos_table=pos_table,
                           time_table=time_table, eps=eps, epilogue=epilogue, out=out,
-                          candidates_only=candidates_only)
+                          candidates_only=candidates_only, pos_clamp=pos_clamp)
     return call()
 
 

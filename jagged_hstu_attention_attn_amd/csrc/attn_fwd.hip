@@ -120,7 +120,7 @@ struct Cfg {
 
 // One stage of the pipeline.  Each stage buffer is its own __shared__ object,
 // so the compiler can tell that the accesses of different stages never alias.
-template <typename T, int DQK, int DV>
+template <typename T, int DQK, int DV, bool CLAMP>
 struct StageBuf {
   using C = Cfg<T, DQK, DV>;
   char k[kBN * C::kKRow];        // keys: row j at byte j * kKRow, chunks swizzled
@@ -131,6 +131,7 @@ struct StageBuf {
   uint32_t tmin, tmax;           // range of ts32 over the valid keys
   int tbad;                      // some key needs the 64-bit time path
   int pad_;
+  float cpos[CLAMP ? 64 : 1];    // clamped-position bias of key (lane % 32): n_h - j
 };
 
 struct TimeTables {
@@ -269,11 +270,15 @@ __device__ inline float silu2(float x) {
   return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x));
 }
 
-template <typename T, int DQK, int DV, bool POS, bool TIME>
+// POSM: 0 = no position bias, 1 = position bias of |i - j|, 2 = of the
+// clamped positions |p_i - p_j| (candidate rows take it from cpos).
+template <typename T, int DQK, int DV, int POSM, bool TIME>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void
 hstu_attn_fwd_kernel(AttnArgs a) {
+  constexpr bool POS = POSM != 0;
+  constexpr bool clamp = POSM == 2;
   using C = Cfg<T, DQK, DV>;
-  using SB = StageBuf<T, DQK, DV>;
+  using SB = StageBuf<T, DQK, DV, clamp>;
   constexpr bool BF = C::kBf16;
   constexpr int ES = C::kEs;
   constexpr int NKC = C::kNKC;
@@ -311,7 +316,7 @@ hstu_attn_fwd_kernel(AttnArgs a) {
   const float am = alpha_zero ? 1.0f : alpha2;   // x2 = am * S + time
   const float pscale = kLog2e / am;              // position bias in accumulator units
   const uint32_t ldk_b = (uint32_t)(a.ld_k * ES), ldv_b = (uint32_t)(a.ld_v * ES);
-  const int my_copies = stage_copies<NK, NV, POS, TIME>(wave);
+  const int my_copies = stage_copies<NK, NV, POS, TIME>(wave) + ((clamp && wave == kTsWave) ? 1 : 0);
 
   if constexpr (TIME) {
     // log2(e) * time table, indexed two ways (see TimeTables)
@@ -377,6 +382,9 @@ hstu_attn_fwd_kernel(AttnArgs a) {
     w_lomax = wave_max(row_valid ? rb.lo : -1);
     w_himin = wave_min(row_valid ? (nonempty ? hi : -1) : 0x7fffffff);
   }
+  // some row of this wave is a candidate whose bias uses clamped positions
+  const bool w_cand = clamp && wave_rows && wr0 + kRows - 1 >= geo.n_h;
+  (void)w_cand;
   auto needs = [&](int kt) __attribute__((always_inline)) {
     const int jb = kt * kBN;
     return wave_rows && jb <= w_jmax && jb + kBN - 1 >= w_jmin;
@@ -442,6 +450,13 @@ hstu_attn_fwd_kernel(AttnArgs a) {
         lds_copy4(ts_base, 8u * (uint32_t)j + 4u * (uint32_t)(lane & 1), lds_off(sb.ts64));
       }
     }
+    if constexpr (POS) {
+      if (clamp && wave == kTsWave) {   // bias of n_h - j (0 for candidate keys)
+        const int d = geo.n_h - (j0 + (lane & (kBN - 1)));
+        const int ix = min(d > 0 ? d : 0, P - 1);
+        lds_copy4(pos_base, 4u * (uint32_t)ix, lds_off(sb.cpos));
+      }
+    }
   };
 
   // row times (loaded in the prologue)
@@ -461,6 +476,7 @@ hstu_attn_fwd_kernel(AttnArgs a) {
         const int e = 64 * (kWaves - 1 - wave) + lane;
         if (e < kDiag) sb.diag[e] *= pscale;
       }
+      if (clamp && wave == kTsWave) sb.cpos[lane] *= pscale;
     }
     if constexpr (TIME) {
       if (wave == kTsWave) {   // lanes 0..31: one key each
@@ -529,6 +545,16 @@ hstu_attn_fwd_kernel(AttnArgs a) {
     for (int r = 0; r < 16; ++r) {
       if constexpr (POS) s[r] = sb.diag[dbase + 8 * (r >> 2) + (r & 3)];
       else s[r] = 0.0f;
+    }
+    if constexpr (clamp) {
+      if (w_cand) {   // candidate rows: bias of the clamped positions
+        const bool cr = i >= geo.n_h;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float cv = sb.cpos[acc_row(r, hh)];
+          s[r] = cr ? cv : s[r];
+        }
+      }
     }
     // K operand of MFMA step c (logical chunk 2c + hh of key row l32)
     auto kread = [&](int c) __attribute__((always_inline)) {
@@ -1008,17 +1034,17 @@ hstu_attn_fwd_kernel(AttnArgs a) {
   }  // planned workgroups
 }
 
-template <typename T, int DQK, int DV, bool POS, bool TIME>
+template <typename T, int DQK, int DV, int POSM, bool TIME>
 static hipError_t launch_one(const AttnArgs& a, int n_wg, hipStream_t stream) {
-  auto kern = hstu_attn_fwd_kernel<T, DQK, DV, POS, TIME>;
+  auto kern = hstu_attn_fwd_kernel<T, DQK, DV, POSM, TIME>;
   hipLaunchKernelGGL(kern, dim3((unsigned)n_wg), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
 // Resident workgroups per CU for one instantiation.
-template <typename T, int DQK, int DV, bool POS, bool TIME>
+template <typename T, int DQK, int DV, int POSM, bool TIME>
 static int blocks_per_cu() {
-  auto kern = hstu_attn_fwd_kernel<T, DQK, DV, POS, TIME>;
+  auto kern = hstu_attn_fwd_kernel<T, DQK, DV, POSM, TIME>;
   int nb = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, kThreads, 0) != hipSuccess)
     return -1;
@@ -1027,33 +1053,37 @@ static int blocks_per_cu() {
 
 template <typename T, int DQK, int DV>
 static hipError_t launch_bias(const AttnArgs& a, int n_wg, hipStream_t stream) {
-  const bool pos = a.pos_len > 0, tim = a.time_len > 0;
-  if (pos && tim) return launch_one<T, DQK, DV, true, true>(a, n_wg, stream);
-  if (pos) return launch_one<T, DQK, DV, true, false>(a, n_wg, stream);
-  if (tim) return launch_one<T, DQK, DV, false, true>(a, n_wg, stream);
-  return launch_one<T, DQK, DV, false, false>(a, n_wg, stream);
+  const bool pos = a.pos_len > 0, tim = a.time_len > 0, cl = a.pos_clamp != 0;
+  if (pos && cl && tim) return launch_one<T, DQK, DV, 2, true>(a, n_wg, stream);
+  if (pos && cl) return launch_one<T, DQK, DV, 2, false>(a, n_wg, stream);
+  if (pos && tim) return launch_one<T, DQK, DV, 1, true>(a, n_wg, stream);
+  if (pos) return launch_one<T, DQK, DV, 1, false>(a, n_wg, stream);
+  if (tim) return launch_one<T, DQK, DV, 0, true>(a, n_wg, stream);
+  return launch_one<T, DQK, DV, 0, false>(a, n_wg, stream);
 }
 
 template <typename T, int DQK, int DV>
-static int bpc_bias(int pos_len, int time_len) {
+static int bpc_bias(int pos_len, int time_len, bool cl) {
   const bool pos = pos_len > 0, tim = time_len > 0;
-  if (pos && tim) return blocks_per_cu<T, DQK, DV, true, true>();
-  if (pos) return blocks_per_cu<T, DQK, DV, true, false>();
-  if (tim) return blocks_per_cu<T, DQK, DV, false, true>();
-  return blocks_per_cu<T, DQK, DV, false, false>();
+  if (pos && cl && tim) return blocks_per_cu<T, DQK, DV, 2, true>();
+  if (pos && cl) return blocks_per_cu<T, DQK, DV, 2, false>();
+  if (pos && tim) return blocks_per_cu<T, DQK, DV, 1, true>();
+  if (pos) return blocks_per_cu<T, DQK, DV, 1, false>();
+  if (tim) return blocks_per_cu<T, DQK, DV, 0, true>();
+  return blocks_per_cu<T, DQK, DV, 0, false>();
 }
 
-int attn_grid(int dtype, int d_qk, int d_v, int pos_len, int time_len) {
+int attn_grid(int dtype, int d_qk, int d_v, int pos_len, int time_len, bool clamp) {
   int bpc = -1;
   if (dtype == 1) {
-    if (d_qk == 128 && d_v == 128) bpc = bpc_bias<__bf16, 128, 128>(pos_len, time_len);
-    if (d_qk == 64 && d_v == 64) bpc = bpc_bias<__bf16, 64, 64>(pos_len, time_len);
-    if (d_qk == 64 && d_v == 128) bpc = bpc_bias<__bf16, 64, 128>(pos_len, time_len);
-    if (d_qk == 128 && d_v == 64) bpc = bpc_bias<__bf16, 128, 64>(pos_len, time_len);
+    if (d_qk == 128 && d_v == 128) bpc = bpc_bias<__bf16, 128, 128>(pos_len, time_len, clamp);
+    if (d_qk == 64 && d_v == 64) bpc = bpc_bias<__bf16, 64, 64>(pos_len, time_len, clamp);
+    if (d_qk == 64 && d_v == 128) bpc = bpc_bias<__bf16, 64, 128>(pos_len, time_len, clamp);
+    if (d_qk == 128 && d_v == 64) bpc = bpc_bias<__bf16, 128, 64>(pos_len, time_len, clamp);
   } else if (dtype == 0) {
-    if (d_qk == 128 && d_v == 128) bpc = bpc_bias<float, 128, 128>(pos_len, time_len);
-    if (d_qk == 64 && d_v == 64) bpc = bpc_bias<float, 64, 64>(pos_len, time_len);
-    if (d_qk == 8 && d_v == 8) bpc = bpc_bias<float, 8, 8>(pos_len, time_len);
+    if (d_qk == 128 && d_v == 128) bpc = bpc_bias<float, 128, 128>(pos_len, time_len, clamp);
+    if (d_qk == 64 && d_v == 64) bpc = bpc_bias<float, 64, 64>(pos_len, time_len, clamp);
+    if (d_qk == 8 && d_v == 8) bpc = bpc_bias<float, 8, 8>(pos_len, time_len, clamp);
   }
   if (bpc <= 0) return -1;
   int dev = 0, cus = 0;

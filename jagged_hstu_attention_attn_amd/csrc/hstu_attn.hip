@@ -37,6 +37,8 @@ int check_desc(const hstu_attn_desc* d) {
   if (d->epilogue != HSTU_EPILOGUE_LN_U && d->epilogue != HSTU_EPILOGUE_NONE &&
       d->epilogue != HSTU_EPILOGUE_LN_ALL_U)
     return fail(HSTU_ERR_INVALID_ARG, "unknown epilogue %d", d->epilogue);
+  if (d->pos_clamp != 0 && d->pos_clamp != 1)
+    return fail(HSTU_ERR_INVALID_ARG, "pos_clamp must be 0 or 1 (%d)", d->pos_clamp);
   if (d->d_qk <= 0 || d->d_v <= 0)
     return fail(HSTU_ERR_INVALID_ARG, "d_qk and d_v must be positive (%d, %d)", d->d_qk, d->d_v);
   if (!hstu::attn_supported(d->dtype, d->d_qk, d->d_v))
@@ -119,26 +121,29 @@ int check_run_args(const hstu_attn_desc* d, const void* q, const void* k, const 
 // kMaxGrid (the most a plan serves).  <= 0 on a HIP error.
 int persistent_grid(const hstu_attn_desc* d) {
   struct Entry {
-    int dev, dtype, d_qk, d_v, pos_len, has_time, grid;
+    int dev, dtype, d_qk, d_v, pos_len, has_time, clamp, grid;
   };
   static thread_local Entry cache[16];
   static thread_local int cache_n = 0;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return -1;
   const int has_time = d->time_table_len > 0;
+  const int clamp = d->pos_clamp != 0 && d->pos_table_len > 0;
   int g = -1;
   for (int i = 0; i < cache_n && i < 16; ++i) {
     const Entry& e = cache[i];
     if (e.dev == dev && e.dtype == d->dtype && e.d_qk == d->d_qk && e.d_v == d->d_v &&
-        e.pos_len == d->pos_table_len && e.has_time == has_time) {
+        e.pos_len == d->pos_table_len && e.has_time == has_time && e.clamp == clamp) {
       g = e.grid;
       break;
     }
   }
   if (g < 0) {
-    g = hstu::attn_grid(d->dtype, d->d_qk, d->d_v, d->pos_table_len, d->time_table_len);
+    g = hstu::attn_grid(d->dtype, d->d_qk, d->d_v, d->pos_table_len, d->time_table_len,
+                        clamp != 0);
     if (g <= 0) return g;
-    cache[cache_n % 16] = Entry{dev, d->dtype, d->d_qk, d->d_v, d->pos_table_len, has_time, g};
+    cache[cache_n % 16] =
+        Entry{dev, d->dtype, d->d_qk, d->d_v, d->pos_table_len, has_time, clamp, g};
     ++cache_n;
   }
   // at least one workgroup per XCD, at most what a plan serves
@@ -283,6 +288,7 @@ int hstu_jagged_attn_run(const hstu_attn_desc* desc, const void* q, const void* 
   a.pos_len = desc->pos_table_len;
   a.time_len = desc->time_table_len;
   a.epilogue = ln_all ? HSTU_EPILOGUE_NONE : desc->epilogue;
+  a.pos_clamp = desc->pos_clamp;
   a.alpha = alpha;
   a.out_scale = (float)(0.69314718055994530942 / (double)n_scale);
   a.ln_eps = desc->ln_eps;
@@ -411,6 +417,7 @@ hstu_attn_desc layer_attn_desc(const hstu_layer_desc* d) {
   a.time_table_len = d->time_table_len;
   a.ln_eps = d->ln_eps;
   a.epilogue = HSTU_EPILOGUE_LN_U;
+  a.pos_clamp = 0;
   return a;
 }
 
@@ -626,6 +633,8 @@ int hstu_jagged_attn_bwd(const hstu_attn_desc* desc, const void* q, const void* 
   if (desc->d_qk != desc->d_v)
     return fail(HSTU_ERR_UNSUPPORTED, "the backward needs d_qk == d_v (%d, %d)", desc->d_qk,
                 desc->d_v);
+  if (desc->pos_clamp != 0)
+    return fail(HSTU_ERR_UNSUPPORTED, "the backward takes the raw position bias (pos_clamp 0)");
   if (desc->num_seqs > 0 && !offsets) return fail(HSTU_ERR_INVALID_ARG, "offsets is NULL");
   if (contextual_len < 0) return fail(HSTU_ERR_INVALID_ARG, "contextual_len < 0");
   if (max_attn_len < 0) return fail(HSTU_ERR_INVALID_ARG, "max_attn_len < 0");

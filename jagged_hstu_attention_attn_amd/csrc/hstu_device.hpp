@@ -201,6 +201,7 @@ struct AttnArgs {
   int32_t pos_len;
   int32_t time_len;
   int32_t epilogue;   // 0 = LayerNorm * U, 1 = none
+  int32_t pos_clamp;  // position bias of |p_i - p_j|, p = min(position, n_h)
   float alpha;
   float out_scale;    // ln(2) / n_scale: SiLU values are formed in log2 units
   float ln_eps;
@@ -323,7 +324,7 @@ hipError_t launch_attn(const AttnArgs& a, int dtype, int d_qk, int d_v, int n_wg
                        hipStream_t stream);
 // Workgroups of the persistent attention launch for this shape on the current
 // device (CUs x resident workgroups per CU), or a negative value on error.
-int attn_grid(int dtype, int d_qk, int d_v, int pos_len, int time_len);
+int attn_grid(int dtype, int d_qk, int d_v, int pos_len, int time_len, bool clamp);
 bool attn_supported(int dtype, int d_qk, int d_v);
 int ln_all_heads_max_width(int dtype);
 hipError_t launch_ln_all_heads(const LnArgs& a, int dtype, hipStream_t stream);

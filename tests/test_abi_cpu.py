@@ -91,6 +91,7 @@ def _fwd(lib, d, ws_bytes=None, **kw):
     ("ld_k", 516, _lib.HSTU_ERR_INVALID_ARG),          # 1032 bytes: not a multiple of 16
     ("ln_eps", 0.0, _lib.HSTU_ERR_INVALID_ARG),
     ("pos_table_len", 9000, _lib.HSTU_ERR_UNSUPPORTED),
+    ("pos_clamp", 2, _lib.HSTU_ERR_INVALID_ARG),
 ])
 def test_bad_descriptor(lib, field, value, code):
     d = _desc(**{field: value})
@@ -183,6 +184,7 @@ def test_backward_validation(lib):
     assert _bwd(lib, _desc(), dq=None) == _lib.HSTU_ERR_INVALID_ARG
     assert _bwd(lib, _desc(), du=None) == _lib.HSTU_ERR_INVALID_ARG
     assert _bwd(lib, _desc(), ws=None) == _lib.HSTU_ERR_WORKSPACE
+    assert _bwd(lib, _desc(pos_clamp=1)) == _lib.HSTU_ERR_UNSUPPORTED
     # du is not needed without the gate
     rc = _bwd(lib, _desc(epilogue=_lib.HSTU_EPILOGUE_NONE), du=None)
     assert rc in (_lib.HSTU_OK, _lib.HSTU_ERR_HIP)

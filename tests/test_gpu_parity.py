@@ -22,10 +22,11 @@ TOL = {"f32": 1e-5, "bf16": 1e-2}
 DEV = "cuda:0"
 
 
-def gpu_forward(inp, epilogue="ln_u", ld=None, out=None):
+def gpu_forward(inp, epilogue="ln_u", ld=None, out=None, pos_clamp=False):
     dev = to_device(inp, DEV, ld=ld)
     o = jagged_attn_fwd(dev["q"], dev["k"], dev["v"], dev["u"], dev["offsets"],
-                        epilogue=epilogue, out=out, **call_kwargs(inp, dev))
+                        epilogue=epilogue, out=out, pos_clamp=pos_clamp,
+                        **call_kwargs(inp, dev))
     torch.cuda.synchronize()
     return o.float().cpu().numpy().astype(np.float64)
 
@@ -40,10 +41,10 @@ def assert_close(gpu, ref, dtype, rows=None):
     return err / max(scale, 1e-300)
 
 
-def ora(inp, epilogue="ln_u", rows=None):
+def ora(inp, epilogue="ln_u", rows=None, pos_clamp=False):
     ep = {"ln_u": oracle.EPILOGUE_LN_U, "none": oracle.EPILOGUE_NONE,
           "ln_all_u": oracle.EPILOGUE_LN_ALL_U}[epilogue]
-    return oracle.forward(inp, epilogue=ep, rows=rows)
+    return oracle.forward(inp, epilogue=ep, rows=rows, pos_clamp=pos_clamp)
 
 
 # ---------------------------------------------------------------------------
@@ -589,3 +590,41 @@ def test_unequal_head_dims_candidates_only(dqk, dv):
     got = _candidates_forward(inp)
     rows = _candidate_rows(inp)
     assert_close(got, ora(inp, rows=rows), "bf16", rows=rows)
+
+
+# ---------------------------------------------------------------------------
+# Position bias at clamped positions (the alternative reading of the
+# candidate clamp of "HSTU-MUSA", section "Mathematical Equivalence").
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 8), ("f32", 64)])
+@pytest.mark.parametrize("epilogue", ["ln_u", "none"])
+def test_pos_clamp(dtype, d, epilogue):
+    inp = make_custom([1, 37, 129, 300, 260, 5], num_heads=2, d_qk=d, d_v=d, dtype=dtype,
+                      seed=91, num_targets=[0, 5, 20, 50, 3, 5], contextual_len=3,
+                      max_attn_len=100, pos_len=512, pos_std=0.3, time_len=16, time_std=0.3,
+                      alpha=1.0 / math.sqrt(d))
+    got = gpu_forward(inp, epilogue, pos_clamp=True)
+    assert_close(got, ora(inp, epilogue, pos_clamp=True), dtype)
+    # history rows are those of the raw reading
+    raw = gpu_forward(inp, epilogue)
+    rows = _candidate_rows(inp)
+    hist = np.setdiff1d(np.arange(inp.total_tokens), rows)
+    assert np.array_equal(got[hist], raw[hist])
+
+
+def test_pos_clamp_ranking_workload():
+    inp = make_inputs("ranking")
+    assert_close(gpu_forward(inp, pos_clamp=True), ora(inp, pos_clamp=True), "bf16")
+
+
+def test_pos_clamp_candidates_only():
+    inp = make_inputs("windowed", num_seqs=2)
+    dev = to_device(inp, DEV)
+    out = torch.full((inp.total_tokens, inp.num_heads, inp.d_v), -5.0, dtype=torch.bfloat16,
+                     device=DEV)
+    jagged_attn_fwd(dev["q"], dev["k"], dev["v"], dev["u"], dev["offsets"], out=out,
+                    candidates_only=True, pos_clamp=True, **call_kwargs(inp, dev))
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().astype(np.float64)
+    rows = _candidate_rows(inp)
+    assert_close(got, ora(inp, rows=rows, pos_clamp=True), "bf16", rows=rows)
