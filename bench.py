@@ -158,6 +158,14 @@ def bench_backward(args, inp) -> int:
     dt = dev["q"].dtype
     g = torch.Generator(device="cuda").manual_seed(0)
     dout = torch.randn(dev["v"].shape, generator=g, device="cuda", dtype=torch.float32).to(dt)
+    o_saved = None
+    if args.saved_o:
+        # the training forward keeps o / n_scale; the backward then skips its recompute
+        from jagged_hstu_attention_attn_amd.api import JaggedAttnCall
+        fwd = JaggedAttnCall(dev["q"], dev["k"], dev["v"], dev["u"], dev["offsets"],
+                             epilogue=args.epilogue, save_o=True, **call_kwargs(inp, dev))
+        fwd()
+        o_saved = fwd.o_raw
     pairs = valid_pairs(inp.offsets, inp.num_targets, inp.contextual_len, inp.max_attn_len)
     H, dqk, dv = inp.num_heads, inp.d_qk, inp.d_v
     fpp = 2.0 * (3 * dqk + 2 * dv)
@@ -166,7 +174,7 @@ def bench_backward(args, inp) -> int:
     log(f"backward: {inp.num_seqs} sequences, {inp.total_tokens} tokens, {pairs} valid "
         f"pairs/head; warmup {args.warmup}")
     for _ in range(args.warmup):
-        call(dout)
+        call(dout, o_saved)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -176,7 +184,7 @@ def bench_backward(args, inp) -> int:
         if flush is not None:
             flush.fill_(s & 0xFF)
         e0.record(stream)
-        call(dout)
+        call(dout, o_saved)
         e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -189,6 +197,7 @@ def bench_backward(args, inp) -> int:
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": inp.dtype, "data": "synthetic",
         "config": {"workload": args.workload, "pass": "backward", "epilogue": args.epilogue,
+                   "o": "saved by the training forward" if args.saved_o else "recomputed",
                    "num_seqs": inp.num_seqs, "total_tokens": inp.total_tokens,
                    "num_heads": H, "d_qk": dqk, "d_v": dv, "valid_pairs_per_head": pairs,
                    "seed": args.seed if args.seed is not None else WORKLOADS[args.workload].seed,
@@ -301,6 +310,8 @@ def main() -> int:
                     help="compute only the candidate rows (history reused; no CPU baseline)")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward (gradients of q, k, v, u and the bias tables)")
+    ap.add_argument("--saved-o", action="store_true",
+                    help="with --backward: take o / n_scale kept by the training forward")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 256 MiB device copy (counter calibration)")
     args = ap.parse_args()

@@ -294,8 +294,9 @@ int hstu_layer_fwd(const hstu_layer_desc* desc, const void* x, const void* w_uvq
  * dpos_table / dtime_table: float32 [P] / [Tt], NULL exactly when the table
  * is.  Every token row of dq, dk, dv (and du unless the epilogue is NONE, in
  * which case du may be NULL and is not touched) and both tables are
- * overwritten.  The raw aggregation o that the gate needs is recomputed (one
- * forward pass with epilogue NONE, rounded to dtype) inside the call.
+ * overwritten.  The raw aggregation o that the gate needs is o_saved when
+ * given, else recomputed (one forward pass with epilogue NONE, rounded to
+ * dtype) inside the call.
  *
  * Execution: a scheduler kernel, then for bf16 (d = 64, 128) a dQ pass over
  * query tiles and a dK/dV pass over key tiles (bf16 MFMA, fp32 accumulation;
@@ -309,15 +310,37 @@ int hstu_layer_fwd(const hstu_layer_desc* desc, const void* x, const void* w_uvq
  */
 size_t hstu_jagged_attn_bwd_workspace_bytes(const hstu_attn_desc* desc);
 
+/*
+ * o_saved: NULL, or the raw aggregation o / n_scale ([total_tokens, H, d_v],
+ * token stride H * d_v, dtype of desc) that hstu_jagged_attn_fwd_train wrote
+ * for these inputs; then the backward skips its forward recompute.
+ */
 int hstu_jagged_attn_bwd(const hstu_attn_desc* desc,
                          const void* q, const void* k, const void* v, const void* u,
                          const int32_t* offsets, const int64_t* timestamps,
                          const int32_t* num_targets, int32_t contextual_len,
                          int32_t max_attn_len, float alpha, float n_scale,
                          const float* pos_table, const float* time_table,
-                         const void* dout, void* dq, void* dk, void* dv, void* du,
+                         const void* dout, const void* o_saved,
+                         void* dq, void* dk, void* dv, void* du,
                          float* dpos_table, float* dtime_table,
                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The forward for training: hstu_jagged_attn_fwd (same arguments, same `out`)
+ * that also writes o_raw = o / n_scale, the aggregation before the gate
+ * ([total_tokens, H, d_v], token stride H * d_v, dtype of desc; 16-byte
+ * aligned, caller-owned), which hstu_jagged_attn_bwd can take as o_saved
+ * instead of recomputing it.  Costs one more write of that tensor.
+ */
+int hstu_jagged_attn_fwd_train(const hstu_attn_desc* desc,
+                               const void* q, const void* k, const void* v, const void* u,
+                               const int32_t* offsets, const int64_t* timestamps,
+                               const int32_t* num_targets, int32_t contextual_len,
+                               int32_t max_attn_len, float alpha, float n_scale,
+                               const float* pos_table, const float* time_table, void* out,
+                               void* o_raw, void* workspace, size_t workspace_bytes,
+                               void* stream);
 
 const char* hstu_last_error(void);
 

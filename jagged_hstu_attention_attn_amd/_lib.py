@@ -38,6 +38,7 @@ EXPORTS = (
     "hstu_jagged_attn_grid",
     "hstu_jagged_attn_bwd_workspace_bytes",
     "hstu_jagged_attn_bwd",
+    "hstu_jagged_attn_fwd_train",
     "hstu_last_error",
 )
 
@@ -126,7 +127,10 @@ def load() -> ctypes.CDLL:
     lib.hstu_jagged_attn_bwd_workspace_bytes.argtypes = [D]
     lib.hstu_jagged_attn_bwd.restype = ctypes.c_int
     lib.hstu_jagged_attn_bwd.argtypes = [D, P, P, P, P, P, P, P, i32, i32, f32, f32, P, P, P,
-                                         P, P, P, P, P, P, P, sz, P]
+                                         P, P, P, P, P, P, P, P, sz, P]
+    lib.hstu_jagged_attn_fwd_train.restype = ctypes.c_int
+    lib.hstu_jagged_attn_fwd_train.argtypes = [D, P, P, P, P, P, P, P, i32, i32, f32, f32, P, P,
+                                               P, P, P, sz, P]
     lib.hstu_last_error.restype = ctypes.c_char_p
     lib.hstu_last_error.argtypes = []
     _lib = lib

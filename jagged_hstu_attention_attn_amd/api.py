@@ -135,7 +135,8 @@ class JaggedAttnCall:
     def __init__(self, q, k, v, u, offsets, *, timestamps=None, num_targets=None,
                  contextual_len=0, max_attn_len=0, alpha, n_scale, pos_table=None,
                  time_table=None, eps=1e-5, epilogue="ln_u", out=None,
-                 candidates_only: bool = False, pos_clamp: bool = False):
+                 candidates_only: bool = False, pos_clamp: bool = False,
+                 save_o: bool = False):
         if not q.is_cuda:
             raise ValueError("tensors must be on a GPU")
         _check_aux(offsets, timestamps, num_targets, pos_table, time_table, q.device)
@@ -154,6 +155,11 @@ class JaggedAttnCall:
                               pos_clamp=pos_clamp)
         self.workspace = torch.empty(workspace_bytes(self.desc), dtype=torch.uint8,
                                      device=q.device)
+        # save_o: the call also keeps o / n_scale before the gate (training)
+        self.o_raw = (torch.empty((q.shape[0], q.shape[1], v.shape[2]), dtype=q.dtype,
+                                  device=q.device) if save_o else None)
+        if save_o and candidates_only:
+            raise ValueError("save_o is for full forwards")
 
     def plan(self) -> None:
         plan(self.desc, self.offsets, self.num_targets, self.contextual_len, self.max_attn_len,
@@ -166,6 +172,14 @@ class JaggedAttnCall:
         return self.out
 
     def __call__(self) -> torch.Tensor:
+        if self.o_raw is not None:
+            _lib.check(_lib.load().hstu_jagged_attn_fwd_train(
+                ctypes.byref(self.desc), _ptr(self.q), _ptr(self.k), _ptr(self.v),
+                _ptr(self.u), _ptr(self.offsets), _ptr(self.timestamps), _ptr(self.num_targets),
+                self.contextual_len, self.max_attn_len, self.alpha, self.n_scale,
+                _ptr(self.pos_table), _ptr(self.time_table), _ptr(self.out), _ptr(self.o_raw),
+                _ptr(self.workspace), int(self.workspace.numel()), _stream(self.q.device)))
+            return self.out
         _run_like("hstu_jagged_attn_fwd_candidates" if self.candidates_only
                   else "hstu_jagged_attn_fwd", self.desc, self.q, self.k, self.v, self.u,
                   self.offsets, self.timestamps, self.num_targets, self.contextual_len,
@@ -225,7 +239,12 @@ class JaggedAttnBwdCall:
         self.dpos = None if pos_table is None else torch.empty_like(pos_table)
         self.dtime = None if time_table is None else torch.empty_like(time_table)
 
-    def __call__(self, dout):
+    def __call__(self, dout, o_saved=None):
+        """o_saved: the raw aggregation a training forward kept (see
+        JaggedAttnCall(save_o=True)), or None to recompute it."""
+        if o_saved is not None and (o_saved.shape != dout.shape or o_saved.dtype != dout.dtype
+                                    or not o_saved.is_contiguous()):
+            raise ValueError("o_saved must be a contiguous tensor shaped and typed like dout")
         if dout.shape != (self.q.shape[0], self.q.shape[1], self.v.shape[2]):
             raise ValueError(f"dout has shape {tuple(dout.shape)}")
         if dout.dtype != self.q.dtype:
@@ -236,7 +255,7 @@ class JaggedAttnBwdCall:
             ctypes.byref(self.desc), _ptr(self.q), _ptr(self.k), _ptr(self.v), _ptr(self.u),
             _ptr(self.offsets), _ptr(self.timestamps), _ptr(self.num_targets),
             self.contextual_len, self.max_attn_len, self.alpha, self.n_scale,
-            _ptr(self.pos_table), _ptr(self.time_table), _ptr(dout), _ptr(self.dq),
+            _ptr(self.pos_table), _ptr(self.time_table), _ptr(dout), _ptr(o_saved), _ptr(self.dq),
             _ptr(self.dk), _ptr(self.dv), _ptr(self.du), _ptr(self.dpos), _ptr(self.dtime),
             _ptr(self.workspace), int(self.workspace.numel()), _stream(self.q.device)))
         return self.dq, self.dk, self.dv, self.du, self.dpos, self.dtime
@@ -245,15 +264,16 @@ class JaggedAttnBwdCall:
 def jagged_attn_bwd(q, k, v, u, offsets, dout, *, timestamps=None, num_targets=None,
                     contextual_len: int = 0, max_attn_len: int = 0, alpha: float,
                     n_scale: float, pos_table=None, time_table=None, eps: float = 1e-5,
-                    epilogue: str = "ln_u"):
+                    epilogue: str = "ln_u", o_saved=None):
     """Gradients (dq, dk, dv, du, dpos, dtime) of sum(dout * forward(...)),
-    computed on the GPU on the current stream."""
+    computed on the GPU on the current stream (o_saved: see
+    JaggedAttnBwdCall.__call__)."""
     call = JaggedAttnBwdCall(q, k, v, u, offsets, timestamps=timestamps,
                              num_targets=num_targets, contextual_len=contextual_len,
                              max_attn_len=max_attn_len, alpha=alpha, n_scale=n_scale,
                              pos_table=pos_table, time_table=time_table, eps=eps,
                              epilogue=epilogue)
-    return call(dout)
+    return call(dout, o_saved)
 
 
 def valid_pairs(offsets, num_targets=None, contextual_len: int = 0, max_attn_len: int = 0) -> int:

@@ -914,6 +914,30 @@ hstu_attn_fwd_kernel(AttnArgs a) {
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[db][r] *= osc;
+  // the aggregation before the gate, kept for the backward (training)
+  if (a.out_raw != nullptr && row_valid) {
+    char* rrow = reinterpret_cast<char*>(a.out_raw) +
+                 ((int64_t)(seq0 + i) * a.ld_raw + (int64_t)h * DV) * ES;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int d0 = 32 * db + 8 * gq + 4 * hh;
+        if (d0 < DV) {
+          if constexpr (BF) {
+            bf16x4 o;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = (__bf16)acc[db][4 * gq + e];
+            *reinterpret_cast<bf16x4*>(rrow + 2 * d0) = o;
+          } else {
+            floatx4 o;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = acc[db][4 * gq + e];
+            *reinterpret_cast<floatx4*>(rrow + 4 * d0) = o;
+          }
+        }
+      }
+  }
   if (ln) {
     float sum = 0.0f;
 #pragma unroll

@@ -240,12 +240,12 @@ int hstu_jagged_attn_plan_candidates(const hstu_attn_desc* desc, const int32_t* 
                    workspace_bytes, stream, true);
 }
 
-int hstu_jagged_attn_run(const hstu_attn_desc* desc, const void* q, const void* k,
-                         const void* v, const void* u, const int32_t* offsets,
-                         const int64_t* timestamps, const int32_t* num_targets,
-                         int32_t contextual_len, int32_t max_attn_len, float alpha,
-                         float n_scale, const float* pos_table, const float* time_table,
-                         void* out, void* workspace, size_t workspace_bytes, void* stream) {
+static int run_impl(const hstu_attn_desc* desc, const void* q, const void* k, const void* v,
+                    const void* u, const int32_t* offsets, const int64_t* timestamps,
+                    const int32_t* num_targets, int32_t contextual_len, int32_t max_attn_len,
+                    float alpha, float n_scale, const float* pos_table,
+                    const float* time_table, void* out, void* o_raw, void* workspace,
+                    size_t workspace_bytes, void* stream) {
   int rc = check_desc(desc);
   if (rc != HSTU_OK) return rc;
   rc = check_plan_args(desc, offsets, contextual_len, max_attn_len, workspace, workspace_bytes);
@@ -289,6 +289,8 @@ int hstu_jagged_attn_run(const hstu_attn_desc* desc, const void* q, const void* 
   a.time_len = desc->time_table_len;
   a.epilogue = ln_all ? HSTU_EPILOGUE_NONE : desc->epilogue;
   a.pos_clamp = desc->pos_clamp;
+  a.out_raw = o_raw;
+  a.ld_raw = (int64_t)desc->num_heads * desc->d_v;
   a.alpha = alpha;
   a.out_scale = (float)(0.69314718055994530942 / (double)n_scale);
   a.ln_eps = desc->ln_eps;
@@ -315,6 +317,41 @@ int hstu_jagged_attn_run(const hstu_attn_desc* desc, const void* q, const void* 
       return fail(HSTU_ERR_HIP, "LayerNorm launch failed: %s", hipGetErrorString(e2));
   }
   return HSTU_OK;
+}
+
+int hstu_jagged_attn_run(const hstu_attn_desc* desc, const void* q, const void* k,
+                         const void* v, const void* u, const int32_t* offsets,
+                         const int64_t* timestamps, const int32_t* num_targets,
+                         int32_t contextual_len, int32_t max_attn_len, float alpha,
+                         float n_scale, const float* pos_table, const float* time_table,
+                         void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  return run_impl(desc, q, k, v, u, offsets, timestamps, num_targets, contextual_len,
+                  max_attn_len, alpha, n_scale, pos_table, time_table, out, nullptr, workspace,
+                  workspace_bytes, stream);
+}
+
+int hstu_jagged_attn_fwd_train(const hstu_attn_desc* desc, const void* q, const void* k,
+                               const void* v, const void* u, const int32_t* offsets,
+                               const int64_t* timestamps, const int32_t* num_targets,
+                               int32_t contextual_len, int32_t max_attn_len, float alpha,
+                               float n_scale, const float* pos_table, const float* time_table,
+                               void* out, void* o_raw, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  int rc = check_desc(desc);
+  if (rc != HSTU_OK) return rc;
+  rc = check_plan_args(desc, offsets, contextual_len, max_attn_len, workspace, workspace_bytes);
+  if (rc != HSTU_OK) return rc;
+  if (desc->num_seqs == 0 || desc->total_tokens == 0) return HSTU_OK;
+  rc = check_run_args(desc, q, k, v, u, timestamps, alpha, n_scale, pos_table, time_table, out);
+  if (rc != HSTU_OK) return rc;
+  if (!o_raw) return fail(HSTU_ERR_INVALID_ARG, "o_raw is NULL");
+  if (!aligned16(o_raw)) return fail(HSTU_ERR_INVALID_ARG, "o_raw is not 16-byte aligned");
+  rc = hstu_jagged_attn_plan(desc, offsets, num_targets, contextual_len, max_attn_len, workspace,
+                             workspace_bytes, stream);
+  if (rc != HSTU_OK) return rc;
+  return run_impl(desc, q, k, v, u, offsets, timestamps, num_targets, contextual_len,
+                  max_attn_len, alpha, n_scale, pos_table, time_table, out, o_raw, workspace,
+                  workspace_bytes, stream);
 }
 
 int hstu_jagged_attn_fwd(const hstu_attn_desc* desc, const void* q, const void* k,
@@ -625,8 +662,8 @@ int hstu_jagged_attn_bwd(const hstu_attn_desc* desc, const void* q, const void* 
                          const int64_t* timestamps, const int32_t* num_targets,
                          int32_t contextual_len, int32_t max_attn_len, float alpha,
                          float n_scale, const float* pos_table, const float* time_table,
-                         const void* dout, void* dq, void* dk, void* dv, void* du,
-                         float* dpos_table, float* dtime_table, void* workspace,
+                         const void* dout, const void* o_saved, void* dq, void* dk, void* dv,
+                         void* du, float* dpos_table, float* dtime_table, void* workspace,
                          size_t workspace_bytes, void* stream) {
   int rc = check_desc(desc);
   if (rc != HSTU_OK) return rc;
@@ -649,6 +686,8 @@ int hstu_jagged_attn_bwd(const hstu_attn_desc* desc, const void* q, const void* 
     return fail(HSTU_ERR_INVALID_ARG, "dpos_table and pos_table_len disagree");
   if ((dtime_table == nullptr) != (desc->time_table_len == 0))
     return fail(HSTU_ERR_INVALID_ARG, "dtime_table and time_table_len disagree");
+  if (o_saved && !aligned16(o_saved))
+    return fail(HSTU_ERR_INVALID_ARG, "o_saved is not 16-byte aligned");
   const bool empty = desc->num_seqs == 0 || desc->total_tokens == 0;
   if (!empty) {
     rc = check_run_args(desc, q, k, v, u, timestamps, alpha, n_scale, pos_table, time_table,
@@ -696,15 +735,20 @@ int hstu_jagged_attn_bwd(const hstu_attn_desc* desc, const void* q, const void* 
   const void* d_o = dout;
   int64_t ld_do = desc->ld_out;
   if (bl.gate) {
-    // the gate needs the raw aggregation o: the forward again with epilogue none
+    // the gate needs the raw aggregation o: the one the training forward kept,
+    // or the forward again with epilogue none
     hstu_attn_desc fd = *desc;
     fd.epilogue = HSTU_EPILOGUE_NONE;
     fd.ld_out = H * desc->d_v;
-    void* o = ws + bl.o_off;
-    rc = hstu_jagged_attn_fwd(&fd, q, k, v, nullptr, offsets, timestamps, num_targets,
-                              contextual_len, max_attn_len, alpha, n_scale, pos_table, time_table,
-                              o, ws, bl.o_off, stream);
-    if (rc != HSTU_OK) return rc;
+    const void* o = o_saved;
+    if (!o) {
+      void* orec = ws + bl.o_off;
+      rc = hstu_jagged_attn_fwd(&fd, q, k, v, nullptr, offsets, timestamps, num_targets,
+                                contextual_len, max_attn_len, alpha, n_scale, pos_table,
+                                time_table, orec, ws, bl.o_off, stream);
+      if (rc != HSTU_OK) return rc;
+      o = orec;
+    }
     hstu::GateBwdArgs ga;
     ga.o = o;
     ga.u = u;

@@ -202,6 +202,8 @@ struct AttnArgs {
   int32_t time_len;
   int32_t epilogue;   // 0 = LayerNorm * U, 1 = none
   int32_t pos_clamp;  // position bias of |p_i - p_j|, p = min(position, n_h)
+  void* out_raw;      // optional: o / n_scale before the gate, [N, H, d_v]
+  int64_t ld_raw;
   float alpha;
   float out_scale;    // ln(2) / n_scale: SiLU values are formed in log2 units
   float ln_eps;

@@ -143,6 +143,19 @@ def test_epilogue_none_does_not_need_u(lib):
     assert rc in (_lib.HSTU_OK, _lib.HSTU_ERR_HIP)   # passes validation
 
 
+def test_fwd_train_needs_o_raw(lib):
+    d = _desc()
+    ws = lib.hstu_jagged_attn_workspace_bytes(ctypes.byref(d))
+    vp = ctypes.c_void_p
+    args = [ctypes.byref(d), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), None, None, 0, 0,
+            0.1, 10.0, None, None, vp(FAKE)]
+    assert lib.hstu_jagged_attn_fwd_train(*args, None, vp(FAKE), ws, None) == \
+        _lib.HSTU_ERR_INVALID_ARG
+    assert "o_raw" in _lib.last_error()
+    assert lib.hstu_jagged_attn_fwd_train(*args, vp(FAKE + 4), vp(FAKE), ws, None) == \
+        _lib.HSTU_ERR_INVALID_ARG
+
+
 def test_valid_call_without_gpu_reports_hip_error(lib):
     import torch
     if torch.cuda.is_available():
@@ -163,14 +176,15 @@ def test_supported_set(lib):
 
 
 def _bwd(lib, d, **kw):
-    args = dict(q=FAKE, k=FAKE, v=FAKE, u=FAKE, offsets=FAKE, dout=FAKE, dq=FAKE, dk=FAKE,
-                dv=FAKE, du=FAKE, ws=FAKE)
+    args = dict(q=FAKE, k=FAKE, v=FAKE, u=FAKE, offsets=FAKE, dout=FAKE, o_saved=None, dq=FAKE,
+                dk=FAKE, dv=FAKE, du=FAKE, ws=FAKE)
     args.update(kw)
     vp = lambda x: None if x is None else ctypes.c_void_p(x)
     ws_bytes = lib.hstu_jagged_attn_bwd_workspace_bytes(ctypes.byref(d)) or 1 << 20
     return lib.hstu_jagged_attn_bwd(
         ctypes.byref(d), vp(args["q"]), vp(args["k"]), vp(args["v"]), vp(args["u"]),
         vp(args["offsets"]), None, None, 0, 0, 0.1, 10.0, None, None, vp(args["dout"]),
+        vp(args["o_saved"]),
         vp(args["dq"]), vp(args["dk"]), vp(args["dv"]), vp(args["du"]), None, None,
         vp(args["ws"]), ws_bytes, None)
 
@@ -192,8 +206,11 @@ def test_backward_validation(lib):
     d = _desc(pos_table_len=16)
     assert lib.hstu_jagged_attn_bwd(
         ctypes.byref(d), *[ctypes.c_void_p(FAKE)] * 5, None, None, 0, 0, 0.1, 10.0,
-        ctypes.c_void_p(FAKE), None, *[ctypes.c_void_p(FAKE)] * 5, None, None,
+        ctypes.c_void_p(FAKE), None, ctypes.c_void_p(FAKE), None,
+        *[ctypes.c_void_p(FAKE)] * 4, None, None,
         ctypes.c_void_p(FAKE), 1 << 30, None) == _lib.HSTU_ERR_INVALID_ARG
+    # o_saved must be aligned
+    assert _bwd(lib, _desc(), o_saved=FAKE + 8) == _lib.HSTU_ERR_INVALID_ARG
 
 
 # The product's host pair count (used for throughput accounting) against the

@@ -196,3 +196,40 @@ def test_bwd_longtail_reduced_with_tables():
     inp = make_inputs("longtail", num_seqs=6)
     dout = make_dout(inp, 14)
     assert_grads(gpu_backward(inp, dout), oracle.backward(inp, dout), "bf16")
+
+
+# ---------------------------------------------------------------------------
+# Training forward keeps o / n_scale; the backward can take it instead of
+# recomputing it.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64)])
+@pytest.mark.parametrize("epilogue", ["ln_u", "ln_all_u"])
+def test_training_forward_and_saved_o(dtype, d, epilogue):
+    from jagged_hstu_attention_attn_amd.api import JaggedAttnCall, jagged_attn_fwd
+    inp = _small(dtype, d, W=60)
+    dev = to_device(inp, DEV)
+    kw = call_kwargs(inp, dev)
+    call = JaggedAttnCall(dev["q"], dev["k"], dev["v"], dev["u"], dev["offsets"],
+                          epilogue=epilogue, save_o=True, **kw)
+    out = call().clone()
+    plain = jagged_attn_fwd(dev["q"], dev["k"], dev["v"], dev["u"], dev["offsets"],
+                            epilogue=epilogue, **kw)
+    raw = jagged_attn_fwd(dev["q"], dev["k"], dev["v"], dev["u"], dev["offsets"],
+                          epilogue="none", **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(out, plain)           # the gate's output is unchanged
+    assert torch.equal(call.o_raw, raw)      # o / n_scale as the forward without gate
+    dout = make_dout(inp, 21)
+    dO = torch.from_numpy(dout).to(DEV, _TORCH[dtype])
+    g_re = jagged_attn_bwd(dev["q"], dev["k"], dev["v"], dev["u"], dev["offsets"], dO,
+                           epilogue=epilogue, **kw)
+    g_re = [None if t is None else t.clone() for t in g_re]
+    g_sv = jagged_attn_bwd(dev["q"], dev["k"], dev["v"], dev["u"], dev["offsets"], dO,
+                           epilogue=epilogue, o_saved=call.o_raw, **kw)
+    torch.cuda.synchronize()
+    for a, b, name in zip(g_re, g_sv, ("dq", "dk", "dv", "du")):
+        assert torch.equal(a, b), name
+    ref = oracle.backward(inp, dout, epilogue=_EP[epilogue])
+    to = lambda t: None if t is None else t.float().cpu().numpy().astype(np.float64)
+    assert_grads(dict(zip(("dq", "dk", "dv", "du", "dpos", "dtime"), (to(t) for t in g_sv))),
+                 ref, dtype, epilogue)
