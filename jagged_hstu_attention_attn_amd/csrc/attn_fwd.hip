@@ -67,6 +67,7 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kMaskedX = -1.0e30f;   // SiLU argument of an illegal pair
 constexpr int64_t kT32Range = int64_t(1) << 30;  // |t - base| below this: 32-bit path
 constexpr int kStages = 4;                       // LDS buffers of the key/value pipeline
 constexpr int kRows = kBM / kWaves;              // query rows per wave
@@ -653,10 +654,9 @@ hstu_attn_fwd_kernel(AttnArgs a) {
       for (int r = 0; r < 16; ++r) x[r] = s[r] * am;
     }
 
-    // ---- SiLU, then zero the illegal pairs ----
-    float av[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) av[r] = silu2(x[r]);
+    // ---- illegal pairs: an argument whose SiLU is exactly -0 (2^1e30 is
+    // +inf, its reciprocal 0); selecting before the SiLU keeps the SiLU and
+    // the aggregation MFMAs in one straight-line stretch ----
     if (!is_full(kt)) {
       const RowBounds rb = row_valid ? row_bounds(geo, i) : RowBounds{kEmptyLo, 0, -1};
       const int jl = jb + 4 * hh - rb.lo, js = jb + 4 * hh - rb.self_j;
@@ -664,9 +664,12 @@ hstu_attn_fwd_kernel(AttnArgs a) {
       for (int r = 0; r < 16; ++r) {
         const int kk = 8 * (r >> 2) + (r & 3);
         const bool ok = (uint32_t)(jl + kk) <= (uint32_t)rb.span || js + kk == 0;
-        av[r] = ok ? av[r] : 0.0f;
+        x[r] = ok ? x[r] : kMaskedX;
       }
     }
+    float av[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) av[r] = silu2(x[r]);
 
     // ---- O^T[d][i] += sum_j V[j][d] * A[i][j] ----
     if constexpr (BF) {
