@@ -179,6 +179,24 @@ int hstu_jagged_attn_run(const hstu_attn_desc* desc,
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * hstu_jagged_attn_run with the attention kernel's own start and end times
+ * taken into two caller-owned HIP events (hipEvent_t, created with timing
+ * enabled, passed as void*; either may be NULL): the launch goes through
+ * hipExtLaunchKernelGGL, whose events carry the kernel's start and stop
+ * timestamps rather than those of markers around it.  A measurement aid:
+ * the work and the result are those of hstu_jagged_attn_run.  With the
+ * all-heads LayerNorm epilogue the events cover the attention kernel only.
+ */
+int hstu_jagged_attn_run_timed(const hstu_attn_desc* desc,
+                               const void* q, const void* k, const void* v, const void* u,
+                               const int32_t* offsets, const int64_t* timestamps,
+                               const int32_t* num_targets, int32_t contextual_len,
+                               int32_t max_attn_len, float alpha, float n_scale,
+                               const float* pos_table, const float* time_table, void* out,
+                               void* workspace, size_t workspace_bytes, void* stream,
+                               void* start_event, void* stop_event);
+
+/*
  * Candidate rows only (candidate micro-batching with history reuse, "Scaling
  * HSTU: ragged execution, candidate amortization and content features",
  * section "Many candidates make reuse valuable").  The candidates of a

@@ -30,6 +30,7 @@ EXPORTS = (
     "hstu_jagged_attn_fwd",
     "hstu_jagged_attn_plan",
     "hstu_jagged_attn_run",
+    "hstu_jagged_attn_run_timed",
     "hstu_jagged_attn_plan_candidates",
     "hstu_jagged_attn_fwd_candidates",
     "hstu_layer_workspace_bytes",
@@ -109,6 +110,8 @@ def load() -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
         fn.argtypes = run_args
+    lib.hstu_jagged_attn_run_timed.restype = ctypes.c_int
+    lib.hstu_jagged_attn_run_timed.argtypes = run_args + [P, P]
     for name in ("hstu_jagged_attn_plan", "hstu_jagged_attn_plan_candidates"):
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int

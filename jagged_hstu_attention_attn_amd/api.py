@@ -113,6 +113,19 @@ def run(desc, q, k, v, u, offsets, timestamps, num_targets, contextual_len, max_
               workspace)
 
 
+def run_timed(desc, q, k, v, u, offsets, timestamps, num_targets, contextual_len,
+              max_attn_len, alpha, n_scale, pos_table, time_table, out, workspace,
+              start: torch.cuda.Event, stop: torch.cuda.Event) -> None:
+    """`run`, with the attention kernel's own start and end times taken into
+    two timing events (each must have been recorded once, so that it exists)."""
+    _lib.check(_lib.load().hstu_jagged_attn_run_timed(
+        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(u), _ptr(offsets),
+        _ptr(timestamps), _ptr(num_targets), int(contextual_len), int(max_attn_len),
+        float(alpha), float(n_scale), _ptr(pos_table), _ptr(time_table), _ptr(out),
+        _ptr(workspace), int(workspace.numel()), _stream(q.device),
+        ctypes.c_void_p(start.cuda_event), ctypes.c_void_p(stop.cuda_event)))
+
+
 def _check_aux(offsets, timestamps, num_targets, pos_table, time_table, device):
     if offsets.dtype != torch.int32 or offsets.dim() != 1 or not offsets.is_contiguous():
         raise TypeError("offsets must be a contiguous int32 vector")
@@ -169,6 +182,13 @@ class JaggedAttnCall:
         run(self.desc, self.q, self.k, self.v, self.u, self.offsets, self.timestamps,
             self.num_targets, self.contextual_len, self.max_attn_len, self.alpha, self.n_scale,
             self.pos_table, self.time_table, self.out, self.workspace)
+        return self.out
+
+    def run_timed(self, start: torch.cuda.Event, stop: torch.cuda.Event) -> torch.Tensor:
+        run_timed(self.desc, self.q, self.k, self.v, self.u, self.offsets, self.timestamps,
+                  self.num_targets, self.contextual_len, self.max_attn_len, self.alpha,
+                  self.n_scale, self.pos_table, self.time_table, self.out, self.workspace,
+                  start, stop)
         return self.out
 
     def __call__(self) -> torch.Tensor:

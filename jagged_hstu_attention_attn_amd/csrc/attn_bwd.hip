@@ -701,7 +701,6 @@ hstu_bwd_dq_kernel(BwdArgs a) {
   }
   PP pp;
   pp.init(st, trev, tful, wave, lane, a.pos_len, 1.0f / am, a.ld_k, a.ld_v);
-  const int dbase = (kBM - 1) - 32 * wave - l32 + 4 * hh;
   const float out_scale = a.alpha * a.inv_scale;
 
   const int n_items = a.hdr[0] * H;
@@ -918,7 +917,6 @@ hstu_bwd_dkv_kernel(BwdArgs a) {
     for (int e = tid; e < P; e += kThreads) hpos[e] = 0.0f;
   PP pp;
   pp.init(st, trev, tful, wave, lane, P, 1.0f / am, a.ld_q, a.ld_do);
-  const int dbase = (kBM - 1) - 32 * wave - l32 + 4 * hh;
   const float k_scale = a.alpha * a.inv_scale, v_scale = a.inv_scale;
 
   const int n_items = a.hdr[0] * H;

@@ -54,6 +54,8 @@
 // "Similar shape, different aggregation").
 #include <type_traits>
 
+#include <hip/hip_ext.h>
+
 #include "hstu_device.hpp"
 
 namespace hstu {
@@ -1062,9 +1064,14 @@ hstu_attn_fwd_kernel(AttnArgs a) {
 }
 
 template <typename T, int DQK, int DV, int POSM, bool TIME>
-static hipError_t launch_one(const AttnArgs& a, int n_wg, hipStream_t stream) {
+static hipError_t launch_one(const AttnArgs& a, int n_wg, hipStream_t stream, hipEvent_t start,
+                             hipEvent_t stop) {
   auto kern = hstu_attn_fwd_kernel<T, DQK, DV, POSM, TIME>;
-  hipLaunchKernelGGL(kern, dim3((unsigned)n_wg), dim3(kThreads), 0, stream, a);
+  if (start || stop)
+    hipExtLaunchKernelGGL(kern, dim3((unsigned)n_wg), dim3(kThreads), 0, stream, start, stop, 0,
+                          a);
+  else
+    hipLaunchKernelGGL(kern, dim3((unsigned)n_wg), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -1079,14 +1086,15 @@ static int blocks_per_cu() {
 }
 
 template <typename T, int DQK, int DV>
-static hipError_t launch_bias(const AttnArgs& a, int n_wg, hipStream_t stream) {
+static hipError_t launch_bias(const AttnArgs& a, int n_wg, hipStream_t stream, hipEvent_t t0,
+                              hipEvent_t t1) {
   const bool pos = a.pos_len > 0, tim = a.time_len > 0, cl = a.pos_clamp != 0;
-  if (pos && cl && tim) return launch_one<T, DQK, DV, 2, true>(a, n_wg, stream);
-  if (pos && cl) return launch_one<T, DQK, DV, 2, false>(a, n_wg, stream);
-  if (pos && tim) return launch_one<T, DQK, DV, 1, true>(a, n_wg, stream);
-  if (pos) return launch_one<T, DQK, DV, 1, false>(a, n_wg, stream);
-  if (tim) return launch_one<T, DQK, DV, 0, true>(a, n_wg, stream);
-  return launch_one<T, DQK, DV, 0, false>(a, n_wg, stream);
+  if (pos && cl && tim) return launch_one<T, DQK, DV, 2, true>(a, n_wg, stream, t0, t1);
+  if (pos && cl) return launch_one<T, DQK, DV, 2, false>(a, n_wg, stream, t0, t1);
+  if (pos && tim) return launch_one<T, DQK, DV, 1, true>(a, n_wg, stream, t0, t1);
+  if (pos) return launch_one<T, DQK, DV, 1, false>(a, n_wg, stream, t0, t1);
+  if (tim) return launch_one<T, DQK, DV, 0, true>(a, n_wg, stream, t0, t1);
+  return launch_one<T, DQK, DV, 0, false>(a, n_wg, stream, t0, t1);
 }
 
 template <typename T, int DQK, int DV>
@@ -1130,16 +1138,16 @@ bool attn_supported(int dtype, int d_qk, int d_v) {
 }
 
 hipError_t launch_attn(const AttnArgs& a, int dtype, int d_qk, int d_v, int n_wg,
-                       hipStream_t stream) {
+                       hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
   if (dtype == 1) {
-    if (d_qk == 128 && d_v == 128) return launch_bias<__bf16, 128, 128>(a, n_wg, stream);
-    if (d_qk == 64 && d_v == 64) return launch_bias<__bf16, 64, 64>(a, n_wg, stream);
-    if (d_qk == 64 && d_v == 128) return launch_bias<__bf16, 64, 128>(a, n_wg, stream);
-    if (d_qk == 128 && d_v == 64) return launch_bias<__bf16, 128, 64>(a, n_wg, stream);
+    if (d_qk == 128 && d_v == 128) return launch_bias<__bf16, 128, 128>(a, n_wg, stream, t0, t1);
+    if (d_qk == 64 && d_v == 64) return launch_bias<__bf16, 64, 64>(a, n_wg, stream, t0, t1);
+    if (d_qk == 64 && d_v == 128) return launch_bias<__bf16, 64, 128>(a, n_wg, stream, t0, t1);
+    if (d_qk == 128 && d_v == 64) return launch_bias<__bf16, 128, 64>(a, n_wg, stream, t0, t1);
   } else if (dtype == 0) {
-    if (d_qk == 128 && d_v == 128) return launch_bias<float, 128, 128>(a, n_wg, stream);
-    if (d_qk == 64 && d_v == 64) return launch_bias<float, 64, 64>(a, n_wg, stream);
-    if (d_qk == 8 && d_v == 8) return launch_bias<float, 8, 8>(a, n_wg, stream);
+    if (d_qk == 128 && d_v == 128) return launch_bias<float, 128, 128>(a, n_wg, stream, t0, t1);
+    if (d_qk == 64 && d_v == 64) return launch_bias<float, 64, 64>(a, n_wg, stream, t0, t1);
+    if (d_qk == 8 && d_v == 8) return launch_bias<float, 8, 8>(a, n_wg, stream, t0, t1);
   }
   return hipErrorInvalidValue;
 }

@@ -245,7 +245,8 @@ static int run_impl(const hstu_attn_desc* desc, const void* q, const void* k, co
                     const int32_t* num_targets, int32_t contextual_len, int32_t max_attn_len,
                     float alpha, float n_scale, const float* pos_table,
                     const float* time_table, void* out, void* o_raw, void* workspace,
-                    size_t workspace_bytes, void* stream) {
+                    size_t workspace_bytes, void* stream, void* t_start = nullptr,
+                    void* t_stop = nullptr) {
   int rc = check_desc(desc);
   if (rc != HSTU_OK) return rc;
   rc = check_plan_args(desc, offsets, contextual_len, max_attn_len, workspace, workspace_bytes);
@@ -295,7 +296,9 @@ static int run_impl(const hstu_attn_desc* desc, const void* q, const void* k, co
   a.out_scale = (float)(0.69314718055994530942 / (double)n_scale);
   a.ln_eps = desc->ln_eps;
   const hipError_t e = hstu::launch_attn(a, desc->dtype, desc->d_qk, desc->d_v, n_wg,
-                                         static_cast<hipStream_t>(stream));
+                                         static_cast<hipStream_t>(stream),
+                                         static_cast<hipEvent_t>(t_start),
+                                         static_cast<hipEvent_t>(t_stop));
   if (e != hipSuccess)
     return fail(HSTU_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
   if (ln_all) {
@@ -328,6 +331,18 @@ int hstu_jagged_attn_run(const hstu_attn_desc* desc, const void* q, const void* 
   return run_impl(desc, q, k, v, u, offsets, timestamps, num_targets, contextual_len,
                   max_attn_len, alpha, n_scale, pos_table, time_table, out, nullptr, workspace,
                   workspace_bytes, stream);
+}
+
+int hstu_jagged_attn_run_timed(const hstu_attn_desc* desc, const void* q, const void* k,
+                               const void* v, const void* u, const int32_t* offsets,
+                               const int64_t* timestamps, const int32_t* num_targets,
+                               int32_t contextual_len, int32_t max_attn_len, float alpha,
+                               float n_scale, const float* pos_table, const float* time_table,
+                               void* out, void* workspace, size_t workspace_bytes, void* stream,
+                               void* start_event, void* stop_event) {
+  return run_impl(desc, q, k, v, u, offsets, timestamps, num_targets, contextual_len,
+                  max_attn_len, alpha, n_scale, pos_table, time_table, out, nullptr, workspace,
+                  workspace_bytes, stream, start_event, stop_event);
 }
 
 int hstu_jagged_attn_fwd_train(const hstu_attn_desc* desc, const void* q, const void* k,

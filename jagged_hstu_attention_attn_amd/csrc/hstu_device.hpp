@@ -322,8 +322,10 @@ struct TabReduceArgs {
 
 // Launchers (defined in the .hip files).
 hipError_t launch_plan(const PlanArgs& a, bool compact, hipStream_t stream);
+// start / stop: when not null, events that take the kernel's own start and
+// end times (hipExtLaunchKernelGGL).
 hipError_t launch_attn(const AttnArgs& a, int dtype, int d_qk, int d_v, int n_wg,
-                       hipStream_t stream);
+                       hipStream_t stream, hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 // Workgroups of the persistent attention launch for this shape on the current
 // device (CUs x resident workgroups per CU), or a negative value on error.
 int attn_grid(int dtype, int d_qk, int d_v, int pos_len, int time_len, bool clamp);

@@ -274,6 +274,31 @@ def test_plan_reuse_across_runs():
     assert_close(o2, ora(inp2), "bf16")
 
 
+def test_run_timed_matches_run():
+    """The timed launch does the same work (bitwise the same output) and its
+    events bracket the attention kernel itself: a positive duration no longer
+    than that between markers recorded around the launch."""
+    inp = make_inputs("ranking", num_seqs=24)
+    dev = to_device(inp, DEV)
+    call = JaggedAttnCall(dev["q"], dev["k"], dev["v"], dev["u"], dev["offsets"],
+                          **call_kwargs(inp, dev))
+    call.plan()
+    ref = call.run().clone()
+    stream = torch.cuda.current_stream()
+    k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    m0, m1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    k0.record(stream)
+    k1.record(stream)
+    call.out.zero_()
+    m0.record(stream)
+    got = call.run_timed(k0, k1)
+    m1.record(stream)
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref)
+    kernel_ms, marker_ms = k0.elapsed_time(k1), m0.elapsed_time(m1)
+    assert 0.0 < kernel_ms <= marker_ms, (kernel_ms, marker_ms)
+
+
 def test_split_items_plan_reuse():
     """One long causal sequence: its last query tiles reach far more key tiles
     than a workgroup's share, so the scheduler splits them along the keys and
