@@ -365,11 +365,12 @@ def main() -> int:
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    steps_ev = [(ev(), ev()) for _ in range(args.steps)]        # around each step
+    parts_ev = [(ev(), ev(), ev()) for _ in range(args.steps)]  # around scheduler / launch
     # the attention kernel's own start / end times (hipExtLaunchKernelGGL);
     # an event exists once recorded
-    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    kev = [(ev(), ev()) for _ in range(args.steps)]
     for k0, k1 in kev:
         k0.record(stream)
         k1.record(stream)
@@ -379,27 +380,31 @@ def main() -> int:
     for s in range(args.steps):
         if flush is not None:
             flush.fill_(s & 0xFF)
-        e0, e1, e2 = evs[s]
+        e0, e1 = steps_ev[s]
         e0.record(stream)
         call.plan()
-        e1.record(stream)
         call.run()
-        e2.record(stream)
+        e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    # The same steps again, the attention launched with events at its own start
-    # and end (a launch that records them lengthens the step, so the step
-    # times above come from plain launches).
-    log(f"timing the attention kernel over {args.steps} more steps")
+    # The same steps again for the parts: markers around the scheduler and the
+    # attention launch, the attention launched with events at its own start
+    # and end (markers inside a step and a launch that records events both
+    # lengthen it, so the step times above come from plain steps).
+    log(f"timing the scheduler and the attention kernel over {args.steps} more steps")
     for s in range(args.steps):
         if flush is not None:
             flush.fill_(s & 0xFF)
+        m0, m1, m2 = parts_ev[s]
+        m0.record(stream)
         call.plan()
+        m1.record(stream)
         call.run_timed(*kev[s])
+        m2.record(stream)
     torch.cuda.synchronize()
-    step_ms = [e0.elapsed_time(e2) for e0, _, e2 in evs]
-    plan_ms = [e0.elapsed_time(e1) for e0, e1, _ in evs]
-    launch_ms = [e1.elapsed_time(e2) for _, e1, e2 in evs]
+    step_ms = [e0.elapsed_time(e1) for e0, e1 in steps_ev]
+    plan_ms = [m0.elapsed_time(m1) for m0, m1, _ in parts_ev]
+    launch_ms = [m1.elapsed_time(m2) for _, m1, m2 in parts_ev]
     attn_ms = [k0.elapsed_time(k1) for k0, k1 in kev]
     ms = sum(step_ms) / len(step_ms)
     attn = sum(attn_ms) / len(attn_ms)
