@@ -119,6 +119,42 @@ def test_bad_arguments(lib, kw, code):
     assert _lib.last_error() != ""
 
 
+def _run(lib, d, fn="hstu_jagged_attn_run", ws_bytes=None, **kw):
+    """hstu_jagged_attn_run, or the timed run (with two NULL events)."""
+    args = dict(q=FAKE, k=FAKE, v=FAKE, u=FAKE, offsets=FAKE, timestamps=None, num_targets=None,
+                contextual_len=0, max_attn_len=0, alpha=0.1, n_scale=10.0, pos_table=None,
+                time_table=None, out=FAKE, ws=FAKE)
+    args.update(kw)
+    if ws_bytes is None:
+        ws_bytes = lib.hstu_jagged_attn_workspace_bytes(ctypes.byref(d)) or 1 << 20
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    call = [ctypes.byref(d), vp(args["q"]), vp(args["k"]), vp(args["v"]), vp(args["u"]),
+            vp(args["offsets"]), vp(args["timestamps"]), vp(args["num_targets"]),
+            args["contextual_len"], args["max_attn_len"], args["alpha"], args["n_scale"],
+            vp(args["pos_table"]), vp(args["time_table"]), vp(args["out"]), vp(args["ws"]),
+            ws_bytes, None]
+    if fn == "hstu_jagged_attn_run_timed":
+        call += [None, None]
+    return getattr(lib, fn)(*call)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), _lib.HSTU_ERR_INVALID_ARG),
+    (dict(v=FAKE + 8), _lib.HSTU_ERR_INVALID_ARG),
+    (dict(n_scale=0.0), _lib.HSTU_ERR_INVALID_ARG),
+    (dict(ws=None), _lib.HSTU_ERR_WORKSPACE),
+])
+def test_timed_run_validates_like_run(lib, kw, code):
+    """The timed run is the run with two events: it rejects the same calls
+    with the same status, before touching the device."""
+    assert _run(lib, _desc(), **kw) == code
+    assert _run(lib, _desc(), fn="hstu_jagged_attn_run_timed", **kw) == code
+    assert _run(lib, _desc(ln_eps=0.0), fn="hstu_jagged_attn_run_timed") == \
+        _lib.HSTU_ERR_INVALID_ARG
+    assert _run(lib, _desc(num_seqs=0, total_tokens=0), fn="hstu_jagged_attn_run_timed",
+                q=None, k=None, v=None, u=None, out=None, offsets=None) == _lib.HSTU_OK
+
+
 def test_time_table_needs_timestamps(lib):
     d = _desc(time_table_len=64)
     assert _fwd(lib, d, time_table=FAKE) == _lib.HSTU_ERR_INVALID_ARG
