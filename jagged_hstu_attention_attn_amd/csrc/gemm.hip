@@ -36,6 +36,7 @@ typedef float g_floatx16 __attribute__((ext_vector_type(16)));
 constexpr int kGB = 128;    // block of C: rows (tokens) and columns (features)
 constexpr int kGK = 64;     // K per stage
 constexpr int kGThreads = 256;
+constexpr int kGXcds = 8;   // XCDs of the MI355X
 
 __device__ inline uint32_t g_lds_off(const void* p) { return (uint32_t)(uintptr_t)p; }
 template <typename V>
@@ -82,7 +83,16 @@ __global__ __launch_bounds__(kGThreads) void hstu_gemm_bt_kernel(GemmArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wn = wave >> 1, wm = wave & 1;   // wave's 64 x 64 sub-block: features wn, tokens wm
-  const int n0 = blockIdx.x * kGB, m0 = blockIdx.y * kGB;
+  // XCD-aware tile order: the MI355X dispatches workgroup g to XCD g % 8,
+  // and each XCD has its own L2.  XCD x takes the contiguous tile range
+  // [x * per, (x + 1) * per) in token-block-major order, so the N / 128
+  // workgroups that read one 128-token block of A run on one XCD, close in
+  // time, and its L2 serves that block to all of them.
+  const int nN = a.N / kGB, nT = nN * ((a.M + kGB - 1) / kGB);
+  const int per = (nT + kGXcds - 1) / kGXcds;
+  const int t = (int)(blockIdx.x % kGXcds) * per + (int)(blockIdx.x / kGXcds);
+  if (t >= nT) return;
+  const int n0 = (t % nN) * kGB, m0 = (t / nN) * kGB;
   const int M = a.M, K = a.K;
   constexpr int kTile = kGB * kGK * 2;   // bytes of one staged 128 x 64 tile
   const uint32_t s0 = g_lds_off(smem);
@@ -202,7 +212,8 @@ bool gemm_shape_ok(int M, int N, int K) { return M >= 0 && N % kGB == 0 && K % k
 
 hipError_t launch_gemm_bt(const GemmArgs& a, hipStream_t stream) {
   if (a.M <= 0) return hipSuccess;
-  const dim3 grid((unsigned)(a.N / kGB), (unsigned)((a.M + kGB - 1) / kGB)), block(kGThreads);
+  const int nT = (a.N / kGB) * ((a.M + kGB - 1) / kGB);
+  const dim3 grid((unsigned)(kGXcds * ((nT + kGXcds - 1) / kGXcds))), block(kGThreads);
   hipLaunchKernelGGL(hstu_gemm_bt_kernel, grid, block, 0, stream, a);
   return hipGetLastError();
 }
