@@ -351,13 +351,23 @@ hstu_attn_fwd_kernel(AttnArgs a) {
     v_off[s] = (uint32_t)row * ldv_b + 16u * (uint32_t)((m % VCH) ^ C::vswz(row));
   }
 
-  // Work walk: planned workgroup v processes units [wg[2v], wg[2v] + wg[2v+1])
-  // in order; a launch of another size than the plan's maps the planned
-  // workgroups onto its own cyclically.
-  const int n_plan = a.hdr[0];
+  // Work walk.  Static plan: planned workgroup v processes units [wg[2v],
+  // wg[2v] + wg[2v+1]) in order; a launch of another size than the plan's
+  // maps the planned workgroups onto its own cyclically.  Work queue (hdr[2]
+  // set): units 0 .. hdr[4] - 1 in decreasing cost; workgroup g starts with
+  // unit g, and during every item it fetches its next unit, gridDim.x plus
+  // the queue counter's previous value, through s_qnext (two slots by item
+  // parity, so a slot is rewritten only after every wave has passed the
+  // barriers of the item that read it).  Indices only grow, so every
+  // workgroup stops once its next unit is past the last.
+  __shared__ int s_qnext[2];
+  const bool queue = a.hdr[2] != 0;
+  const int n_plan = queue ? (int)gridDim.x : a.hdr[0];
+  int q_item = 0;   // items this workgroup has started (queue slot parity)
   for (int v = blockIdx.x; v < n_plan; v += gridDim.x) {
-  const int u_begin = a.wg[2 * v], u_end = u_begin + a.wg[2 * v + 1];
-  for (int u = u_begin; u < u_end; ++u) {
+  const int u_begin = queue ? (int)blockIdx.x : a.wg[2 * v];
+  const int u_end = queue ? a.hdr[4] : u_begin + a.wg[2 * v + 1];
+  for (int u = u_begin; u < u_end; u = queue ? s_qnext[(q_item++) & 1] : u + 1) {
   const int4 it = a.units[2 * u];
   const int4 ch = a.units[2 * u + 1];   // key tiles [ch.x, ch.y]; split slot, chunk
   const int seq0 = it.x, L = it.y;
@@ -728,10 +738,20 @@ hstu_attn_fwd_kernel(AttnArgs a) {
   // copies ahead); then the third stage.
   issue_stage(B0{}, kt_lo);
   if (kt_lo + 1 <= kt_hi) issue_stage(B1{}, kt_lo + 1);
+  // Queue: the counter's previous value, fetched by wave 0's lane 0 and read
+  // by it only, after the wait below.  Left unset in the other lanes: a
+  // default value there would make the compiler merge the two right here,
+  // which waits for the atomic and for every copy issued before it.
+  int q_fetch;
+  if (queue && tid == 0) q_fetch = atomicAdd(const_cast<int32_t*>(a.hdr) + 3, 1);
   int64_t ti64 = 0;   // this lane's row time (prologue only)
   if constexpr (TIME) {
+    // Neither value is used before the wait below: a use here (a select
+    // between them, say) would make the compiler wait for every copy issued
+    // so far, the stages above included.  Rows past the tile take the last
+    // row's time; their scores are never used.
     tbase = a.timestamps[seq0 + i0];
-    ti64 = row_valid ? a.timestamps[seq0 + i] : tbase;
+    ti64 = a.timestamps[seq0 + min(i, i1 - 1)];
   }
   // Q tile: every wave copies its 32 rows into LDS with whole-row copies (1 KB
   // per copy; stage buffers 2 and 3 are not in use yet), then reads its MFMA
@@ -769,6 +789,15 @@ hstu_attn_fwd_kernel(AttnArgs a) {
     }
   }
   wait_vmem<0>();
+  asm volatile("" : "+v"(q_fetch));   // a plain value from here: no wait of its own
+  if (queue && tid == 0) {
+    s_qnext[q_item & 1] = (int)gridDim.x + q_fetch;   // published by the barrier below
+    // Every processed unit makes one fetch, so the counter ends at the
+    // number of units: the fetch that returned the last value was the run's
+    // last, and its workgroup rewinds the counter for the next run of the
+    // same plan.
+    if (q_fetch == u_end - 1) const_cast<int32_t*>(a.hdr)[3] = 0;
+  }
 #pragma unroll
   for (int c = 0; C::kQLds && c < NKC; ++c) {
     if constexpr (BF) {

@@ -105,13 +105,16 @@ constexpr int kMaxGrid = 1024;      // most workgroups one plan serves
 constexpr int kCostOverhead = 6;    // fixed cost of an item, in key tiles
 constexpr int kMinChunk = 8;        // fewest key tiles of a chunk of a split item
 constexpr int kPlanLdsItems = 4096; // plans of up to this many items stay in LDS
+constexpr int kSortBuckets = 16;     // key-tile counts the queue order tells apart
 // Unit flag (bit 31 of the chunk word): the unit's query tiles start at the
 // history end n_h instead of row 0 (candidates-only plans).
 constexpr int kUnitCandRows = int(0x80000000u);
 
 struct PlanLayout {
   size_t hdr_off;      // int32[64]: [0] workgroups the plan was made for,
-                       //   [1] 1 for a candidates-only plan
+                       //   [1] 1 for a candidates-only plan, [2] 1 when the
+                       //   units form a work queue (see the scheduler), [3]
+                       //   the queue's counter, [4] the number of units
   size_t units_off;    // int4[2 * units_max]: (seq start, L, n_h, qt*H + h),
                        //   (kt_begin, kt_end, split slot or -1, chunk << 16 | chunks)
   size_t wg_off;       // int32[2 * kMaxGrid]: (first unit, units) per workgroup

@@ -24,6 +24,13 @@
 //      pointwise aggregation is a sum over keys, so the chunks' partial
 //      outputs add up exactly to the item's output.
 //
+// Batches whose sequences all fit two query tiles (every item under 2 x
+// kMinChunk key tiles, so none is split, and few key tiles shared between
+// items) are planned as a work queue instead: the units in decreasing cost
+// (a counting sort on their key-tile count), taken by the attention
+// workgroups one at a time from a counter, which balances them like
+// longest-first list scheduling.
+//
 // One workgroup of 1024 threads, five phases; the per-item arrays stay in LDS
 // up to kPlanLdsItems items.  Everything stays on the device, so the
 // caller's stream never synchronises with the host.
@@ -185,6 +192,21 @@ __device__ inline int dealt_item(int j, int n, int n_wg) {
   return t * n_wg + c;
 }
 
+// Queue-order bucket of query tile qt of sequence b (0 = the most key
+// tiles): the key tiles its mask lets it reach, as item_geo_of counts them.
+__device__ inline int tile_bucket(int b, int qt, const int32_t* slen, const int32_t* hist,
+                                  const PlanArgs& a, bool cand_only) {
+  SeqGeom g;
+  g.L = slen[b];
+  g.n_h = hist[b];
+  g.c = clampi(a.contextual_len, 0, g.n_h);
+  g.W = a.max_attn_len;
+  const int i0 = row_base(g.n_h, cand_only) + qt * kBM, i1 = min(i0 + kBM, g.L);
+  int jlo, jhi;
+  tile_key_range(g, i0, i1, jlo, jhi);
+  return kSortBuckets - min(jhi / kBN - jlo / kBN + 1, kSortBuckets);
+}
+
 // I: type of the cost prefix sums (int when they fit, else int64_t).  LDS:
 // the per-item arrays live in LDS (at most kPlanLdsItems items) instead of
 // the workspace.
@@ -201,6 +223,9 @@ __global__ __launch_bounds__(kPlanThreads) void hstu_plan_kernel(PlanArgs a) {
   __shared__ int s_iseq[kItems];
   __shared__ I s_line[kItems + 1];
   __shared__ I s_ub[kItems + 1];
+  __shared__ int s_sorted[LDS ? kItems : 1];   // queue order: line position -> item
+  __shared__ int s_bcnt[kSortBuckets];
+  __shared__ int s_long;
 
   const int tid = threadIdx.x;
   const int B = a.num_seqs, H = a.num_heads, n_wg = a.n_wg;
@@ -213,6 +238,9 @@ __global__ __launch_bounds__(kPlanThreads) void hstu_plan_kernel(PlanArgs a) {
   int32_t* hist = seq + 3 * LD;   // [B] history tokens (L minus clamped candidates)
 
   for (int v = tid; v < kMaxGrid; v += kPlanThreads) s_cnt[v] = 0;
+  if (tid == 0) s_long = 0;
+  if (tid < kSortBuckets) s_bcnt[tid] = 0;
+  __syncthreads();
 
   // 1. Per sequence: geometry and the first item (exclusive scan of nq * H).
   int carry = 0;
@@ -227,6 +255,10 @@ __global__ __launch_bounds__(kPlanThreads) void hstu_plan_kernel(PlanArgs a) {
       slen[b] = L;
       hist[b] = L - clampi(nt, 0, L);
       cnt = (L - row_base(hist[b], cand) + kBM - 1) / kBM * H;
+      if (L - row_base(hist[b], cand) > 2 * kBM) s_long = 1;
+      else if (LDS)
+        for (int qt = 0; qt * kBM < L - row_base(hist[b], cand); ++qt)
+          atomicAdd(&s_bcnt[tile_bucket(b, qt, slen, hist, a, cand)], H);
     }
     int tot;
     const int ex = block_excl_scan(cnt, s_ws32, tot);
@@ -234,6 +266,26 @@ __global__ __launch_bounds__(kPlanThreads) void hstu_plan_kernel(PlanArgs a) {
     carry += tot;
   }
   const int n = min(carry, a.items_max);   // never beyond the scratch's capacity
+
+  const bool queue = LDS && s_long == 0 && n == carry;
+  if (queue) {
+    if (tid < 64) {   // bucket starts: exclusive scan over the buckets
+      const int c = tid < kSortBuckets ? s_bcnt[tid] : 0;
+      const int inc = wave_incl_scan(c);
+      if (tid < kSortBuckets) s_bcnt[tid] = inc - c;
+    }
+    __syncthreads();
+    for (int b = tid; b < B; b += kPlanThreads) {   // ties in any order
+      const int nq = (slen[b] - row_base(hist[b], cand) + kBM - 1) / kBM;
+      for (int qt = 0; qt < nq; ++qt) {
+        const int pos = atomicAdd(&s_bcnt[tile_bucket(b, qt, slen, hist, a, cand)], H);
+        for (int h = 0; h < H; ++h) s_sorted[pos + h] = base[b] + h * nq + (nq - 1 - qt);
+      }
+    }
+    __syncthreads();
+  }
+  // item at line position j
+  auto item_at = [&](int j) { return queue ? s_sorted[j] : dealt_item(j, n, n_wg); };
 
   int* cost = s_cost;
   int* iseq = s_iseq;
@@ -254,7 +306,7 @@ __global__ __launch_bounds__(kPlanThreads) void hstu_plan_kernel(PlanArgs a) {
     const int j = j0 + tid;
     int c = 0;
     if (j < n) {
-      const int k = dealt_item(j, n, n_wg);
+      const int k = item_at(j);
       const int b = seq_of(k, base, B);
       const ItemGeo g = item_geo_of(k, b, base, slen, hist, a.contextual_len, a.max_attn_len, cand);
       c = g.kt_hi - g.kt_lo + 1 + kCostOverhead;
@@ -290,7 +342,7 @@ __global__ __launch_bounds__(kPlanThreads) void hstu_plan_kernel(PlanArgs a) {
 
   // 4. Units, one per chunk in line order; count the units of every workgroup.
   for (int j = tid; j < n; j += kPlanThreads) {
-    const int k = dealt_item(j, n, n_wg), b = iseq[j];
+    const int k = item_at(j), b = iseq[j];
     const ItemGeo g = item_geo_of(k, b, base, slen, hist, a.contextual_len, a.max_attn_len, cand);
     const int4 it = make_int4(start[b], slen[b], g.n_h, g.qt * H + g.h);
     const int u0 = (int)(ub[j] & kLow), slot0 = (int)(ub[j] >> kShift);
@@ -322,6 +374,9 @@ __global__ __launch_bounds__(kPlanThreads) void hstu_plan_kernel(PlanArgs a) {
   if (tid == 0) {
     a.hdr[0] = n_wg;
     a.hdr[1] = cand ? 1 : 0;
+    a.hdr[2] = queue ? 1 : 0;
+    a.hdr[3] = 0;
+    a.hdr[4] = (int)(ucarry & kLow);
   }
 }
 
