@@ -223,7 +223,6 @@ __global__ __launch_bounds__(kPlanThreads) void hstu_plan_kernel(PlanArgs a) {
   __shared__ int s_iseq[kItems];
   __shared__ I s_line[kItems + 1];
   __shared__ I s_ub[kItems + 1];
-  __shared__ int s_sorted[LDS ? kItems : 1];   // queue order: line position -> item
   __shared__ int s_bcnt[kSortBuckets];
   __shared__ int s_long;
 
@@ -267,8 +266,10 @@ __global__ __launch_bounds__(kPlanThreads) void hstu_plan_kernel(PlanArgs a) {
   }
   const int n = min(carry, a.items_max);   // never beyond the scratch's capacity
 
-  const bool queue = LDS && s_long == 0 && n == carry;
-  if (queue) {
+  // Work queue: the units, one per item (none is split), in decreasing cost
+  // straight from the counting sort; the attention kernel reads nothing else
+  // of the plan in this mode.
+  if (LDS && s_long == 0 && n == carry) {
     if (tid < 64) {   // bucket starts: exclusive scan over the buckets
       const int c = tid < kSortBuckets ? s_bcnt[tid] : 0;
       const int inc = wave_incl_scan(c);
@@ -276,16 +277,34 @@ __global__ __launch_bounds__(kPlanThreads) void hstu_plan_kernel(PlanArgs a) {
     }
     __syncthreads();
     for (int b = tid; b < B; b += kPlanThreads) {   // ties in any order
-      const int nq = (slen[b] - row_base(hist[b], cand) + kBM - 1) / kBM;
-      for (int qt = 0; qt < nq; ++qt) {
-        const int pos = atomicAdd(&s_bcnt[tile_bucket(b, qt, slen, hist, a, cand)], H);
-        for (int h = 0; h < H; ++h) s_sorted[pos + h] = base[b] + h * nq + (nq - 1 - qt);
+      const int i_b = row_base(hist[b], cand);
+      SeqGeom g;
+      g.L = slen[b];
+      g.n_h = hist[b];
+      g.c = clampi(a.contextual_len, 0, g.n_h);
+      g.W = a.max_attn_len;
+      for (int qt = 0; i_b + qt * kBM < g.L; ++qt) {
+        const int i0 = i_b + qt * kBM, i1 = min(i0 + kBM, g.L);
+        int jlo, jhi;
+        tile_key_range(g, i0, i1, jlo, jhi);
+        const int kt_lo = jlo / kBN, kt_hi = jhi / kBN;
+        const int pos = atomicAdd(&s_bcnt[kSortBuckets - min(kt_hi - kt_lo + 1, kSortBuckets)], H);
+        const int4 ch = make_int4(kt_lo, kt_hi, -1, (cand ? kUnitCandRows : 0) | 1);
+        for (int h = 0; h < H; ++h) {
+          a.units[2 * (pos + h)] = make_int4(start[b], g.L, g.n_h, qt * H + h);
+          a.units[2 * (pos + h) + 1] = ch;
+        }
       }
     }
-    __syncthreads();
+    if (tid == 0) {
+      a.hdr[0] = n_wg;
+      a.hdr[1] = cand ? 1 : 0;
+      a.hdr[2] = 1;
+      a.hdr[3] = 0;
+      a.hdr[4] = n;
+    }
+    return;
   }
-  // item at line position j
-  auto item_at = [&](int j) { return queue ? s_sorted[j] : dealt_item(j, n, n_wg); };
 
   int* cost = s_cost;
   int* iseq = s_iseq;
@@ -306,7 +325,7 @@ __global__ __launch_bounds__(kPlanThreads) void hstu_plan_kernel(PlanArgs a) {
     const int j = j0 + tid;
     int c = 0;
     if (j < n) {
-      const int k = item_at(j);
+      const int k = dealt_item(j, n, n_wg);
       const int b = seq_of(k, base, B);
       const ItemGeo g = item_geo_of(k, b, base, slen, hist, a.contextual_len, a.max_attn_len, cand);
       c = g.kt_hi - g.kt_lo + 1 + kCostOverhead;
@@ -342,7 +361,7 @@ __global__ __launch_bounds__(kPlanThreads) void hstu_plan_kernel(PlanArgs a) {
 
   // 4. Units, one per chunk in line order; count the units of every workgroup.
   for (int j = tid; j < n; j += kPlanThreads) {
-    const int k = item_at(j), b = iseq[j];
+    const int k = dealt_item(j, n, n_wg), b = iseq[j];
     const ItemGeo g = item_geo_of(k, b, base, slen, hist, a.contextual_len, a.max_attn_len, cand);
     const int4 it = make_int4(start[b], slen[b], g.n_h, g.qt * H + g.h);
     const int u0 = (int)(ub[j] & kLow), slot0 = (int)(ub[j] >> kShift);
@@ -374,7 +393,7 @@ __global__ __launch_bounds__(kPlanThreads) void hstu_plan_kernel(PlanArgs a) {
   if (tid == 0) {
     a.hdr[0] = n_wg;
     a.hdr[1] = cand ? 1 : 0;
-    a.hdr[2] = queue ? 1 : 0;
+    a.hdr[2] = 0;
     a.hdr[3] = 0;
     a.hdr[4] = (int)(ucarry & kLow);
   }
