@@ -192,19 +192,28 @@ __device__ inline int dealt_item(int j, int n, int n_wg) {
   return t * n_wg + c;
 }
 
-// Queue-order bucket of query tile qt of sequence b (0 = the most key
-// tiles): the key tiles its mask lets it reach, as item_geo_of counts them.
-__device__ inline int tile_bucket(int b, int qt, const int32_t* slen, const int32_t* hist,
-                                  const PlanArgs& a, bool cand_only) {
+// Sequence geometry of sequence b for the mask rules.
+__device__ inline SeqGeom seq_geom(int b, const int32_t* slen, const int32_t* hist,
+                                   const PlanArgs& a) {
   SeqGeom g;
   g.L = slen[b];
   g.n_h = hist[b];
   g.c = clampi(a.contextual_len, 0, g.n_h);
   g.W = a.max_attn_len;
-  const int i0 = row_base(g.n_h, cand_only) + qt * kBM, i1 = min(i0 + kBM, g.L);
+  return g;
+}
+
+// Key tiles [kt_lo, kt_hi] that query tile qt (first row i_b + qt * kBM) can
+// reach, as item_geo_of counts them, and its queue-order bucket (0 = the most
+// key tiles).  The count and the scatter of the queue order both use it, so
+// they agree on every bucket.
+__device__ inline int tile_bucket(const SeqGeom& g, int i_b, int qt, int& kt_lo, int& kt_hi) {
+  const int i0 = i_b + qt * kBM, i1 = min(i0 + kBM, g.L);
   int jlo, jhi;
   tile_key_range(g, i0, i1, jlo, jhi);
-  return kSortBuckets - min(jhi / kBN - jlo / kBN + 1, kSortBuckets);
+  kt_lo = jlo / kBN;
+  kt_hi = jhi / kBN;
+  return kSortBuckets - min(kt_hi - kt_lo + 1, kSortBuckets);
 }
 
 // I: type of the cost prefix sums (int when they fit, else int64_t).  LDS:
@@ -254,10 +263,15 @@ __global__ __launch_bounds__(kPlanThreads) void hstu_plan_kernel(PlanArgs a) {
       slen[b] = L;
       hist[b] = L - clampi(nt, 0, L);
       cnt = (L - row_base(hist[b], cand) + kBM - 1) / kBM * H;
-      if (L - row_base(hist[b], cand) > 2 * kBM) s_long = 1;
-      else if (LDS)
-        for (int qt = 0; qt * kBM < L - row_base(hist[b], cand); ++qt)
-          atomicAdd(&s_bcnt[tile_bucket(b, qt, slen, hist, a, cand)], H);
+      if (L - row_base(hist[b], cand) > 2 * kBM) {
+        s_long = 1;
+      } else if (LDS) {
+        const SeqGeom g = seq_geom(b, slen, hist, a);
+        const int i_b = row_base(g.n_h, cand);
+        int kt_lo, kt_hi;
+        for (int qt = 0; i_b + qt * kBM < L; ++qt)
+          atomicAdd(&s_bcnt[tile_bucket(g, i_b, qt, kt_lo, kt_hi)], H);
+      }
     }
     int tot;
     const int ex = block_excl_scan(cnt, s_ws32, tot);
@@ -277,18 +291,11 @@ __global__ __launch_bounds__(kPlanThreads) void hstu_plan_kernel(PlanArgs a) {
     }
     __syncthreads();
     for (int b = tid; b < B; b += kPlanThreads) {   // ties in any order
-      const int i_b = row_base(hist[b], cand);
-      SeqGeom g;
-      g.L = slen[b];
-      g.n_h = hist[b];
-      g.c = clampi(a.contextual_len, 0, g.n_h);
-      g.W = a.max_attn_len;
+      const SeqGeom g = seq_geom(b, slen, hist, a);
+      const int i_b = row_base(g.n_h, cand);
       for (int qt = 0; i_b + qt * kBM < g.L; ++qt) {
-        const int i0 = i_b + qt * kBM, i1 = min(i0 + kBM, g.L);
-        int jlo, jhi;
-        tile_key_range(g, i0, i1, jlo, jhi);
-        const int kt_lo = jlo / kBN, kt_hi = jhi / kBN;
-        const int pos = atomicAdd(&s_bcnt[kSortBuckets - min(kt_hi - kt_lo + 1, kSortBuckets)], H);
+        int kt_lo, kt_hi;
+        const int pos = atomicAdd(&s_bcnt[tile_bucket(g, i_b, qt, kt_lo, kt_hi)], H);
         const int4 ch = make_int4(kt_lo, kt_hi, -1, (cand ? kUnitCandRows : 0) | 1);
         for (int h = 0; h < H; ++h) {
           a.units[2 * (pos + h)] = make_int4(start[b], g.L, g.n_h, qt * H + h);
