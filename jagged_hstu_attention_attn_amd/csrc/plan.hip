@@ -24,9 +24,10 @@
 //      pointwise aggregation is a sum over keys, so the chunks' partial
 //      outputs add up exactly to the item's output.
 //
-// Batches whose sequences all fit two query tiles (every item under 2 x
-// kMinChunk key tiles, so none is split, and few key tiles shared between
-// items) are planned as a work queue instead: the units in decreasing cost
+// Batches whose sequences all fit two query tiles (rows computed) and whose
+// items all stay under 2 x kMinChunk key tiles (so none would be split; a
+// candidate tile behind a long history reaches more) are planned as a work
+// queue instead: the units in decreasing cost
 // (a counting sort on their key-tile count), taken by the attention
 // workgroups one at a time from a counter, which balances them like
 // longest-first list scheduling.
@@ -233,7 +234,7 @@ __global__ __launch_bounds__(kPlanThreads) void hstu_plan_kernel(PlanArgs a) {
   __shared__ I s_line[kItems + 1];
   __shared__ I s_ub[kItems + 1];
   __shared__ int s_bcnt[kSortBuckets];
-  __shared__ int s_long;
+  __shared__ int s_long;   // some item needs the static plan
 
   const int tid = threadIdx.x;
   const int B = a.num_seqs, H = a.num_heads, n_wg = a.n_wg;
@@ -269,8 +270,10 @@ __global__ __launch_bounds__(kPlanThreads) void hstu_plan_kernel(PlanArgs a) {
         const SeqGeom g = seq_geom(b, slen, hist, a);
         const int i_b = row_base(g.n_h, cand);
         int kt_lo, kt_hi;
-        for (int qt = 0; i_b + qt * kBM < L; ++qt)
+        for (int qt = 0; i_b + qt * kBM < L; ++qt) {
           atomicAdd(&s_bcnt[tile_bucket(g, i_b, qt, kt_lo, kt_hi)], H);
+          if (kt_hi - kt_lo + 1 >= 2 * kMinChunk) s_long = 1;   // the static plan would split it
+        }
       }
     }
     int tot;

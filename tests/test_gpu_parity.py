@@ -321,6 +321,33 @@ def test_split_items_plan_reuse():
     assert np.array_equal(o1, o2) and np.array_equal(o1, o3)
 
 
+@pytest.mark.parametrize("lengths,targets,window", [
+    ([256, 1, 0, 130, 129], [20, 0, 0, 5, 129], 0),   # every sequence within two query tiles
+    ([256, 257, 40], [0, 30, 3], 100),                 # one sequence of three tiles
+    ([5, 17, 3], [2, 17, 0], 4),                       # fewer units than workgroups
+])
+def test_queue_boundaries_plan_reuse(lengths, targets, window):
+    """Batches at the edge of the work-queue mode (sequences of at most 256
+    rows take units from a counter in decreasing cost; a longer one switches
+    the batch to the static plan).  Three runs of one plan -- the counter must
+    rewind after the last fetch, also when workgroups stay idle -- match the
+    oracle and each other bitwise."""
+    inp = make_custom(lengths, num_heads=3, d_qk=64, d_v=64, dtype="bf16", seed=21,
+                      num_targets=targets, contextual_len=3, max_attn_len=window,
+                      pos_len=512, time_len=64, alpha=0.125)
+    dev = to_device(inp, DEV)
+    call = JaggedAttnCall(dev["q"], dev["k"], dev["v"], dev["u"], dev["offsets"],
+                          **call_kwargs(inp, dev))
+    call.plan()
+    outs = []
+    for _ in range(3):
+        call.out.zero_()
+        outs.append(call.run().float().cpu().numpy().astype(np.float64))
+    torch.cuda.synchronize()
+    assert_close(outs[0], ora(inp), "bf16")
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+
+
 @pytest.mark.parametrize("dtype,d", [("f32", 8), ("bf16", 64)])
 def test_large_batch_plan(dtype, d):
     """More sequences than the scheduler keeps in LDS (2048) and more items
