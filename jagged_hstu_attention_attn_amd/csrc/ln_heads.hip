@@ -9,6 +9,8 @@
 // (epilogue "none") and this pass, one wave per token, reads the token's
 // row (heads are consecutive d_v blocks), forms mean and variance with wave
 // reductions, and writes (O - mean) * rstd * U back in place.
+#include <type_traits>
+
 #include "hstu_device.hpp"
 
 namespace hstu {
@@ -24,10 +26,11 @@ __device__ inline float wave_sum(float x) {
   return x;
 }
 
-// T: element type; EPC: elements per 16-byte chunk.
+// T: element type; EPC: elements per 16-byte chunk; NCH: chunks per lane
+// (the row width rounded up to a power of two, so registers fit the row).
 // When the plan covered the candidate rows only (plan header word 1), rows
 // of the history are left alone: they were not computed by this run.
-template <typename T, int EPC>
+template <typename T, int EPC, int NCH>
 __global__ __launch_bounds__(256) void hstu_ln_all_heads_kernel(LnArgs a) {
   T* out = static_cast<T*>(a.out);
   const T* u = static_cast<const T*>(a.u);
@@ -50,23 +53,22 @@ __global__ __launch_bounds__(256) void hstu_ln_all_heads_kernel(LnArgs a) {
   const int chunks = width / EPC;
   T* row = out + t * ld_out;
   const T* urow = u + t * ld_u;
-  float x[kLnChunks][EPC];
+  // The U chunks are loaded together with the outputs, so the token's two
+  // reads overlap instead of waiting for the reductions.
+  using Vec = typename std::conditional<EPC == 8, bf16x8_ln, floatx4_ln>::type;
+  float x[NCH][EPC];
+  Vec uv[NCH];
   float sum = 0.0f;
 #pragma unroll
-  for (int c = 0; c < kLnChunks; ++c) {
+  for (int c = 0; c < NCH; ++c) {
     const int ch = lane + 64 * c;
 #pragma unroll
     for (int e = 0; e < EPC; ++e) x[c][e] = 0.0f;
     if (ch < chunks) {
-      if constexpr (EPC == 8) {
-        const bf16x8_ln v = *reinterpret_cast<const bf16x8_ln*>(row + EPC * ch);
+      const Vec v = *reinterpret_cast<const Vec*>(row + EPC * ch);
+      uv[c] = *reinterpret_cast<const Vec*>(urow + EPC * ch);
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) x[c][e] = (float)v[e];
-      } else {
-        const floatx4_ln v = *reinterpret_cast<const floatx4_ln*>(row + EPC * ch);
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) x[c][e] = v[e];
-      }
+      for (int e = 0; e < EPC; ++e) x[c][e] = (float)v[e];
 #pragma unroll
       for (int e = 0; e < EPC; ++e) sum += x[c][e];
     }
@@ -74,43 +76,46 @@ __global__ __launch_bounds__(256) void hstu_ln_all_heads_kernel(LnArgs a) {
   const float mean = wave_sum(sum) / (float)width;
   float sq = 0.0f;
 #pragma unroll
-  for (int c = 0; c < kLnChunks; ++c)
+  for (int c = 0; c < NCH; ++c)
     if (lane + 64 * c < chunks) {
 #pragma unroll
       for (int e = 0; e < EPC; ++e) sq += (x[c][e] - mean) * (x[c][e] - mean);
     }
   const float rstd = rsqrtf(wave_sum(sq) / (float)width + eps);
 #pragma unroll
-  for (int c = 0; c < kLnChunks; ++c) {
+  for (int c = 0; c < NCH; ++c) {
     const int ch = lane + 64 * c;
     if (ch < chunks) {
-      if constexpr (EPC == 8) {
-        const bf16x8_ln uu = *reinterpret_cast<const bf16x8_ln*>(urow + EPC * ch);
-        bf16x8_ln o;
+      Vec o;
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) o[e] = (__bf16)((x[c][e] - mean) * rstd * (float)uu[e]);
-        *reinterpret_cast<bf16x8_ln*>(row + EPC * ch) = o;
-      } else {
-        const floatx4_ln uu = *reinterpret_cast<const floatx4_ln*>(urow + EPC * ch);
-        floatx4_ln o;
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) o[e] = (x[c][e] - mean) * rstd * uu[e];
-        *reinterpret_cast<floatx4_ln*>(row + EPC * ch) = o;
-      }
+      for (int e = 0; e < EPC; ++e) o[e] = (T)((x[c][e] - mean) * rstd * (float)uv[c][e]);
+      *reinterpret_cast<Vec*>(row + EPC * ch) = o;
     }
   }
 }
 
 int ln_all_heads_max_width(int dtype) { return 64 * kLnChunks * (dtype == 1 ? 8 : 4); }
 
+template <typename T, int EPC>
+hipError_t launch_width(const LnArgs& a, const dim3& grid, hipStream_t stream) {
+  const int nch = (a.width / EPC + 63) / 64;
+  const dim3 block(256);
+  if (nch <= 1)
+    hipLaunchKernelGGL((hstu_ln_all_heads_kernel<T, EPC, 1>), grid, block, 0, stream, a);
+  else if (nch <= 2)
+    hipLaunchKernelGGL((hstu_ln_all_heads_kernel<T, EPC, 2>), grid, block, 0, stream, a);
+  else if (nch <= 4)
+    hipLaunchKernelGGL((hstu_ln_all_heads_kernel<T, EPC, 4>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((hstu_ln_all_heads_kernel<T, EPC, kLnChunks>), grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_ln_all_heads(const LnArgs& a, int dtype, hipStream_t stream) {
   if (a.n_tok <= 0) return hipSuccess;
-  const dim3 grid((unsigned)((a.n_tok + 3) / 4)), block(256);
-  if (dtype == 1)
-    hipLaunchKernelGGL((hstu_ln_all_heads_kernel<__bf16, 8>), grid, block, 0, stream, a);
-  else
-    hipLaunchKernelGGL((hstu_ln_all_heads_kernel<float, 4>), grid, block, 0, stream, a);
-  return hipGetLastError();
+  const dim3 grid((unsigned)((a.n_tok + 3) / 4));
+  return dtype == 1 ? launch_width<__bf16, 8>(a, grid, stream)
+                    : launch_width<float, 4>(a, grid, stream);
 }
 
 }  // namespace hstu

@@ -468,6 +468,18 @@ def test_ln_all_heads(name, kw, dtype):
     assert_close(gpu_forward(inp, epilogue="ln_all_u"), ora(inp, "ln_all_u"), dtype)
 
 
+@pytest.mark.parametrize("heads,d,dtype", [(16, 128, "bf16"), (32, 128, "bf16"),
+                                           (16, 128, "f32"), (3, 64, "bf16")])
+def test_ln_all_heads_widths(heads, d, dtype):
+    """Token widths H * d_v that take 4 and 8 16-byte chunks per lane in the
+    all-heads LayerNorm pass (1 and 2 come from the workloads above), and a
+    width of 24 chunks that leaves most lanes idle."""
+    inp = make_custom([37, 130, 5], num_heads=heads, d_qk=d, d_v=d, dtype=dtype, seed=5,
+                      num_targets=[4, 20, 0], contextual_len=2, pos_len=256, time_len=64,
+                      alpha=1.0 / math.sqrt(d))
+    assert_close(gpu_forward(inp, epilogue="ln_all_u"), ora(inp, "ln_all_u"), dtype)
+
+
 def test_ln_all_heads_strided_and_candidates():
     inp = make_inputs("layer", num_seqs=5)
     assert_close(gpu_forward(inp, epilogue="ln_all_u", ld=2048), ora(inp, "ln_all_u"), "bf16")
