@@ -168,7 +168,11 @@ int hstu_jagged_attn_plan(const hstu_attn_desc* desc, const int32_t* offsets,
  * `workspace` with the same offsets, num_targets, contextual_len,
  * max_attn_len and shapes.  Requires n_scale > 0 and finite, alpha finite;
  * timestamps non-NULL iff time_table non-NULL.  Writes every row of `out`
- * exactly once and nothing else.
+ * exactly once and nothing else.  The workspace also holds counters the run
+ * uses and leaves rearmed for the next run of the same plan (the work-queue
+ * counter of a batch of short sequences, the arrival counters of items split
+ * along keys): runs that share a workspace must be ordered (one stream, or
+ * synchronised); two at once on one workspace race.
  */
 int hstu_jagged_attn_run(const hstu_attn_desc* desc,
                          const void* q, const void* k, const void* v, const void* u,
