@@ -233,6 +233,7 @@ __global__ __launch_bounds__(kPlanThreads) void hstu_plan_kernel(PlanArgs a) {
   __shared__ int s_iseq[kItems];
   __shared__ I s_line[kItems + 1];
   __shared__ I s_ub[kItems + 1];
+  __shared__ int2 s_geo[kItems];   // LDS plans: first key tile, qt * H + h of each item
   __shared__ int s_bcnt[kSortBuckets];
   __shared__ int s_long;   // some item needs the static plan
 
@@ -341,6 +342,7 @@ __global__ __launch_bounds__(kPlanThreads) void hstu_plan_kernel(PlanArgs a) {
       c = g.kt_hi - g.kt_lo + 1 + kCostOverhead;
       cost[j] = c;
       iseq[j] = b;
+      if constexpr (LDS) s_geo[j] = make_int2(g.kt_lo, g.qt * H + g.h);
     }
     I tot;
     const I ex = block_excl_scan((I)c, s_ws, tot);
@@ -371,14 +373,24 @@ __global__ __launch_bounds__(kPlanThreads) void hstu_plan_kernel(PlanArgs a) {
 
   // 4. Units, one per chunk in line order; count the units of every workgroup.
   for (int j = tid; j < n; j += kPlanThreads) {
-    const int k = dealt_item(j, n, n_wg), b = iseq[j];
-    const ItemGeo g = item_geo_of(k, b, base, slen, hist, a.contextual_len, a.max_attn_len, cand);
-    const int4 it = make_int4(start[b], slen[b], g.n_h, g.qt * H + g.h);
+    const int b = iseq[j];
+    int kt_lo, qh;   // the geometry phase 2 found (LDS plans keep it)
+    if constexpr (LDS) {
+      const int2 gg = s_geo[j];
+      kt_lo = gg.x;
+      qh = gg.y;
+    } else {
+      const ItemGeo g = item_geo_of(dealt_item(j, n, n_wg), b, base, slen, hist,
+                                    a.contextual_len, a.max_attn_len, cand);
+      kt_lo = g.kt_lo;
+      qh = g.qt * H + g.h;
+    }
+    const int4 it = make_int4(start[b], slen[b], hist[b], qh);
     const int u0 = (int)(ub[j] & kLow), slot0 = (int)(ub[j] >> kShift);
     const int nc = (int)(ub[j + 1] & kLow) - u0;
-    item_chunks(line[j], cost[j], g.kt_hi - g.kt_lo + 1, T, [&](int c, int tb, int te, int r) {
+    item_chunks(line[j], cost[j], cost[j] - kCostOverhead, T, [&](int c, int tb, int te, int r) {
       a.units[2 * (u0 + c)] = it;
-      a.units[2 * (u0 + c) + 1] = make_int4(g.kt_lo + tb, g.kt_lo + te - 1, nc > 1 ? slot0 : -1,
+      a.units[2 * (u0 + c) + 1] = make_int4(kt_lo + tb, kt_lo + te - 1, nc > 1 ? slot0 : -1,
                                             (cand ? kUnitCandRows : 0) | (c << 16) | nc);
       atomicAdd(&s_cnt[share_wg(r, n_wg)], 1);
     });
