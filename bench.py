@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Throughput of the jagged HSTU attention forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload ranking]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload windowed]
 
 A step is one pass of the whole hot path (scheduler kernel + attention kernel)
 over one batch of seeded synthetic inputs already resident in HBM.  Before
@@ -9,6 +9,12 @@ every timed step a 1 GiB buffer is rewritten (outside the timed events) so
 that the 256 MB last-level cache holds none of the inputs.  Prints one JSON
 line with valid-pair TFLOP/s, tokens/s, the attention kernel's roofline
 position and the fp64 CPU oracle timed on this host as a baseline.
+
+The default workload is the largest one that fits one GPU, the windowed
+batch (16 sequences of 2048-8192 tokens, window 1024, 50 candidates each),
+whose attention is bound by the bf16 matrix cores; the line also carries a
+`secondary` record for the short ranking batch, bound by HBM bandwidth,
+measured the same way in the same run (skip it with --no-secondary).
 """
 from __future__ import annotations
 
@@ -27,7 +33,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "jagged HSTU attn fwd TFLOP/s (valid pairs) + % bf16 MFMA peak; tokens/s"
-PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}      # dense MFMA peaks, MI355X
+PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}      # dense MFMA peaks, MI355X (256 CU x 2.4 GHz)
 PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = ["jagged_hstu_attention_attn_amd/csrc/attn_fwd.hip",
                   "jagged_hstu_attention_attn_amd/csrc/hstu_device.hpp"]
@@ -295,12 +301,15 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="ranking",
+    ap.add_argument("--workload", default="windowed",
                     choices=["tiny", "ranking", "longtail", "windowed", "layer"])
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--no-flush", action="store_true", help="keep inputs cache-resident")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the secondary (ranking, HBM-bound) record")
+    ap.add_argument("--secondary-steps", type=int, default=50)
     ap.add_argument("--epilogue", default="ln_u", choices=["ln_u", "none", "ln_all_u"],
                     help="per-head LayerNorm * U (default), none, or one LayerNorm over all heads")
     ap.add_argument("--full-layer", action="store_true",
@@ -312,6 +321,8 @@ def main() -> int:
                     help="time the backward (gradients of q, k, v, u and the bias tables)")
     ap.add_argument("--saved-o", action="store_true",
                     help="with --backward: take o / n_scale kept by the training forward")
+    ap.add_argument("--fwd-kernel", default="auto", choices=["auto", "four_wave", "eight_wave"],
+                    help="forward kernel: chosen by batch shape (auto), or forced")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 256 MiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -333,10 +344,10 @@ def main() -> int:
         log(f"copied {n} bytes 5 times")
         return 0
 
-    from jagged_hstu_attention_attn_amd.api import JaggedAttnCall, valid_pairs
-    from jagged_hstu_attention_attn_amd.device_inputs import call_kwargs, to_device
-    from jagged_hstu_attention_attn_amd.inputs import WORKLOADS, make_inputs
+    from jagged_hstu_attention_attn_amd.api import set_fwd_kernel
+    from jagged_hstu_attention_attn_amd.inputs import make_inputs
 
+    set_fwd_kernel(args.fwd_kernel)
     log(f"workload {args.workload}: generating inputs")
     inp = make_inputs(args.workload, seed=args.seed)
     if args.full_layer:
@@ -346,38 +357,66 @@ def main() -> int:
         return bench_layer(args, inp)
     if args.backward:
         return bench_backward(args, inp)
+    result = measure_forward(args, inp, args.workload, args.steps, args.warmup)
+    if not args.no_cpu_baseline and not args.candidates_only:
+        log("timing the fp64 CPU oracle")
+        result["cpu_baseline"] = cpu_baseline(inp, 2.0 * (inp.d_qk + inp.d_v), args.cpu_budget)
+    if (not args.no_secondary and args.workload != "ranking" and args.seed is None
+            and not args.candidates_only and args.epilogue == "ln_u"):
+        del inp
+        log("secondary record: ranking batch")
+        sec_inp = make_inputs("ranking")
+        sec = measure_forward(args, sec_inp, "ranking", args.secondary_steps,
+                              min(args.warmup, 10))
+        keep = ("value", "unit", "ms_per_step", "steps", "warmup", "config", "tokens_per_s",
+                "pct_bf16_mfma_peak", "pct_hbm_peak", "plan_us", "roofline")
+        result["secondary"] = {k: sec[k] for k in keep}
+        result["secondary"]["why"] = ("the short ranking batch, whose attention is bound by HBM "
+                                      "bandwidth (arithmetic intensity 31 flop/B)")
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def measure_forward(args, inp, workload: str, steps: int, warmup: int) -> dict:
+    """Times `steps` forward steps (scheduler + attention) of one batch after
+    `warmup` untimed ones, then the same steps again with the attention
+    kernel's own start/end events; returns the result record."""
+    import torch
+    from jagged_hstu_attention_attn_amd.api import JaggedAttnCall, valid_pairs
+    from jagged_hstu_attention_attn_amd.device_inputs import call_kwargs, to_device
+    from jagged_hstu_attention_attn_amd.inputs import WORKLOADS
+
     dev = to_device(inp, "cuda")
     call = JaggedAttnCall(dev["q"], dev["k"], dev["v"], dev["u"], dev["offsets"],
                           candidates_only=args.candidates_only, epilogue=args.epilogue,
                           **call_kwargs(inp, dev))
     if args.candidates_only:
         pairs, flops, byts = candidate_rows_work(inp)
-        args.no_cpu_baseline = True
     else:
         pairs = valid_pairs(inp.offsets, inp.num_targets, inp.contextual_len, inp.max_attn_len)
         flops, byts = algorithmic(inp, pairs)
     flush = None if args.no_flush else torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
 
-    log(f"{inp.num_seqs} sequences, {inp.total_tokens} tokens, {pairs} valid pairs/head; "
-        f"warmup {args.warmup}")
-    for _ in range(args.warmup):
+    log(f"{workload}: {inp.num_seqs} sequences, {inp.total_tokens} tokens, {pairs} valid "
+        f"pairs/head; warmup {warmup}")
+    for _ in range(warmup):
         call()
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
     ev = lambda: torch.cuda.Event(enable_timing=True)
-    steps_ev = [(ev(), ev()) for _ in range(args.steps)]        # around each step
-    parts_ev = [(ev(), ev(), ev()) for _ in range(args.steps)]  # around scheduler / launch
+    steps_ev = [(ev(), ev()) for _ in range(steps)]        # around each step
+    parts_ev = [(ev(), ev(), ev()) for _ in range(steps)]  # around scheduler / launch
     # the attention kernel's own start / end times (hipExtLaunchKernelGGL);
     # an event exists once recorded
-    kev = [(ev(), ev()) for _ in range(args.steps)]
+    kev = [(ev(), ev()) for _ in range(steps)]
     for k0, k1 in kev:
         k0.record(stream)
         k1.record(stream)
-    log(f"timing {args.steps} steps")
+    log(f"{workload}: timing {steps} steps")
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    for s in range(args.steps):
+    for s in range(steps):
         if flush is not None:
             flush.fill_(s & 0xFF)
         e0, e1 = steps_ev[s]
@@ -391,8 +430,8 @@ def main() -> int:
     # attention launch, the attention launched with events at its own start
     # and end (markers inside a step and a launch that records events both
     # lengthen it, so the step times above come from plain steps).
-    log(f"timing the scheduler and the attention kernel over {args.steps} more steps")
-    for s in range(args.steps):
+    log(f"{workload}: timing the scheduler and the attention kernel over {steps} more steps")
+    for s in range(steps):
         if flush is not None:
             flush.fill_(s & 0xFF)
         m0, m1, m2 = parts_ev[s]
@@ -410,8 +449,9 @@ def main() -> int:
     attn = sum(attn_ms) / len(attn_ms)
     launch = sum(launch_ms) / len(launch_ms)
     plan = sum(plan_ms) / len(plan_ms)
-    log(f"step {ms * 1e3:.1f} us (plan {plan * 1e3:.1f} us, attention kernel {attn * 1e3:.1f} us, "
-        f"{launch * 1e3:.1f} us between markers around its launch), wall {wall:.3f} s")
+    log(f"{workload}: step {ms * 1e3:.1f} us (plan {plan * 1e3:.1f} us, attention kernel "
+        f"{attn * 1e3:.1f} us, {launch * 1e3:.1f} us between markers around its launch), "
+        f"wall {wall:.3f} s")
 
     tflops = flops / (ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[inp.dtype]
@@ -426,9 +466,16 @@ def main() -> int:
         achieved = flops / (attn * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                 "frac": achieved / peak}
-    roof["traffic"] = (None if args.candidates_only or args.epilogue != "ln_u"
-                       else traffic_from_profile(args.workload))
-    roof["kernel"] = "hstu_attn_fwd_kernel"
+    traffic = (None if args.candidates_only or args.epilogue != "ln_u"
+               else traffic_from_profile(workload))
+    roof["traffic"] = traffic
+    roof["traffic_source"] = (
+        f"profiles/attn_fwd_{workload}_traffic.md: rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE "
+        "runs of bench.py, scaled by the copy calibration, taken on the current kernel source"
+        if traffic is not None else
+        "null: no counter summary taken on the current kernel source")
+    roof["kernel"] = ("hstu_attn_fwd_pp_kernel" if call.kernel_name() == "eight_wave"
+                      else "hstu_attn_fwd_kernel")
     roof["kernel_us"] = attn * 1e3
     roof["kernel_timing"] = ("HIP events taken at the kernel's own start and end, over a "
                              "second pass of the same steps")
@@ -436,13 +483,13 @@ def main() -> int:
     roof["algorithmic_bytes"] = byts
     roof["algorithmic_flops"] = flops
 
-    result = {
+    return {
         "metric": METRIC,
         "value": tflops,
         "unit": "TFLOP/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": ms,
         "higher_is_better": True,
         "scaling": "weak",
@@ -450,7 +497,7 @@ def main() -> int:
         "dtype": inp.dtype,
         "data": "synthetic",
         "config": {
-            "workload": args.workload,
+            "workload": workload,
             "rows": "candidates" if args.candidates_only else "all",
             "epilogue": args.epilogue,
             "num_seqs": inp.num_seqs,
@@ -459,7 +506,7 @@ def main() -> int:
             "d_qk": inp.d_qk,
             "d_v": inp.d_v,
             "valid_pairs_per_head": pairs,
-            "seed": args.seed if args.seed is not None else WORKLOADS[args.workload].seed,
+            "seed": args.seed if args.seed is not None else WORKLOADS[workload].seed,
             "cache_flushed": flush is not None,
             "parallelism": "single GPU",
         },
@@ -470,11 +517,6 @@ def main() -> int:
         "wall_s": wall,
         "roofline": roof,
     }
-    if not args.no_cpu_baseline:
-        log("timing the fp64 CPU oracle")
-        result["cpu_baseline"] = cpu_baseline(inp, 2.0 * (inp.d_qk + inp.d_v), args.cpu_budget)
-    print(json.dumps(result), flush=True)
-    return 0
 
 
 if __name__ == "__main__":

@@ -249,6 +249,26 @@ int64_t hstu_jagged_attn_valid_pairs(int32_t num_seqs, const int32_t* offsets_ho
 int hstu_jagged_attn_grid(const hstu_attn_desc* desc);
 
 /*
+ * Forward kernel choice.  Two kernels compute the same forward over the same
+ * work list and workspace: a four-wave kernel (two workgroups per CU) and,
+ * for bf16 with d_qk = d_v = 128, an eight-wave kernel (one workgroup per CU)
+ * whose two waves per SIMD alternate between matrix-core and vector work and
+ * which splits each item's key tiles between its two groups of four waves.
+ * AUTO (the default) takes the four-wave kernel (the eight-wave one is
+ * selected explicitly; see the design notes for its measured standing).
+ * The setting is process-wide; a plan and the runs that use it must see the
+ * same setting (the launch size depends on it).  Both kernels meet the same
+ * tolerance against the oracle; their outputs differ in the last bits
+ * (different summation order).  hstu_jagged_attn_set_fwd_kernel returns
+ * HSTU_OK, or HSTU_ERR_INVALID_ARG for an unknown mode.
+ * hstu_jagged_attn_fwd_kernel_of returns the kernel `desc` would run
+ * (FOUR_WAVE or EIGHT_WAVE), or -1 on a bad desc.
+ */
+enum { HSTU_FWD_KERNEL_AUTO = 0, HSTU_FWD_KERNEL_FOUR_WAVE = 1, HSTU_FWD_KERNEL_EIGHT_WAVE = 2 };
+int hstu_jagged_attn_set_fwd_kernel(int32_t mode);
+int hstu_jagged_attn_fwd_kernel_of(const hstu_attn_desc* desc);
+
+/*
  * Full HSTU layer forward, bf16 (the block of "HSTU tensor by tensor: SiLU
  * aggregation, temporal bias and gating": sections "Follow the U, V, Q and K
  * branches", "Trace four projections" and the teaching equation of "Similar
@@ -291,7 +311,6 @@ int hstu_layer_fwd(const hstu_layer_desc* desc, const void* x, const void* w_uvq
                    const float* pos_table, const float* time_table, void* y, void* workspace,
                    size_t workspace_bytes, void* stream);
 
-/* Thread-local message for the last failing call of this thread ("" if none). */
 /*
  * Backward of the attention (dtype, shapes, strides, rules and epilogue of
  * `desc`, the same inputs as the forward).  Given dout = dLoss/d(out) it
@@ -364,6 +383,7 @@ int hstu_jagged_attn_fwd_train(const hstu_attn_desc* desc,
                                void* o_raw, void* workspace, size_t workspace_bytes,
                                void* stream);
 
+/* Thread-local message for the last failing call of this thread ("" if none). */
 const char* hstu_last_error(void);
 
 #ifdef __cplusplus

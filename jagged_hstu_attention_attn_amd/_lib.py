@@ -22,6 +22,9 @@ HSTU_DTYPE_BF16 = 1
 HSTU_EPILOGUE_LN_U = 0
 HSTU_EPILOGUE_NONE = 1
 HSTU_EPILOGUE_LN_ALL_U = 2
+HSTU_FWD_KERNEL_AUTO = 0
+HSTU_FWD_KERNEL_FOUR_WAVE = 1
+HSTU_FWD_KERNEL_EIGHT_WAVE = 2
 
 # every function the header declares
 EXPORTS = (
@@ -37,6 +40,8 @@ EXPORTS = (
     "hstu_layer_fwd",
     "hstu_jagged_attn_valid_pairs",
     "hstu_jagged_attn_grid",
+    "hstu_jagged_attn_set_fwd_kernel",
+    "hstu_jagged_attn_fwd_kernel_of",
     "hstu_jagged_attn_bwd_workspace_bytes",
     "hstu_jagged_attn_bwd",
     "hstu_jagged_attn_fwd_train",
@@ -126,6 +131,10 @@ def load() -> ctypes.CDLL:
     lib.hstu_jagged_attn_valid_pairs.argtypes = [i32, P, P, i32, i32]
     lib.hstu_jagged_attn_grid.restype = ctypes.c_int
     lib.hstu_jagged_attn_grid.argtypes = [D]
+    lib.hstu_jagged_attn_set_fwd_kernel.restype = ctypes.c_int
+    lib.hstu_jagged_attn_set_fwd_kernel.argtypes = [i32]
+    lib.hstu_jagged_attn_fwd_kernel_of.restype = ctypes.c_int
+    lib.hstu_jagged_attn_fwd_kernel_of.argtypes = [D]
     lib.hstu_jagged_attn_bwd_workspace_bytes.restype = sz
     lib.hstu_jagged_attn_bwd_workspace_bytes.argtypes = [D]
     lib.hstu_jagged_attn_bwd.restype = ctypes.c_int

@@ -74,6 +74,39 @@ def make_desc(q, k, v, u, out, num_seqs: int, *, pos_table=None, time_table=None
     return d
 
 
+FWD_KERNELS = {"auto": _lib.HSTU_FWD_KERNEL_AUTO, "four_wave": _lib.HSTU_FWD_KERNEL_FOUR_WAVE,
+               "eight_wave": _lib.HSTU_FWD_KERNEL_EIGHT_WAVE}
+
+
+def set_fwd_kernel(name: str) -> None:
+    """Process-wide forward kernel choice ("auto", "four_wave", "eight_wave");
+    a plan and the runs that use it must see the same choice."""
+    _lib.check(_lib.load().hstu_jagged_attn_set_fwd_kernel(FWD_KERNELS[name]))
+
+
+def fwd_kernel_of(desc: _lib.HstuAttnDesc) -> str:
+    """Which forward kernel the library runs for `desc` under the current choice."""
+    r = _lib.load().hstu_jagged_attn_fwd_kernel_of(ctypes.byref(desc))
+    if r < 0:
+        raise _lib.HstuError(r, _lib.last_error())
+    return {v: k for k, v in FWD_KERNELS.items()}[r]
+
+
+class fwd_kernel:
+    """Context manager: run the enclosed calls with one forward kernel."""
+
+    def __init__(self, name: str):
+        self.name = name
+
+    def __enter__(self):
+        set_fwd_kernel(self.name)
+        return self
+
+    def __exit__(self, *exc):
+        set_fwd_kernel("auto")
+        return False
+
+
 def workspace_bytes(desc: _lib.HstuAttnDesc) -> int:
     n = _lib.load().hstu_jagged_attn_workspace_bytes(ctypes.byref(desc))
     if n == 0:
@@ -173,6 +206,10 @@ class JaggedAttnCall:
                                   device=q.device) if save_o else None)
         if save_o and candidates_only:
             raise ValueError("save_o is for full forwards")
+
+    def kernel_name(self) -> str:
+        """The forward kernel this call runs under the current choice."""
+        return fwd_kernel_of(self.desc)
 
     def plan(self) -> None:
         plan(self.desc, self.offsets, self.num_targets, self.contextual_len, self.max_attn_len,

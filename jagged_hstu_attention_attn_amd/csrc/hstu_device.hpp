@@ -333,6 +333,19 @@ hipError_t launch_attn(const AttnArgs& a, int dtype, int d_qk, int d_v, int n_wg
 // device (CUs x resident workgroups per CU), or a negative value on error.
 int attn_grid(int dtype, int d_qk, int d_v, int pos_len, int time_len, bool clamp);
 bool attn_supported(int dtype, int d_qk, int d_v);
+// The eight-wave forward for long sequences (attn_fwd_pp.hip): bf16, d_qk =
+// d_v = 128; same units, workspace and arguments as launch_attn.
+bool attn_pp_supported(int dtype, int d_qk, int d_v);
+int attn_pp_grid(int pos_len, int time_len, bool clamp);
+hipError_t launch_attn_pp(const AttnArgs& a, int n_wg, hipStream_t stream,
+                          hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
+// Batches whose mean sequence length reaches this many tokens take the
+// eight-wave kernel (short sequences give it too few key blocks per item to
+// fill its pipeline; the four-wave kernel runs two workgroups per CU).
+constexpr int kPPMinMeanLen = 512;
+// Whether the automatic choice may take the eight-wave kernel at all: off
+// while it measures slower than the four-wave kernel on the long batches.
+constexpr bool kPPAuto = false;
 int ln_all_heads_max_width(int dtype);
 hipError_t launch_ln_all_heads(const LnArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_bwd_plan(const BwdPlanArgs& a, hipStream_t stream);
