@@ -192,6 +192,15 @@ def test_bwd_long_workloads_sampled(name, pick):
     assert_grads(got, ref, "bf16", tokens=(idx, slice(None)), tables=False)
 
 
+def test_bwd_windowed_four_sequences_with_tables():
+    """Four whole sequences of the windowed workload (2048-8192 tokens, window
+    1024, 50 candidates): every token gradient and both table gradients."""
+    print("case bwd windowed 4 sequences", flush=True)
+    inp = make_inputs("windowed", num_seqs=4)
+    dout = make_dout(inp, 15)
+    assert_grads(gpu_backward(inp, dout), oracle.backward(inp, dout), "bf16")
+
+
 def test_bwd_longtail_reduced_with_tables():
     inp = make_inputs("longtail", num_seqs=6)
     dout = make_dout(inp, 14)

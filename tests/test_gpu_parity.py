@@ -117,6 +117,58 @@ def test_full_size_sampled_rows(name):
     assert_close(gpu_forward(inp), ora(inp, rows=rows), "bf16", rows=rows)
 
 
+@pytest.mark.parametrize("seed", [1234, 1, 2, 3, 4])
+@pytest.mark.parametrize("name", ["longtail", "windowed"])
+def test_long_workloads_whole_output(name, seed):
+    """The whole output of the full-size long-tail and windowed batches (the
+    configuration the benchmark times) against the whole fp64 oracle."""
+    print(f"case whole {name} seed {seed}", flush=True)
+    inp = make_inputs(name, seed=seed)
+    assert_close(gpu_forward(inp), ora(inp), "bf16")
+
+
+def _zero_pattern_windows(inp, epilogue_rows=128):
+    """Zero pattern of every allowed / masked pair of a one-sequence batch:
+    for each window of 128 keys [j0, j0 + 128), V is one-hot over the window
+    (key j0 + e sets column e), so with epilogue NONE out[i, e] = a_{i, j0+e},
+    nonzero exactly where the pair is allowed (scores stay away from 0)."""
+    assert inp.num_seqs == 1 and inp.num_heads == 1 and inp.d_v == 128
+    L = int(inp.lengths[0])
+    T = 0 if inp.num_targets is None else int(inp.num_targets[0])
+    mask = oracle._dense_mask(L, T, inp.contextual_len, inp.max_attn_len, L)
+    for j0 in range(0, L, epilogue_rows):
+        inp.v[:] = 0
+        for e in range(min(epilogue_rows, L - j0)):
+            inp.v[j0 + e, 0, e] = 1.0
+        out = gpu_forward(inp, "none")[:, 0, :]
+        w = min(epilogue_rows, L - j0)
+        got = out[:, :w] != 0
+        bad = np.argwhere(got != mask[:, j0:j0 + w])
+        assert bad.size == 0, f"window {j0}: {len(bad)} pairs differ, first (i, j) = " \
+                              f"{(int(bad[0][0]), j0 + int(bad[0][1]))}"
+        assert np.all(out[:, w:] == 0)
+
+
+def test_zero_pattern_windowed_sequence():
+    """A windowed sequence of 2600 tokens (window 1024, 50 candidates whose
+    window is clamped at the history end): every query tile, both window
+    edges, the candidate block and the split items of the static plan."""
+    print("case zero pattern windowed", flush=True)
+    inp = make_custom([2600], num_heads=1, d_qk=128, d_v=128, dtype="bf16", seed=41,
+                      num_targets=[50], max_attn_len=1024, pos_len=4096, pos_std=0.2,
+                      time_len=64, alpha=0.05)
+    _zero_pattern_windows(inp)
+
+
+def test_zero_pattern_longtail_sequence():
+    """A long causal sequence with a 6-token bidirectional prefix, long enough
+    that its last query tiles are split along the keys."""
+    print("case zero pattern longtail", flush=True)
+    inp = make_custom([3000], num_heads=1, d_qk=128, d_v=128, dtype="bf16", seed=42,
+                      contextual_len=6, pos_len=4096, pos_std=0.2, time_len=64, alpha=0.05)
+    _zero_pattern_windows(inp)
+
+
 def test_windowed_one_sequence_full():
     inp = make_inputs("windowed", num_seqs=1)
     assert_close(gpu_forward(inp), ora(inp), "bf16")
@@ -528,6 +580,13 @@ def test_layer_forward_full_size_sampled_rows():
     inp = make_inputs("layer")
     rows = _sample_rows(inp, 300, 9)
     assert_close(gpu_layer(inp), oracle.layer_forward(inp, rows=rows), "bf16", rows=rows)
+
+
+def test_layer_forward_full_size_whole_output():
+    """The full layer batch (64 sequences, hidden 512): every output row."""
+    print("case whole layer", flush=True)
+    inp = make_inputs("layer")
+    assert_close(gpu_layer(inp), oracle.layer_forward(inp), "bf16")
 
 
 # ---------------------------------------------------------------------------

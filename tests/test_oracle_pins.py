@@ -460,6 +460,129 @@ def test_layer_single_token_closed_form(oracle_mod):
     assert np.abs(y - want).max() < 1e-6 * np.abs(want).max()
 
 
+def _allowed_count(oracle_mod, inp, b, i):
+    """Allowed keys of row i of sequence b, counted with the rule predicate
+    (pinned by the hand-worked masks and the dense brute force)."""
+    L = int(inp.lengths[b])
+    t = 0 if inp.num_targets is None else int(inp.num_targets[b])
+    return sum(oracle_mod.allowed(L, t, inp.contextual_len, inp.max_attn_len, i, j)
+               for j in range(L))
+
+
+def _silu(z):
+    return z / (1.0 + np.exp(-z))
+
+
+def _ln_rows(a, eps):
+    mu = a.mean(axis=-1, keepdims=True)
+    return (a - mu) / np.sqrt(((a - mu) ** 2).mean(axis=-1, keepdims=True) + eps)
+
+
+@pytest.mark.parametrize("rules", [dict(num_targets=[3, 0, 5], contextual_len=2),
+                                   dict(num_targets=[2, 4, 0], max_attn_len=5)])
+def test_layer_constant_branches_closed_form(oracle_mod, rules):
+    """Zero projection weights and a different bias on every column make the
+    four branches per-head constant vectors, U = SiLU(b_U), V = SiLU(b_V),
+    Q = SiLU(b_Q), K = SiLU(b_K) (the split order U | V | Q | K, the bias and
+    SiLU on every column, "HSTU tensor by tensor": "Trace four projections").
+    With no bias tables every allowed score of head h is alpha <Q_h, K_h>, so
+    row i aggregates n_i SiLU(s_h) / n_scale V_h, n_i = its allowed keys; the
+    closed form needs no attention loop.  A wrong block order, a missing bias
+    or SiLU skipped on a block all change the result."""
+    H, d, D = 2, 16, 64
+    rng = np.random.default_rng(60)
+    inp = make_custom([9, 14, 6], num_heads=H, d_qk=d, d_v=d, seed=60, alpha=0.7,
+                      n_scale=11.0, **rules)
+    inp.pos_table = inp.time_table = inp.timestamps = None
+    N = inp.total_tokens
+    bias = rng.standard_normal(4 * H * d)
+    inp.layer = {"x": rng.standard_normal((N, D)), "w_uvqk": np.zeros((4 * H * d, D)),
+                 "b_uvqk": bias, "w_o": 0.3 * rng.standard_normal((D, H * d))}
+    y = oracle_mod.layer_forward(inp)
+
+    U, V, Q, K = (_silu(bias[k * H * d:(k + 1) * H * d]).reshape(H, d) for k in range(4))
+    s = inp.alpha * (Q * K).sum(-1)                        # [H]
+    eps = float(np.float32(inp.eps))
+    want = np.empty_like(y)
+    for b in range(inp.num_seqs):
+        s0 = int(inp.offsets[b])
+        for i in range(int(inp.lengths[b])):
+            c = _allowed_count(oracle_mod, inp, b, i) * _silu(s) / inp.n_scale   # [H]
+            gate = U * _ln_rows(c[:, None] * V, eps)        # [H, d]
+            want[s0 + i] = inp.layer["x"][s0 + i] + inp.layer["w_o"] @ gate.reshape(-1)
+    assert np.abs(y - want).max() <= 1e-12 * np.abs(want).max()
+    # the same closed form with the U and V blocks exchanged is far off
+    swapped = np.empty_like(y)
+    for b in range(inp.num_seqs):
+        s0 = int(inp.offsets[b])
+        for i in range(int(inp.lengths[b])):
+            c = _allowed_count(oracle_mod, inp, b, i) * _silu(s) / inp.n_scale
+            gate = V * _ln_rows(c[:, None] * U, eps)
+            swapped[s0 + i] = inp.layer["x"][s0 + i] + inp.layer["w_o"] @ gate.reshape(-1)
+    assert np.abs(y - swapped).max() > 1e-3 * np.abs(want).max()
+
+
+def test_layer_u_branch_reads_normalised_input(oracle_mod):
+    """Only the U block of the projection has weights; V, Q, K are constant
+    (biases), and W_o = [I; 0] copies the gated heads into the first H d
+    columns of y - x.  Then (y - x)[:, :Hd] = SiLU(LN(x) W_U^T + b_U) * g_i with
+    g_i the closed-form normalised aggregate of the constant V, and LN(x) is
+    torch's layer_norm (no affine, eps from the inputs).  Rows scaled by 1e-3
+    have a variance below eps, so a wrong epsilon shows."""
+    torch = pytest.importorskip("torch")
+    H, d, D = 2, 16, 64
+    rng = np.random.default_rng(61)
+    inp = make_custom([7, 12], num_heads=H, d_qk=d, d_v=d, seed=61, alpha=0.4, n_scale=9.0,
+                      num_targets=[2, 3])
+    inp.pos_table = inp.time_table = inp.timestamps = None
+    N, Hd = inp.total_tokens, H * d
+    x = rng.standard_normal((N, D))
+    x[::3] *= 1e-3
+    w = np.zeros((4 * Hd, D))
+    w[:Hd] = 0.5 * rng.standard_normal((Hd, D))
+    bias = rng.standard_normal(4 * Hd)
+    w_o = np.zeros((D, Hd))
+    w_o[:Hd, :Hd] = np.eye(Hd)
+    inp.layer = {"x": x, "w_uvqk": w, "b_uvqk": bias, "w_o": w_o}
+    y = oracle_mod.layer_forward(inp)
+
+    eps = float(np.float32(inp.eps))
+    xn = torch.nn.functional.layer_norm(torch.from_numpy(x), (D,), eps=eps).numpy()
+    U = _silu(xn @ w[:Hd].T + bias[:Hd]).reshape(N, H, d)
+    V, Q, K = (_silu(bias[k * Hd:(k + 1) * Hd]).reshape(H, d) for k in (1, 2, 3))
+    s = inp.alpha * (Q * K).sum(-1)
+    got = (y - x)[:, :Hd].reshape(N, H, d)
+    assert np.all((y - x)[:, Hd:] == 0)
+    for b in range(inp.num_seqs):
+        s0 = int(inp.offsets[b])
+        for i in range(int(inp.lengths[b])):
+            c = _allowed_count(oracle_mod, inp, b, i) * _silu(s) / inp.n_scale
+            want = U[s0 + i] * _ln_rows(c[:, None] * V, eps)
+            assert np.abs(got[s0 + i] - want).max() <= 1e-12 * max(np.abs(want).max(), 1e-300)
+
+
+def test_layer_head_relabelling_invariance(oracle_mod):
+    """Heads are independent and each is a contiguous d-wide slice of every
+    branch block: relabelling the heads the same way in all four blocks of the
+    projection and in the columns of W_o leaves the layer output unchanged."""
+    inp = _small_layer(62, [11, 25, 4], targets=[3, 5, 0])
+    H, d = inp.num_heads, inp.d_v
+    y = oracle_mod.layer_forward(inp)
+    perm = np.array([1, 0])
+    L = inp.layer
+    rows = np.concatenate([blk * H * d + (perm[h] * d + np.arange(d))
+                           for blk in range(4) for h in range(H)])
+    cols = np.concatenate([perm[h] * d + np.arange(d) for h in range(H)])
+    inp2 = dataclasses.replace(inp, layer={"x": L["x"], "w_uvqk": L["w_uvqk"][rows],
+                                           "b_uvqk": L["b_uvqk"][rows],
+                                           "w_o": L["w_o"][:, cols]})
+    y2 = oracle_mod.layer_forward(inp2)
+    assert np.abs(y - y2).max() <= 1e-12 * np.abs(y).max()
+    # relabelling only the projection (not W_o) does change it
+    inp3 = dataclasses.replace(inp2, layer=dict(inp2.layer, w_o=L["w_o"]))
+    assert np.abs(y - oracle_mod.layer_forward(inp3)).max() > 1e-6 * np.abs(y).max()
+
+
 def test_layer_rows_subset(oracle_mod):
     inp = _small_layer(52, [30, 9, 40], targets=[3, 0, 5])
     full = oracle_mod.layer_forward(inp)
