@@ -125,10 +125,12 @@ int hstu_jagged_attn_supported(int32_t dtype, int32_t d_qk, int32_t d_v);
 
 /*
  * Workspace bytes the call needs for `desc`: the scheduler's work list, the
- * arrival counters and the fp32 partial outputs of items split along keys.
- * Depends on num_seqs, total_tokens, num_heads and d_v only (no device
- * query).  Returns 0 and sets
- * the error message if desc is invalid.
+ * arrival counters and the fp32 partial outputs of items split along keys
+ * (2 x 1024 slots of 128 x d_v floats, reserved only when total_tokens >=
+ * 481, the shortest sequence in which an item can reach the 16 key tiles the
+ * scheduler splits).  Depends on num_seqs, total_tokens, num_heads and d_v
+ * only (no device query).  Returns 0 and sets the error message if desc is
+ * invalid.
  */
 size_t hstu_jagged_attn_workspace_bytes(const hstu_attn_desc* desc);
 

@@ -27,6 +27,14 @@ size_t elem_size(int32_t dtype) { return dtype == HSTU_DTYPE_BF16 ? 2 : 4; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Work-list layout of a forward call.  Partial-output slots are reserved
+// only when an item of the batch can be split along its keys (some sequence
+// may reach kMinSplitTokens) and the call allows splitting.
+hstu::PlanLayout fwd_layout(const hstu_attn_desc* d, bool no_split = false) {
+  const bool splits = !no_split && (int64_t)d->total_tokens >= hstu::kMinSplitTokens;
+  return hstu::plan_layout(d->num_seqs, d->total_tokens, d->num_heads, d->d_v, splits);
+}
+
 int check_desc(const hstu_attn_desc* d) {
   if (!d) return fail(HSTU_ERR_INVALID_ARG, "desc is NULL");
   if (d->num_seqs < 0) return fail(HSTU_ERR_INVALID_ARG, "num_seqs < 0 (%d)", d->num_seqs);
@@ -74,18 +82,19 @@ int check_desc(const hstu_attn_desc* d) {
       return fail(HSTU_ERR_INVALID_ARG, "%s * element size must be a multiple of 16 bytes",
                   x.name);
   }
-  const hstu::PlanLayout pl = hstu::plan_layout(d->num_seqs, d->total_tokens, H, d->d_v);
+  const hstu::PlanLayout pl = fwd_layout(d);
   if (2 * pl.units_max > 0x7fffffffLL || (int64_t)d->num_seqs * H > 0x7fffffffLL)
     return fail(HSTU_ERR_UNSUPPORTED, "too many work items (%lld)", (long long)pl.items_max);
   return HSTU_OK;
 }
 
 int check_plan_args(const hstu_attn_desc* d, const int32_t* offsets, int32_t contextual_len,
-                    int32_t max_attn_len, const void* ws, size_t ws_bytes) {
+                    int32_t max_attn_len, const void* ws, size_t ws_bytes,
+                    bool no_split = false) {
   if (d->num_seqs > 0 && !offsets) return fail(HSTU_ERR_INVALID_ARG, "offsets is NULL");
   if (contextual_len < 0) return fail(HSTU_ERR_INVALID_ARG, "contextual_len < 0");
   if (max_attn_len < 0) return fail(HSTU_ERR_INVALID_ARG, "max_attn_len < 0");
-  const size_t need = hstu::plan_layout(d->num_seqs, d->total_tokens, d->num_heads, d->d_v).total;
+  const size_t need = fwd_layout(d, no_split).total;
   if (!ws) return fail(HSTU_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", need);
   if (ws_bytes < need)
     return fail(HSTU_ERR_WORKSPACE, "workspace has %zu bytes, need %zu", ws_bytes, need);
@@ -179,8 +188,8 @@ struct PlanPtrs {
   int64_t slot_floats;
 };
 
-PlanPtrs plan_ptrs(const hstu_attn_desc* d, void* ws) {
-  const hstu::PlanLayout pl = hstu::plan_layout(d->num_seqs, d->total_tokens, d->num_heads, d->d_v);
+PlanPtrs plan_ptrs(const hstu_attn_desc* d, void* ws, bool no_split = false) {
+  const hstu::PlanLayout pl = fwd_layout(d, no_split);
   char* base = static_cast<char*>(ws);
   PlanPtrs p;
   p.hdr = reinterpret_cast<int32_t*>(base + pl.hdr_off);
@@ -204,19 +213,21 @@ int hstu_jagged_attn_supported(int32_t dtype, int32_t d_qk, int32_t d_v) {
 
 size_t hstu_jagged_attn_workspace_bytes(const hstu_attn_desc* desc) {
   if (check_desc(desc) != HSTU_OK) return 0;
-  return hstu::plan_layout(desc->num_seqs, desc->total_tokens, desc->num_heads, desc->d_v).total;
+  return fwd_layout(desc).total;
 }
 
 static int plan_impl(const hstu_attn_desc* desc, const int32_t* offsets,
                      const int32_t* num_targets, int32_t contextual_len, int32_t max_attn_len,
-                     void* workspace, size_t workspace_bytes, void* stream, bool cand_only) {
+                     void* workspace, size_t workspace_bytes, void* stream, bool cand_only,
+                     bool no_split = false) {
   int rc = check_desc(desc);
   if (rc != HSTU_OK) return rc;
-  rc = check_plan_args(desc, offsets, contextual_len, max_attn_len, workspace, workspace_bytes);
+  rc = check_plan_args(desc, offsets, contextual_len, max_attn_len, workspace, workspace_bytes,
+                       no_split);
   if (rc != HSTU_OK) return rc;
   if (desc->num_seqs == 0 || desc->total_tokens == 0) return HSTU_OK;
-  const hstu::PlanLayout pl = hstu::plan_layout(desc->num_seqs, desc->total_tokens, desc->num_heads, desc->d_v);
-  const PlanPtrs pp = plan_ptrs(desc, workspace);
+  const hstu::PlanLayout pl = fwd_layout(desc, no_split);
+  const PlanPtrs pp = plan_ptrs(desc, workspace, no_split);
   const int n_wg = persistent_grid(desc);
   if (n_wg <= 0) return fail(HSTU_ERR_HIP, "cannot query the device for the launch size");
   hstu::PlanArgs a;
@@ -229,6 +240,7 @@ static int plan_impl(const hstu_attn_desc* desc, const int32_t* offsets,
   a.items_max = (int32_t)pl.items_max;
   a.n_wg = n_wg;
   a.cand_only = cand_only ? 1 : 0;
+  a.no_split = pl.slots_max == 0 ? 1 : 0;
   a.hdr = pp.hdr;
   a.units = pp.units;
   a.wg = pp.wg;
@@ -264,10 +276,11 @@ static int run_impl(const hstu_attn_desc* desc, const void* q, const void* k, co
                     float alpha, float n_scale, const float* pos_table,
                     const float* time_table, void* out, void* o_raw, void* workspace,
                     size_t workspace_bytes, void* stream, void* t_start = nullptr,
-                    void* t_stop = nullptr) {
+                    void* t_stop = nullptr, bool no_split = false) {
   int rc = check_desc(desc);
   if (rc != HSTU_OK) return rc;
-  rc = check_plan_args(desc, offsets, contextual_len, max_attn_len, workspace, workspace_bytes);
+  rc = check_plan_args(desc, offsets, contextual_len, max_attn_len, workspace, workspace_bytes,
+                       no_split);
   if (rc != HSTU_OK) return rc;
   if (desc->num_seqs == 0 || desc->total_tokens == 0) return HSTU_OK;
   rc = check_run_args(desc, q, k, v, u, timestamps, alpha, n_scale, pos_table, time_table, out);
@@ -275,7 +288,7 @@ static int run_impl(const hstu_attn_desc* desc, const void* q, const void* k, co
 
   const int n_wg = persistent_grid(desc);
   if (n_wg <= 0) return fail(HSTU_ERR_HIP, "cannot query the device for the launch size");
-  const PlanPtrs pp = plan_ptrs(desc, workspace);
+  const PlanPtrs pp = plan_ptrs(desc, workspace, no_split);
   hstu::AttnArgs a;
   a.q = q;
   a.k = k;
@@ -516,8 +529,8 @@ LayerLayout layer_layout(const hstu_layer_desc* d) {
   l.uvqk_off = hstu::align256(l.xn_off + (size_t)N * d->hidden * 2);
   l.attn_off = hstu::align256(l.uvqk_off + (size_t)N * l.uvqk_w * 2);
   l.attn_ws_off = hstu::align256(l.attn_off + (size_t)N * H * d->d_v * 2);
-  l.total = l.attn_ws_off +
-            hstu::plan_layout(d->num_seqs, d->total_tokens, d->num_heads, d->d_v).total;
+  const hstu_attn_desc a_desc = layer_attn_desc(d);
+  l.total = l.attn_ws_off + fwd_layout(&a_desc).total;
   return l;
 }
 
@@ -650,7 +663,7 @@ BwdLayout bwd_layout(const hstu_attn_desc* d) {
   const size_t es = elem_size(d->dtype);
   const size_t rows = (size_t)(N * H * d->d_v) * es;
   const int64_t G = hstu::bwd_groups_max(d->num_seqs, N);
-  size_t off = l.gate ? hstu::plan_layout(d->num_seqs, N, H, d->d_v).total : 0;
+  size_t off = l.gate ? fwd_layout(d).total : 0;
   l.o_off = hstu::align256(off);
   off = l.o_off + (l.gate ? rows : 0);
   l.do_off = hstu::align256(off);

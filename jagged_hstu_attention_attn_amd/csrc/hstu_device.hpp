@@ -140,13 +140,21 @@ __host__ inline bool plan_is_compact(int64_t items_max, int64_t total_tokens) {
   return items_max <= kPlanLdsItems && total_tokens < (int64_t(1) << 21);
 }
 
+// The scheduler splits only items of at least 2 kMinChunk key tiles, which
+// needs a sequence of at least this many tokens: a batch with fewer tokens in
+// all never uses the partial-output slots.
+constexpr int64_t kMinSplitTokens = (2 * kMinChunk - 1) * kBN + 1;
+
+// Work-list layout.  `splits`: the plan may split items along their keys
+// (then it holds 2 kMaxGrid partial-output slots); without, it keeps every
+// item whole and holds none.
 __host__ inline PlanLayout plan_layout(int64_t num_seqs, int64_t total_tokens, int64_t heads,
-                                       int64_t d_v) {
+                                       int64_t d_v, bool splits) {
   PlanLayout p;
   // sum_b ceil(L_b / BM) <= (N + B*(BM-1)) / BM
   p.items_max = (total_tokens + num_seqs * (kBM - 1)) / kBM * heads;
   p.units_max = p.items_max + kMaxGrid;
-  p.slots_max = 2 * kMaxGrid;
+  p.slots_max = splits ? 2 * kMaxGrid : 0;
   p.slot_floats = (int64_t)kBM * 32 * ((d_v + 31) / 32);
   const size_t im = (size_t)(p.items_max > 0 ? p.items_max : 1);
   const bool big_b = num_seqs > kPlanLdsSeqs, big_i = !plan_is_compact(p.items_max, total_tokens);
@@ -172,6 +180,7 @@ struct PlanArgs {
   int32_t items_max;     // capacity of the item scratch
   int32_t n_wg;          // workgroups of the attention launch (<= kMaxGrid)
   int32_t cand_only;     // 1: only the candidate rows [n_h, L), tiled from n_h
+  int32_t no_split;      // 1: keep every item whole (no partial-output slots)
   int32_t* hdr;
   int4* units;
   int32_t* wg;

@@ -85,8 +85,8 @@ __device__ inline V block_excl_scan(V x, V* ws, V& total) {
 }
 
 // Chunks of an item spanning cost units [P, P + cost) of a line cut into
-// shares of T units.  An item under 2 * kMinChunk tiles stays whole and goes
-// to the share holding its midpoint.  Otherwise each multiple rT strictly
+// shares of T units.  An item under 2 * kMinChunk tiles (or any item when
+// splitting is off) stays whole and goes to the share holding its midpoint.  Otherwise each multiple rT strictly
 // inside the span is a candidate cut at tile offset
 // t = floor((rT - P) * tiles / cost).  A cut that would
 // close a chunk of fewer than kMinChunk tiles instead hands the open chunk to
@@ -95,9 +95,9 @@ __device__ inline V block_excl_scan(V x, V* ws, V& total) {
 // to share r.  Owners never decrease along the line.  Returns the number of
 // chunks.
 template <typename I, typename F>
-__device__ inline int item_chunks(I P, int cost, int tiles, I T, F&& f) {
+__device__ inline int item_chunks(I P, int cost, int tiles, I T, bool may_split, F&& f) {
   using U = typename std::make_unsigned<I>::type;   // products stay below 2^(bits of I)
-  if (tiles < 2 * kMinChunk) {   // never split: the share holding its midpoint takes it
+  if (!may_split || tiles < 2 * kMinChunk) {   // whole: the share holding its midpoint takes it
     f(0, 0, tiles, (int)((P + cost / 2) / T));
     return 1;
   }
@@ -360,7 +360,8 @@ __global__ __launch_bounds__(kPlanThreads) void hstu_plan_kernel(PlanArgs a) {
     I packed = 0;
     if (j < n) {
       const int c = cost[j];
-      const int nc = item_chunks(line[j], c, c - kCostOverhead, T, [](int, int, int, int) {});
+      const int nc = item_chunks(line[j], c, c - kCostOverhead, T, a.no_split == 0,
+                                 [](int, int, int, int) {});
       packed = (I)nc | ((I)(nc > 1 ? nc : 0) << kShift);
     }
     I tot;
@@ -388,7 +389,8 @@ __global__ __launch_bounds__(kPlanThreads) void hstu_plan_kernel(PlanArgs a) {
     const int4 it = make_int4(start[b], slen[b], hist[b], qh);
     const int u0 = (int)(ub[j] & kLow), slot0 = (int)(ub[j] >> kShift);
     const int nc = (int)(ub[j + 1] & kLow) - u0;
-    item_chunks(line[j], cost[j], cost[j] - kCostOverhead, T, [&](int c, int tb, int te, int r) {
+    item_chunks(line[j], cost[j], cost[j] - kCostOverhead, T, a.no_split == 0,
+                [&](int c, int tb, int te, int r) {
       a.units[2 * (u0 + c)] = it;
       a.units[2 * (u0 + c) + 1] = make_int4(kt_lo + tb, kt_lo + te - 1, nc > 1 ? slot0 : -1,
                                             (cand ? kUnitCandRows : 0) | (c << 16) | nc);

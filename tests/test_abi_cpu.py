@@ -310,3 +310,14 @@ def test_forward_kernel_choice(lib):
         assert lib.hstu_jagged_attn_fwd_kernel_of(ctypes.byref(_desc(num_heads=0))) == -1
     finally:
         lib.hstu_jagged_attn_set_fwd_kernel(_lib.HSTU_FWD_KERNEL_AUTO)
+
+
+def test_workspace_holds_partials_only_when_items_can_split(lib):
+    """The scheduler splits only items of 16 or more key tiles, which needs a
+    sequence of at least 481 tokens: smaller batches get a workspace without
+    the fp32 partial-output slots (2 x 1024 slots of 128 x d_v floats)."""
+    small = lib.hstu_jagged_attn_workspace_bytes(ctypes.byref(_desc(num_seqs=2, total_tokens=480)))
+    big = lib.hstu_jagged_attn_workspace_bytes(ctypes.byref(_desc(num_seqs=2, total_tokens=481)))
+    slots = 2 * 1024 * 128 * 128 * 4
+    assert 0 < small < 1 << 20
+    assert big - small >= slots
