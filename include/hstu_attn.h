@@ -234,6 +234,29 @@ int hstu_jagged_attn_fwd_candidates(const hstu_attn_desc* desc,
                                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * hstu_jagged_attn_fwd without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The same forward (scheduler +
+ * attention, same arguments, errors and tolerance; items are never split
+ * along their keys, so the output may differ from hstu_jagged_attn_fwd's in
+ * the last bits), with the work list in an 8 MiB array of the library that
+ * each GPU it runs on holds from module load until the process ends.  It
+ * calls no allocator: the array's device address is looked up once per
+ * device on the first call there.  Batches whose work list exceeds the array
+ * (about 250,000 work items) return HSTU_ERR_WORKSPACE with a message naming
+ * both sizes.  Every call on one GPU uses the same array and each call
+ * rewrites all of it that the call reads: calls that overlap on one GPU
+ * (other streams, other threads) race; order them.
+ */
+int hstu_jagged_attn_fwd_noalloc(const hstu_attn_desc* desc,
+                                 const void* q, const void* k, const void* v, const void* u,
+                                 const int32_t* offsets, const int64_t* timestamps,
+                                 const int32_t* num_targets, int32_t contextual_len,
+                                 int32_t max_attn_len, float alpha, float n_scale,
+                                 const float* pos_table, const float* time_table, void* out,
+                                 void* stream);
+
+/*
  * Host helper for throughput accounting: the exact number of allowed (i, j)
  * pairs of the batch, per head, from HOST copies of offsets and num_targets
  * (num_targets may be NULL).  Returns -1 and sets the message on bad input.

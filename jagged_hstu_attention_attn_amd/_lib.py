@@ -36,6 +36,7 @@ EXPORTS = (
     "hstu_jagged_attn_run_timed",
     "hstu_jagged_attn_plan_candidates",
     "hstu_jagged_attn_fwd_candidates",
+    "hstu_jagged_attn_fwd_noalloc",
     "hstu_layer_workspace_bytes",
     "hstu_layer_fwd",
     "hstu_jagged_attn_valid_pairs",
@@ -131,6 +132,9 @@ def load() -> ctypes.CDLL:
     lib.hstu_jagged_attn_valid_pairs.argtypes = [i32, P, P, i32, i32]
     lib.hstu_jagged_attn_grid.restype = ctypes.c_int
     lib.hstu_jagged_attn_grid.argtypes = [D]
+    lib.hstu_jagged_attn_fwd_noalloc.restype = ctypes.c_int
+    lib.hstu_jagged_attn_fwd_noalloc.argtypes = [D, P, P, P, P, P, P, P, i32, i32, f32, f32, P,
+                                                 P, P, P]
     lib.hstu_jagged_attn_set_fwd_kernel.restype = ctypes.c_int
     lib.hstu_jagged_attn_set_fwd_kernel.argtypes = [i32]
     lib.hstu_jagged_attn_fwd_kernel_of.restype = ctypes.c_int

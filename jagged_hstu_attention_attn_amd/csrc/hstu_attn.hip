@@ -4,6 +4,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstdarg>
+#include <mutex>
 #include <cstdio>
 #include <cstring>
 
@@ -446,6 +447,90 @@ int hstu_jagged_attn_fwd_candidates(const hstu_attn_desc* desc, const void* q, c
   return hstu_jagged_attn_run(desc, q, k, v, u, offsets, timestamps, num_targets, contextual_len,
                               max_attn_len, alpha, n_scale, pos_table, time_table, out,
                               workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+// ---- allocation-free forward ---------------------------------------------
+//
+// hstu_jagged_attn_fwd_noalloc keeps its work list in `scratch`, an array of
+// this file that every GPU the library runs on holds from module load until
+// the process ends.  Host code never passes the array's name to a kernel or a
+// copy (on the host it is only a stand-in for the symbol): its device address
+// is looked up once per device with hipGetSymbolAddress, with that device
+// current, and that address is what the scheduler and attention kernels take.
+// The call plans without key splits, so the array holds the unit list, the
+// per-workgroup shares and, for large batches, the scheduler's per-sequence
+// and per-item scratch -- never partial outputs.
+namespace {
+
+constexpr size_t kScratchBytes = size_t(8) << 20;   // 8 MiB per device
+constexpr int kScratchDevices = 64;
+
+}  // namespace
+
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevices] = {};
+
+// Device address of `scratch` on the current device, looked up on the first
+// call on that device; a negative status (message set) on failure.
+int scratch_on_current_device(void** out) {
+  int dev = 0;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(HSTU_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kScratchDevices)
+    return fail(HSTU_ERR_UNSUPPORTED, "device %d is beyond the %d the allocation-free call serves",
+                dev, kScratchDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    const hipError_t r = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (r != hipSuccess || ptr == nullptr)
+      return fail(HSTU_ERR_HIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+                  hipGetErrorString(r));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return HSTU_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int hstu_jagged_attn_fwd_noalloc(const hstu_attn_desc* desc, const void* q, const void* k,
+                                 const void* v, const void* u, const int32_t* offsets,
+                                 const int64_t* timestamps, const int32_t* num_targets,
+                                 int32_t contextual_len, int32_t max_attn_len, float alpha,
+                                 float n_scale, const float* pos_table,
+                                 const float* time_table, void* out, void* stream) {
+  int rc = check_desc(desc);
+  if (rc != HSTU_OK) return rc;
+  if (desc->num_seqs > 0 && !offsets) return fail(HSTU_ERR_INVALID_ARG, "offsets is NULL");
+  if (contextual_len < 0) return fail(HSTU_ERR_INVALID_ARG, "contextual_len < 0");
+  if (max_attn_len < 0) return fail(HSTU_ERR_INVALID_ARG, "max_attn_len < 0");
+  const size_t need = fwd_layout(desc, true).total;
+  if (need > kScratchBytes)
+    return fail(HSTU_ERR_WORKSPACE,
+                "the batch needs %zu bytes of work list; the allocation-free call holds %zu "
+                "(use hstu_jagged_attn_fwd with a caller workspace)",
+                need, kScratchBytes);
+  if (desc->num_seqs == 0 || desc->total_tokens == 0) return HSTU_OK;
+  rc = check_run_args(desc, q, k, v, u, timestamps, alpha, n_scale, pos_table, time_table, out);
+  if (rc != HSTU_OK) return rc;
+  void* ws = nullptr;
+  rc = scratch_on_current_device(&ws);
+  if (rc != HSTU_OK) return rc;
+  rc = plan_impl(desc, offsets, num_targets, contextual_len, max_attn_len, ws, kScratchBytes,
+                 stream, false, true);
+  if (rc != HSTU_OK) return rc;
+  return run_impl(desc, q, k, v, u, offsets, timestamps, num_targets, contextual_len,
+                  max_attn_len, alpha, n_scale, pos_table, time_table, out, nullptr, ws,
+                  kScratchBytes, stream, nullptr, nullptr, true);
 }
 
 int64_t hstu_jagged_attn_valid_pairs(int32_t num_seqs, const int32_t* offsets_host,
