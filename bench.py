@@ -321,7 +321,8 @@ def main() -> int:
                     help="time the backward (gradients of q, k, v, u and the bias tables)")
     ap.add_argument("--saved-o", action="store_true",
                     help="with --backward: take o / n_scale kept by the training forward")
-    ap.add_argument("--fwd-kernel", default="auto", choices=["auto", "four_wave", "eight_wave"],
+    ap.add_argument("--fwd-kernel", default="auto",
+                    choices=["auto", "four_wave", "eight_wave", "sixteen_row"],
                     help="forward kernel: chosen by batch shape (auto), or forced")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 256 MiB device copy (counter calibration)")
@@ -474,8 +475,9 @@ def measure_forward(args, inp, workload: str, steps: int, warmup: int) -> dict:
         "runs of bench.py, scaled by the copy calibration, taken on the current kernel source"
         if traffic is not None else
         "null: no counter summary taken on the current kernel source")
-    roof["kernel"] = ("hstu_attn_fwd_pp_kernel" if call.kernel_name() == "eight_wave"
-                      else "hstu_attn_fwd_kernel")
+    roof["kernel"] = {"eight_wave": "hstu_attn_fwd_pp_kernel",
+                      "sixteen_row": "hstu_attn_fwd_w16_kernel"}.get(call.kernel_name(),
+                                                                     "hstu_attn_fwd_kernel")
     roof["kernel_us"] = attn * 1e3
     roof["kernel_timing"] = ("HIP events taken at the kernel's own start and end, over a "
                              "second pass of the same steps")

@@ -289,7 +289,12 @@ int hstu_jagged_attn_grid(const hstu_attn_desc* desc);
  * hstu_jagged_attn_fwd_kernel_of returns the kernel `desc` would run
  * (FOUR_WAVE or EIGHT_WAVE), or -1 on a bad desc.
  */
-enum { HSTU_FWD_KERNEL_AUTO = 0, HSTU_FWD_KERNEL_FOUR_WAVE = 1, HSTU_FWD_KERNEL_EIGHT_WAVE = 2 };
+enum {
+  HSTU_FWD_KERNEL_AUTO = 0,
+  HSTU_FWD_KERNEL_FOUR_WAVE = 1,
+  HSTU_FWD_KERNEL_EIGHT_WAVE = 2,
+  HSTU_FWD_KERNEL_SIXTEEN_ROW = 3
+};
 int hstu_jagged_attn_set_fwd_kernel(int32_t mode);
 int hstu_jagged_attn_fwd_kernel_of(const hstu_attn_desc* desc);
 

@@ -25,6 +25,7 @@ HSTU_EPILOGUE_LN_ALL_U = 2
 HSTU_FWD_KERNEL_AUTO = 0
 HSTU_FWD_KERNEL_FOUR_WAVE = 1
 HSTU_FWD_KERNEL_EIGHT_WAVE = 2
+HSTU_FWD_KERNEL_SIXTEEN_ROW = 3
 
 # every function the header declares
 EXPORTS = (

@@ -127,18 +127,19 @@ int check_run_args(const hstu_attn_desc* d, const void* q, const void* k, const 
   return HSTU_OK;
 }
 
-// Which forward kernel runs: HSTU_FWD_KERNEL_AUTO picks the eight-wave
-// kernel for bf16 d = 128 batches whose mean sequence length is at least
-// kPPMinMeanLen tokens when kPPAuto is set, the four-wave kernel otherwise.
+// Which forward kernel runs: HSTU_FWD_KERNEL_AUTO takes the sixteen-row
+// kernel where it is built (bf16, d = 128) and the four-wave kernel
+// elsewhere; the eight-wave kernel runs only when chosen explicitly.
 std::atomic<int> g_fwd_kernel{HSTU_FWD_KERNEL_AUTO};
 
-bool use_pp(const hstu_attn_desc* d) {
-  if (!hstu::attn_pp_supported(d->dtype, d->d_qk, d->d_v)) return false;
+int fwd_kernel_choice(const hstu_attn_desc* d) {
   const int mode = g_fwd_kernel.load(std::memory_order_relaxed);
-  if (mode == HSTU_FWD_KERNEL_FOUR_WAVE) return false;
-  if (mode == HSTU_FWD_KERNEL_EIGHT_WAVE) return true;
-  return hstu::kPPAuto &&
-         (int64_t)d->total_tokens >= (int64_t)hstu::kPPMinMeanLen * d->num_seqs;
+  if (mode == HSTU_FWD_KERNEL_EIGHT_WAVE && hstu::attn_pp_supported(d->dtype, d->d_qk, d->d_v))
+    return HSTU_FWD_KERNEL_EIGHT_WAVE;
+  const bool w16 = hstu::attn_w16_supported(d->dtype, d->d_qk, d->d_v);
+  if (mode == HSTU_FWD_KERNEL_SIXTEEN_ROW && w16) return HSTU_FWD_KERNEL_SIXTEEN_ROW;
+  if (mode == HSTU_FWD_KERNEL_AUTO && w16 && hstu::kW16Auto) return HSTU_FWD_KERNEL_SIXTEEN_ROW;
+  return HSTU_FWD_KERNEL_FOUR_WAVE;
 }
 
 // Workgroups of the persistent attention launch: CUs x resident workgroups
@@ -146,7 +147,7 @@ bool use_pp(const hstu_attn_desc* d) {
 // kMaxGrid (the most a plan serves).  <= 0 on a HIP error.
 int persistent_grid(const hstu_attn_desc* d) {
   struct Entry {
-    int dev, dtype, d_qk, d_v, pos_len, has_time, clamp, pp, grid;
+    int dev, dtype, d_qk, d_v, pos_len, has_time, clamp, kern, grid;
   };
   static thread_local Entry cache[16];
   static thread_local int cache_n = 0;
@@ -154,24 +155,27 @@ int persistent_grid(const hstu_attn_desc* d) {
   if (hipGetDevice(&dev) != hipSuccess) return -1;
   const int has_time = d->time_table_len > 0;
   const int clamp = d->pos_clamp != 0 && d->pos_table_len > 0;
-  const int pp = use_pp(d) ? 1 : 0;
+  const int kern = fwd_kernel_choice(d);
   int g = -1;
   for (int i = 0; i < cache_n && i < 16; ++i) {
     const Entry& e = cache[i];
     if (e.dev == dev && e.dtype == d->dtype && e.d_qk == d->d_qk && e.d_v == d->d_v &&
         e.pos_len == d->pos_table_len && e.has_time == has_time && e.clamp == clamp &&
-        e.pp == pp) {
+        e.kern == kern) {
       g = e.grid;
       break;
     }
   }
   if (g < 0) {
-    g = pp ? hstu::attn_pp_grid(d->pos_table_len, d->time_table_len, clamp != 0)
-           : hstu::attn_grid(d->dtype, d->d_qk, d->d_v, d->pos_table_len, d->time_table_len,
-                             clamp != 0);
+    g = kern == HSTU_FWD_KERNEL_EIGHT_WAVE
+            ? hstu::attn_pp_grid(d->pos_table_len, d->time_table_len, clamp != 0)
+        : kern == HSTU_FWD_KERNEL_SIXTEEN_ROW
+            ? hstu::attn_w16_grid(d->pos_table_len, d->time_table_len, clamp != 0)
+            : hstu::attn_grid(d->dtype, d->d_qk, d->d_v, d->pos_table_len, d->time_table_len,
+                              clamp != 0);
     if (g <= 0) return g;
     cache[cache_n % 16] =
-        Entry{dev, d->dtype, d->d_qk, d->d_v, d->pos_table_len, has_time, clamp, pp, g};
+        Entry{dev, d->dtype, d->d_qk, d->d_v, d->pos_table_len, has_time, clamp, kern, g};
     ++cache_n;
   }
   // at least one workgroup per XCD, at most what a plan serves
@@ -327,14 +331,13 @@ static int run_impl(const hstu_attn_desc* desc, const void* q, const void* k, co
   a.alpha = alpha;
   a.out_scale = (float)(0.69314718055994530942 / (double)n_scale);
   a.ln_eps = desc->ln_eps;
+  const int kern = fwd_kernel_choice(desc);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipEvent_t e0 = static_cast<hipEvent_t>(t_start), e1 = static_cast<hipEvent_t>(t_stop);
   const hipError_t e =
-      use_pp(desc) ? hstu::launch_attn_pp(a, n_wg, static_cast<hipStream_t>(stream),
-                                          static_cast<hipEvent_t>(t_start),
-                                          static_cast<hipEvent_t>(t_stop))
-                   : hstu::launch_attn(a, desc->dtype, desc->d_qk, desc->d_v, n_wg,
-                                       static_cast<hipStream_t>(stream),
-                                       static_cast<hipEvent_t>(t_start),
-                                       static_cast<hipEvent_t>(t_stop));
+      kern == HSTU_FWD_KERNEL_EIGHT_WAVE    ? hstu::launch_attn_pp(a, n_wg, st, e0, e1)
+      : kern == HSTU_FWD_KERNEL_SIXTEEN_ROW ? hstu::launch_attn_w16(a, n_wg, st, e0, e1)
+          : hstu::launch_attn(a, desc->dtype, desc->d_qk, desc->d_v, n_wg, st, e0, e1);
   if (e != hipSuccess)
     return fail(HSTU_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
   if (ln_all) {
@@ -556,7 +559,7 @@ int64_t hstu_jagged_attn_valid_pairs(int32_t num_seqs, const int32_t* offsets_ho
 
 int hstu_jagged_attn_set_fwd_kernel(int32_t mode) {
   if (mode != HSTU_FWD_KERNEL_AUTO && mode != HSTU_FWD_KERNEL_FOUR_WAVE &&
-      mode != HSTU_FWD_KERNEL_EIGHT_WAVE)
+      mode != HSTU_FWD_KERNEL_EIGHT_WAVE && mode != HSTU_FWD_KERNEL_SIXTEEN_ROW)
     return fail(HSTU_ERR_INVALID_ARG, "unknown forward kernel mode %d", mode);
   g_fwd_kernel.store(mode, std::memory_order_relaxed);
   return HSTU_OK;
@@ -564,7 +567,7 @@ int hstu_jagged_attn_set_fwd_kernel(int32_t mode) {
 
 int hstu_jagged_attn_fwd_kernel_of(const hstu_attn_desc* desc) {
   if (check_desc(desc) != HSTU_OK) return -1;
-  return use_pp(desc) ? HSTU_FWD_KERNEL_EIGHT_WAVE : HSTU_FWD_KERNEL_FOUR_WAVE;
+  return fwd_kernel_choice(desc);
 }
 
 int hstu_jagged_attn_grid(const hstu_attn_desc* desc) {

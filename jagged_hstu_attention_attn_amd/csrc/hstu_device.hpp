@@ -348,6 +348,13 @@ bool attn_pp_supported(int dtype, int d_qk, int d_v);
 int attn_pp_grid(int pos_len, int time_len, bool clamp);
 hipError_t launch_attn_pp(const AttnArgs& a, int n_wg, hipStream_t stream,
                           hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
+// The sixteen-row forward (attn_fwd_w16.hip): bf16, d_qk = d_v = 128; eight
+// waves of 16 query rows per workgroup, four waves per SIMD; same units,
+// workspace and arguments as launch_attn.
+bool attn_w16_supported(int dtype, int d_qk, int d_v);
+int attn_w16_grid(int pos_len, int time_len, bool clamp);
+hipError_t launch_attn_w16(const AttnArgs& a, int n_wg, hipStream_t stream,
+                           hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 // Batches whose mean sequence length reaches this many tokens take the
 // eight-wave kernel (short sequences give it too few key blocks per item to
 // fill its pipeline; the four-wave kernel runs two workgroups per CU).
@@ -355,6 +362,8 @@ constexpr int kPPMinMeanLen = 512;
 // Whether the automatic choice may take the eight-wave kernel at all: off
 // while it measures slower than the four-wave kernel on the long batches.
 constexpr bool kPPAuto = false;
+// Whether the automatic choice takes the sixteen-row kernel where it is built.
+constexpr bool kW16Auto = false;
 int ln_all_heads_max_width(int dtype);
 hipError_t launch_ln_all_heads(const LnArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_bwd_plan(const BwdPlanArgs& a, hipStream_t stream);

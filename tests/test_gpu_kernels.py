@@ -1,11 +1,11 @@
-"""The eight-wave forward kernel against the fp64 oracle.
+"""The eight-wave and sixteen-row forward kernels against the fp64 oracle.
 
-Under the default choice the library runs the eight-wave kernel only for
-batches of long sequences (the long-tail and windowed workloads of
-test_gpu_parity.py take it); here it is forced on the small ragged batches of
-every mask rule, the tile-edge lengths, split items, candidate rows and the
-clamped-position bias, so that its geometry is checked where the four-wave
-kernel's is.  Tolerance: max|gpu - oracle| <= 1e-2 * max|oracle| (bf16).
+The library picks a forward kernel by shape (see the header); every test here
+forces each of the bf16 d = 128 kernels in turn on the small ragged batches of
+every mask rule, the tile-edge lengths, windows, split items, candidate rows,
+the clamped-position bias and the exact zero pattern, so that every kernel's
+geometry is checked where the four-wave kernel's is.  Tolerance:
+max|gpu - oracle| <= 1e-2 * max|oracle| (bf16).
 """
 import math
 
@@ -20,13 +20,25 @@ from jagged_hstu_attention_attn_amd.inputs import make_custom, make_inputs
 
 pytestmark = pytest.mark.gpu
 
+
+@pytest.fixture(params=["eight_wave", "sixteen_row"], autouse=True)
+def kernel(request):
+    """The forward kernel every call of the test is forced to."""
+    global _KERNEL
+    _KERNEL = request.param
+    yield request.param
+    _KERNEL = None
+
+
+_KERNEL = None
+
 DEV = "cuda:0"
 EDGE_LENGTHS = [0, 1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 257, 300]
 
 
-def _fwd(inp, epilogue="ln_u", kernel="eight_wave", ld=None, pos_clamp=False, out=None,
+def _fwd(inp, epilogue="ln_u", kernel=None, ld=None, pos_clamp=False, out=None,
          candidates_only=False):
-    with fwd_kernel(kernel):
+    with fwd_kernel(kernel or _KERNEL):
         dev = to_device(inp, DEV, ld=ld)
         o = jagged_attn_fwd(dev["q"], dev["k"], dev["v"], dev["u"], dev["offsets"],
                             epilogue=epilogue, pos_clamp=pos_clamp, out=out,
@@ -51,7 +63,7 @@ def _close(gpu, ref, rows=None, tol=1e-2):
 
 @pytest.mark.parametrize("rules", ["causal", "targets", "prefix", "window", "all"])
 def test_pp_edges(rules):
-    print(f"case pp_edges {rules}", flush=True)
+    print(f"case {_KERNEL} edges {rules}", flush=True)
     rng = np.random.default_rng(hash(rules) % 1000)
     lengths = list(EDGE_LENGTHS)
     B = len(lengths)
@@ -74,7 +86,7 @@ def test_pp_edges(rules):
 
 @pytest.mark.parametrize("W", [1, 31, 32, 33, 127, 128, 129, 1024])
 def test_pp_window_sizes(W):
-    print(f"case pp_window {W}", flush=True)
+    print(f"case {_KERNEL} window {W}", flush=True)
     inp = make_custom([1500, 129, 700], num_heads=1, d_qk=128, d_v=128, dtype="bf16", seed=W,
                       num_targets=[25, 3, 50], max_attn_len=W, pos_len=4096, time_len=64,
                       alpha=1 / math.sqrt(128))
@@ -82,7 +94,7 @@ def test_pp_window_sizes(W):
 
 
 def test_pp_no_bias_tables_and_alpha_zero():
-    print("case pp_no_bias", flush=True)
+    print(f"case {_KERNEL} no_bias", flush=True)
     inp = make_custom([5, 300, 77, 640], num_heads=3, d_qk=128, d_v=128, dtype="bf16", seed=2,
                       alpha=0.2)
     _close(_fwd(inp), _ora(inp))
@@ -93,7 +105,7 @@ def test_pp_no_bias_tables_and_alpha_zero():
 
 def test_pp_wide_timestamp_span():
     """Spans past 2^30 s: the 64-bit time-bucket path."""
-    print("case pp_wide_ts", flush=True)
+    print(f"case {_KERNEL} wide_ts", flush=True)
     inp = make_custom([450, 40], num_heads=2, d_qk=128, d_v=128, dtype="bf16", seed=9,
                       time_len=64, time_std=0.5, pos_len=64, alpha=0.3)
     rng = np.random.default_rng(1)
@@ -108,7 +120,7 @@ def test_pp_wide_timestamp_span():
 
 
 def test_pp_unsorted_timestamps():
-    print("case pp_unsorted_ts", flush=True)
+    print(f"case {_KERNEL} unsorted_ts", flush=True)
     inp = make_custom([390, 33], num_heads=1, d_qk=128, d_v=128, dtype="bf16", seed=4,
                       time_len=40, time_std=0.5, alpha=0.5 / math.sqrt(128))
     rng = np.random.default_rng(3)
@@ -119,13 +131,13 @@ def test_pp_unsorted_timestamps():
 
 @pytest.mark.parametrize("name,n", [("ranking", 40), ("longtail", 8), ("windowed", 1)])
 def test_pp_workloads(name, n):
-    print(f"case pp_workload {name} {n}", flush=True)
+    print(f"case {_KERNEL} workload {name} {n}", flush=True)
     inp = make_inputs(name, num_seqs=n)
     _close(_fwd(inp), _ora(inp))
 
 
 def test_pp_strided_views():
-    print("case pp_strided", flush=True)
+    print(f"case {_KERNEL} strided", flush=True)
     inp = make_inputs("layer", num_seqs=4)
     a = _fwd(inp, ld=2048)
     b = _fwd(inp)
@@ -136,10 +148,10 @@ def test_pp_strided_views():
 def test_pp_split_items_plan_reuse():
     """Long causal sequence: its last tiles are split along the keys; two runs
     of one plan and a fresh plan agree bitwise and with the oracle."""
-    print("case pp_split", flush=True)
+    print(f"case {_KERNEL} split", flush=True)
     inp = make_custom([4096, 700, 33], num_heads=2, d_qk=128, d_v=128, dtype="bf16", seed=8,
                       contextual_len=6, pos_len=4096, time_len=64, alpha=0.0884)
-    with fwd_kernel("eight_wave"):
+    with fwd_kernel(_KERNEL):
         dev = to_device(inp, DEV)
         call = JaggedAttnCall(dev["q"], dev["k"], dev["v"], dev["u"], dev["offsets"],
                               **call_kwargs(inp, dev))
@@ -155,7 +167,7 @@ def test_pp_split_items_plan_reuse():
 
 
 def test_pp_candidates_only():
-    print("case pp_candidates", flush=True)
+    print(f"case {_KERNEL} candidates", flush=True)
     inp = make_inputs("windowed", num_seqs=2)
     N, H, dv = inp.total_tokens, inp.num_heads, inp.d_v
     out = torch.full((N, H, dv), -5.0, dtype=torch.bfloat16, device=DEV)
@@ -172,7 +184,7 @@ def test_pp_candidates_only():
 
 @pytest.mark.parametrize("epilogue", ["ln_u", "none"])
 def test_pp_pos_clamp(epilogue):
-    print(f"case pp_pos_clamp {epilogue}", flush=True)
+    print(f"case {_KERNEL} pos_clamp {epilogue}", flush=True)
     inp = make_custom([1, 37, 129, 300, 260, 700], num_heads=2, d_qk=128, d_v=128,
                       dtype="bf16", seed=91, num_targets=[0, 5, 20, 50, 3, 40],
                       contextual_len=3, max_attn_len=100, pos_len=512, pos_std=0.3,
@@ -184,7 +196,7 @@ def test_pp_zero_pattern_exact():
     """One-hot V over keys [0, 128) and no epilogue: out[i, j] = a_ij, so the
     zeros of those columns are exactly the masked pairs, for rows spread over
     several query tiles and both key halves of the workgroup."""
-    print("case pp_zero_pattern", flush=True)
+    print(f"case {_KERNEL} zero_pattern", flush=True)
     lengths, nt, W = [700, 300], [40, 10], 90
     inp = make_custom(lengths, num_heads=1, d_qk=128, d_v=128, dtype="bf16", seed=5,
                       num_targets=nt, contextual_len=3, max_attn_len=W, pos_len=1024,
@@ -203,11 +215,11 @@ def test_pp_zero_pattern_exact():
 
 
 def test_pp_matches_four_wave():
-    """Both kernels on one long-tail batch: each within tolerance of the
-    oracle, and of each other."""
-    print("case pp_vs_four_wave", flush=True)
+    """The forced kernel and the four-wave kernel on one long-tail batch: each
+    within tolerance of the oracle, and of each other."""
+    print(f"case {_KERNEL} vs_four_wave", flush=True)
     inp = make_inputs("longtail", num_seqs=6, seed=3)
-    a = _fwd(inp, kernel="eight_wave")
+    a = _fwd(inp)
     b = _fwd(inp, kernel="four_wave")
     ref = _ora(inp)
     _close(a, ref)
