@@ -274,20 +274,23 @@ int64_t hstu_jagged_attn_valid_pairs(int32_t num_seqs, const int32_t* offsets_ho
 int hstu_jagged_attn_grid(const hstu_attn_desc* desc);
 
 /*
- * Forward kernel choice.  Two kernels compute the same forward over the same
- * work list and workspace: a four-wave kernel (two workgroups per CU) and,
- * for bf16 with d_qk = d_v = 128, an eight-wave kernel (one workgroup per CU)
- * whose two waves per SIMD alternate between matrix-core and vector work and
- * which splits each item's key tiles between its two groups of four waves.
- * AUTO (the default) takes the four-wave kernel (the eight-wave one is
- * selected explicitly; see the design notes for its measured standing).
- * The setting is process-wide; a plan and the runs that use it must see the
- * same setting (the launch size depends on it).  Both kernels meet the same
- * tolerance against the oracle; their outputs differ in the last bits
- * (different summation order).  hstu_jagged_attn_set_fwd_kernel returns
- * HSTU_OK, or HSTU_ERR_INVALID_ARG for an unknown mode.
- * hstu_jagged_attn_fwd_kernel_of returns the kernel `desc` would run
- * (FOUR_WAVE or EIGHT_WAVE), or -1 on a bad desc.
+ * Forward kernel choice.  Three kernels compute the same forward over the
+ * same work list and workspace: a four-wave kernel (32 query rows per wave,
+ * two workgroups per CU, every supported dtype and head size) and, for bf16
+ * with d_qk = d_v = 128, a sixteen-row kernel (16 query rows per wave, eight
+ * waves per workgroup, four waves per SIMD) and an eight-wave kernel (one
+ * workgroup per CU whose two waves per SIMD alternate between matrix-core
+ * and vector work).  AUTO (the default) takes the sixteen-row kernel where
+ * it is built and the four-wave kernel elsewhere; the eight-wave kernel runs
+ * only when chosen.  The setting is process-wide; a plan and the runs that
+ * use it must see the same setting (the launch size depends on it).  All
+ * kernels meet the same tolerance against the oracle; their outputs differ
+ * in the last bits (different summation order).
+ * hstu_jagged_attn_set_fwd_kernel returns HSTU_OK, or HSTU_ERR_INVALID_ARG
+ * for an unknown mode.  hstu_jagged_attn_fwd_kernel_of returns the kernel
+ * `desc` would run (FOUR_WAVE, EIGHT_WAVE or SIXTEEN_ROW), or -1 on a bad
+ * desc.  A mode whose kernel does not support `desc` falls back to the
+ * four-wave kernel.
  */
 enum {
   HSTU_FWD_KERNEL_AUTO = 0,

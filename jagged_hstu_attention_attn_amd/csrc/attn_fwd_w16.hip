@@ -111,8 +111,6 @@ hstu_attn_fwd_w16_kernel(AttnArgs a) {
   // (part w - 5), wave 4 the raw timestamps, wave 3 the clamped-position bias
   constexpr int kTsW = 4, kCposW = 3, kDiagW0 = 5;
   static_assert(kDiagW0 + kDiagCopies <= kW16Waves, "enough waves for the bias copies");
-  const int my_copies = 2 + ((POS && wave >= kDiagW0) ? 1 : 0) + ((TIME && wave == kTsW) ? 1 : 0) +
-                        ((clamp && wave == kCposW) ? 1 : 0);
 
   // Per-lane values are derived from an opaque lane index inside the loops
   // (the compiler cannot hoist them): recomputing costs a few vector
@@ -503,16 +501,16 @@ hstu_attn_fwd_w16_kernel(AttnArgs a) {
     w_tmin = wave_min(row_valid ? ti32 : 0xffffffffu);
     w_tmax = wave_max(row_valid ? ti32 : 0u);
   }
-  finish_stage(B0{}, kt_lo);   // stage kt_lo+1 is finished by the first step
+  finish_stage(B0{}, kt_lo);
+  if (kt_lo + 1 <= kt_hi) finish_stage(B1{}, kt_lo + 1);
   stage_barrier();             // also publishes the time tables; Q reads are done
-  if (kt_lo + 2 <= kt_hi) issue_stage(B2{}, kt_lo + 2);
 
   // Epilogue staging: the 16 rows of wave w in stage buffer
   // ((kt_hi - kt_lo) + 1 + w / 4) % 4 at 4 KB * (w % 4) -- a buffer that
   // neither the last block nor any copy in flight touches.
   const bool ln_ep = a.epilogue == 0;
   auto ep_lds = [&]() __attribute__((always_inline)) -> uint32_t {
-    const int b_ep = ((kt_hi - kt_lo) + 1 + (wave >> 2)) & (kW16Stages - 1);
+    const int b_ep = (((kt_hi - kt_lo) & ~1) + 2 + (wave >> 2)) & (kW16Stages - 1);
     return (b_ep == 0 ? lds_off(st0.k) : b_ep == 1 ? lds_off(st1.k) : b_ep == 2 ? lds_off(st2.k)
                                                                                : lds_off(st3.k)) +
            (uint32_t)((wave & 3) * kW16Rows * ROWB);
@@ -535,32 +533,32 @@ hstu_attn_fwd_w16_kernel(AttnArgs a) {
     }
   };
 
-  // One pipeline step on key block kt held in buffer `bufc`: copy block kt+3
-  // into the buffer freed by the previous barrier, compute block kt, then
-  // (own copies of block kt+1 landed) finish block kt+1 and synchronise.
+  // One pipeline step on the key blocks kt, kt + 1 held in buffers `bufc`,
+  // `bufc` + 1: copy blocks kt + 2, kt + 3 into the other two buffers (freed
+  // by the previous barrier), compute both blocks, then (this wave's copies
+  // landed) finish the next two and synchronise.
   auto step = [&](auto bufc, int kt) __attribute__((always_inline)) {
     constexpr int b = decltype(bufc)::value;
     using N1 = std::integral_constant<int, (b + 1) % kW16Stages>;
+    using N2 = std::integral_constant<int, (b + 2) % kW16Stages>;
     using N3 = std::integral_constant<int, (b + 3) % kW16Stages>;
-    const bool more3 = kt + 3 <= kt_hi, more2 = kt + 2 <= kt_hi;
-    if (more3) issue_stage(N3{}, kt + 3);
-    if (kt + 1 <= kt_hi) {
-      wait_vmem_n(more3 ? 2 * my_copies : (more2 ? my_copies : 0));
-      finish_stage(N1{}, kt + 1);
-    } else {
-      issue_u();
-    }
+    const bool has1 = kt + 1 <= kt_hi, next0 = kt + 2 <= kt_hi, next1 = kt + 3 <= kt_hi;
+    if (next0) issue_stage(N2{}, kt + 2);
+    else issue_u();
+    if (next1) issue_stage(N3{}, kt + 3);
     if (needs(kt)) block(stage(bufc), kt);
-    if (kt + 1 <= kt_hi) stage_barrier();
+    if (has1 && needs(kt + 1)) block(stage(N1{}), kt + 1);
+    if (next0) {
+      wait_vmem<0>();
+      finish_stage(N2{}, kt + 2);
+      if (next1) finish_stage(N3{}, kt + 3);
+      stage_barrier();
+    }
   };
   for (int kt = kt_lo;; kt += kW16Stages) {
     step(B0{}, kt);
-    if (kt + 1 > kt_hi) break;
-    step(B1{}, kt + 1);
     if (kt + 2 > kt_hi) break;
     step(B2{}, kt + 2);
-    if (kt + 3 > kt_hi) break;
-    step(B3{}, kt + 3);
     if (kt + 4 > kt_hi) break;
   }
 

@@ -362,8 +362,9 @@ constexpr int kPPMinMeanLen = 512;
 // Whether the automatic choice may take the eight-wave kernel at all: off
 // while it measures slower than the four-wave kernel on the long batches.
 constexpr bool kPPAuto = false;
-// Whether the automatic choice takes the sixteen-row kernel where it is built.
-constexpr bool kW16Auto = false;
+// Whether the automatic choice takes the sixteen-row kernel where it is built
+// (it measures faster than the four-wave kernel on long and short batches).
+constexpr bool kW16Auto = true;
 int ln_all_heads_max_width(int dtype);
 hipError_t launch_ln_all_heads(const LnArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_bwd_plan(const BwdPlanArgs& a, hipStream_t stream);

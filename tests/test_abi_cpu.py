@@ -287,17 +287,19 @@ def test_loader_fails_loudly_without_library(tmp_path, monkeypatch):
 
 
 def test_forward_kernel_choice(lib):
-    """AUTO takes the four-wave kernel; the setter forces either one where it
-    is supported (a host decision: no HIP call is made)."""
+    """AUTO takes the sixteen-row kernel for bf16 with d = 128 and the
+    four-wave kernel elsewhere; the setter forces a kernel where it is
+    supported (a host decision: no HIP call is made)."""
     eight, four = _lib.HSTU_FWD_KERNEL_EIGHT_WAVE, _lib.HSTU_FWD_KERNEL_FOUR_WAVE
+    w16 = _lib.HSTU_FWD_KERNEL_SIXTEEN_ROW
     long_d = _desc(num_seqs=16, total_tokens=16 * 512)
     short_d = _desc(num_seqs=16, total_tokens=16 * 512 - 1)
     f32_d = _desc(num_seqs=1, total_tokens=4096, dtype=_lib.HSTU_DTYPE_F32)
     d64 = _desc(num_seqs=1, total_tokens=4096, d_qk=64, d_v=64, ld_q=256, ld_k=256, ld_v=256,
                 ld_u=256, ld_out=256)
     try:
-        assert lib.hstu_jagged_attn_fwd_kernel_of(ctypes.byref(long_d)) == four
-        assert lib.hstu_jagged_attn_fwd_kernel_of(ctypes.byref(short_d)) == four
+        assert lib.hstu_jagged_attn_fwd_kernel_of(ctypes.byref(long_d)) == w16
+        assert lib.hstu_jagged_attn_fwd_kernel_of(ctypes.byref(short_d)) == w16
         assert lib.hstu_jagged_attn_fwd_kernel_of(ctypes.byref(f32_d)) == four
         assert lib.hstu_jagged_attn_fwd_kernel_of(ctypes.byref(d64)) == four
         assert lib.hstu_jagged_attn_set_fwd_kernel(eight) == _lib.HSTU_OK
@@ -306,6 +308,9 @@ def test_forward_kernel_choice(lib):
         assert lib.hstu_jagged_attn_fwd_kernel_of(ctypes.byref(long_d)) == eight
         assert lib.hstu_jagged_attn_set_fwd_kernel(four) == _lib.HSTU_OK
         assert lib.hstu_jagged_attn_fwd_kernel_of(ctypes.byref(long_d)) == four
+        assert lib.hstu_jagged_attn_set_fwd_kernel(w16) == _lib.HSTU_OK
+        assert lib.hstu_jagged_attn_fwd_kernel_of(ctypes.byref(long_d)) == w16
+        assert lib.hstu_jagged_attn_fwd_kernel_of(ctypes.byref(d64)) == four      # unsupported
         assert lib.hstu_jagged_attn_set_fwd_kernel(7) == _lib.HSTU_ERR_INVALID_ARG
         assert lib.hstu_jagged_attn_fwd_kernel_of(ctypes.byref(_desc(num_heads=0))) == -1
     finally:

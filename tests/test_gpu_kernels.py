@@ -1,11 +1,12 @@
-"""The eight-wave and sixteen-row forward kernels against the fp64 oracle.
+"""Each bf16 d = 128 forward kernel (four-wave, eight-wave, sixteen-row)
+against the fp64 oracle.
 
-The library picks a forward kernel by shape (see the header); every test here
-forces each of the bf16 d = 128 kernels in turn on the small ragged batches of
-every mask rule, the tile-edge lengths, windows, split items, candidate rows,
-the clamped-position bias and the exact zero pattern, so that every kernel's
-geometry is checked where the four-wave kernel's is.  Tolerance:
-max|gpu - oracle| <= 1e-2 * max|oracle| (bf16).
+The library picks a forward kernel by shape (see the header: the sixteen-row
+one for bf16 with d = 128); every test here forces each kernel in turn on the
+small ragged batches of every mask rule, the tile-edge lengths, windows, split
+items, candidate rows, the clamped-position bias and the exact zero pattern,
+so that every kernel's geometry is checked, not only the automatic choice's.
+Tolerance: max|gpu - oracle| <= 1e-2 * max|oracle| (bf16).
 """
 import math
 
@@ -21,7 +22,7 @@ from jagged_hstu_attention_attn_amd.inputs import make_custom, make_inputs
 pytestmark = pytest.mark.gpu
 
 
-@pytest.fixture(params=["eight_wave", "sixteen_row"], autouse=True)
+@pytest.fixture(params=["four_wave", "eight_wave", "sixteen_row"], autouse=True)
 def kernel(request):
     """The forward kernel every call of the test is forced to."""
     global _KERNEL
@@ -214,13 +215,14 @@ def test_pp_zero_pattern_exact():
             assert np.array_equal(out[s + i, 0, :len(want)] != 0, want), (b, i)
 
 
-def test_pp_matches_four_wave():
-    """The forced kernel and the four-wave kernel on one long-tail batch: each
+def test_pp_matches_other_kernel():
+    """The forced kernel and another kernel on one long-tail batch: each
     within tolerance of the oracle, and of each other."""
-    print(f"case {_KERNEL} vs_four_wave", flush=True)
+    other = "sixteen_row" if _KERNEL == "four_wave" else "four_wave"
+    print(f"case {_KERNEL} vs_{other}", flush=True)
     inp = make_inputs("longtail", num_seqs=6, seed=3)
     a = _fwd(inp)
-    b = _fwd(inp, kernel="four_wave")
+    b = _fwd(inp, kernel=other)
     ref = _ora(inp)
     _close(a, ref)
     _close(b, ref)
