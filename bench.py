@@ -35,18 +35,26 @@ sys.path.insert(0, ROOT)
 METRIC = "jagged HSTU attn fwd TFLOP/s (valid pairs) + % bf16 MFMA peak; tokens/s"
 PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}      # dense MFMA peaks, MI355X (256 CU x 2.4 GHz)
 PEAK_HBM_GBS = 8000.0
-KERNEL_SOURCES = ["jagged_hstu_attention_attn_amd/csrc/attn_fwd.hip",
-                  "jagged_hstu_attention_attn_amd/csrc/hstu_device.hpp"]
+_CSRC = "jagged_hstu_attention_attn_amd/csrc/"
+# The sources each forward kernel is built from: a counter summary is valid
+# for the kernel and source hash it records.
+KERNEL_SOURCES = {
+    "hstu_attn_fwd_kernel": ["attn_fwd.hip", "attn_common.hpp", "hstu_device.hpp"],
+    "hstu_attn_fwd_w16_kernel": ["attn_fwd_w16.hip", "attn_common.hpp", "hstu_device.hpp"],
+    "hstu_attn_fwd_pp_kernel": ["attn_fwd_pp.hip", "attn_common.hpp", "hstu_device.hpp"],
+}
+KERNEL_OF_CHOICE = {"four_wave": "hstu_attn_fwd_kernel", "sixteen_row": "hstu_attn_fwd_w16_kernel",
+                    "eight_wave": "hstu_attn_fwd_pp_kernel"}
 
 
 def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(kernel: str) -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
+    for rel in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, _CSRC + rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
@@ -219,16 +227,19 @@ def bench_backward(args, inp) -> int:
     return 0
 
 
-def traffic_from_profile(workload: str):
+def traffic_from_profile(workload: str, kernel: str):
     """HBM bytes per attention launch from the committed counter summary, if
-    it was taken on the current kernel source; else None."""
+    it was taken on `kernel` as its source stands; else None."""
     path = os.path.join(ROOT, "profiles", f"attn_fwd_{workload}_traffic.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
+    m_kern = re.search(r"^kernel:\s*(\S+)", text, re.M)
     m_sha = re.search(r"kernel_source_sha:\s*([0-9a-f]+)", text)
     m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not m_sha or not m_bytes or m_sha.group(1) != kernel_source_hash():
+    if not m_kern or not m_sha or not m_bytes or m_kern.group(1) != kernel:
+        return None
+    if m_sha.group(1) != kernel_source_hash(kernel):
         return None
     return float(m_bytes.group(1))
 
@@ -467,17 +478,16 @@ def measure_forward(args, inp, workload: str, steps: int, warmup: int) -> dict:
         achieved = flops / (attn * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                 "frac": achieved / peak}
+    kernel = KERNEL_OF_CHOICE.get(call.kernel_name(), "hstu_attn_fwd_kernel")
     traffic = (None if args.candidates_only or args.epilogue != "ln_u"
-               else traffic_from_profile(workload))
+               else traffic_from_profile(workload, kernel))
     roof["traffic"] = traffic
     roof["traffic_source"] = (
         f"profiles/attn_fwd_{workload}_traffic.md: rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE "
-        "runs of bench.py, scaled by the copy calibration, taken on the current kernel source"
+        "runs of bench.py, scaled by the copy calibration, taken on this kernel's current source"
         if traffic is not None else
-        "null: no counter summary taken on the current kernel source")
-    roof["kernel"] = {"eight_wave": "hstu_attn_fwd_pp_kernel",
-                      "sixteen_row": "hstu_attn_fwd_w16_kernel"}.get(call.kernel_name(),
-                                                                     "hstu_attn_fwd_kernel")
+        "null: no counter summary taken on this kernel's current source")
+    roof["kernel"] = kernel
     roof["kernel_us"] = attn * 1e3
     roof["kernel_timing"] = ("HIP events taken at the kernel's own start and end, over a "
                              "second pass of the same steps")
