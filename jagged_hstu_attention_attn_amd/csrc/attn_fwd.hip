@@ -96,10 +96,17 @@ __host__ __device__ constexpr int stage_copies(int w) {
          ((POS && w > kTsWave) ? 1 : 0) + ((TIME && w == kTsWave) ? 1 : 0);
 }
 
+// Waves per SIMD the kernel is built for: two workgroups per CU (a wave has
+// 256 registers) up to d = 128; with d = 256 the 32 x 256 fp32 output tile
+// alone takes 128 registers and the Q operands 64, so one workgroup per CU
+// (512 registers a wave, four 33 KB stage buffers of LDS).
+template <int DQK, int DV>
+constexpr int kWavesPerSimd = (DQK > 128 || DV > 128) ? 1 : 2;
+
 // POSM: 0 = no position bias, 1 = position bias of |i - j|, 2 = of the
 // clamped positions |p_i - p_j| (candidate rows take it from cpos).
 template <typename T, int DQK, int DV, int POSM, bool TIME>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<DQK, DV>))) void
 hstu_attn_fwd_kernel(AttnArgs a) {
   constexpr bool POS = POSM != 0;
   constexpr bool clamp = POSM == 2;
@@ -974,6 +981,7 @@ int attn_grid(int dtype, int d_qk, int d_v, int pos_len, int time_len, bool clam
     if (d_qk == 64 && d_v == 64) bpc = bpc_bias<__bf16, 64, 64>(pos_len, time_len, clamp);
     if (d_qk == 64 && d_v == 128) bpc = bpc_bias<__bf16, 64, 128>(pos_len, time_len, clamp);
     if (d_qk == 128 && d_v == 64) bpc = bpc_bias<__bf16, 128, 64>(pos_len, time_len, clamp);
+    if (d_qk == 256 && d_v == 256) bpc = bpc_bias<__bf16, 256, 256>(pos_len, time_len, clamp);
   } else if (dtype == 0) {
     if (d_qk == 128 && d_v == 128) bpc = bpc_bias<float, 128, 128>(pos_len, time_len, clamp);
     if (d_qk == 64 && d_v == 64) bpc = bpc_bias<float, 64, 64>(pos_len, time_len, clamp);
@@ -990,7 +998,8 @@ int attn_grid(int dtype, int d_qk, int d_v, int pos_len, int time_len, bool clam
 bool attn_supported(int dtype, int d_qk, int d_v) {
   if (dtype == 1)
     return (d_qk == 128 && d_v == 128) || (d_qk == 64 && d_v == 64) ||
-           (d_qk == 64 && d_v == 128) || (d_qk == 128 && d_v == 64);
+           (d_qk == 64 && d_v == 128) || (d_qk == 128 && d_v == 64) ||
+           (d_qk == 256 && d_v == 256);
   if (dtype == 0) return (d_qk == 128 && d_v == 128) || (d_qk == 64 && d_v == 64) ||
                          (d_qk == 8 && d_v == 8);
   return false;
@@ -1003,6 +1012,7 @@ hipError_t launch_attn(const AttnArgs& a, int dtype, int d_qk, int d_v, int n_wg
     if (d_qk == 64 && d_v == 64) return launch_bias<__bf16, 64, 64>(a, n_wg, stream, t0, t1);
     if (d_qk == 64 && d_v == 128) return launch_bias<__bf16, 64, 128>(a, n_wg, stream, t0, t1);
     if (d_qk == 128 && d_v == 64) return launch_bias<__bf16, 128, 64>(a, n_wg, stream, t0, t1);
+    if (d_qk == 256 && d_v == 256) return launch_bias<__bf16, 256, 256>(a, n_wg, stream, t0, t1);
   } else if (dtype == 0) {
     if (d_qk == 128 && d_v == 128) return launch_bias<float, 128, 128>(a, n_wg, stream, t0, t1);
     if (d_qk == 64 && d_v == 64) return launch_bias<float, 64, 64>(a, n_wg, stream, t0, t1);

@@ -821,6 +821,9 @@ int hstu_jagged_attn_bwd(const hstu_attn_desc* desc, const void* q, const void* 
   if (desc->d_qk != desc->d_v)
     return fail(HSTU_ERR_UNSUPPORTED, "the backward needs d_qk == d_v (%d, %d)", desc->d_qk,
                 desc->d_v);
+  if (desc->d_qk != 64 && desc->d_qk != 128)
+    return fail(HSTU_ERR_UNSUPPORTED, "the backward supports d = 64 and d = 128 (not %d)",
+                desc->d_qk);
   if (desc->pos_clamp != 0)
     return fail(HSTU_ERR_UNSUPPORTED, "the backward takes the raw position bias (pos_clamp 0)");
   if (desc->num_seqs > 0 && !offsets) return fail(HSTU_ERR_INVALID_ARG, "offsets is NULL");

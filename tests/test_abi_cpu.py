@@ -205,6 +205,9 @@ def test_supported_set(lib):
     assert lib.hstu_jagged_attn_supported(1, 128, 128) == 1
     assert lib.hstu_jagged_attn_supported(1, 64, 128) == 1
     assert lib.hstu_jagged_attn_supported(1, 128, 64) == 1
+    assert lib.hstu_jagged_attn_supported(1, 256, 256) == 1
+    assert lib.hstu_jagged_attn_supported(1, 256, 128) == 0
+    assert lib.hstu_jagged_attn_supported(0, 256, 256) == 0
     assert lib.hstu_jagged_attn_supported(0, 8, 8) == 1
     assert lib.hstu_jagged_attn_supported(1, 8, 8) == 0
     assert lib.hstu_jagged_attn_supported(0, 64, 128) == 0
@@ -235,6 +238,11 @@ def test_backward_validation(lib):
     assert _bwd(lib, _desc(), du=None) == _lib.HSTU_ERR_INVALID_ARG
     assert _bwd(lib, _desc(), ws=None) == _lib.HSTU_ERR_WORKSPACE
     assert _bwd(lib, _desc(pos_clamp=1)) == _lib.HSTU_ERR_UNSUPPORTED
+    # d = 256: forward only
+    d256 = _desc(d_qk=256, d_v=256, ld_q=1024, ld_k=1024, ld_v=1024, ld_u=1024, ld_out=1024)
+    assert lib.hstu_jagged_attn_workspace_bytes(ctypes.byref(d256)) > 0
+    assert _bwd(lib, d256) == _lib.HSTU_ERR_UNSUPPORTED
+    assert "d = 64 and d = 128" in _lib.last_error()
     # du is not needed without the gate
     rc = _bwd(lib, _desc(epilogue=_lib.HSTU_EPILOGUE_NONE), du=None)
     assert rc in (_lib.HSTU_OK, _lib.HSTU_ERR_HIP)

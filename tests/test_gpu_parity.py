@@ -51,7 +51,7 @@ def ora(inp, epilogue="ln_u", rows=None, pos_clamp=False):
 # Worked example of "HSTU tensor by tensor", section "SiLU aggregation
 # coefficients are not probabilities", on the device.
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("dtype,d", [("f32", 8), ("bf16", 128), ("f32", 128)])
+@pytest.mark.parametrize("dtype,d", [("f32", 8), ("bf16", 128), ("f32", 128), ("bf16", 256)])
 def test_worked_example(dtype, d):
     inp = make_custom([2], d_qk=d, d_v=d, dtype=dtype, alpha=1.0, n_scale=1.0)
     inp.q[:] = 0; inp.k[:] = 0; inp.v[:] = 0; inp.u[:] = 1
@@ -191,7 +191,8 @@ def test_layer_strided_views():
 EDGE_LENGTHS = [0, 1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 257, 300]
 
 
-@pytest.mark.parametrize("dtype,d", [("f32", 8), ("bf16", 128), ("bf16", 64), ("f32", 64)])
+@pytest.mark.parametrize("dtype,d", [("f32", 8), ("bf16", 128), ("bf16", 64), ("f32", 64),
+                                     ("bf16", 256)])
 @pytest.mark.parametrize("rules", ["causal", "targets", "prefix", "window", "all"])
 def test_edges(dtype, d, rules):
     rng = np.random.default_rng(hash(rules) % 1000)
@@ -228,7 +229,7 @@ def test_no_bias_tables():
     assert_close(gpu_forward(inp), ora(inp), "bf16")
 
 
-@pytest.mark.parametrize("dtype,d", [("f32", 8), ("bf16", 128)])
+@pytest.mark.parametrize("dtype,d", [("f32", 8), ("bf16", 128), ("bf16", 256)])
 def test_wide_timestamp_span_uses_exact_buckets(dtype, d):
     """Gaps of ~2^27 s push spans past 2^30, the 64-bit bucket path."""
     inp = make_custom([150, 40], num_heads=2, d_qk=d, d_v=d, dtype=dtype, seed=9,
@@ -371,6 +372,22 @@ def test_split_items_plan_reuse():
                                      np.arange(4096, 4829, 41)]))
     assert_close(o1, ora(inp, rows=rows), "bf16", rows=rows)
     assert np.array_equal(o1, o2) and np.array_equal(o1, o3)
+
+
+def test_d256_split_items_candidates_and_clamp():
+    """bf16 with d_qk = d_v = 256 (one workgroup per CU): a 2200-token
+    sequence whose last query tiles are split along the keys, candidates,
+    a contextual prefix and both position-bias readings, on sampled rows of
+    the long sequence and all rows of the short ones."""
+    print("case d256 split/candidates/clamp", flush=True)
+    inp = make_custom([2200, 700, 33], num_heads=2, d_qk=256, d_v=256, dtype="bf16", seed=12,
+                      num_targets=[40, 5, 3], contextual_len=6, pos_len=4096, time_len=64,
+                      alpha=1.0 / 16)
+    rows = np.unique(np.concatenate([np.arange(2048, 2200), np.arange(0, 2200, 61),
+                                     np.arange(2200, inp.total_tokens)]))
+    for clamp in (False, True):
+        assert_close(gpu_forward(inp, pos_clamp=clamp), ora(inp, rows=rows, pos_clamp=clamp),
+                     "bf16", rows=rows)
 
 
 @pytest.mark.parametrize("lengths,targets,window", [
@@ -611,7 +628,7 @@ def _perturb(inp, rows, seed=5):
     return out
 
 
-@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 8)])
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 8), ("bf16", 256)])
 def test_future_perturbation_bitwise(dtype, d):
     inp = make_custom([300, 90], num_heads=2, d_qk=d, d_v=d, dtype=dtype, seed=21,
                       num_targets=[12, 5], pos_len=512, time_len=64, alpha=0.2)
