@@ -38,6 +38,8 @@
 // "Similar shape, different aggregation").
 #include <hip/hip_ext.h>
 
+#include <cstddef>
+
 #include "attn_common.hpp"
 
 namespace hstu {
@@ -60,9 +62,12 @@ struct W16Stage {
   uint32_t ts32[kBN];           // key timestamps relative to the item's base
   uint32_t tmin, tmax;          // range of ts32 over the valid keys
   int tbad;                     // some key needs the 64-bit time path
-  int pad_;
+  int pad_;                     // (tmin .. pad_: one 16-byte read)
   float cpos[CLAMP ? 64 : 4];   // clamped-position bias of key (lane % 32): n_h - j
 };
+
+static_assert(offsetof(W16Stage<false>, tmin) % 16 == 0 && offsetof(W16Stage<true>, tmin) % 16 == 0,
+              "the key-time range is one aligned 16-byte read");
 
 // Physical 16-byte chunk of logical chunk c in staged row `row`.
 __device__ inline int w16_kchunk(int c, int row) { return c ^ (row & 15); }
@@ -121,6 +126,13 @@ hstu_attn_fwd_w16_kernel(AttnArgs a) {
     asm volatile("" : "+v"(ln));
     return ln;
   };
+
+  // This lane's K/V copy offsets within a stage of whole rows: row 4w + l/16
+  // of the block, swizzled chunk of l % 16 (kernel constants; the last block
+  // of a sequence clamps its rows instead).
+  const int cp_row = 4 * wave + (lane >> 4);
+  const uint32_t ko_full = (uint32_t)cp_row * ldk_b + 16u * (uint32_t)w16_kchunk(lane & 15, cp_row);
+  const uint32_t vo_full = (uint32_t)cp_row * ldv_b + 16u * (uint32_t)w16_vchunk(lane & 15, cp_row);
 
   if constexpr (TIME) {
     const int Tt = a.time_len;
@@ -194,10 +206,13 @@ hstu_attn_fwd_w16_kernel(AttnArgs a) {
     SB& sb = stage(bufc);
     const int j0 = kt * kBN;
     const int ln = opaque_lane();
-    const int row = 4 * wave + (ln >> 4);
-    const uint32_t r = (uint32_t)min(row, L - 1 - j0);
-    const uint32_t ko = r * ldk_b + 16u * (uint32_t)w16_kchunk(ln & 15, row);
-    const uint32_t vo = r * ldv_b + 16u * (uint32_t)w16_vchunk(ln & 15, row);
+    uint32_t ko = ko_full, vo = vo_full;
+    if (j0 + kBN > L) {   // the sequence's last block: rows past its end repeat row L - 1
+      const int row = 4 * wave + (ln >> 4);
+      const uint32_t r = (uint32_t)min(row, L - 1 - j0);
+      ko = r * ldk_b + 16u * (uint32_t)w16_kchunk(ln & 15, row);
+      vo = r * ldv_b + 16u * (uint32_t)w16_vchunk(ln & 15, row);
+    }
     const uint64_t kb = kseq + (uint64_t)j0 * ldk_b, vb = vseq + (uint64_t)j0 * ldv_b;
     if (kv_nt) {
       lds_copy16_nt(kb, ko, lds_off(sb.k) + 1024u * (uint32_t)wave);
@@ -280,15 +295,20 @@ hstu_attn_fwd_w16_kernel(AttnArgs a) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc[t][e] = 0.0f;
 
-  auto time_const = [&](SB& sb, float& tb) __attribute__((always_inline)) -> bool {
-    if (!w_t_ok || uni(sb.tbad) != 0) return false;
-    const uint32_t kmin = (uint32_t)uni((int)sb.tmin), kmax = (uint32_t)uni((int)sb.tmax);
-    uint32_t dmin = 0;
-    if (w_tmin > kmax) dmin = w_tmin - kmax;
-    if (kmin > w_tmax) dmin = kmin - w_tmax;
-    const uint32_t dmax = max(w_tmax > kmin ? w_tmax - kmin : 0u,
-                              kmax > w_tmin ? kmax - w_tmin : 0u);
-    const int z0 = uni(__builtin_clz(dmin + 1u)), z1 = uni(__builtin_clz(dmax + 1u));
+  // Whether every (row, key) time gap of this wave and a block falls in one
+  // bucket, from the block's key-time range `kr` (tmin, tmax, tbad as the
+  // stage holds them, loaded with the block's first LDS reads); then `tb` is
+  // that bucket's bias.  Uniform values throughout: the distances between
+  // the wave's and the block's time ranges are written as max - b (scalar
+  // ALU) rather than saturating differences (vector ALU).
+  auto time_const = [&](const uint4& kr, float& tb) __attribute__((always_inline)) -> bool {
+    if (!w_t_ok || uni((int)kr.z) != 0) return false;
+    const uint32_t kmin = (uint32_t)uni((int)kr.x), kmax = (uint32_t)uni((int)kr.y);
+    const uint32_t wmin = (uint32_t)uni((int)w_tmin), wmax = (uint32_t)uni((int)w_tmax);
+    // ranges [wmin, wmax] and [kmin, kmax]: at most one of the two gaps is positive
+    const uint32_t dmin = (max(wmin, kmax) - kmax) + (max(kmin, wmax) - wmax);
+    const uint32_t dmax = max(max(wmax, kmin) - kmin, max(kmax, wmin) - wmin);
+    const int z0 = __builtin_clz(dmin + 1u), z1 = __builtin_clz(dmax + 1u);
     if (z0 != z1) return false;
     tb = __builtin_bit_cast(float, uni(__builtin_bit_cast(int, tt.trev[z0])));
     return true;
@@ -301,6 +321,8 @@ hstu_attn_fwd_w16_kernel(AttnArgs a) {
     const int l16 = lane & 15, g4 = lane >> 4;
     // ---- score start (position bias) and the first half of the K operands
     floatx4v s0, s1;
+    uint4 kr = {0u, 0u, 0u, 0u};   // key-time range of the block (TIME)
+    if constexpr (TIME) kr = *reinterpret_cast<const uint4*>(&sb.tmin);
     const int dbase = (kBM - 1) - kW16Rows * wave - l16 + 4 * g4;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -378,7 +400,7 @@ hstu_attn_fwd_w16_kernel(AttnArgs a) {
     float x[8];
     if constexpr (TIME) {
       float tb = 0.0f;
-      if (time_const(sb, tb)) {
+      if (time_const(kr, tb)) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           x[e] = fmaf(s0[e], am, tb);
