@@ -13,9 +13,9 @@
 // Work items are the scheduler's units (sequence, head, 128-row query tile,
 // key-tile range), as for the other forward kernels; wave w owns rows
 // i0 + 16w .. i0 + 16w + 15.  Keys are staged 32 at a time in four LDS
-// buffers, copied from HBM straight into LDS (global_load_lds) three stages
-// ahead, one barrier per stage.  Per 32-key block and wave, with
-// v_mfma_f32_16x16x32_bf16:
+// buffers, copied from HBM straight into LDS (global_load_lds); a step
+// computes two key blocks while the next two are copied, one barrier per
+// step.  Per 32-key block and wave, with v_mfma_f32_16x16x32_bf16:
 //   S^T = K Q^T + C       two 16-key x 16-row tiles; lane l holds keys
 //                         16 t + 4 (l / 16) + i (t = 0, 1; i = 0..3) of row
 //                         l % 16, the accumulator starting at the position bias
@@ -112,9 +112,16 @@ hstu_attn_fwd_w16_kernel(AttnArgs a) {
   const float pscale = kLog2e / am;              // position bias in accumulator units
   const uint32_t ldk_b = (uint32_t)(a.ld_k * 2), ldv_b = (uint32_t)(a.ld_v * 2);
   // copies of one stage: wave w copies 1 KB chunk w of the keys and of the
-  // values (rows 4w .. 4w + 3); waves 5-7 gather the position-bias diagonal
-  // (part w - 5), wave 4 the raw timestamps, wave 3 the clamped-position bias
+  // values (rows 4w .. 4w + 3); the bias inputs go to "role" waves, which a
+  // stage in an odd buffer maps to wave role ^ 4 (the two stages of a step
+  // split that work between the two halves of the workgroup, which would
+  // otherwise wait at the barrier for one half): roles 5-7 gather the
+  // position-bias diagonal (part role - 5), role 4 the raw timestamps, role
+  // 3 the clamped-position bias
   constexpr int kTsW = 4, kCposW = 3, kDiagW0 = 5;
+  auto role_wave = [&](auto bufc) __attribute__((always_inline)) {
+    return (decltype(bufc)::value & 1) ? (wave ^ 4) : wave;
+  };
   static_assert(kDiagW0 + kDiagCopies <= kW16Waves, "enough waves for the bias copies");
 
   // Per-lane values are derived from an opaque lane index inside the loops
@@ -221,21 +228,22 @@ hstu_attn_fwd_w16_kernel(AttnArgs a) {
       lds_copy16(kb, ko, lds_off(sb.k) + 1024u * (uint32_t)wave);
       lds_copy16(vb, vo, lds_off(sb.v) + 1024u * (uint32_t)wave);
     }
+    const int rw = role_wave(bufc);
     if constexpr (POS) {
-      if (wave >= kDiagW0) {
-        const int p = wave - kDiagW0;
+      if (rw >= kDiagW0) {
+        const int p = rw - kDiagW0;
         const int d = i0 - j0 + (kBM - 1) - (64 * p + ln);
         const int ix = min(d < 0 ? -d : d, P - 1);
         lds_copy4(pos_base, 4u * (uint32_t)ix, lds_off(sb.diag) + 256u * (uint32_t)p);
       }
-      if (clamp && wave == kCposW) {   // bias of n_h - j (0 for candidate keys)
+      if (clamp && rw == kCposW) {   // bias of n_h - j (0 for candidate keys)
         const int d = geo.n_h - (j0 + (ln & (kBN - 1)));
         const int ix = min(d > 0 ? d : 0, P - 1);
         lds_copy4(pos_base, 4u * (uint32_t)ix, lds_off(sb.cpos));
       }
     }
     if constexpr (TIME) {
-      if (wave == kTsW) {
+      if (rw == kTsW) {
         const int j = min(j0 + (ln >> 1), L - 1);
         lds_copy4(ts_base, 8u * (uint32_t)j + 4u * (uint32_t)(ln & 1), lds_off(sb.ts64));
       }
@@ -254,15 +262,16 @@ hstu_attn_fwd_w16_kernel(AttnArgs a) {
   auto finish_stage = [&](auto bufc, int kt) __attribute__((always_inline)) {
     SB& sb = stage(bufc);
     const int ln = opaque_lane();
+    const int rw = role_wave(bufc);
     if constexpr (POS) {
-      if (wave >= kDiagW0) {
-        const int e = 64 * (wave - kDiagW0) + ln;
+      if (rw >= kDiagW0) {
+        const int e = 64 * (rw - kDiagW0) + ln;
         if (e < kDiag) sb.diag[e] *= pscale;
       }
-      if (clamp && wave == kCposW) sb.cpos[ln] *= pscale;
+      if (clamp && rw == kCposW) sb.cpos[ln] *= pscale;
     }
     if constexpr (TIME) {
-      if (wave == kTsW) {
+      if (rw == kTsW) {
         const int kl = ln & (kBN - 1);
         const int64_t tj = sb.ts64[kl];
         const int64_t rel = tj - tbase;
