@@ -15,13 +15,16 @@
 // Tiling: a workgroup of 4 waves computes a 128 x 128 block of C; wave (wn,
 // wm) holds 64 x 64 of it as 2 x 2 tiles of v_mfma_f32_32x32x16_bf16 with the
 // weight rows on the MFMA's M side and the tokens on N, so each lane ends up
-// with 16 outputs of one token.  K advances 64 at a time through two LDS
+// with 16 outputs of one token.  K advances 32 at a time through two LDS
 // stages filled by global_load_lds_dwordx4 (16-byte chunks XOR-swizzled by
-// row), one stage ahead.  The epilogue parks the fp32 block in LDS (64 KB,
-// the two stages' space) and writes whole rows: every lane finishes 8
-// consecutive outputs of one token (bias, SiLU, residual, bf16) and stores
-// them as one 16-byte chunk, 8 full 128-byte lines per wave instruction.
-// Requires N % 128 == 0, K % 64 == 0, 16-byte aligned rows; M is arbitrary.
+// row), one stage ahead: 32 KB of LDS and at most 128 registers, so four
+// workgroups share a CU and one's loads and epilogue overlap the others'
+// matrix work (a tile is only K / 32 stages long).  The epilogue parks the
+// fp32 block in LDS 64 token rows at a time (the two stages' space) and
+// writes whole rows: every lane finishes 8 consecutive outputs of one token
+// (bias, SiLU, residual, bf16) and stores them as one 16-byte chunk, 8 full
+// 128-byte lines per wave instruction.
+// Requires N % 128 == 0, K % 32 == 0, 16-byte aligned rows; M is arbitrary.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -34,7 +37,7 @@ typedef float g_floatx4 __attribute__((ext_vector_type(4)));
 typedef float g_floatx16 __attribute__((ext_vector_type(16)));
 
 constexpr int kGB = 128;    // block of C: rows (tokens) and columns (features)
-constexpr int kGK = 64;     // K per stage
+constexpr int kGK = 32;     // K per stage
 constexpr int kGThreads = 256;
 constexpr int kGXcds = 8;   // XCDs of the MI355X
 
@@ -74,12 +77,16 @@ __device__ inline void g_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Staged tile: 128 rows x 64 k (128 bytes = 8 chunks per row); physical chunk
-// c of row r holds logical chunk c ^ (r & 7).
-__device__ inline int g_swz(int r) { return r & 7; }
+// Staged tile: 128 rows x 32 k (64 bytes = 4 chunks per row); physical chunk
+// c of row r holds logical chunk c ^ ((r >> 2) & 3): the 16 rows one
+// 16-lane phase of a fragment read touches land on 16 different 16-byte
+// bank groups.
+__device__ inline int g_swz(int r) { return (r >> 2) & 3; }
 
-__global__ __launch_bounds__(kGThreads) void hstu_gemm_bt_kernel(GemmArgs a) {
+__global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(4))) void
+hstu_gemm_bt_kernel(GemmArgs a) {
   __shared__ __align__(16) char smem[2 * 2 * kGB * kGK * 2];   // 2 stages x (W, X) tiles
+  static_assert(2 * 2 * kGB * kGK * 2 == 64 * 512, "half the fp32 block fits the stages");
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wn = wave >> 1, wm = wave & 1;   // wave's 64 x 64 sub-block: features wn, tokens wm
@@ -94,7 +101,7 @@ __global__ __launch_bounds__(kGThreads) void hstu_gemm_bt_kernel(GemmArgs a) {
   if (t >= nT) return;
   const int n0 = (t % nN) * kGB, m0 = (t / nN) * kGB;
   const int M = a.M, K = a.K;
-  constexpr int kTile = kGB * kGK * 2;   // bytes of one staged 128 x 64 tile
+  constexpr int kTile = kGB * kGK * 2;   // bytes of one staged 128 x 32 tile
   const uint32_t s0 = g_lds_off(smem);
   auto w_tile = [&](int st) { return s0 + (uint32_t)(st * 2 * kTile); };
   auto x_tile = [&](int st) { return s0 + (uint32_t)(st * 2 * kTile + kTile); };
@@ -104,12 +111,12 @@ __global__ __launch_bounds__(kGThreads) void hstu_gemm_bt_kernel(GemmArgs a) {
   const uint32_t ldb_b = (uint32_t)(a.ldb * 2), lda_b = (uint32_t)(a.lda * 2);
   const int m_last = min(kGB, M - m0) - 1;   // rows past M repeat the last token
 
-  // Stage kb: each wave copies 4 + 4 chunks-of-64-lanes of the two tiles.
+  // Stage kb: each wave copies 2 + 2 chunks-of-64-lanes of the two tiles.
   auto issue = [&](int st, int kb) __attribute__((always_inline)) {
     const uint32_t kbyte = (uint32_t)kb * kGK * 2;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int n = s * 4 + wave, m = 64 * n + lane, r = m >> 3, c = m & 7;
+    for (int s = 0; s < 2; ++s) {
+      const int n = s * 4 + wave, m = 64 * n + lane, r = m >> 2, c = m & 3;
       const uint32_t coff = kbyte + 16u * (uint32_t)(c ^ g_swz(r));
       g_lds_copy16(wb, (uint32_t)r * ldb_b + coff, w_tile(st) + 1024u * (uint32_t)n);
       g_lds_copy16(xb, (uint32_t)min(r, m_last) * lda_b + coff, x_tile(st) + 1024u * (uint32_t)n);
@@ -130,7 +137,7 @@ __global__ __launch_bounds__(kGThreads) void hstu_gemm_bt_kernel(GemmArgs a) {
     const int st = kb & 1;
     if (kb + 1 < nkb) {
       issue(st ^ 1, kb + 1);
-      __builtin_amdgcn_s_waitcnt(8 | (7 << 4) | (15 << 8));   // vmcnt(8): stage kb landed
+      __builtin_amdgcn_s_waitcnt(4 | (7 << 4) | (15 << 8));   // vmcnt(4): stage kb landed
     } else {
       __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));   // vmcnt(0)
     }
@@ -142,8 +149,8 @@ __global__ __launch_bounds__(kGThreads) void hstu_gemm_bt_kernel(GemmArgs a) {
       for (int i = 0; i < 2; ++i) {
         const int rw = 64 * wn + 32 * i + l32, rx = 64 * wm + 32 * i + l32;
         const int c = 2 * ks + hh;
-        wf[i] = g_lds_ld<g_bf16x8>(w_tile(st) + (uint32_t)(rw * 128 + 16 * (c ^ g_swz(rw))));
-        xf[i] = g_lds_ld<g_bf16x8>(x_tile(st) + (uint32_t)(rx * 128 + 16 * (c ^ g_swz(rx))));
+        wf[i] = g_lds_ld<g_bf16x8>(w_tile(st) + (uint32_t)(rw * 64 + 16 * (c ^ g_swz(rw))));
+        xf[i] = g_lds_ld<g_bf16x8>(x_tile(st) + (uint32_t)(rx * 64 + 16 * (c ^ g_swz(rx))));
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
@@ -154,57 +161,66 @@ __global__ __launch_bounds__(kGThreads) void hstu_gemm_bt_kernel(GemmArgs a) {
     g_barrier();   // the stage may be refilled by the next iteration's copies
   }
 
-  // Epilogue.  acc[i][j][r]: feature 64wn + 32i + 8(r/4) + 4hh + r%4 of token
-  // 64wm + 32j + l32.  fp32 block C[token][feature] in LDS, 512 bytes per
-  // token row, 16-byte chunk c of row t at physical chunk c ^ (t & 15).
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int t = 64 * wm + 32 * j + l32;
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int f = 64 * wn + 32 * i + 8 * g + 4 * hh;   // 4 consecutive features
-        g_floatx4 v;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e];
-        g_lds_st<g_floatx4>(s0 + (uint32_t)(t * 512 + 16 * ((f >> 2) ^ (t & 15))), v);
-      }
-    }
-  __syncthreads();
-  // 128 rows x 16 chunks of 8 outputs; thread handles chunk (tid & 15) of
-  // rows (tid >> 4) + 16 p
+  // Epilogue, in two halves of 64 tokens (the waves with wm == half park
+  // theirs).  acc[i][j][r]: feature 64wn + 32i + 8(r/4) + 4hh + r%4 of token
+  // 64wm + 32j + l32.  fp32 half-block C[token][feature] in LDS, 512 bytes
+  // per token row, 16-byte chunk c of row t at physical chunk c ^ (t & 15).
   const int oc = tid & 15;
 #pragma unroll
-  for (int p = 0; p < 8; ++p) {
-    const int t = (tid >> 4) + 16 * p;
-    if (m0 + t > M - 1) continue;
-    const int f = 8 * oc;   // features f .. f+7 of the block
-    const g_floatx4 lo = g_lds_ld<g_floatx4>(s0 + (uint32_t)(t * 512 + 16 * ((f >> 2) ^ (t & 15))));
-    const g_floatx4 hi =
-        g_lds_ld<g_floatx4>(s0 + (uint32_t)(t * 512 + 16 * (((f >> 2) + 1) ^ (t & 15))));
-    float y[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    if (a.bias) {
-      const g_bf16x8 b = *reinterpret_cast<const g_bf16x8*>(a.bias + n0 + f);
+  for (int half = 0; half < 2; ++half) {
+    if (wm == half) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) y[e] += (float)b[e];
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int t = 32 * j + l32;
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int f = 64 * wn + 32 * i + 8 * g + 4 * hh;   // 4 consecutive features
+            g_floatx4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e];
+            g_lds_st<g_floatx4>(s0 + (uint32_t)(t * 512 + 16 * ((f >> 2) ^ (t & 15))), v);
+          }
+        }
     }
-    if (a.act_silu) {
+    __syncthreads();
+    // 64 rows x 16 chunks of 8 outputs; thread handles chunk (tid & 15) of
+    // rows (tid >> 4) + 16 p
 #pragma unroll
-      for (int e = 0; e < 8; ++e)   // y * sigmoid(y) = y / (1 + 2^(-y log2 e))
-        y[e] = y[e] * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * y[e]));
+    for (int p = 0; p < 4; ++p) {
+      const int t = (tid >> 4) + 16 * p;
+      const int tt = 64 * half + t;   // token within the block
+      if (m0 + tt > M - 1) continue;
+      const int f = 8 * oc;   // features f .. f+7 of the block
+      const g_floatx4 lo =
+          g_lds_ld<g_floatx4>(s0 + (uint32_t)(t * 512 + 16 * ((f >> 2) ^ (t & 15))));
+      const g_floatx4 hi =
+          g_lds_ld<g_floatx4>(s0 + (uint32_t)(t * 512 + 16 * (((f >> 2) + 1) ^ (t & 15))));
+      float y[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      if (a.bias) {
+        const g_bf16x8 b = *reinterpret_cast<const g_bf16x8*>(a.bias + n0 + f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] += (float)b[e];
+      }
+      if (a.act_silu) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)   // y * sigmoid(y) = y / (1 + 2^(-y log2 e))
+          y[e] = y[e] * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * y[e]));
+      }
+      const int64_t row = m0 + tt;
+      if (a.residual) {
+        const g_bf16x8 rsd =
+            *reinterpret_cast<const g_bf16x8*>(a.residual + row * a.ldr + n0 + f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] += (float)rsd[e];
+      }
+      g_bf16x8 o;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = (__bf16)y[e];
+      *reinterpret_cast<g_bf16x8*>(a.C + row * a.ldc + n0 + f) = o;
     }
-    const int64_t row = m0 + t;
-    if (a.residual) {
-      const g_bf16x8 rsd =
-          *reinterpret_cast<const g_bf16x8*>(a.residual + row * a.ldr + n0 + f);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) y[e] += (float)rsd[e];
-    }
-    g_bf16x8 o;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = (__bf16)y[e];
-    *reinterpret_cast<g_bf16x8*>(a.C + row * a.ldc + n0 + f) = o;
+    if (half == 0) __syncthreads();   // the first half is read before the second lands
   }
 }
 
