@@ -1541,6 +1541,14 @@ int bwd_grid(int dtype, int d, int pos_len, int time_len, int which) {
   return g < kMaxGrid ? g : kMaxGrid;
 }
 
+// Head sizes the backward is built for (d_qk == d_v == d): bf16 MFMA
+// passes for 64 and 128, the fp32 kernels for 8, 64 and 128.
+bool bwd_supported(int dtype, int d) {
+  if (dtype == 1) return d == 64 || d == 128;
+  if (dtype == 0) return d == 8 || d == 64 || d == 128;
+  return false;
+}
+
 hipError_t launch_bwd(const BwdArgs& a, int dtype, int d, int which, int n_wg,
                       hipStream_t stream) {
   if (dtype == 1) {

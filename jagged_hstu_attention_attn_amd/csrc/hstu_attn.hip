@@ -821,8 +821,9 @@ int hstu_jagged_attn_bwd(const hstu_attn_desc* desc, const void* q, const void* 
   if (desc->d_qk != desc->d_v)
     return fail(HSTU_ERR_UNSUPPORTED, "the backward needs d_qk == d_v (%d, %d)", desc->d_qk,
                 desc->d_v);
-  if (desc->d_qk != 64 && desc->d_qk != 128)
-    return fail(HSTU_ERR_UNSUPPORTED, "the backward supports d = 64 and d = 128 (not %d)",
+  if (!hstu::bwd_supported(desc->dtype, desc->d_qk))
+    return fail(HSTU_ERR_UNSUPPORTED,
+                "the backward is built for d = 64, 128 (bf16) and 8, 64, 128 (fp32), not %d",
                 desc->d_qk);
   if (desc->pos_clamp != 0)
     return fail(HSTU_ERR_UNSUPPORTED, "the backward takes the raw position bias (pos_clamp 0)");

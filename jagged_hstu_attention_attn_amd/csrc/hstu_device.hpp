@@ -367,6 +367,7 @@ constexpr bool kPPAuto = false;
 constexpr bool kW16Auto = true;
 int ln_all_heads_max_width(int dtype);
 hipError_t launch_ln_all_heads(const LnArgs& a, int dtype, hipStream_t stream);
+bool bwd_supported(int dtype, int d);
 hipError_t launch_bwd_plan(const BwdPlanArgs& a, hipStream_t stream);
 hipError_t launch_gate_bwd(const GateBwdArgs& a, int dtype, hipStream_t stream);
 // Backward passes: which = 0 (dQ), 1 (dK with the table sums; also dV for

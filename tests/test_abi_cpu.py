@@ -242,7 +242,11 @@ def test_backward_validation(lib):
     d256 = _desc(d_qk=256, d_v=256, ld_q=1024, ld_k=1024, ld_v=1024, ld_u=1024, ld_out=1024)
     assert lib.hstu_jagged_attn_workspace_bytes(ctypes.byref(d256)) > 0
     assert _bwd(lib, d256) == _lib.HSTU_ERR_UNSUPPORTED
-    assert "d = 64 and d = 128" in _lib.last_error()
+    assert "d = 64, 128 (bf16)" in _lib.last_error()
+    # fp32 d = 8 is built: it passes the shape check (and then needs a GPU)
+    d8 = _desc(d_qk=8, d_v=8, dtype=_lib.HSTU_DTYPE_F32, ld_q=32, ld_k=32, ld_v=32, ld_u=32,
+               ld_out=32)
+    assert _bwd(lib, d8) in (_lib.HSTU_OK, _lib.HSTU_ERR_HIP)
     # du is not needed without the gate
     rc = _bwd(lib, _desc(epilogue=_lib.HSTU_EPILOGUE_NONE), du=None)
     assert rc in (_lib.HSTU_OK, _lib.HSTU_ERR_HIP)
