@@ -184,7 +184,7 @@ class JaggedAttnCall:
                  contextual_len=0, max_attn_len=0, alpha, n_scale, pos_table=None,
                  time_table=None, eps=1e-5, epilogue="ln_u", out=None,
                  candidates_only: bool = False, pos_clamp: bool = False,
-                 save_o: bool = False):
+                 save_o: bool = False, workspace: Optional[torch.Tensor] = None):
         if not q.is_cuda:
             raise ValueError("tensors must be on a GPU")
         _check_aux(offsets, timestamps, num_targets, pos_table, time_table, q.device)
@@ -201,8 +201,12 @@ class JaggedAttnCall:
         self.desc = make_desc(q, k, v, u, out, offsets.numel() - 1, pos_table=pos_table,
                               time_table=time_table, eps=eps, epilogue=epilogue,
                               pos_clamp=pos_clamp)
-        self.workspace = torch.empty(workspace_bytes(self.desc), dtype=torch.uint8,
-                                     device=q.device)
+        need = workspace_bytes(self.desc)
+        if workspace is not None and (workspace.dtype != torch.uint8 or workspace.numel() < need
+                                      or workspace.device != q.device):
+            raise ValueError(f"workspace must be a uint8 tensor of >= {need} bytes on {q.device}")
+        self.workspace = (workspace[:need] if workspace is not None else
+                          torch.empty(need, dtype=torch.uint8, device=q.device))
         # save_o: the call also keeps o / n_scale before the gate (training)
         self.o_raw = (torch.empty((q.shape[0], q.shape[1], v.shape[2]), dtype=q.dtype,
                                   device=q.device) if save_o else None)
@@ -247,6 +251,21 @@ class JaggedAttnCall:
         return self.out
 
 
+# One-shot calls reuse one workspace per (device, stream): work on a stream
+# runs in order, so a call's scratch is free again for the next call on that
+# stream.  The cache keeps the largest size asked for (until the process ends).
+_ws_cache: dict = {}
+
+
+def _stream_workspace(device, nbytes: int) -> torch.Tensor:
+    key = (torch.device(device).index, torch.cuda.current_stream(device).cuda_stream)
+    ws = _ws_cache.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+        _ws_cache[key] = ws
+    return ws
+
+
 def jagged_attn_fwd(q, k, v, u, offsets, *, timestamps=None, num_targets=None,
                     contextual_len: int = 0, max_attn_len: int = 0, alpha: float,
                     n_scale: float, pos_table=None, time_table=None, eps: float = 1e-5,
@@ -254,12 +273,20 @@ def jagged_attn_fwd(q, k, v, u, offsets, *, timestamps=None, num_targets=None,
                     candidates_only: bool = False, pos_clamp: bool = False) -> torch.Tensor:
     """One full forward (scheduler + attention) on the current stream.  With
     `candidates_only`, only the candidate rows of `out` are computed and
-    written (history rows keep their contents)."""
+    written (history rows keep their contents).  The scheduler's workspace
+    is reused across calls on the same device and stream."""
+    if not q.is_cuda:
+        raise ValueError("tensors must be on a GPU")
+    if out is None:
+        out = torch.empty((q.shape[0], q.shape[1], v.shape[2]), dtype=q.dtype, device=q.device)
+    desc = make_desc(q, k, v, u, out, offsets.numel() - 1, pos_table=pos_table,
+                     time_table=time_table, eps=eps, epilogue=epilogue, pos_clamp=pos_clamp)
+    ws = _stream_workspace(q.device, workspace_bytes(desc))
     call = JaggedAttnCall(q, k, v, u, offsets, timestamps=timestamps, num_targets=num_targets,
                           contextual_len=contextual_len, max_attn_len=max_attn_len,
                           alpha=alpha, n_scale=n_scale, pos_table=pos_table,
                           time_table=time_table, eps=eps, epilogue=epilogue, out=out,
-                          candidates_only=candidates_only, pos_clamp=pos_clamp)
+                          candidates_only=candidates_only, pos_clamp=pos_clamp, workspace=ws)
     return call()
 
 

@@ -768,3 +768,37 @@ def test_pos_clamp_candidates_only():
     got = out.float().cpu().numpy().astype(np.float64)
     rows = _candidate_rows(inp)
     assert_close(got, ora(inp, rows=rows, pos_clamp=True), "bf16", rows=rows)
+
+
+def test_one_shot_calls_share_a_stream_workspace():
+    """jagged_attn_fwd keeps one workspace per (device, stream): calls of
+    different sizes in a row (the workspace grows, then is reused) and a call
+    on a second stream give the same output as a call with its own
+    workspace; a too-small caller workspace is refused."""
+    from jagged_hstu_attention_attn_amd import api
+    print("case one-shot workspace reuse", flush=True)
+    small = make_custom([40, 130], num_heads=2, d_qk=128, d_v=128, dtype="bf16", seed=3,
+                        pos_len=256, time_len=64, alpha=0.1)
+    big = make_inputs("longtail", num_seqs=6, seed=5)   # items long enough to split
+    outs = []
+    for inp in (small, big, small, big):
+        outs.append(gpu_forward(inp))
+    s2 = torch.cuda.Stream()
+    with torch.cuda.stream(s2):
+        o2 = gpu_forward(small)
+    torch.cuda.synchronize()
+    for inp, o in ((small, outs[0]), (big, outs[1])):
+        dev = to_device(inp, DEV)
+        own = JaggedAttnCall(dev["q"], dev["k"], dev["v"], dev["u"], dev["offsets"],
+                             **call_kwargs(inp, dev))()
+        torch.cuda.synchronize()
+        assert np.array_equal(o, own.float().cpu().numpy().astype(np.float64))
+    assert np.array_equal(outs[0], outs[2]) and np.array_equal(outs[1], outs[3])
+    assert np.array_equal(outs[0], o2)
+    assert_close(outs[1], ora(big), "bf16")
+    dev = to_device(small, DEV)
+    with pytest.raises(ValueError):
+        JaggedAttnCall(dev["q"], dev["k"], dev["v"], dev["u"], dev["offsets"],
+                       workspace=torch.empty(16, dtype=torch.uint8, device=DEV),
+                       **call_kwargs(small, dev))
+    assert len(api._ws_cache) >= 2
