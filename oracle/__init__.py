@@ -68,7 +68,7 @@ def _load():
             P, i64, P, i64, P, i64, P, i64,
             P, P, i32, i32, f64, f64,
             P, i32, P, i32, f64, i32, P, i64,
-            P, P, P, P, P, P, i32]
+            P, P, P, P, P, P, i32, i32]
         lib.hstu_oracle_count_allowed.restype = i64
         lib.hstu_oracle_count_allowed.argtypes = [i32, P, P, i32, i32]
         lib.hstu_oracle_time_bucket.restype = ctypes.c_int
@@ -191,10 +191,11 @@ def layer_forward(inp, *, rows=None, nthreads: Optional[int] = None) -> np.ndarr
 def backward_arrays(offsets, q, k, v, u, dout, *, timestamps=None, num_targets=None,
                     contextual_len=0, max_attn_len=0, alpha=1.0, n_scale=1.0,
                     pos_table=None, time_table=None, eps=1e-5, epilogue=EPILOGUE_LN_U,
-                    nthreads: Optional[int] = None) -> dict:
+                    nthreads: Optional[int] = None, pos_clamp=False) -> dict:
     """fp64 gradients of sum(dout * forward(...)) with respect to q, k, v, u,
-    pos_table and time_table (the C oracle's chain rule; [N, H, d] arrays).
-    Returns a dict with keys dq, dk, dv, du, dpos (or None), dtime (or None)."""
+    pos_table and time_table (the C oracle's chain rule; [N, H, d] arrays;
+    `pos_clamp` as for `forward`).  Returns a dict with keys dq, dk, dv, du,
+    dpos (or None), dtime (or None)."""
     lib = _load()
     offsets = np.ascontiguousarray(offsets, dtype=np.int32)
     q = np.ascontiguousarray(q, dtype=np.float64)
@@ -223,20 +224,21 @@ def backward_arrays(offsets, q, k, v, u, dout, *, timestamps=None, num_targets=N
         float(np.float32(eps)), int(epilogue), _ptr(dout), H * dv,
         _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["du"]),
         _ptr(g["dpos"]), _ptr(g["dtime"]),
-        int(nthreads if nthreads is not None else default_threads()))
+        int(nthreads if nthreads is not None else default_threads()), int(bool(pos_clamp)))
     if rc != 0:
         raise ValueError("oracle rejected its arguments")
     return g
 
 
-def backward(inp, dout, *, epilogue=EPILOGUE_LN_U, nthreads: Optional[int] = None) -> dict:
+def backward(inp, dout, *, epilogue=EPILOGUE_LN_U, nthreads: Optional[int] = None,
+             pos_clamp=False) -> dict:
     """fp64 gradients for a `JaggedInputs` batch and output gradient `dout`."""
     return backward_arrays(
         inp.offsets, inp.q, inp.k, inp.v, inp.u, dout, timestamps=inp.timestamps,
         num_targets=inp.num_targets, contextual_len=inp.contextual_len,
         max_attn_len=inp.max_attn_len, alpha=inp.alpha, n_scale=inp.n_scale,
         pos_table=inp.pos_table, time_table=inp.time_table, eps=inp.eps,
-        epilogue=epilogue, nthreads=nthreads)
+        epilogue=epilogue, nthreads=nthreads, pos_clamp=pos_clamp)
 
 
 def count_allowed(offsets, num_targets=None, contextual_len=0, max_attn_len=0) -> int:

@@ -307,7 +307,7 @@ int hstu_oracle_bwd(int num_seqs, const int32_t* offsets, int num_heads, int d_q
                     const double* pos_table, int pos_len, const double* time_table,
                     int time_len, double eps, int epilogue, const double* dout,
                     int64_t ld_out, double* dq, double* dk, double* dv, double* du,
-                    double* dpos, double* dtime, int nthreads) {
+                    double* dpos, double* dtime, int nthreads, int pos_clamp) {
   if (num_seqs < 0 || num_heads <= 0 || d_qk <= 0 || d_v <= 0) return -1;
   if ((pos_table != NULL && dpos == NULL) || (time_table != NULL && dtime == NULL)) return -1;
   int64_t n_tok = num_seqs > 0 ? (int64_t)offsets[num_seqs] : 0;
@@ -337,7 +337,7 @@ int hstu_oracle_bwd(int num_seqs, const int32_t* offsets, int num_heads, int d_q
   int rc = hstu_oracle_fwd(num_seqs, offsets, num_heads, d_qk, d_v, q, ld_q, k, ld_k, v, ld_v,
                            u, ld_u, timestamps, num_targets, contextual_len, max_attn_len,
                            alpha, n_scale, pos_table, pos_len, time_table, time_len, eps,
-                           ORACLE_EPILOGUE_NONE, o, width, NULL, nthreads, 0);
+                           ORACLE_EPILOGUE_NONE, o, width, NULL, nthreads, pos_clamp);
   if (rc != 0) {
     free(o);
     free(dO);
@@ -424,7 +424,11 @@ int hstu_oracle_bwd(int num_seqs, const int32_t* offsets, int num_heads, int d_q
           int64_t pidx = 0;
           int bidx = 0;
           if (pos_table) {
-            int64_t rel = i >= j ? i - j : j - i;
+            /* the forward's position index: |i - j|, or with pos_clamp the
+               distance of the clamped positions min(position, n_h) */
+            int64_t pi = pos_clamp && i > g.n_h ? g.n_h : i;
+            int64_t pj = pos_clamp && j > g.n_h ? g.n_h : j;
+            int64_t rel = pi >= pj ? pi - pj : pj - pi;
             pidx = rel < pos_len - 1 ? rel : pos_len - 1;
             s += pos_table[pidx];
           }

@@ -36,7 +36,7 @@ int hstu_oracle_bwd(int num_seqs, const int32_t* offsets, int num_heads, int d_q
                     const double* pos_table, int pos_len, const double* time_table,
                     int time_len, double eps, int epilogue, const double* dout,
                     int64_t ld_out, double* dq, double* dk, double* dv, double* du,
-                    double* dpos, double* dtime, int nthreads);
+                    double* dpos, double* dtime, int nthreads, int pos_clamp);
 }
 
 static int g_checks = 0;
@@ -275,7 +275,6 @@ static void oracle_case(const std::vector<int32_t>& lengths, int H, int d, int W
                           1, clamp ? 1 : 0) == 0);
     for (double e : out) CHECK(std::isfinite(e));
   }
-  if (clamp) return;   // the backward takes the raw position bias
   std::vector<double> dout(n_el), dq(n_el), dk(n_el), dv(n_el), du(n_el), dpos(P), dtime(T);
   for (auto& e : dout) e = nd(rng);
   for (int ep = 0; ep < 3; ++ep) {
@@ -283,7 +282,7 @@ static void oracle_case(const std::vector<int32_t>& lengths, int H, int d, int W
                           u.data(), ld, ts.data(), targets ? nt.data() : nullptr, c, W, 0.3,
                           64.0, pos.data(), P, tim.data(), T, 1e-5, ep, dout.data(), ld,
                           dq.data(), dk.data(), dv.data(), du.data(), dpos.data(), dtime.data(),
-                          1) == 0);
+                          1, clamp ? 1 : 0) == 0);
     for (auto* x : {&dq, &dk, &dv, &du, &dpos, &dtime})
       for (double e : *x) CHECK(std::isfinite(e));
   }

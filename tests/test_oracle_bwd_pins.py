@@ -20,15 +20,16 @@ _KEYS = {"q": "dq", "k": "dk", "v": "dv", "u": "du", "pos_table": "dpos",
          "time_table": "dtime"}
 
 
-def _loss(oracle_mod, inp, dout, epilogue, **repl):
+def _loss(oracle_mod, inp, dout, epilogue, pos_clamp=False, **repl):
     x = dataclasses.replace(inp, **repl)
-    return float((oracle_mod.forward(x, epilogue=epilogue, nthreads=2) * dout).sum())
+    return float((oracle_mod.forward(x, epilogue=epilogue, nthreads=2,
+                                     pos_clamp=pos_clamp) * dout).sum())
 
 
-def _fd_dir(oracle_mod, inp, dout, epilogue, name, direction, h=1e-6):
+def _fd_dir(oracle_mod, inp, dout, epilogue, name, direction, h=1e-6, pos_clamp=False):
     x = getattr(inp, name).astype(np.float64)
-    plus = _loss(oracle_mod, inp, dout, epilogue, **{name: x + h * direction})
-    minus = _loss(oracle_mod, inp, dout, epilogue, **{name: x - h * direction})
+    plus = _loss(oracle_mod, inp, dout, epilogue, pos_clamp, **{name: x + h * direction})
+    minus = _loss(oracle_mod, inp, dout, epilogue, pos_clamp, **{name: x - h * direction})
     return (plus - minus) / (2 * h)
 
 
@@ -130,3 +131,31 @@ def test_empty_batch(oracle_mod):
     g = oracle_mod.backward(inp, np.zeros((0, 1, 4)), epilogue=0)
     assert g["dq"].shape == (0, 1, 4)
     assert not np.any(g["dpos"]) and not np.any(g["dtime"])
+
+
+@pytest.mark.parametrize("geom", ["all_rules", "window"])
+def test_clamped_position_bias_gradients(oracle_mod, geom):
+    """With the position bias taken at clamped positions (p = min(position,
+    n_h), the candidate clamp of the mask applied to the bias), every
+    gradient still equals the central difference of the clamped forward:
+    along random directions for all inputs and entry by entry for the
+    position table, whose candidate pairs now land on |n_h - j|.  The
+    clamped and raw readings must differ here (the geometry has candidates
+    whose bias index changes)."""
+    inp, dout = _case(geom, seed=17)
+    g = oracle_mod.backward(inp, dout, epilogue=0, nthreads=2, pos_clamp=True)
+    raw = oracle_mod.backward(inp, dout, epilogue=0, nthreads=2)
+    assert not np.allclose(g["dpos"], raw["dpos"])
+    rng = np.random.default_rng(9)
+    for name, key in _KEYS.items():
+        x = getattr(inp, name)
+        d = rng.standard_normal(x.shape)
+        fd = _fd_dir(oracle_mod, inp, dout, 0, name, d, pos_clamp=True)
+        an = float((g[key] * d).sum())
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (name, fd, an)
+    n = inp.pos_table.shape[0]
+    for e in range(n):
+        d = np.zeros(n)
+        d[e] = 1.0
+        fd = _fd_dir(oracle_mod, inp, dout, 0, "pos_table", d, pos_clamp=True)
+        assert abs(fd - g["dpos"][e]) <= 1e-6 * max(1.0, abs(g["dpos"][e])), e
