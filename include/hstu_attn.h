@@ -36,9 +36,9 @@
  * position bias uses |p_i - p_j| instead, the clamp p = min(position, n_h) of
  * the candidate rule applied to the bias too (so candidates, all at the
  * history end, become interchangeable; "Scaling HSTU", section "Many
- * candidates make reuse valuable").  The backward takes pos_clamp = 0 only.  LayerNorm is taken per
- * (token, head) over d_v, without affine weights, with biased variance and
- * epsilon desc->ln_eps.
+ * candidates make reuse valuable"); the backward differentiates either
+ * reading.  LayerNorm is taken per (token, head) over d_v, without affine
+ * weights, with biased variance and epsilon desc->ln_eps.
  *
  * Memory layout.  q, k: [total_tokens, H, d_qk]; v, u, out: [total_tokens, H,
  * d_v].  Element (t, h, e) of tensor x lives at x + t*ld_x + h*d + e (ld_x in
@@ -111,7 +111,7 @@ typedef struct {
   float ln_eps;           /* LayerNorm epsilon (> 0 and finite)                   */
   int32_t epilogue;       /* hstu_epilogue                                        */
   int32_t pos_clamp;      /* 0: position bias of |i-j| (default); 1: of |p_i-p_j|  */
-                          /* with p = min(position, n_h) (forward only, see above) */
+                          /* with p = min(position, n_h) (see above)              */
 } hstu_attn_desc;
 
 /*

@@ -298,7 +298,7 @@ class JaggedAttnBwdCall:
 
     def __init__(self, q, k, v, u, offsets, *, timestamps=None, num_targets=None,
                  contextual_len=0, max_attn_len=0, alpha, n_scale, pos_table=None,
-                 time_table=None, eps=1e-5, epilogue="ln_u"):
+                 time_table=None, eps=1e-5, epilogue="ln_u", pos_clamp: bool = False):
         if not q.is_cuda:
             raise ValueError("tensors must be on a GPU")
         _check_aux(offsets, timestamps, num_targets, pos_table, time_table, q.device)
@@ -311,7 +311,8 @@ class JaggedAttnBwdCall:
         shape_o = (q.shape[0], q.shape[1], v.shape[2])
         out_like = torch.empty(shape_o, dtype=q.dtype, device=q.device)
         self.desc = make_desc(q, k, v, u, out_like, offsets.numel() - 1, pos_table=pos_table,
-                              time_table=time_table, eps=eps, epilogue=epilogue)
+                              time_table=time_table, eps=eps, epilogue=epilogue,
+                              pos_clamp=pos_clamp)
         n = _lib.load().hstu_jagged_attn_bwd_workspace_bytes(ctypes.byref(self.desc))
         if n == 0:
             raise _lib.HstuError(_lib.HSTU_ERR_INVALID_ARG, _lib.last_error())
@@ -350,15 +351,16 @@ class JaggedAttnBwdCall:
 def jagged_attn_bwd(q, k, v, u, offsets, dout, *, timestamps=None, num_targets=None,
                     contextual_len: int = 0, max_attn_len: int = 0, alpha: float,
                     n_scale: float, pos_table=None, time_table=None, eps: float = 1e-5,
-                    epilogue: str = "ln_u", o_saved=None):
+                    epilogue: str = "ln_u", o_saved=None, pos_clamp: bool = False):
     """Gradients (dq, dk, dv, du, dpos, dtime) of sum(dout * forward(...)),
     computed on the GPU on the current stream (o_saved: see
-    JaggedAttnBwdCall.__call__)."""
+    JaggedAttnBwdCall.__call__; pos_clamp: the position bias at clamped
+    positions, as for the forward)."""
     call = JaggedAttnBwdCall(q, k, v, u, offsets, timestamps=timestamps,
                              num_targets=num_targets, contextual_len=contextual_len,
                              max_attn_len=max_attn_len, alpha=alpha, n_scale=n_scale,
                              pos_table=pos_table, time_table=time_table, eps=eps,
-                             epilogue=epilogue)
+                             epilogue=epilogue, pos_clamp=pos_clamp)
     return call(dout, o_saved)
 
 

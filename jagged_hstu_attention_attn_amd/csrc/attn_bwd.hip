@@ -428,6 +428,8 @@ struct BStage {
   uint32_t tmin, tmax;         // range of ts32 over the valid partners
   int tbad;                    // some partner needs the 64-bit time path
   int pad_;
+  float cpos[64];              // dQ pass, clamped positions: bias of key (lane % 32),
+                               // pos[min(max(n_h - j, 0), P-1)] (scaled)
 };
 
 __host__ __device__ constexpr int copies_of_wave(int count, int w) {
@@ -441,7 +443,9 @@ __host__ __device__ constexpr int copies_of_wave(int count, int w) {
 //   i - j = dc + ds * f  (dQ: dc = i0 - j0 + 127, ds = -1; dK/dV: dc = ib -
 //   j0 - 127, ds = +1), and the lane of fixed token 32w + l32 finds register
 //   r's partner at f = dbase + 8(r/4) + r%4, dbase = 127 - 32w - l32 + 4hh.
-template <int D, bool POS, bool TIME>
+// CPS: the dQ pass with the position bias at clamped positions (each step
+// also gathers the bias of its keys at the candidates' position n_h).
+template <int D, bool POS, bool TIME, bool CPS = false>
 struct Pipe {
   using C = BCfg<D>;
   using SB = BStage<D>;
@@ -454,6 +458,8 @@ struct Pipe {
   uint32_t xoff[C::kCpW], yoff[C::kCpW];
   uint32_t ldx_b, ldy_b;
   int my_copies;
+  static constexpr bool cp_stage = POS && CPS;
+  int n_h;   // history length of the current item (cp_stage)
   // fixed-side times
   int64_t tbase;
   uint32_t tf32;
@@ -463,6 +469,7 @@ struct Pipe {
   __device__ void init(SB* s, const float* tr, const float* tf, int w, int l, int pos_len,
                        float ps, int64_t ldx, int64_t ldy) {
     st = s;
+    n_h = 0;
     trev = tr;
     tful = tf;
     wave = w;
@@ -478,7 +485,7 @@ struct Pipe {
       yoff[s2] = (uint32_t)row * ldy_b + 16u * (uint32_t)((m % C::kCh) ^ C::swz(row));
     }
     my_copies = 2 * copies_of_wave(C::kTileCp, wave) + ((POS && wave > kTsWave) ? 1 : 0) +
-                ((TIME && wave == kTsWave) ? 1 : 0);
+                ((TIME && wave == kTsWave) ? 1 : 0) + ((cp_stage && wave == kTsWave) ? 1 : 0);
   }
 
   // Copy partner tokens [p0, p0 + 32) of sequence length L (rows past the
@@ -512,6 +519,11 @@ struct Pipe {
         const int ix = min(d < 0 ? -d : d, P - 1);
         lds_copy4(pos_base, 4u * (uint32_t)ix, lds_off(sb.diag) + 256u * (uint32_t)p);
       }
+      if (cp_stage && wave == kTsWave) {   // bias of n_h - j (0 for candidate keys)
+        const int d = n_h - (p0 + (lane & (kStep - 1)));
+        const int ix = min(d > 0 ? d : 0, P - 1);
+        lds_copy4(pos_base, 4u * (uint32_t)ix, lds_off(sb.cpos));
+      }
     }
     if constexpr (TIME) {
       if (wave == kTsWave) {
@@ -531,6 +543,7 @@ struct Pipe {
         const int e = 64 * (kWaves - 1 - wave) + lane;
         if (e < kDiagN) sb.diag[e] *= pscale;
       }
+      if (cp_stage && wave == kTsWave) sb.cpos[lane] *= pscale;
     }
     if constexpr (TIME) {
       if (wave == kTsWave) {
@@ -679,12 +692,13 @@ __device__ inline float sigm(float x) {
   return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-kLog2e * x));
 }
 
-template <int D, bool POS, bool TIME>
+// CL: position bias at the clamped positions min(position, n_h).
+template <int D, bool POS, bool TIME, bool CL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void
 hstu_bwd_dq_kernel(BwdArgs a) {
   using C = BCfg<D>;
   using SB = BStage<D>;
-  using PP = Pipe<D, POS, TIME>;
+  using PP = Pipe<D, POS, TIME, CL>;
   constexpr int NC = C::kNC, NDB = C::kNDB;
   __shared__ __align__(16) SB st[kStages];
   __shared__ float trev[32], tful[64];
@@ -718,6 +732,9 @@ hstu_bwd_dq_kernel(BwdArgs a) {
 
     const int wr0 = i0 + 32 * wave, i = wr0 + l32;
     const bool row_valid = i < i1, wave_rows = wr0 < i1;
+    pp.n_h = geo.n_h;
+    // rows of candidates take the bias of the clamped positions from cpos
+    const bool w_cand = PP::cp_stage && wave_rows && wr0 + 31 >= geo.n_h;
     int w_jmin, w_jmax, w_lomax, w_himin;
     const RowBounds rb = row_valid ? row_bounds(geo, i) : RowBounds{kEmptyLo, 0, -1};
     {
@@ -797,6 +814,11 @@ hstu_bwd_dq_kernel(BwdArgs a) {
         const uint32_t xt = lds_off(sb.x), yt = lds_off(sb.y);
         const int ol = opaque_lane(), ol32 = ol & 31, ohh = ol >> 5;
         floatx16 s = pp.diag_init(sb, (kBM - 1) - 32 * wave - ol32 + 4 * ohh);
+        if (PP::cp_stage && w_cand) {
+          const bool cr = i >= geo.n_h;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[r] = cr ? sb.cpos[acc_row(r, ohh)] : s[r];
+        }
         s = PP::contract(xt, ol32, ohh, qf, s);
         __builtin_amdgcn_sched_barrier(0);
         floatx16 da = {};
@@ -888,7 +910,7 @@ hstu_bwd_dq_kernel(BwdArgs a) {
 // 2 = dV only.  At d = 128 the fused pass would need more registers than two
 // waves per SIMD leave (K and V operands plus two 32 x 128 fp32
 // accumulators), so it runs as passes 1 and 2, which recompute S.
-template <int D, bool POS, bool TIME, int M>
+template <int D, bool POS, bool TIME, int M, bool CL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void
 hstu_bwd_dkv_kernel(BwdArgs a) {
   constexpr bool DK = M != 2, DV = M != 1, TABS = DK;
@@ -935,6 +957,17 @@ hstu_bwd_dkv_kernel(BwdArgs a) {
     const int wk0 = j0 + 32 * wave, j = wk0 + l32;
     const bool key_valid = j < j1, wave_keys = wk0 < j1;
     const RowBounds cb = key_valid ? col_bounds(geo, j) : RowBounds{kEmptyLo, 0, -1};
+    // Position bias at clamped positions: candidate rows i >= n_h see this
+    // lane's key j at pos[min(max(n_h - j, 0), P-1)] (one value per lane);
+    // their share of the position-table gradient collects in cacc.
+    constexpr bool clamp = POS && CL;
+    int c_ix = 0;
+    float c_bias = 0.0f, cacc = 0.0f;
+    if constexpr (clamp) {
+      const int d = geo.n_h - j;
+      c_ix = min(d > 0 ? d : 0, P - 1);
+      c_bias = a.pos_table[c_ix] * (1.0f / am);
+    }
     int w_rmin, w_rmax, w_lomax, w_himin;
     {
       const bool nonempty = cb.lo != kEmptyLo;
@@ -1017,6 +1050,11 @@ hstu_bwd_dkv_kernel(BwdArgs a) {
         const int ol = opaque_lane(), ol32 = ol & 31, ohh = ol >> 5;
         // S[i][j] (rows in registers, this lane's key in the column)
         floatx16 s = pp.diag_init(sb, (kBM - 1) - 32 * wave - ol32 + 4 * ohh);
+        const bool step_cand = clamp && ib + kStep - 1 >= geo.n_h;
+        if (step_cand) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[r] = ib + acc_row(r, ohh) >= geo.n_h ? c_bias : s[r];
+        }
         s = PP::contract(xt, ol32, ohh, kf, s);
         __builtin_amdgcn_sched_barrier(0);
         floatx16 da = {};
@@ -1105,6 +1143,12 @@ hstu_bwd_dkv_kernel(BwdArgs a) {
                 if constexpr (DV) pa[gq >> 1][4 * (gq & 1) + e] = (__bf16)aa;
                 if constexpr (DK) pd[gq >> 1][4 * (gq & 1) + e] = (__bf16)d;
                 dg[e] = d;
+                if constexpr (clamp && TABS) {
+                  if (step_cand && ib + acc_row(r, hh) >= geo.n_h) {   // clamped index
+                    cacc += d;
+                    dg[e] = 0.0f;
+                  }
+                }
                 if constexpr (TIME && TABS) {
                   if constexpr (MODE != 0) {
                     if (r == 0) {
@@ -1166,6 +1210,10 @@ hstu_bwd_dkv_kernel(BwdArgs a) {
       b = b1;
     }
 
+    if constexpr (clamp && TABS) {
+      if (key_valid && cacc != 0.0f)
+        __hip_atomic_fetch_add(&hpos[c_ix], cacc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
     if (key_valid) {
       char* dk = reinterpret_cast<char*>(a.dk) + ((int64_t)(seq0 + j) * a.ld_k + (int64_t)h * D) * 2;
       char* dv = reinterpret_cast<char*>(a.dv) + ((int64_t)(seq0 + j) * a.ld_v + (int64_t)h * D) * 2;
@@ -1270,7 +1318,14 @@ __device__ inline int seq_of(const int32_t* offsets, int num_seqs, int t) {
   return lo;
 }
 
-// Score of (i, j) of one head: alpha <qi, kj> + biases (lanes hold e = lane + 64 m).
+// Position of token x for the position bias: x, or with the bias at clamped
+// positions min(x, n_h).
+__device__ inline int bias_pos(const BwdArgs& a, const SeqGeom& g, int x) {
+  return a.pos_clamp && x > g.n_h ? g.n_h : x;
+}
+
+// Score of (i, j) of one head: alpha <qi, kj> + biases (lanes hold e = lane + 64 m);
+// i and j are the bias positions of the pair.
 template <int E>
 __device__ inline float f32_score(const BwdArgs& a, const float* qi, const float* kj, int i, int j,
                                   int64_t ti, int64_t tj, int& pidx, int& tidx) {
@@ -1329,7 +1384,7 @@ __global__ __launch_bounds__(256) void hstu_bwd_dq_f32_kernel(BwdArgs a, int num
     }
     int pidx = 0, tidx = 0;
     const int64_t tj = a.time_len > 0 ? a.timestamps[seq0 + j] : 0;
-    const float s = f32_score<E>(a, qi, kj, i, j, ti, tj, pidx, tidx);
+    const float s = f32_score<E>(a, qi, kj, bias_pos(a, geo, i), bias_pos(a, geo, j), ti, tj, pidx, tidx);
     float dd = 0.0f;
 #pragma unroll
     for (int m = 0; m < E; ++m) dd += doi[m] * vj[m];
@@ -1390,7 +1445,7 @@ __global__ __launch_bounds__(256) void hstu_bwd_dkv_f32_kernel(BwdArgs a, int nu
     }
     int pidx = 0, tidx = 0;
     const int64_t ti = a.time_len > 0 ? a.timestamps[seq0 + i] : 0;
-    const float s = f32_score<E>(a, qi, kj, i, j, ti, tj, pidx, tidx);
+    const float s = f32_score<E>(a, qi, kj, bias_pos(a, geo, i), bias_pos(a, geo, j), ti, tj, pidx, tidx);
     float dd = 0.0f;
 #pragma unroll
     for (int m = 0; m < E; ++m) dd += doi[m] * vj[m];
@@ -1429,54 +1484,58 @@ size_t dkv_dyn_lds(int which, int pos_len) {
   return (POS && which == 1) ? sizeof(float) * (size_t)pos_len : 0;
 }
 
-template <int D, bool POS, bool TIME>
+template <int D, bool POS, bool TIME, bool CL>
 int bpc_one(int which, int pos_len) {
   int nb = 0;
   hipError_t e;
   const size_t dyn = dkv_dyn_lds<D, POS, TIME>(which, pos_len);
   if (which == 1)
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &nb, hstu_bwd_dkv_kernel<D, POS, TIME, kv_mode_tab<D>()>, kThreads, dyn);
+        &nb, hstu_bwd_dkv_kernel<D, POS, TIME, kv_mode_tab<D>(), CL>, kThreads, dyn);
   else if (which == 2)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, hstu_bwd_dkv_kernel<D, POS, TIME, 2>,
-                                                     kThreads, 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &nb, hstu_bwd_dkv_kernel<D, POS, TIME, 2, CL>, kThreads, 0);
   else
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, hstu_bwd_dq_kernel<D, POS, TIME>,
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, hstu_bwd_dq_kernel<D, POS, TIME, CL>,
                                                      kThreads, 0);
   return e == hipSuccess ? nb : -1;
 }
 
 template <int D>
-int bpc_d(int which, int pos_len, int time_len) {
-  const bool pos = pos_len > 0, tim = time_len > 0;
-  if (pos && tim) return bpc_one<D, true, true>(which, pos_len);
-  if (pos) return bpc_one<D, true, false>(which, pos_len);
-  if (tim) return bpc_one<D, false, true>(which, pos_len);
-  return bpc_one<D, false, false>(which, pos_len);
+int bpc_d(int which, int pos_len, int time_len, bool clamp) {
+  const bool pos = pos_len > 0, tim = time_len > 0, cl = pos && clamp;
+  if (cl && tim) return bpc_one<D, true, true, true>(which, pos_len);
+  if (cl) return bpc_one<D, true, false, true>(which, pos_len);
+  if (pos && tim) return bpc_one<D, true, true, false>(which, pos_len);
+  if (pos) return bpc_one<D, true, false, false>(which, pos_len);
+  if (tim) return bpc_one<D, false, true, false>(which, pos_len);
+  return bpc_one<D, false, false, false>(which, pos_len);
 }
 
-template <int D, bool POS, bool TIME>
+template <int D, bool POS, bool TIME, bool CL>
 hipError_t launch_mfma_one(const BwdArgs& a, int which, int n_wg, hipStream_t stream) {
   const size_t dyn = dkv_dyn_lds<D, POS, TIME>(which, a.pos_len);
   if (which == 1)
-    hipLaunchKernelGGL((hstu_bwd_dkv_kernel<D, POS, TIME, kv_mode_tab<D>()>),
+    hipLaunchKernelGGL((hstu_bwd_dkv_kernel<D, POS, TIME, kv_mode_tab<D>(), CL>),
                        dim3((unsigned)n_wg), dim3(kThreads), dyn, stream, a);
   else if (which == 2)
-    hipLaunchKernelGGL((hstu_bwd_dkv_kernel<D, POS, TIME, 2>), dim3((unsigned)n_wg),
+    hipLaunchKernelGGL((hstu_bwd_dkv_kernel<D, POS, TIME, 2, CL>), dim3((unsigned)n_wg),
                        dim3(kThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL((hstu_bwd_dq_kernel<D, POS, TIME>), dim3((unsigned)n_wg), dim3(kThreads),
-                       0, stream, a);
+    hipLaunchKernelGGL((hstu_bwd_dq_kernel<D, POS, TIME, CL>), dim3((unsigned)n_wg),
+                       dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_mfma_d(const BwdArgs& a, int which, int n_wg, hipStream_t stream) {
-  const bool pos = a.pos_len > 0, tim = a.time_len > 0;
-  if (pos && tim) return launch_mfma_one<D, true, true>(a, which, n_wg, stream);
-  if (pos) return launch_mfma_one<D, true, false>(a, which, n_wg, stream);
-  if (tim) return launch_mfma_one<D, false, true>(a, which, n_wg, stream);
-  return launch_mfma_one<D, false, false>(a, which, n_wg, stream);
+  const bool pos = a.pos_len > 0, tim = a.time_len > 0, cl = pos && a.pos_clamp != 0;
+  if (cl && tim) return launch_mfma_one<D, true, true, true>(a, which, n_wg, stream);
+  if (cl) return launch_mfma_one<D, true, false, true>(a, which, n_wg, stream);
+  if (pos && tim) return launch_mfma_one<D, true, true, false>(a, which, n_wg, stream);
+  if (pos) return launch_mfma_one<D, true, false, false>(a, which, n_wg, stream);
+  if (tim) return launch_mfma_one<D, false, true, false>(a, which, n_wg, stream);
+  return launch_mfma_one<D, false, false, false>(a, which, n_wg, stream);
 }
 
 template <int D>
@@ -1526,12 +1585,12 @@ hipError_t launch_gate_bwd(const GateBwdArgs& a, int dtype, hipStream_t stream) 
   return dtype == 1 ? launch_gate_t<__bf16, 8>(a, stream) : launch_gate_t<float, 4>(a, stream);
 }
 
-int bwd_grid(int dtype, int d, int pos_len, int time_len, int which) {
+int bwd_grid(int dtype, int d, int pos_len, int time_len, int which, bool clamp) {
   if (dtype != 1) return 1;   // fp32 kernels are not persistent
   if (which == 2 && d != 128) return 0;   // no separate dV pass
   int bpc = -1;
-  if (d == 128) bpc = bpc_d<128>(which, pos_len, time_len);
-  if (d == 64) bpc = bpc_d<64>(which, pos_len, time_len);
+  if (d == 128) bpc = bpc_d<128>(which, pos_len, time_len, clamp);
+  if (d == 64) bpc = bpc_d<64>(which, pos_len, time_len, clamp);
   if (bpc <= 0) return -1;
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess) return -1;

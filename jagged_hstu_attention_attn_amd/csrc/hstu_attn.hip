@@ -781,21 +781,24 @@ BwdLayout bwd_layout(const hstu_attn_desc* d) {
 // Workgroups of a persistent backward pass (cached per device and variant).
 int bwd_pass_grid(const hstu_attn_desc* d, int which) {
   struct Entry {
-    int dev, d, pos_len, has_time, which, grid;
+    int dev, d, pos_len, has_time, clamp, which, grid;
   };
   static thread_local Entry cache[16];
   static thread_local int cache_n = 0;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return -1;
   const int has_time = d->time_table_len > 0 ? 1 : 0;
+  const int clamp = d->pos_clamp != 0 && d->pos_table_len > 0 ? 1 : 0;
   for (int e = 0; e < cache_n && e < 16; ++e) {
     const Entry& c = cache[e];
     if (c.dev == dev && c.d == d->d_v && c.pos_len == d->pos_table_len &&
-        c.has_time == has_time && c.which == which)
+        c.has_time == has_time && c.clamp == clamp && c.which == which)
       return c.grid;
   }
-  const int g = hstu::bwd_grid(d->dtype, d->d_v, d->pos_table_len, d->time_table_len, which);
-  if (g >= 0) cache[cache_n++ % 16] = Entry{dev, d->d_v, d->pos_table_len, has_time, which, g};
+  const int g = hstu::bwd_grid(d->dtype, d->d_v, d->pos_table_len, d->time_table_len, which,
+                               clamp != 0);
+  if (g >= 0)
+    cache[cache_n++ % 16] = Entry{dev, d->d_v, d->pos_table_len, has_time, clamp, which, g};
   return g;
 }
 
@@ -825,8 +828,6 @@ int hstu_jagged_attn_bwd(const hstu_attn_desc* desc, const void* q, const void* 
     return fail(HSTU_ERR_UNSUPPORTED,
                 "the backward is built for d = 64, 128 (bf16) and 8, 64, 128 (fp32), not %d",
                 desc->d_qk);
-  if (desc->pos_clamp != 0)
-    return fail(HSTU_ERR_UNSUPPORTED, "the backward takes the raw position bias (pos_clamp 0)");
   if (desc->num_seqs > 0 && !offsets) return fail(HSTU_ERR_INVALID_ARG, "offsets is NULL");
   if (contextual_len < 0) return fail(HSTU_ERR_INVALID_ARG, "contextual_len < 0");
   if (max_attn_len < 0) return fail(HSTU_ERR_INVALID_ARG, "max_attn_len < 0");
@@ -954,6 +955,7 @@ int hstu_jagged_attn_bwd(const hstu_attn_desc* desc, const void* q, const void* 
   ba.n_tok = desc->total_tokens;
   ba.alpha = alpha;
   ba.inv_scale = (float)(1.0 / (double)n_scale);
+  ba.pos_clamp = desc->pos_clamp != 0 && desc->pos_table_len > 0;
   if (!bf16) {
     e = hstu::launch_bwd(ba, desc->dtype, desc->d_v, 0, desc->num_seqs, s);
     if (e == hipSuccess) e = hstu::launch_bwd(ba, desc->dtype, desc->d_v, 1, desc->num_seqs, s);

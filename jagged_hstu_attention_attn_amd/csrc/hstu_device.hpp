@@ -305,6 +305,7 @@ struct BwdArgs {
   int32_t n_tok;
   float alpha;
   float inv_scale;           // 1 / n_scale
+  int32_t pos_clamp;         // position bias of the clamped positions min(p, n_h)
 };
 
 struct GateBwdArgs {
@@ -375,7 +376,7 @@ hipError_t launch_gate_bwd(const GateBwdArgs& a, int dtype, hipStream_t stream);
 // persistent launch size (CUs x resident workgroups per CU), 0 for a pass
 // that does not exist, or a negative value on error; for fp32 n_wg of
 // launch_bwd is the number of sequences instead.
-int bwd_grid(int dtype, int d, int pos_len, int time_len, int which);
+int bwd_grid(int dtype, int d, int pos_len, int time_len, int which, bool clamp = false);
 hipError_t launch_bwd(const BwdArgs& a, int dtype, int d, int which, int n_wg,
                       hipStream_t stream);
 hipError_t launch_tab_reduce(const TabReduceArgs& a, hipStream_t stream);

@@ -217,8 +217,8 @@ static void abi_checks() {
     CHECK(bwd(b, kFake, kFake, 1u << 30) == HSTU_ERR_UNSUPPORTED);   // forward-only shape
     check_message();
     b = base_desc();
-    b.pos_clamp = 1;
-    CHECK(bwd(b, kFake, kFake, 1u << 30) == HSTU_ERR_UNSUPPORTED);
+    b.pos_clamp = 2;   // a flag: 0 or 1
+    CHECK(bwd(b, kFake, kFake, 1u << 30) == HSTU_ERR_INVALID_ARG);
   }
 
   // layer

@@ -33,11 +33,11 @@ def make_dout(inp, seed=0):
     return bf16_round(x) if inp.dtype == "bf16" else x
 
 
-def gpu_backward(inp, dout, epilogue="ln_u"):
+def gpu_backward(inp, dout, epilogue="ln_u", pos_clamp=False):
     dev = to_device(inp, DEV)
     dO = torch.from_numpy(np.ascontiguousarray(dout, dtype=np.float32)).to(DEV, _TORCH[inp.dtype])
     g = jagged_attn_bwd(dev["q"], dev["k"], dev["v"], dev["u"], dev["offsets"], dO,
-                        epilogue=epilogue, **call_kwargs(inp, dev))
+                        epilogue=epilogue, pos_clamp=pos_clamp, **call_kwargs(inp, dev))
     torch.cuda.synchronize()
     to = lambda t: None if t is None else t.float().cpu().numpy().astype(np.float64)
     return dict(zip(("dq", "dk", "dv", "du", "dpos", "dtime"), (to(t) for t in g)))
@@ -201,6 +201,17 @@ def test_bwd_windowed_four_sequences_with_tables():
     assert_grads(gpu_backward(inp, dout), oracle.backward(inp, dout), "bf16")
 
 
+def test_bwd_windowed_clamped_position_bias():
+    """Two whole sequences of the windowed workload with the position bias at
+    clamped positions: the 50 candidates of each see the history at pos[n_h -
+    j]; every token gradient and both table gradients."""
+    print("case bwd windowed 2 sequences pos_clamp", flush=True)
+    inp = make_inputs("windowed", num_seqs=2)
+    dout = make_dout(inp, 16)
+    assert_grads(gpu_backward(inp, dout, pos_clamp=True),
+                 oracle.backward(inp, dout, pos_clamp=True), "bf16")
+
+
 def test_bwd_longtail_reduced_with_tables():
     inp = make_inputs("longtail", num_seqs=6)
     dout = make_dout(inp, 14)
@@ -242,3 +253,26 @@ def test_training_forward_and_saved_o(dtype, d, epilogue):
     to = lambda t: None if t is None else t.float().cpu().numpy().astype(np.float64)
     assert_grads(dict(zip(("dq", "dk", "dv", "du", "dpos", "dtime"), (to(t) for t in g_sv))),
                  ref, dtype, epilogue)
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 8)])
+def test_bwd_clamped_position_bias(dtype, d):
+    """Position bias at the clamped positions min(position, n_h): candidate
+    rows see history key j at pos[n_h - j] and themselves at pos[0].  Every
+    gradient, both tables included, against the oracle's backward with the
+    same reading; candidate tiles past the first query tile, a window and a
+    prefix, lengths at tile edges.  The raw reading's position-table gradient
+    differs here (the clamp is exercised)."""
+    print(f"case bwd pos_clamp {dtype} d={d}", flush=True)
+    lengths = [300, 129, 40, 5]
+    inp = make_custom(lengths, num_heads=2, d_qk=d, d_v=d, dtype=dtype, seed=23,
+                      num_targets=[150, 40, 7, 2], contextual_len=3, max_attn_len=96,
+                      pos_len=320, pos_std=0.3, time_len=32, time_std=0.3,
+                      alpha=1.0 / np.sqrt(d))
+    dout = make_dout(inp, seed=4)
+    for epilogue in ("ln_u", "none"):
+        ref = oracle.backward(inp, dout, epilogue=_EP[epilogue], pos_clamp=True)
+        got = gpu_backward(inp, dout, epilogue, pos_clamp=True)
+        assert_grads(got, ref, dtype, epilogue)
+    raw = oracle.backward(inp, dout, epilogue=_EP["ln_u"])
+    assert not np.allclose(raw["dpos"], ref["dpos"])
