@@ -418,10 +418,11 @@ struct BCfg {
   }
 };
 
-template <int D>
+// DX: head size of the x rows (K or Q: d_qk), DY: of the y rows (V or dO: d_v).
+template <int DX, int DY>
 struct BStage {
-  char x[kStep * 2 * D];       // K (dQ pass) or Q (dK/dV pass) rows, chunks swizzled
-  char y[kStep * 2 * D];       // V or dO rows
+  char x[kStep * 2 * DX];      // K (dQ pass) or Q (dK/dV pass) rows, chunks swizzled
+  char y[kStep * 2 * DY];      // V or dO rows
   float diag[kDiagCp * 64];    // position bias by i - j (scaled), see diag_rel
   int64_t ts64[kStep];         // raw partner timestamps
   uint32_t ts32[kStep];        // partner timestamps relative to the item's base
@@ -445,17 +446,18 @@ __host__ __device__ constexpr int copies_of_wave(int count, int w) {
 //   r's partner at f = dbase + 8(r/4) + r%4, dbase = 127 - 32w - l32 + 4hh.
 // CPS: the dQ pass with the position bias at clamped positions (each step
 // also gathers the bias of its keys at the candidates' position n_h).
-template <int D, bool POS, bool TIME, bool CPS = false>
+template <int DX, int DY, bool POS, bool TIME, bool CPS = false>
 struct Pipe {
-  using C = BCfg<D>;
-  using SB = BStage<D>;
+  using CX = BCfg<DX>;   // x rows (d_qk)
+  using CY = BCfg<DY>;   // y rows (d_v)
+  using SB = BStage<DX, DY>;
   SB* st;                 // kStages buffers
   const float* trev;      // trev[z] = time[min(31 - z, Tt - 1)], z = clz(1 + |dt|)
   const float* tful;      // tful[b] = time[min(b, Tt - 1)]
   int wave, lane;
   int P;
   float pscale;
-  uint32_t xoff[C::kCpW], yoff[C::kCpW];
+  uint32_t xoff[CX::kCpW], yoff[CY::kCpW];
   uint32_t ldx_b, ldy_b;
   int my_copies;
   static constexpr bool cp_stage = POS && CPS;
@@ -479,12 +481,17 @@ struct Pipe {
     ldx_b = (uint32_t)(ldx * 2);
     ldy_b = (uint32_t)(ldy * 2);
 #pragma unroll
-    for (int s2 = 0; s2 < C::kCpW; ++s2) {
-      const int m = 64 * (s2 * kWaves + wave) + lane, row = m / C::kCh;
-      xoff[s2] = (uint32_t)row * ldx_b + 16u * (uint32_t)((m % C::kCh) ^ C::swz(row));
-      yoff[s2] = (uint32_t)row * ldy_b + 16u * (uint32_t)((m % C::kCh) ^ C::swz(row));
+    for (int s2 = 0; s2 < CX::kCpW; ++s2) {
+      const int m = 64 * (s2 * kWaves + wave) + lane, row = m / CX::kCh;
+      xoff[s2] = (uint32_t)row * ldx_b + 16u * (uint32_t)((m % CX::kCh) ^ CX::swz(row));
     }
-    my_copies = 2 * copies_of_wave(C::kTileCp, wave) + ((POS && wave > kTsWave) ? 1 : 0) +
+#pragma unroll
+    for (int s2 = 0; s2 < CY::kCpW; ++s2) {
+      const int m = 64 * (s2 * kWaves + wave) + lane, row = m / CY::kCh;
+      yoff[s2] = (uint32_t)row * ldy_b + 16u * (uint32_t)((m % CY::kCh) ^ CY::swz(row));
+    }
+    my_copies = copies_of_wave(CX::kTileCp, wave) + copies_of_wave(CY::kTileCp, wave) +
+                ((POS && wave > kTsWave) ? 1 : 0) +
                 ((TIME && wave == kTsWave) ? 1 : 0) + ((cp_stage && wave == kTsWave) ? 1 : 0);
   }
 
@@ -497,18 +504,28 @@ struct Pipe {
     const bool whole = p0 + kStep <= L;
     const uint64_t xb = xbase + (uint64_t)p0 * ldx_b, yb = ybase + (uint64_t)p0 * ldy_b;
 #pragma unroll
-    for (int s2 = 0; s2 < C::kCpW; ++s2) {
+    for (int s2 = 0; s2 < CX::kCpW; ++s2) {
       const int n = s2 * kWaves + wave;
-      if (n < C::kTileCp) {
-        uint32_t ox = xoff[s2], oy = yoff[s2];
+      if (n < CX::kTileCp) {
+        uint32_t ox = xoff[s2];
         if (!whole) {
-          const int m = 64 * n + lane, row = m / C::kCh;
+          const int m = 64 * n + lane, row = m / CX::kCh;
           const uint32_t rr = (uint32_t)min(row, L - 1 - p0);
-          const uint32_t ch = 16u * (uint32_t)((m % C::kCh) ^ C::swz(row));
-          ox = rr * ldx_b + ch;
-          oy = rr * ldy_b + ch;
+          ox = rr * ldx_b + 16u * (uint32_t)((m % CX::kCh) ^ CX::swz(row));
         }
         lds_copy16(xb, ox, lds_off(sb.x) + 1024u * (uint32_t)n);
+      }
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < CY::kCpW; ++s2) {
+      const int n = s2 * kWaves + wave;
+      if (n < CY::kTileCp) {
+        uint32_t oy = yoff[s2];
+        if (!whole) {
+          const int m = 64 * n + lane, row = m / CY::kCh;
+          const uint32_t rr = (uint32_t)min(row, L - 1 - p0);
+          oy = rr * ldy_b + 16u * (uint32_t)((m % CY::kCh) ^ CY::swz(row));
+        }
         lds_copy16(yb, oy, lds_off(sb.y) + 1024u * (uint32_t)n);
       }
     }
@@ -643,19 +660,20 @@ struct Pipe {
     return s;
   }
 
-  // acc += tile rows (A, row reads) x f (B operands in registers), over d,
-  // with the operand reads issued in two halves.
+  // acc += tile rows (A, row reads) x f (B operands in registers), over the
+  // d of side CC, with the operand reads issued in two halves.
+  template <typename CC>
   __device__ static floatx16 contract(uint32_t tile, int l32, int hh, const bf16x8* f,
                                       floatx16 acc) {
-    constexpr int NH = C::kNC / 2;
+    constexpr int NH = CC::kNC / 2;
     bf16x8 op[NH];
 #pragma unroll
-    for (int c = 0; c < NH; ++c) op[c] = row_op(tile, l32, hh, c);
+    for (int c = 0; c < NH; ++c) op[c] = row_op<CC>(tile, l32, hh, c);
 #pragma unroll
     for (int c = 0; c < NH; ++c)
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[c], f[c], acc, 0, 0, 0);
 #pragma unroll
-    for (int c = 0; c < NH; ++c) op[c] = row_op(tile, l32, hh, NH + c);
+    for (int c = 0; c < NH; ++c) op[c] = row_op<CC>(tile, l32, hh, NH + c);
 #pragma unroll
     for (int c = 0; c < NH; ++c)
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[c], f[NH + c], acc, 0, 0, 0);
@@ -663,9 +681,10 @@ struct Pipe {
   }
 
   // Row-read A operand (rows l32 of a staged tile, logical chunk 2c + hh).
+  template <typename CC>
   __device__ static bf16x8 row_op(uint32_t tile, int l32, int hh, int c) {
-    return lds_ld<bf16x8>(tile + (uint32_t)(l32 * C::kRow) +
-                          16u * (uint32_t)((2 * c + hh) ^ C::swz(l32)));
+    return lds_ld<bf16x8>(tile + (uint32_t)(l32 * CC::kRow) +
+                          16u * (uint32_t)((2 * c + hh) ^ CC::swz(l32)));
   }
   // Transposed A operand of d-block db and contraction block ins: lane
   // (e = 32 db + l32, half hh) gets the tile's rows 16 ins + 4hh + {0..3} and
@@ -673,14 +692,15 @@ struct Pipe {
   // coefficients it multiplies.  ds_read_b64_tr_b16: in each 16-lane group,
   // lane 4e'+q reads 4 values of row e' at columns 4q..4q+3 of the group's 16
   // columns, and lane c of the group receives column c of the 4 rows.
+  template <typename CC>
   __device__ static bf16x8 tr_op(uint32_t tile, int lane, int db, int ins) {
     const int gl = lane & 15, grp = lane >> 4, er = gl >> 2, h2 = lane >> 5;
     const int col = 32 * db + 16 * (grp & 1) + 4 * (gl & 3);
     const int r0 = 16 * ins + 4 * h2 + er, r1 = r0 + 8;
-    const uint32_t a0 = tile + (uint32_t)(r0 * C::kRow) +
-                        16u * (uint32_t)((col >> 3) ^ C::swz(r0)) + 2u * (uint32_t)(col & 7);
-    const uint32_t a1 = tile + (uint32_t)(r1 * C::kRow) +
-                        16u * (uint32_t)((col >> 3) ^ C::swz(r1)) + 2u * (uint32_t)(col & 7);
+    const uint32_t a0 = tile + (uint32_t)(r0 * CC::kRow) +
+                        16u * (uint32_t)((col >> 3) ^ CC::swz(r0)) + 2u * (uint32_t)(col & 7);
+    const uint32_t a1 = tile + (uint32_t)(r1 * CC::kRow) +
+                        16u * (uint32_t)((col >> 3) ^ CC::swz(r1)) + 2u * (uint32_t)(col & 7);
     const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_ptr4(a0));
     const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_ptr4(a1));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -693,13 +713,14 @@ __device__ inline float sigm(float x) {
 }
 
 // CL: position bias at the clamped positions min(position, n_h).
-template <int D, bool POS, bool TIME, bool CL>
+template <int DQK, int DV, bool POS, bool TIME, bool CL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void
 hstu_bwd_dq_kernel(BwdArgs a) {
-  using C = BCfg<D>;
-  using SB = BStage<D>;
-  using PP = Pipe<D, POS, TIME, CL>;
-  constexpr int NC = C::kNC, NDB = C::kNDB;
+  using CX = BCfg<DQK>;   // K rows
+  using CY = BCfg<DV>;    // V rows
+  using SB = BStage<DQK, DV>;
+  using PP = Pipe<DQK, DV, POS, TIME, CL>;
+  constexpr int NCX = CX::kNC, NCY = CY::kNC, NDB = CX::kNDB;
   __shared__ __align__(16) SB st[kStages];
   __shared__ float trev[32], tful[64];
 
@@ -753,9 +774,9 @@ hstu_bwd_dq_kernel(BwdArgs a) {
     }
 
     const uint64_t kseq = uni_ptr(reinterpret_cast<const char*>(a.k) +
-                                  ((int64_t)seq0 * a.ld_k + (int64_t)h * D) * 2);
+                                  ((int64_t)seq0 * a.ld_k + (int64_t)h * DQK) * 2);
     const uint64_t vseq = uni_ptr(reinterpret_cast<const char*>(a.v) +
-                                  ((int64_t)seq0 * a.ld_v + (int64_t)h * D) * 2);
+                                  ((int64_t)seq0 * a.ld_v + (int64_t)h * DV) * 2);
     const uint64_t pos_base = POS ? uni_ptr(a.pos_table) : 0;
     const uint64_t ts_base = TIME ? uni_ptr(a.timestamps + seq0) : 0;
     auto issue = [&](int b, int kt) __attribute__((always_inline)) {
@@ -766,19 +787,22 @@ hstu_bwd_dq_kernel(BwdArgs a) {
     issue(0, kt_lo);
     if (kt_lo + 1 <= kt_hi) issue(1, kt_lo + 1);
     // Q and dO rows of this lane (B operands), row times
-    bf16x8 qf[NC], dof[NC];
+    bf16x8 qf[NCX], dof[NCY];
     {
       const int ir = min(i, i1 - 1);
       const char* qrow = reinterpret_cast<const char*>(a.q) +
-                         ((int64_t)(seq0 + ir) * a.ld_q + (int64_t)h * D) * 2;
+                         ((int64_t)(seq0 + ir) * a.ld_q + (int64_t)h * DQK) * 2;
       const char* drow = reinterpret_cast<const char*>(a.dout) +
-                         ((int64_t)(seq0 + ir) * a.ld_do + (int64_t)h * D) * 2;
+                         ((int64_t)(seq0 + ir) * a.ld_do + (int64_t)h * DV) * 2;
       const bf16x8 z = {};
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
+      for (int c = 0; c < NCX; ++c) {
         const bf16x8 qv = *reinterpret_cast<const bf16x8*>(qrow + 16 * (2 * c + hh));
-        const bf16x8 dv = *reinterpret_cast<const bf16x8*>(drow + 16 * (2 * c + hh));
         qf[c] = (row_valid && !alpha_zero) ? qv : z;
+      }
+#pragma unroll
+      for (int c = 0; c < NCY; ++c) {
+        const bf16x8 dv = *reinterpret_cast<const bf16x8*>(drow + 16 * (2 * c + hh));
         dof[c] = row_valid ? dv : z;
       }
     }
@@ -819,10 +843,10 @@ hstu_bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) s[r] = cr ? sb.cpos[acc_row(r, ohh)] : s[r];
         }
-        s = PP::contract(xt, ol32, ohh, qf, s);
+        s = PP::template contract<CX>(xt, ol32, ohh, qf, s);
         __builtin_amdgcn_sched_barrier(0);
         floatx16 da = {};
-        da = PP::contract(yt, ol32, ohh, dof, da);
+        da = PP::template contract<CY>(yt, ol32, ohh, dof, da);
         __builtin_amdgcn_sched_barrier(0);
 
         // dS^T = dA^T SiLU'(x), zero on illegal pairs (time bias, SiLU'
@@ -875,7 +899,8 @@ hstu_bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
           for (int u2 = 0; u2 < 2; ++u2)
 #pragma unroll
-            for (int ins = 0; ins < 2; ++ins) kt4[2 * u2 + ins] = PP::tr_op(xt, ol, db + u2, ins);
+            for (int ins = 0; ins < 2; ++ins)
+              kt4[2 * u2 + ins] = PP::template tr_op<CX>(xt, ol, db + u2, ins);
 #pragma unroll
           for (int u2 = 0; u2 < 2; ++u2)
 #pragma unroll
@@ -891,7 +916,8 @@ hstu_bwd_dq_kernel(BwdArgs a) {
 
     // dq row i: acc[db][r] holds d-index 32 db + acc_row(r, hh)
     if (row_valid) {
-      char* dst = reinterpret_cast<char*>(a.dq) + ((int64_t)(seq0 + i) * a.ld_q + (int64_t)h * D) * 2;
+      char* dst =
+          reinterpret_cast<char*>(a.dq) + ((int64_t)(seq0 + i) * a.ld_q + (int64_t)h * DQK) * 2;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -910,14 +936,16 @@ hstu_bwd_dq_kernel(BwdArgs a) {
 // 2 = dV only.  At d = 128 the fused pass would need more registers than two
 // waves per SIMD leave (K and V operands plus two 32 x 128 fp32
 // accumulators), so it runs as passes 1 and 2, which recompute S.
-template <int D, bool POS, bool TIME, int M, bool CL>
+template <int DQK, int DVV, bool POS, bool TIME, int M, bool CL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void
 hstu_bwd_dkv_kernel(BwdArgs a) {
   constexpr bool DK = M != 2, DV = M != 1, TABS = DK;
-  using C = BCfg<D>;
-  using SB = BStage<D>;
-  using PP = Pipe<D, POS, TIME>;
-  constexpr int NC = C::kNC, NDB = C::kNDB;
+  using CX = BCfg<DQK>;   // Q rows
+  using CY = BCfg<DVV>;   // dO rows
+  using SB = BStage<DQK, DVV>;
+  using PP = Pipe<DQK, DVV, POS, TIME>;
+  constexpr int NCX = CX::kNC, NCY = CY::kNC, NDBX = CX::kNDB, NDBY = CY::kNDB;
+  constexpr int NDBM = NDBX > NDBY ? NDBX : NDBY;
   __shared__ __align__(16) SB st[kStages];
   __shared__ float trev[32], tful[64];
   __shared__ float htime[(TIME && TABS) ? kTimeBins * 32 : 1];   // [bin][lane % 32]
@@ -985,9 +1013,9 @@ hstu_bwd_dkv_kernel(BwdArgs a) {
     }
 
     const uint64_t qseq = uni_ptr(reinterpret_cast<const char*>(a.q) +
-                                  ((int64_t)seq0 * a.ld_q + (int64_t)h * D) * 2);
+                                  ((int64_t)seq0 * a.ld_q + (int64_t)h * DQK) * 2);
     const uint64_t dseq = uni_ptr(reinterpret_cast<const char*>(a.dout) +
-                                  ((int64_t)seq0 * a.ld_do + (int64_t)h * D) * 2);
+                                  ((int64_t)seq0 * a.ld_do + (int64_t)h * DVV) * 2);
     const uint64_t pos_base = POS ? uni_ptr(a.pos_table) : 0;
     const uint64_t ts_base = TIME ? uni_ptr(a.timestamps + seq0) : 0;
     auto issue = [&](int b, int stp) __attribute__((always_inline)) {
@@ -998,20 +1026,25 @@ hstu_bwd_dkv_kernel(BwdArgs a) {
     issue(0, st_lo);
     if (st_lo + 1 <= st_hi) issue(1, st_lo + 1);
     // K and V rows of this lane's key (B operands), key times
-    bf16x8 kf[NC], vf[DK ? NC : 1];
+    bf16x8 kf[NCX], vf[DK ? NCY : 1];
     {
       const int jr = min(j, j1 - 1);
       const char* krow = reinterpret_cast<const char*>(a.k) +
-                         ((int64_t)(seq0 + jr) * a.ld_k + (int64_t)h * D) * 2;
+                         ((int64_t)(seq0 + jr) * a.ld_k + (int64_t)h * DQK) * 2;
       const char* vrow = reinterpret_cast<const char*>(a.v) +
-                         ((int64_t)(seq0 + jr) * a.ld_v + (int64_t)h * D) * 2;
+                         ((int64_t)(seq0 + jr) * a.ld_v + (int64_t)h * DVV) * 2;
       const bf16x8 z = {};
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
+      for (int c = 0; c < NCX; ++c) {
         const bf16x8 kv = *reinterpret_cast<const bf16x8*>(krow + 16 * (2 * c + hh));
-        const bf16x8 vv = DK ? *reinterpret_cast<const bf16x8*>(vrow + 16 * (2 * c + hh)) : z;
         kf[c] = (key_valid && !alpha_zero) ? kv : z;
-        if constexpr (DK) vf[c] = key_valid ? vv : z;
+      }
+      if constexpr (DK) {
+#pragma unroll
+        for (int c = 0; c < NCY; ++c) {
+          const bf16x8 vv = *reinterpret_cast<const bf16x8*>(vrow + 16 * (2 * c + hh));
+          vf[c] = key_valid ? vv : z;
+        }
       }
     }
     int64_t tj64 = 0;
@@ -1025,14 +1058,16 @@ hstu_bwd_dkv_kernel(BwdArgs a) {
     pp.finish(0, st_lo * kStep, L);
     stage_barrier();
 
-    floatx16 acck[DK ? NDB : 1], accv[DV ? NDB : 1];
+    floatx16 acck[DK ? NDBX : 1], accv[DV ? NDBY : 1];
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+    for (int r = 0; r < 16; ++r) {
+      if constexpr (DK)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        if constexpr (DK) acck[db][r] = 0.0f;
-        if constexpr (DV) accv[db][r] = 0.0f;
-      }
+        for (int db = 0; db < NDBX; ++db) acck[db][r] = 0.0f;
+      if constexpr (DV)
+#pragma unroll
+        for (int db = 0; db < NDBY; ++db) accv[db][r] = 0.0f;
+    }
 
     int b = 0;
     for (int stp = st_lo; stp <= st_hi; ++stp) {
@@ -1055,11 +1090,11 @@ hstu_bwd_dkv_kernel(BwdArgs a) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) s[r] = ib + acc_row(r, ohh) >= geo.n_h ? c_bias : s[r];
         }
-        s = PP::contract(xt, ol32, ohh, kf, s);
+        s = PP::template contract<CX>(xt, ol32, ohh, kf, s);
         __builtin_amdgcn_sched_barrier(0);
         floatx16 da = {};
         if constexpr (DK) {
-          da = PP::contract(yt, ol32, ohh, vf, da);
+          da = PP::template contract<CY>(yt, ol32, ohh, vf, da);
           __builtin_amdgcn_sched_barrier(0);
         }
         // A and dS (time bias, SiLU, SiLU', mask, bf16 packing and the table
@@ -1187,21 +1222,26 @@ hstu_bwd_dkv_kernel(BwdArgs a) {
         __builtin_amdgcn_sched_barrier(0);
         // dV^T += dO^T A and dK^T += Q^T dS, one d-block of operands at a time
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
+        for (int db = 0; db < NDBM; ++db) {
+          const bool dvb = DV && db < NDBY, dkb = DK && db < NDBX;   // compile-time after unrolling
           bf16x8 t4[4];
 #pragma unroll
           for (int ins = 0; ins < 2; ++ins) {
-            if constexpr (DV) t4[ins] = PP::tr_op(yt, ol, db, ins);
-            if constexpr (DK) t4[2 + ins] = PP::tr_op(xt, ol, db, ins);
+            if (dvb) t4[ins] = PP::template tr_op<CY>(yt, ol, db, ins);
+            if (dkb) t4[2 + ins] = PP::template tr_op<CX>(xt, ol, db, ins);
           }
 #pragma unroll
           for (int ins = 0; ins < 2; ++ins) {
-            if constexpr (DV)
-              accv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t4[ins], pa[ins], accv[db], 0,
-                                                                0, 0);
-            if constexpr (DK)
-              acck[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t4[2 + ins], pd[ins], acck[db],
-                                                                0, 0, 0);
+            if constexpr (DV) {
+              if (dvb)
+                accv[db < NDBY ? db : 0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    t4[ins], pa[ins], accv[db < NDBY ? db : 0], 0, 0, 0);
+            }
+            if constexpr (DK) {
+              if (dkb)
+                acck[db < NDBX ? db : 0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    t4[2 + ins], pd[ins], acck[db < NDBX ? db : 0], 0, 0, 0);
+            }
           }
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -1215,26 +1255,32 @@ hstu_bwd_dkv_kernel(BwdArgs a) {
         __hip_atomic_fetch_add(&hpos[c_ix], cacc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
     if (key_valid) {
-      char* dk = reinterpret_cast<char*>(a.dk) + ((int64_t)(seq0 + j) * a.ld_k + (int64_t)h * D) * 2;
-      char* dv = reinterpret_cast<char*>(a.dv) + ((int64_t)(seq0 + j) * a.ld_v + (int64_t)h * D) * 2;
+      char* dk =
+          reinterpret_cast<char*>(a.dk) + ((int64_t)(seq0 + j) * a.ld_k + (int64_t)h * DQK) * 2;
+      char* dv =
+          reinterpret_cast<char*>(a.dv) + ((int64_t)(seq0 + j) * a.ld_v + (int64_t)h * DVV) * 2;
+      if constexpr (DK) {
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+        for (int db = 0; db < NDBX; ++db)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int off = 2 * (32 * db + 8 * g + 4 * hh);
-          if constexpr (DK) {
+          for (int g = 0; g < 4; ++g) {
             bf16x4 ok4;
 #pragma unroll
             for (int e = 0; e < 4; ++e) ok4[e] = (__bf16)(acck[db][4 * g + e] * k_scale);
-            *reinterpret_cast<bf16x4*>(dk + off) = ok4;
+            *reinterpret_cast<bf16x4*>(dk + 2 * (32 * db + 8 * g + 4 * hh)) = ok4;
           }
-          if constexpr (DV) {
+      }
+      if constexpr (DV) {
+#pragma unroll
+        for (int db = 0; db < NDBY; ++db)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
             bf16x4 ov4;
 #pragma unroll
             for (int e = 0; e < 4; ++e) ov4[e] = (__bf16)(accv[db][4 * g + e] * v_scale);
-            *reinterpret_cast<bf16x4*>(dv + off) = ov4;
+            *reinterpret_cast<bf16x4*>(dv + 2 * (32 * db + 8 * g + 4 * hh)) = ov4;
           }
-        }
+      }
     }
     stage_barrier();
   }
@@ -1476,66 +1522,70 @@ __global__ __launch_bounds__(256) void hstu_bwd_dkv_f32_kernel(BwdArgs a, int nu
 // ---------------------------------------------------------------------------
 // Which backward kernel: 0 = dQ, 1 = the pass that sums the tables (dK, or
 // dK and dV fused), 2 = the dV-only pass (d = 128).
-template <int D>
-constexpr int kv_mode_tab() { return D == 128 ? 1 : 0; }
+// The dK/dV pass: fused (0) when both head sizes are 64; with a 128-wide
+// side the two accumulators need more registers than two waves per SIMD
+// leave, so dK (with the table sums, 1) and dV (2) run as two passes.
+template <int DQK, int DV>
+constexpr int kv_mode_tab() { return (DQK == 128 || DV == 128) ? 1 : 0; }
 
-template <int D, bool POS, bool TIME>
+template <bool POS>
 size_t dkv_dyn_lds(int which, int pos_len) {
   return (POS && which == 1) ? sizeof(float) * (size_t)pos_len : 0;
 }
 
-template <int D, bool POS, bool TIME, bool CL>
+template <int DQK, int DV, bool POS, bool TIME, bool CL>
 int bpc_one(int which, int pos_len) {
   int nb = 0;
   hipError_t e;
-  const size_t dyn = dkv_dyn_lds<D, POS, TIME>(which, pos_len);
+  const size_t dyn = dkv_dyn_lds<POS>(which, pos_len);
   if (which == 1)
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &nb, hstu_bwd_dkv_kernel<D, POS, TIME, kv_mode_tab<D>(), CL>, kThreads, dyn);
+        &nb, hstu_bwd_dkv_kernel<DQK, DV, POS, TIME, kv_mode_tab<DQK, DV>(), CL>, kThreads, dyn);
   else if (which == 2)
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &nb, hstu_bwd_dkv_kernel<D, POS, TIME, 2, CL>, kThreads, 0);
+        &nb, hstu_bwd_dkv_kernel<DQK, DV, POS, TIME, 2, CL>, kThreads, 0);
   else
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, hstu_bwd_dq_kernel<D, POS, TIME, CL>,
-                                                     kThreads, 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &nb, hstu_bwd_dq_kernel<DQK, DV, POS, TIME, CL>, kThreads, 0);
   return e == hipSuccess ? nb : -1;
 }
 
-template <int D>
+template <int DQK, int DV>
 int bpc_d(int which, int pos_len, int time_len, bool clamp) {
   const bool pos = pos_len > 0, tim = time_len > 0, cl = pos && clamp;
-  if (cl && tim) return bpc_one<D, true, true, true>(which, pos_len);
-  if (cl) return bpc_one<D, true, false, true>(which, pos_len);
-  if (pos && tim) return bpc_one<D, true, true, false>(which, pos_len);
-  if (pos) return bpc_one<D, true, false, false>(which, pos_len);
-  if (tim) return bpc_one<D, false, true, false>(which, pos_len);
-  return bpc_one<D, false, false, false>(which, pos_len);
+  if (cl && tim) return bpc_one<DQK, DV, true, true, true>(which, pos_len);
+  if (cl) return bpc_one<DQK, DV, true, false, true>(which, pos_len);
+  if (pos && tim) return bpc_one<DQK, DV, true, true, false>(which, pos_len);
+  if (pos) return bpc_one<DQK, DV, true, false, false>(which, pos_len);
+  if (tim) return bpc_one<DQK, DV, false, true, false>(which, pos_len);
+  return bpc_one<DQK, DV, false, false, false>(which, pos_len);
 }
 
-template <int D, bool POS, bool TIME, bool CL>
+template <int DQK, int DV, bool POS, bool TIME, bool CL>
 hipError_t launch_mfma_one(const BwdArgs& a, int which, int n_wg, hipStream_t stream) {
-  const size_t dyn = dkv_dyn_lds<D, POS, TIME>(which, a.pos_len);
+  const size_t dyn = dkv_dyn_lds<POS>(which, a.pos_len);
   if (which == 1)
-    hipLaunchKernelGGL((hstu_bwd_dkv_kernel<D, POS, TIME, kv_mode_tab<D>(), CL>),
+    hipLaunchKernelGGL((hstu_bwd_dkv_kernel<DQK, DV, POS, TIME, kv_mode_tab<DQK, DV>(), CL>),
                        dim3((unsigned)n_wg), dim3(kThreads), dyn, stream, a);
   else if (which == 2)
-    hipLaunchKernelGGL((hstu_bwd_dkv_kernel<D, POS, TIME, 2, CL>), dim3((unsigned)n_wg),
+    hipLaunchKernelGGL((hstu_bwd_dkv_kernel<DQK, DV, POS, TIME, 2, CL>), dim3((unsigned)n_wg),
                        dim3(kThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL((hstu_bwd_dq_kernel<D, POS, TIME, CL>), dim3((unsigned)n_wg),
+    hipLaunchKernelGGL((hstu_bwd_dq_kernel<DQK, DV, POS, TIME, CL>), dim3((unsigned)n_wg),
                        dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
-template <int D>
+template <int DQK, int DV>
 hipError_t launch_mfma_d(const BwdArgs& a, int which, int n_wg, hipStream_t stream) {
+  if (which == 2 && kv_mode_tab<DQK, DV>() == 0) return hipSuccess;   // fused in pass 1
   const bool pos = a.pos_len > 0, tim = a.time_len > 0, cl = pos && a.pos_clamp != 0;
-  if (cl && tim) return launch_mfma_one<D, true, true, true>(a, which, n_wg, stream);
-  if (cl) return launch_mfma_one<D, true, false, true>(a, which, n_wg, stream);
-  if (pos && tim) return launch_mfma_one<D, true, true, false>(a, which, n_wg, stream);
-  if (pos) return launch_mfma_one<D, true, false, false>(a, which, n_wg, stream);
-  if (tim) return launch_mfma_one<D, false, true, false>(a, which, n_wg, stream);
-  return launch_mfma_one<D, false, false, false>(a, which, n_wg, stream);
+  if (cl && tim) return launch_mfma_one<DQK, DV, true, true, true>(a, which, n_wg, stream);
+  if (cl) return launch_mfma_one<DQK, DV, true, false, true>(a, which, n_wg, stream);
+  if (pos && tim) return launch_mfma_one<DQK, DV, true, true, false>(a, which, n_wg, stream);
+  if (pos) return launch_mfma_one<DQK, DV, true, false, false>(a, which, n_wg, stream);
+  if (tim) return launch_mfma_one<DQK, DV, false, true, false>(a, which, n_wg, stream);
+  return launch_mfma_one<DQK, DV, false, false, false>(a, which, n_wg, stream);
 }
 
 template <int D>
@@ -1585,12 +1635,20 @@ hipError_t launch_gate_bwd(const GateBwdArgs& a, int dtype, hipStream_t stream) 
   return dtype == 1 ? launch_gate_t<__bf16, 8>(a, stream) : launch_gate_t<float, 4>(a, stream);
 }
 
-int bwd_grid(int dtype, int d, int pos_len, int time_len, int which, bool clamp) {
+int bwd_grid(int dtype, int d_qk, int d_v, int pos_len, int time_len, int which,
+             bool clamp) {
   if (dtype != 1) return 1;   // fp32 kernels are not persistent
-  if (which == 2 && d != 128) return 0;   // no separate dV pass
   int bpc = -1;
-  if (d == 128) bpc = bpc_d<128>(which, pos_len, time_len, clamp);
-  if (d == 64) bpc = bpc_d<64>(which, pos_len, time_len, clamp);
+  if (d_qk == 128 && d_v == 128) {
+    bpc = bpc_d<128, 128>(which, pos_len, time_len, clamp);
+  } else if (d_qk == 64 && d_v == 64) {
+    if (which == 2) return 0;   // no separate dV pass
+    bpc = bpc_d<64, 64>(which, pos_len, time_len, clamp);
+  } else if (d_qk == 64 && d_v == 128) {
+    bpc = bpc_d<64, 128>(which, pos_len, time_len, clamp);
+  } else if (d_qk == 128 && d_v == 64) {
+    bpc = bpc_d<128, 64>(which, pos_len, time_len, clamp);
+  }
   if (bpc <= 0) return -1;
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess) return -1;
@@ -1600,28 +1658,30 @@ int bwd_grid(int dtype, int d, int pos_len, int time_len, int which, bool clamp)
   return g < kMaxGrid ? g : kMaxGrid;
 }
 
-// Head sizes the backward is built for (d_qk == d_v == d): bf16 MFMA
-// passes for 64 and 128, the fp32 kernels for 8, 64 and 128.
-bool bwd_supported(int dtype, int d) {
-  if (dtype == 1) return d == 64 || d == 128;
-  if (dtype == 0) return d == 8 || d == 64 || d == 128;
+// Head sizes the backward is built for: bf16 MFMA passes for d_qk, d_v in
+// {64, 128} (equal or not), the fp32 kernels for d_qk == d_v in {8, 64, 128}.
+bool bwd_supported(int dtype, int d_qk, int d_v) {
+  if (dtype == 1) return (d_qk == 64 || d_qk == 128) && (d_v == 64 || d_v == 128);
+  if (dtype == 0) return d_qk == d_v && (d_qk == 8 || d_qk == 64 || d_qk == 128);
   return false;
 }
 
-hipError_t launch_bwd(const BwdArgs& a, int dtype, int d, int which, int n_wg,
+hipError_t launch_bwd(const BwdArgs& a, int dtype, int d_qk, int d_v, int which, int n_wg,
                       hipStream_t stream) {
   if (dtype == 1) {
-    if (which == 2 && d != 128) return hipSuccess;
-    if (d == 128) return launch_mfma_d<128>(a, which, n_wg, stream);
-    if (d == 64) return launch_mfma_d<64>(a, which, n_wg, stream);
+    if (d_qk == 128 && d_v == 128) return launch_mfma_d<128, 128>(a, which, n_wg, stream);
+    if (d_qk == 64 && d_v == 64) return launch_mfma_d<64, 64>(a, which, n_wg, stream);
+    if (d_qk == 64 && d_v == 128) return launch_mfma_d<64, 128>(a, which, n_wg, stream);
+    if (d_qk == 128 && d_v == 64) return launch_mfma_d<128, 64>(a, which, n_wg, stream);
     return hipErrorInvalidValue;
   }
   // fp32: one kernel per side; n_wg carries the number of sequences
   if (which == 2) return hipSuccess;
+  if (d_qk != d_v) return hipErrorInvalidValue;
   const bool kv = which == 1;
-  if (d == 128) return launch_f32_d<128>(a, kv, n_wg, stream);
-  if (d == 64) return launch_f32_d<64>(a, kv, n_wg, stream);
-  if (d == 8) return launch_f32_d<8>(a, kv, n_wg, stream);
+  if (d_qk == 128) return launch_f32_d<128>(a, kv, n_wg, stream);
+  if (d_qk == 64) return launch_f32_d<64>(a, kv, n_wg, stream);
+  if (d_qk == 8) return launch_f32_d<8>(a, kv, n_wg, stream);
   return hipErrorInvalidValue;
 }
 

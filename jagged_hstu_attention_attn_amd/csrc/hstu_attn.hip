@@ -781,7 +781,7 @@ BwdLayout bwd_layout(const hstu_attn_desc* d) {
 // Workgroups of a persistent backward pass (cached per device and variant).
 int bwd_pass_grid(const hstu_attn_desc* d, int which) {
   struct Entry {
-    int dev, d, pos_len, has_time, clamp, which, grid;
+    int dev, d_qk, d_v, pos_len, has_time, clamp, which, grid;
   };
   static thread_local Entry cache[16];
   static thread_local int cache_n = 0;
@@ -791,14 +791,15 @@ int bwd_pass_grid(const hstu_attn_desc* d, int which) {
   const int clamp = d->pos_clamp != 0 && d->pos_table_len > 0 ? 1 : 0;
   for (int e = 0; e < cache_n && e < 16; ++e) {
     const Entry& c = cache[e];
-    if (c.dev == dev && c.d == d->d_v && c.pos_len == d->pos_table_len &&
+    if (c.dev == dev && c.d_qk == d->d_qk && c.d_v == d->d_v && c.pos_len == d->pos_table_len &&
         c.has_time == has_time && c.clamp == clamp && c.which == which)
       return c.grid;
   }
-  const int g = hstu::bwd_grid(d->dtype, d->d_v, d->pos_table_len, d->time_table_len, which,
-                               clamp != 0);
+  const int g = hstu::bwd_grid(d->dtype, d->d_qk, d->d_v, d->pos_table_len, d->time_table_len,
+                               which, clamp != 0);
   if (g >= 0)
-    cache[cache_n++ % 16] = Entry{dev, d->d_v, d->pos_table_len, has_time, clamp, which, g};
+    cache[cache_n++ % 16] =
+        Entry{dev, d->d_qk, d->d_v, d->pos_table_len, has_time, clamp, which, g};
   return g;
 }
 
@@ -821,13 +822,11 @@ int hstu_jagged_attn_bwd(const hstu_attn_desc* desc, const void* q, const void* 
                          size_t workspace_bytes, void* stream) {
   int rc = check_desc(desc);
   if (rc != HSTU_OK) return rc;
-  if (desc->d_qk != desc->d_v)
-    return fail(HSTU_ERR_UNSUPPORTED, "the backward needs d_qk == d_v (%d, %d)", desc->d_qk,
-                desc->d_v);
-  if (!hstu::bwd_supported(desc->dtype, desc->d_qk))
+  if (!hstu::bwd_supported(desc->dtype, desc->d_qk, desc->d_v))
     return fail(HSTU_ERR_UNSUPPORTED,
-                "the backward is built for d = 64, 128 (bf16) and 8, 64, 128 (fp32), not %d",
-                desc->d_qk);
+                "the backward is built for d_qk, d_v in {64, 128} (bf16) and d_qk == d_v in "
+                "{8, 64, 128} (fp32), not (%d, %d)",
+                desc->d_qk, desc->d_v);
   if (desc->num_seqs > 0 && !offsets) return fail(HSTU_ERR_INVALID_ARG, "offsets is NULL");
   if (contextual_len < 0) return fail(HSTU_ERR_INVALID_ARG, "contextual_len < 0");
   if (max_attn_len < 0) return fail(HSTU_ERR_INVALID_ARG, "max_attn_len < 0");
@@ -957,8 +956,8 @@ int hstu_jagged_attn_bwd(const hstu_attn_desc* desc, const void* q, const void* 
   ba.inv_scale = (float)(1.0 / (double)n_scale);
   ba.pos_clamp = desc->pos_clamp != 0 && desc->pos_table_len > 0;
   if (!bf16) {
-    e = hstu::launch_bwd(ba, desc->dtype, desc->d_v, 0, desc->num_seqs, s);
-    if (e == hipSuccess) e = hstu::launch_bwd(ba, desc->dtype, desc->d_v, 1, desc->num_seqs, s);
+    e = hstu::launch_bwd(ba, desc->dtype, desc->d_qk, desc->d_v, 0, desc->num_seqs, s);
+    if (e == hipSuccess) e = hstu::launch_bwd(ba, desc->dtype, desc->d_qk, desc->d_v, 1, desc->num_seqs, s);
     if (e == hipSuccess && tables)
       e = hstu::launch_tab64_finish(tab64, dpos_table, dtime_table, desc->pos_table_len,
                                     desc->time_table_len, s);
@@ -981,11 +980,11 @@ int hstu_jagged_attn_bwd(const hstu_attn_desc* desc, const void* q, const void* 
   if (e != hipSuccess)
     return fail(HSTU_ERR_HIP, "backward scheduler launch failed: %s", hipGetErrorString(e));
   ba.list = pa.list_q;
-  e = hstu::launch_bwd(ba, desc->dtype, desc->d_v, 0, n_q, s);
+  e = hstu::launch_bwd(ba, desc->dtype, desc->d_qk, desc->d_v, 0, n_q, s);
   if (e != hipSuccess) return fail(HSTU_ERR_HIP, "dQ launch failed: %s", hipGetErrorString(e));
   ba.list = pa.list_kv;
-  e = hstu::launch_bwd(ba, desc->dtype, desc->d_v, 1, n_kv, s);
-  if (e == hipSuccess && n_v > 0) e = hstu::launch_bwd(ba, desc->dtype, desc->d_v, 2, n_v, s);
+  e = hstu::launch_bwd(ba, desc->dtype, desc->d_qk, desc->d_v, 1, n_kv, s);
+  if (e == hipSuccess && n_v > 0) e = hstu::launch_bwd(ba, desc->dtype, desc->d_qk, desc->d_v, 2, n_v, s);
   if (e != hipSuccess) return fail(HSTU_ERR_HIP, "dK/dV launch failed: %s", hipGetErrorString(e));
   if (desc->pos_table_len > 0 || desc->time_table_len > 0) {
     hstu::TabReduceArgs ra;

@@ -368,7 +368,7 @@ constexpr bool kPPAuto = false;
 constexpr bool kW16Auto = true;
 int ln_all_heads_max_width(int dtype);
 hipError_t launch_ln_all_heads(const LnArgs& a, int dtype, hipStream_t stream);
-bool bwd_supported(int dtype, int d);
+bool bwd_supported(int dtype, int d_qk, int d_v);
 hipError_t launch_bwd_plan(const BwdPlanArgs& a, hipStream_t stream);
 hipError_t launch_gate_bwd(const GateBwdArgs& a, int dtype, hipStream_t stream);
 // Backward passes: which = 0 (dQ), 1 (dK with the table sums; also dV for
@@ -376,8 +376,9 @@ hipError_t launch_gate_bwd(const GateBwdArgs& a, int dtype, hipStream_t stream);
 // persistent launch size (CUs x resident workgroups per CU), 0 for a pass
 // that does not exist, or a negative value on error; for fp32 n_wg of
 // launch_bwd is the number of sequences instead.
-int bwd_grid(int dtype, int d, int pos_len, int time_len, int which, bool clamp = false);
-hipError_t launch_bwd(const BwdArgs& a, int dtype, int d, int which, int n_wg,
+int bwd_grid(int dtype, int d_qk, int d_v, int pos_len, int time_len, int which,
+             bool clamp = false);
+hipError_t launch_bwd(const BwdArgs& a, int dtype, int d_qk, int d_v, int which, int n_wg,
                       hipStream_t stream);
 hipError_t launch_tab_reduce(const TabReduceArgs& a, hipStream_t stream);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream);

@@ -207,9 +207,9 @@ static void abi_checks() {
   CHECK(bwd(d, kFake, kFake, bws - 1) == HSTU_ERR_WORKSPACE);
   {
     hstu_attn_desc b = base_desc();
-    b.d_qk = 64;
-    b.ld_q = b.ld_k = 256;
-    CHECK(bwd(b, kFake, kFake, 1u << 30) == HSTU_ERR_UNSUPPORTED);   // d_qk != d_v
+    b.d_qk = 256;
+    b.ld_q = b.ld_k = 1024;
+    CHECK(bwd(b, kFake, kFake, 1u << 30) == HSTU_ERR_UNSUPPORTED);   // no such forward
     check_message();
     b = base_desc();
     b.d_qk = b.d_v = 256;

@@ -229,11 +229,10 @@ def _bwd(lib, d, **kw):
 
 
 def test_backward_validation(lib):
-    # unequal head dims: the forward supports them, the backward does not
+    # unequal bf16 head dims pass the checks (and then need a GPU)
     d = _desc(d_qk=64, d_v=128, ld_q=256, ld_k=256)
     assert lib.hstu_jagged_attn_workspace_bytes(ctypes.byref(d)) > 0
-    assert _bwd(lib, d) == _lib.HSTU_ERR_UNSUPPORTED
-    assert "d_qk == d_v" in _lib.last_error()
+    assert _bwd(lib, d) in (_lib.HSTU_OK, _lib.HSTU_ERR_HIP)
     assert _bwd(lib, _desc(), dq=None) == _lib.HSTU_ERR_INVALID_ARG
     assert _bwd(lib, _desc(), du=None) == _lib.HSTU_ERR_INVALID_ARG
     assert _bwd(lib, _desc(), ws=None) == _lib.HSTU_ERR_WORKSPACE
@@ -244,7 +243,7 @@ def test_backward_validation(lib):
     d256 = _desc(d_qk=256, d_v=256, ld_q=1024, ld_k=1024, ld_v=1024, ld_u=1024, ld_out=1024)
     assert lib.hstu_jagged_attn_workspace_bytes(ctypes.byref(d256)) > 0
     assert _bwd(lib, d256) == _lib.HSTU_ERR_UNSUPPORTED
-    assert "d = 64, 128 (bf16)" in _lib.last_error()
+    assert "d_qk, d_v in {64, 128} (bf16)" in _lib.last_error()
     # fp32 d = 8 is built: it passes the shape check (and then needs a GPU)
     d8 = _desc(d_qk=8, d_v=8, dtype=_lib.HSTU_DTYPE_F32, ld_q=32, ld_k=32, ld_v=32, ld_u=32,
                ld_out=32)

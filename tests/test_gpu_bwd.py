@@ -98,6 +98,36 @@ def test_bwd_small_bf16(epilogue, d, W):
 
 
 @pytest.mark.parametrize("epilogue", ["ln_u", "none", "ln_all_u"])
+@pytest.mark.parametrize("dqk,dv", [(64, 128), (128, 64)])
+@pytest.mark.parametrize("W", [0, 100])
+def test_bwd_unequal_head_dims(epilogue, dqk, dv, W):
+    """Q/K and U/V head widths that differ (the pages allow it: "HSTU tensor
+    by tensor", section "Trace four projections"): every gradient and both
+    tables against the oracle, every mask rule, several tiles."""
+    print(f"case bwd unequal dims {dqk}/{dv} W={W} {epilogue}", flush=True)
+    inp = make_custom([1, 37, 129, 300, 260, 5], num_heads=2, d_qk=dqk, d_v=dv, dtype="bf16",
+                      seed=6, num_targets=[0, 5, 20, 50, 3, 5], contextual_len=3,
+                      max_attn_len=W, pos_len=64, pos_std=0.3, time_len=16, time_std=0.3,
+                      alpha=1.0 / np.sqrt(dqk))
+    dout = make_dout(inp, 7)
+    ref = oracle.backward(inp, dout, epilogue=_EP[epilogue])
+    assert_grads(gpu_backward(inp, dout, epilogue), ref, "bf16", epilogue)
+
+
+def test_bwd_unequal_head_dims_clamped_long():
+    """d_qk = 64, d_v = 128 on one whole windowed sequence with the
+    clamped-position bias: gradients and both tables."""
+    print("case bwd unequal dims long clamp", flush=True)
+    base = make_inputs("windowed", num_seqs=1)
+    inp = make_custom([int(base.offsets[1])], num_heads=2, d_qk=64, d_v=128, dtype="bf16",
+                      seed=8, num_targets=[50], max_attn_len=1024, pos_len=4096,
+                      pos_std=0.02, time_len=64, time_std=0.02, alpha=0.125)
+    dout = make_dout(inp, 9)
+    assert_grads(gpu_backward(inp, dout, pos_clamp=True),
+                 oracle.backward(inp, dout, pos_clamp=True), "bf16")
+
+
+@pytest.mark.parametrize("epilogue", ["ln_u", "none", "ln_all_u"])
 @pytest.mark.parametrize("d", [8, 64])
 def test_bwd_small_f32(epilogue, d):
     inp = _small("f32", d, W=40)
