@@ -802,3 +802,18 @@ def test_one_shot_calls_share_a_stream_workspace():
                        workspace=torch.empty(16, dtype=torch.uint8, device=DEV),
                        **call_kwargs(small, dev))
     assert len(api._ws_cache) >= 2
+
+
+def test_d256_candidates_only_and_ln_all_heads():
+    """bf16 d = 256 through the candidates-only call (history rows untouched)
+    and the LayerNorm-over-all-heads epilogue (H * d_v = 1024)."""
+    print("case d256 candidates-only / ln_all_u", flush=True)
+    inp = make_custom([300, 140, 33], num_heads=4, d_qk=256, d_v=256, dtype="bf16", seed=44,
+                      num_targets=[60, 20, 5], contextual_len=2, pos_len=512, time_len=64,
+                      alpha=1.0 / 16)
+    got = _candidates_forward(inp)
+    rows = _candidate_rows(inp)
+    hist = np.setdiff1d(np.arange(inp.total_tokens), rows)
+    assert np.all(got[hist] == -5.0), "history rows were written"
+    assert_close(got, ora(inp, rows=rows), "bf16", rows=rows)
+    assert_close(gpu_forward(inp, epilogue="ln_all_u"), ora(inp, "ln_all_u"), "bf16")
