@@ -38,10 +38,12 @@ PEAK_HBM_GBS = 8000.0
 _CSRC = "jagged_hstu_attention_attn_amd/csrc/"
 # The sources each forward kernel is built from: a counter summary is valid
 # for the kernel and source hash it records.
-KERNEL_SOURCES = {
-    "hstu_attn_fwd_kernel": ["attn_fwd.hip", "attn_common.hpp", "hstu_device.hpp"],
-    "hstu_attn_fwd_w16_kernel": ["attn_fwd_w16.hip", "attn_common.hpp", "hstu_device.hpp"],
-    "hstu_attn_fwd_pp_kernel": ["attn_fwd_pp.hip", "attn_common.hpp", "hstu_device.hpp"],
+KERNEL_SOURCES = {   # the kernel and the scheduler whose work order sets its traffic
+    "hstu_attn_fwd_kernel": ["attn_fwd.hip", "attn_common.hpp", "hstu_device.hpp", "plan.hip"],
+    "hstu_attn_fwd_w16_kernel": ["attn_fwd_w16.hip", "attn_common.hpp", "hstu_device.hpp",
+                                 "plan.hip"],
+    "hstu_attn_fwd_pp_kernel": ["attn_fwd_pp.hip", "attn_common.hpp", "hstu_device.hpp",
+                                "plan.hip"],
 }
 KERNEL_OF_CHOICE = {"four_wave": "hstu_attn_fwd_kernel", "sixteen_row": "hstu_attn_fwd_w16_kernel",
                     "eight_wave": "hstu_attn_fwd_pp_kernel"}

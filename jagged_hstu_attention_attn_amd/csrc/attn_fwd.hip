@@ -1,8 +1,8 @@
 // attn_fwd.hip -- gfx950 (CDNA4) jagged HSTU attention forward.
 //
 // A persistent launch: every workgroup (4 waves) repeatedly takes a
-// (sequence, head, 128-row query tile) item from its XCD's queue (see
-// plan.hip); the workgroups of one queue share it cyclically.  Wave w owns
+// (sequence, head, 128-row query tile) unit from the scheduler's plan (see
+// plan.hip): its own list of units, or a work queue it shares.  Wave w owns
 // query rows i0+32w .. i0+32w+31 of an item; lane (l % 32) owns one query row
 // and the lane half (l / 32) splits the contraction dimension, which is the
 // operand layout of the 32x32 MFMA (v_mfma_f32_32x32x16_bf16; 32x32x2 for
@@ -175,20 +175,22 @@ hstu_attn_fwd_kernel(AttnArgs a) {
 
   // Work walk.  Static plan: planned workgroup v processes units [wg[2v],
   // wg[2v] + wg[2v+1]) in order; a launch of another size than the plan's
-  // maps the planned workgroups onto its own cyclically.  Work queue (hdr[2]
-  // set): units 0 .. hdr[4] - 1 in decreasing cost; workgroup g starts with
-  // unit g, and during every item it fetches its next unit, gridDim.x plus
-  // the queue counter's previous value, through s_qnext (two slots by item
-  // parity, so a slot is rewritten only after every wave has passed the
-  // barriers of the item that read it).  Indices only grow, so every
-  // workgroup stops once its next unit is past the last.
+  // maps the planned workgroups onto its own cyclically.  Queue modes (hdr[2]
+  // set; one queue, or one per XCD): the workgroup starts with unit
+  // first + w of its queue (work_queue), and during every item it fetches
+  // its next unit, first + n plus the queue counter's previous value,
+  // through s_qnext (two slots by item parity, so a slot is rewritten only
+  // after every wave has passed the barriers of the item that read it).
+  // Indices only grow, so every workgroup stops once its next unit is past
+  // its queue's last.
   __shared__ int s_qnext[2];
-  const bool queue = a.hdr[2] != 0;
+  const bool queue = a.hdr[2] != kPlanStatic;
+  const WorkQueue wkq = work_queue(a.hdr);
   const int n_plan = queue ? (int)gridDim.x : a.hdr[0];
   int q_item = 0;   // items this workgroup has started (queue slot parity)
   for (int v = blockIdx.x; v < n_plan; v += gridDim.x) {
-  const int u_begin = queue ? (int)blockIdx.x : a.wg[2 * v];
-  const int u_end = queue ? a.hdr[4] : u_begin + a.wg[2 * v + 1];
+  const int u_begin = queue ? wkq.first + wkq.w : a.wg[2 * v];
+  const int u_end = queue ? wkq.end : u_begin + a.wg[2 * v + 1];
   for (int u = u_begin; u < u_end; u = queue ? s_qnext[(q_item++) & 1] : u + 1) {
   const int4 it = a.units[2 * u];
   const int4 ch = a.units[2 * u + 1];   // key tiles [ch.x, ch.y]; split slot, chunk
@@ -565,7 +567,7 @@ hstu_attn_fwd_kernel(AttnArgs a) {
   // default value there would make the compiler merge the two right here,
   // which waits for the atomic and for every copy issued before it.
   int q_fetch;
-  if (queue && tid == 0) q_fetch = atomicAdd(const_cast<int32_t*>(a.hdr) + 3, 1);
+  if (queue && tid == 0) q_fetch = atomicAdd(const_cast<int32_t*>(a.hdr) + wkq.ctr, 1);
   int64_t ti64 = 0;   // this lane's row time (prologue only)
   if constexpr (TIME) {
     // Neither value is used before the wait below: a use here (a select
@@ -613,12 +615,12 @@ hstu_attn_fwd_kernel(AttnArgs a) {
   wait_vmem<0>();
   asm volatile("" : "+v"(q_fetch));   // a plain value from here: no wait of its own
   if (queue && tid == 0) {
-    s_qnext[q_item & 1] = (int)gridDim.x + q_fetch;   // published by the barrier below
+    s_qnext[q_item & 1] = wkq.first + wkq.n + q_fetch;   // published by the barrier below
     // Every processed unit makes one fetch, so the counter ends at the
     // number of units: the fetch that returned the last value was the run's
     // last, and its workgroup rewinds the counter for the next run of the
     // same plan.
-    if (q_fetch == u_end - 1) const_cast<int32_t*>(a.hdr)[3] = 0;
+    if (q_fetch == wkq.end - wkq.first - 1) const_cast<int32_t*>(a.hdr)[wkq.ctr] = 0;
   }
 #pragma unroll
   for (int c = 0; C::kQLds && c < NKC; ++c) {

@@ -121,13 +121,14 @@ hstu_attn_fwd_pp_kernel(AttnArgs a) {
            ((TIME && wave >= 6 && wave - 6 == b) ? 1 : 0) + ((clamp && wave == b) ? 1 : 0);
   };
 
-  // Work walk (as the four-wave kernel): static plan or work queue.
-  const bool queue = a.hdr[2] != 0;
+  // Work walk (as the four-wave kernel): static plan or work queues.
+  const bool queue = a.hdr[2] != kPlanStatic;
+  const WorkQueue wkq = work_queue(a.hdr);
   const int n_plan = queue ? (int)gridDim.x : a.hdr[0];
   int q_item = 0;
   for (int v = blockIdx.x; v < n_plan; v += gridDim.x) {
-  const int u_begin = queue ? (int)blockIdx.x : a.wg[2 * v];
-  const int u_end = queue ? a.hdr[4] : u_begin + a.wg[2 * v + 1];
+  const int u_begin = queue ? wkq.first + wkq.w : a.wg[2 * v];
+  const int u_end = queue ? wkq.end : u_begin + a.wg[2 * v + 1];
   for (int u = u_begin; u < u_end; u = queue ? s_qnext[(q_item++) & 1] : u + 1) {
   const int4 it = a.units[2 * u];
   const int4 ch = a.units[2 * u + 1];
@@ -481,7 +482,7 @@ hstu_attn_fwd_pp_kernel(AttnArgs a) {
   issue_step(0);
   issue_step(1);
   int q_fetch;
-  if (queue && tid == 0) q_fetch = atomicAdd(const_cast<int32_t*>(a.hdr) + 3, 1);
+  if (queue && tid == 0) q_fetch = atomicAdd(const_cast<int32_t*>(a.hdr) + wkq.ctr, 1);
   int64_t ti64 = 0;
   if constexpr (TIME) {
     tbase = a.timestamps[seq0 + i0];
@@ -506,8 +507,8 @@ hstu_attn_fwd_pp_kernel(AttnArgs a) {
   wait_vmem<0>();
   asm volatile("" : "+v"(q_fetch));
   if (queue && tid == 0) {
-    s_qnext[q_item & 1] = (int)gridDim.x + q_fetch;
-    if (q_fetch == u_end - 1) const_cast<int32_t*>(a.hdr)[3] = 0;
+    s_qnext[q_item & 1] = wkq.first + wkq.n + q_fetch;
+    if (q_fetch == wkq.end - wkq.first - 1) const_cast<int32_t*>(a.hdr)[wkq.ctr] = 0;
   }
   if constexpr (TIME) {
     asm volatile("" : "+v"(ti64));

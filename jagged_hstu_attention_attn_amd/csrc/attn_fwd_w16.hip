@@ -147,13 +147,14 @@ hstu_attn_fwd_w16_kernel(AttnArgs a) {
     if (tid < 64) tt.tful[tid] = kLog2e * a.time_table[min(tid, Tt - 1)];
   }
 
-  // Work walk: static plan or work queue (see the scheduler).
-  const bool queue = a.hdr[2] != 0;
+  // Work walk (as the four-wave kernel): static plan or work queues.
+  const bool queue = a.hdr[2] != kPlanStatic;
+  const WorkQueue wkq = work_queue(a.hdr);
   const int n_plan = queue ? (int)gridDim.x : a.hdr[0];
   int q_item = 0;
   for (int v = blockIdx.x; v < n_plan; v += gridDim.x) {
-  const int u_begin = queue ? (int)blockIdx.x : a.wg[2 * v];
-  const int u_end = queue ? a.hdr[4] : u_begin + a.wg[2 * v + 1];
+  const int u_begin = queue ? wkq.first + wkq.w : a.wg[2 * v];
+  const int u_end = queue ? wkq.end : u_begin + a.wg[2 * v + 1];
   for (int u = u_begin; u < u_end; u = queue ? s_qnext[(q_item++) & 1] : u + 1) {
   const int4 it = a.units[2 * u];
   const int4 ch = a.units[2 * u + 1];
@@ -169,6 +170,19 @@ hstu_attn_fwd_w16_kernel(AttnArgs a) {
   int jlo, jhi;
   tile_key_range(geo, i0, i1, jlo, jhi);
   const int kt_lo = max(jlo / kBN, ch.x), kt_hi = min(jhi / kBN, ch.y);
+  // Key blocks are walked from a rotation of [kt_lo, kt_hi]: no softmax, so
+  // the order is free.  Under a window a tile's range starts four blocks
+  // after its predecessor's, and walking in plain order would have the next
+  // tile read a block four steps later, after the workgroups of an L2 have
+  // read as much again as that L2 holds.  Walking so that step s takes the
+  // block kt = s (mod nk) lets the neighbouring tiles of one L2, whose
+  // ranges have the same length, read each block at about the same time.
+  const int nk = kt_hi - kt_lo + 1;
+  const int rot = (geo.W > 0 && nk > 1) ? (nk - kt_lo % nk) % nk : 0;
+  auto blk = [&](int s) __attribute__((always_inline)) {
+    const int t = s + rot;
+    return kt_lo + (t >= nk ? t - nk : t);
+  };
 
   // ---- per-lane query row and the wave's uniform key bounds --------------
   const int wr0 = i0 + wave * kW16Rows;
@@ -478,10 +492,10 @@ hstu_attn_fwd_w16_kernel(AttnArgs a) {
   };
 
   // ---- item prologue -------------------------------------------------------
-  issue_stage(B0{}, kt_lo);
-  if (kt_lo + 1 <= kt_hi) issue_stage(B1{}, kt_lo + 1);
+  issue_stage(B0{}, blk(0));
+  if (nk > 1) issue_stage(B1{}, blk(1));
   int q_fetch;
-  if (queue && tid == 0) q_fetch = atomicAdd(const_cast<int32_t*>(a.hdr) + 3, 1);
+  if (queue && tid == 0) q_fetch = atomicAdd(const_cast<int32_t*>(a.hdr) + wkq.ctr, 1);
   int64_t ti64 = 0;
   if constexpr (TIME) {
     tbase = a.timestamps[seq0 + i0];
@@ -508,8 +522,8 @@ hstu_attn_fwd_w16_kernel(AttnArgs a) {
   wait_vmem<0>();
   asm volatile("" : "+v"(q_fetch));
   if (queue && tid == 0) {
-    s_qnext[q_item & 1] = (int)gridDim.x + q_fetch;
-    if (q_fetch == u_end - 1) const_cast<int32_t*>(a.hdr)[3] = 0;
+    s_qnext[q_item & 1] = wkq.first + wkq.n + q_fetch;
+    if (q_fetch == wkq.end - wkq.first - 1) const_cast<int32_t*>(a.hdr)[wkq.ctr] = 0;
   }
   {
     const int ln = opaque_lane();
@@ -532,8 +546,8 @@ hstu_attn_fwd_w16_kernel(AttnArgs a) {
     w_tmin = wave_min(row_valid ? ti32 : 0xffffffffu);
     w_tmax = wave_max(row_valid ? ti32 : 0u);
   }
-  finish_stage(B0{}, kt_lo);
-  if (kt_lo + 1 <= kt_hi) finish_stage(B1{}, kt_lo + 1);
+  finish_stage(B0{}, blk(0));
+  if (nk > 1) finish_stage(B1{}, blk(1));
   stage_barrier();             // also publishes the time tables; Q reads are done
 
   // Epilogue staging: the 16 rows of wave w in stage buffer
@@ -564,33 +578,34 @@ hstu_attn_fwd_w16_kernel(AttnArgs a) {
     }
   };
 
-  // One pipeline step on the key blocks kt, kt + 1 held in buffers `bufc`,
-  // `bufc` + 1: copy blocks kt + 2, kt + 3 into the other two buffers (freed
+  // One pipeline step on the walk's blocks s, s + 1 held in buffers `bufc`,
+  // `bufc` + 1: copy blocks s + 2, s + 3 into the other two buffers (freed
   // by the previous barrier), compute both blocks, then (this wave's copies
   // landed) finish the next two and synchronise.
-  auto step = [&](auto bufc, int kt) __attribute__((always_inline)) {
+  auto step = [&](auto bufc, int s) __attribute__((always_inline)) {
     constexpr int b = decltype(bufc)::value;
     using N1 = std::integral_constant<int, (b + 1) % kW16Stages>;
     using N2 = std::integral_constant<int, (b + 2) % kW16Stages>;
     using N3 = std::integral_constant<int, (b + 3) % kW16Stages>;
-    const bool has1 = kt + 1 <= kt_hi, next0 = kt + 2 <= kt_hi, next1 = kt + 3 <= kt_hi;
-    if (next0) issue_stage(N2{}, kt + 2);
+    const bool has1 = s + 1 < nk, next0 = s + 2 < nk, next1 = s + 3 < nk;
+    const int kt = blk(s), kt1 = blk(s + 1), kt2 = blk(s + 2), kt3 = blk(s + 3);
+    if (next0) issue_stage(N2{}, kt2);
     else issue_u();
-    if (next1) issue_stage(N3{}, kt + 3);
+    if (next1) issue_stage(N3{}, kt3);
     if (needs(kt)) block(stage(bufc), kt);
-    if (has1 && needs(kt + 1)) block(stage(N1{}), kt + 1);
+    if (has1 && needs(kt1)) block(stage(N1{}), kt1);
     if (next0) {
       wait_vmem<0>();
-      finish_stage(N2{}, kt + 2);
-      if (next1) finish_stage(N3{}, kt + 3);
+      finish_stage(N2{}, kt2);
+      if (next1) finish_stage(N3{}, kt3);
       stage_barrier();
     }
   };
-  for (int kt = kt_lo;; kt += kW16Stages) {
-    step(B0{}, kt);
-    if (kt + 2 > kt_hi) break;
-    step(B2{}, kt + 2);
-    if (kt + 4 > kt_hi) break;
+  for (int s = 0;; s += kW16Stages) {
+    step(B0{}, s);
+    if (s + 2 >= nk) break;
+    step(B2{}, s + 2);
+    if (s + 4 >= nk) break;
   }
 
   // ---- chunk of a split item: publish the partial output; the chunk that

@@ -109,12 +109,46 @@ constexpr int kSortBuckets = 16;     // key-tile counts the queue order tells ap
 // Unit flag (bit 31 of the chunk word): the unit's query tiles start at the
 // history end n_h instead of row 0 (candidates-only plans).
 constexpr int kUnitCandRows = int(0x80000000u);
+// Plan modes (header word 2): the static plan, one work queue, or one work
+// queue per XCD.
+constexpr int kPlanStatic = 0, kPlanQueue = 1, kPlanXcdQueues = 2;
+constexpr int kHdrXcdCtr = 8;     // header words 8 .. 15: the XCD queues' counters
+constexpr int kHdrXcdBound = 16;  // words 16 .. 24: XCD x's units are [w[16 + x], w[17 + x])
+
+// The queue a workgroup of the attention launch takes units from (queue
+// modes).  Units [first, end) are shared by n workgroups; the workgroup with
+// index w among them starts with unit first + w, and each fetch from counter
+// word `ctr` returns how many units its queue has handed out after the first
+// n, so its next unit is first + n + that value.  Per-XCD queues serve the
+// workgroups g with g % 8 == x (the XCD g runs on).
+struct WorkQueue {
+  int first, end, n, w, ctr;
+};
+__device__ inline WorkQueue work_queue(const int32_t* hdr) {
+  WorkQueue q;
+  if (hdr[2] == kPlanXcdQueues) {
+    const int x = (int)blockIdx.x % kXcds;
+    q.first = hdr[kHdrXcdBound + x];
+    q.end = hdr[kHdrXcdBound + x + 1];
+    q.n = ((int)gridDim.x - x + kXcds - 1) / kXcds;
+    q.w = (int)blockIdx.x / kXcds;
+    q.ctr = kHdrXcdCtr + x;
+  } else {
+    q.first = 0;
+    q.end = hdr[4];
+    q.n = (int)gridDim.x;
+    q.w = (int)blockIdx.x;
+    q.ctr = 3;
+  }
+  return q;
+}
 
 struct PlanLayout {
   size_t hdr_off;      // int32[64]: [0] workgroups the plan was made for,
-                       //   [1] 1 for a candidates-only plan, [2] 1 when the
-                       //   units form a work queue (see the scheduler), [3]
-                       //   the queue's counter, [4] the number of units
+                       //   [1] 1 for a candidates-only plan, [2] the plan
+                       //   mode (kPlan*), [3] the single queue's counter,
+                       //   [4] the number of units, [8 .. 24] the XCD
+                       //   queues' counters and unit ranges
   size_t units_off;    // int4[2 * units_max]: (seq start, L, n_h, qt*H + h),
                        //   (kt_begin, kt_end, split slot or -1, chunk << 16 | chunks)
   size_t wg_off;       // int32[2 * kMaxGrid]: (first unit, units) per workgroup

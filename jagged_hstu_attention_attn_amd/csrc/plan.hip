@@ -32,6 +32,13 @@
 // workgroups one at a time from a counter, which balances them like
 // longest-first list scheduling.
 //
+// Batches whose items are all small against a workgroup's share (the
+// largest costs at most a quarter of it: many windowed tiles, say) are
+// planned as one work queue per XCD instead: XCD x takes a contiguous,
+// cost-balanced range of the items in list order, so the workgroups of one
+// L2 always work on neighbouring tiles, and the range's last items go in
+// decreasing cost.
+//
 // One workgroup of 1024 threads, five phases; the per-item arrays stay in LDS
 // up to kPlanLdsItems items.  Everything stays on the device, so the
 // caller's stream never synchronises with the host.
@@ -236,6 +243,8 @@ __global__ __launch_bounds__(kPlanThreads) void hstu_plan_kernel(PlanArgs a) {
   __shared__ int2 s_geo[kItems];   // LDS plans: first key tile, qt * H + h of each item
   __shared__ int s_bcnt[kSortBuckets];
   __shared__ int s_long;   // some item needs the static plan
+  __shared__ int s_maxc;   // the largest item cost
+  __shared__ int s_xb[kXcds + 1];   // per-XCD queues: first item of each XCD's range
 
   const int tid = threadIdx.x;
   const int B = a.num_seqs, H = a.num_heads, n_wg = a.n_wg;
@@ -249,6 +258,7 @@ __global__ __launch_bounds__(kPlanThreads) void hstu_plan_kernel(PlanArgs a) {
 
   for (int v = tid; v < kMaxGrid; v += kPlanThreads) s_cnt[v] = 0;
   if (tid == 0) s_long = 0;
+  if (tid == 0) s_maxc = 0;
   if (tid < kSortBuckets) s_bcnt[tid] = 0;
   __syncthreads();
 
@@ -310,7 +320,7 @@ __global__ __launch_bounds__(kPlanThreads) void hstu_plan_kernel(PlanArgs a) {
     if (tid == 0) {
       a.hdr[0] = n_wg;
       a.hdr[1] = cand ? 1 : 0;
-      a.hdr[2] = 1;
+      a.hdr[2] = kPlanQueue;
       a.hdr[3] = 0;
       a.hdr[4] = n;
     }
@@ -343,6 +353,7 @@ __global__ __launch_bounds__(kPlanThreads) void hstu_plan_kernel(PlanArgs a) {
       cost[j] = c;
       iseq[j] = b;
       if constexpr (LDS) s_geo[j] = make_int2(g.kt_lo, g.qt * H + g.h);
+      atomicMax(&s_maxc, c);
     }
     I tot;
     const I ex = block_excl_scan((I)c, s_ws, tot);
@@ -352,6 +363,85 @@ __global__ __launch_bounds__(kPlanThreads) void hstu_plan_kernel(PlanArgs a) {
   const I C = ccarry;
   const I T = C > 0 ? (C + n_wg - 1) / n_wg : 1;   // cost of one share
   __syncthreads();
+
+  // Per-XCD work queues, when the largest item costs at most a quarter of a
+  // share: XCD x takes a contiguous range of the items in list order, cut
+  // where the items' cost midpoints pass x / 8 of the total, and its
+  // workgroups take the range's units in that order from one counter.  The
+  // workgroups of one L2 then work on neighbouring query tiles of one
+  // (sequence, head) at any time, whatever the item costs (the dealt
+  // shares drift apart in time when the costs differ, which loses that
+  // reuse).  The range's last items, one per workgroup of the XCD, go in
+  // decreasing cost, which evens out the end like longest-first list
+  // scheduling.  Nothing is split.
+  if constexpr (LDS) {
+    if (n == carry && (I)s_maxc * 4 <= T) {
+      // costs, geometry and cost prefix sums in list order (the dealt-order
+      // arrays are no longer read)
+      if (tid <= kXcds) s_xb[tid] = tid == 0 ? 0 : n;
+      I lcarry = 0;
+      for (int k0 = 0; k0 < n; k0 += kPlanThreads) {
+        const int k = k0 + tid;
+        int c = 0;
+        if (k < n) {
+          const int b = seq_of(k, base, B);
+          const ItemGeo g =
+              item_geo_of(k, b, base, slen, hist, a.contextual_len, a.max_attn_len, cand);
+          c = g.kt_hi - g.kt_lo + 1 + kCostOverhead;
+          cost[k] = c;
+          iseq[k] = b;
+          s_geo[k] = make_int2(g.kt_lo, g.qt * H + g.h);
+        }
+        I tot;
+        const I ex = block_excl_scan((I)c, s_ws, tot);
+        if (k < n) line[k] = lcarry + ex;
+        lcarry += tot;
+      }
+      __syncthreads();
+      // XCD x starts at the first item whose cost midpoint is at or past
+      // x C / 8; `reached` counts the x in 1 .. 7 an item's midpoint passes
+      auto reached = [&](int k) {
+        const int64_t m2 = 2 * (int64_t)line[k] + cost[k];   // twice the midpoint
+        return (int)min((int64_t)(kXcds - 1), 4 * m2 / (int64_t)C);
+      };
+      for (int k = tid; k < n; k += kPlanThreads) {
+        const int hi = reached(k), lo = k > 0 ? reached(k - 1) : 0;
+        for (int x = lo + 1; x <= hi; ++x) s_xb[x] = k;
+      }
+      __syncthreads();
+      for (int k = tid; k < n; k += kPlanThreads) {
+        int x = 0;
+        while (x < kXcds - 1 && s_xb[x + 1] <= k) ++x;
+        const int r_lo = s_xb[x], r_hi = s_xb[x + 1];
+        const int tail = min(xcd_wgs(n_wg, x), r_hi - r_lo);
+        int uix = k;
+        if (k >= r_hi - tail) {   // decreasing cost, ties in list order
+          const int c = cost[k];
+          int rank = 0;
+          for (int k2 = r_hi - tail; k2 < r_hi; ++k2) {
+            const int c2 = cost[k2];
+            rank += (c2 > c || (c2 == c && k2 < k)) ? 1 : 0;
+          }
+          uix = r_hi - tail + rank;
+        }
+        const int b = iseq[k];
+        const int2 gg = s_geo[k];
+        a.units[2 * uix] = make_int4(start[b], slen[b], hist[b], gg.y);
+        a.units[2 * uix + 1] = make_int4(gg.x, gg.x + cost[k] - kCostOverhead - 1, -1,
+                                         (cand ? kUnitCandRows : 0) | 1);
+      }
+      if (tid == 0) {
+        a.hdr[0] = n_wg;
+        a.hdr[1] = cand ? 1 : 0;
+        a.hdr[2] = kPlanXcdQueues;
+        a.hdr[3] = 0;
+        a.hdr[4] = n;
+      }
+      if (tid < kXcds) a.hdr[kHdrXcdCtr + tid] = 0;
+      if (tid <= kXcds) a.hdr[kHdrXcdBound + tid] = s_xb[tid];
+      return;
+    }
+  }
 
   // 3. Chunks per item; prefix sums of the units and of the split chunks.
   I ucarry = 0;
@@ -417,7 +507,7 @@ __global__ __launch_bounds__(kPlanThreads) void hstu_plan_kernel(PlanArgs a) {
   if (tid == 0) {
     a.hdr[0] = n_wg;
     a.hdr[1] = cand ? 1 : 0;
-    a.hdr[2] = 0;
+    a.hdr[2] = kPlanStatic;
     a.hdr[3] = 0;
     a.hdr[4] = (int)(ucarry & kLow);
   }

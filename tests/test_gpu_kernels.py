@@ -227,3 +227,52 @@ def test_pp_matches_other_kernel():
     _close(a, ref)
     _close(b, ref)
     _close(a, b)
+
+
+_XCD_CASE = {}
+
+
+def _xcd_case():
+    """Many windowed sequences of four query tiles: every item reaches at most
+    five key tiles, small against a workgroup's share of the batch, so the
+    scheduler plans one work queue per XCD.  The oracle runs once for all
+    kernels."""
+    if not _XCD_CASE:
+        rng = np.random.default_rng(41)
+        B = 200   # the work list's item bound stays within the scheduler's LDS lists
+        lengths = [int(x) for x in rng.integers(400, 513, size=B)]
+        nt = [int(x) for x in rng.integers(0, 30, size=B)]
+        inp = make_custom(lengths, num_heads=4, d_qk=128, d_v=128, dtype="bf16", seed=41,
+                          num_targets=nt, contextual_len=2, max_attn_len=32, pos_len=1024,
+                          pos_std=0.2, time_len=64, time_std=0.2, alpha=1.0 / math.sqrt(128))
+        _XCD_CASE["inp"] = inp
+        _XCD_CASE["ref"] = _ora(inp)
+    return _XCD_CASE["inp"], _XCD_CASE["ref"]
+
+
+def test_pp_xcd_queues_plan_reuse():
+    """Per-XCD work queues: the plan header names the mode (word 2 == 2) and
+    eight unit ranges that tile the units in order; three runs of one plan --
+    every XCD's counter must rewind after its last fetch -- match the oracle
+    and each other bitwise."""
+    print(f"case {_KERNEL} xcd_queues", flush=True)
+    inp, ref = _xcd_case()
+    with fwd_kernel(_KERNEL):
+        dev = to_device(inp, DEV)
+        call = JaggedAttnCall(dev["q"], dev["k"], dev["v"], dev["u"], dev["offsets"],
+                              **call_kwargs(inp, dev))
+        call.plan()
+        hdr = call.workspace[:256].view(torch.int32).cpu().numpy()
+        outs = []
+        for _ in range(3):
+            call.out.zero_()
+            outs.append(call.run().float().cpu().numpy().astype(np.float64))
+        torch.cuda.synchronize()
+        hdr_after = call.workspace[:256].view(torch.int32).cpu().numpy()
+    assert hdr[2] == 2, f"plan mode {hdr[2]}"
+    n_units = int(hdr[4])
+    bounds = hdr[16:25]
+    assert bounds[0] == 0 and bounds[8] == n_units and np.all(np.diff(bounds) >= 0), bounds
+    assert np.all(hdr_after[8:16] == 0), "an XCD counter was not rewound"
+    _close(outs[0], ref)
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
