@@ -44,6 +44,7 @@
 // caller's stream never synchronises with the host.
 #include <type_traits>
 
+#include "attn_common.hpp"
 #include "hstu_device.hpp"
 
 namespace hstu {
@@ -200,6 +201,13 @@ __device__ inline int dealt_item(int j, int n, int n_wg) {
   return t * n_wg + c;
 }
 
+// Inverse of dealt_item: the line position of item k.
+__device__ inline int dealt_pos(int k, int n, int n_wg) {
+  const int full = n / n_wg, extra = n - full * n_wg;
+  const int t = k / n_wg, c = k - t * n_wg;
+  return (c < extra ? c * (full + 1) : extra * (full + 1) + (c - extra) * full) + t;
+}
+
 // Sequence geometry of sequence b for the mask rules.
 __device__ inline SeqGeom seq_geom(int b, const int32_t* slen, const int32_t* hist,
                                    const PlanArgs& a) {
@@ -353,8 +361,9 @@ __global__ __launch_bounds__(kPlanThreads) void hstu_plan_kernel(PlanArgs a) {
       cost[j] = c;
       iseq[j] = b;
       if constexpr (LDS) s_geo[j] = make_int2(g.kt_lo, g.qt * H + g.h);
-      atomicMax(&s_maxc, c);
     }
+    const int wmax = wave_max(c);   // one LDS atomic per wave
+    if ((tid & 63) == 0) atomicMax(&s_maxc, wmax);
     I tot;
     const I ex = block_excl_scan((I)c, s_ws, tot);
     if (j < n) line[j] = ccarry + ex;
@@ -376,58 +385,62 @@ __global__ __launch_bounds__(kPlanThreads) void hstu_plan_kernel(PlanArgs a) {
   // scheduling.  Nothing is split.
   if constexpr (LDS) {
     if (n == carry && (I)s_maxc * 4 <= T) {
-      // costs, geometry and cost prefix sums in list order (the dealt-order
-      // arrays are no longer read)
+      // list-order costs (into `line`) and their exclusive prefix sums (into
+      // `ub`), read from the dealt-order arrays at dealt_pos(k)
       if (tid <= kXcds) s_xb[tid] = tid == 0 ? 0 : n;
       I lcarry = 0;
       for (int k0 = 0; k0 < n; k0 += kPlanThreads) {
         const int k = k0 + tid;
-        int c = 0;
-        if (k < n) {
-          const int b = seq_of(k, base, B);
-          const ItemGeo g =
-              item_geo_of(k, b, base, slen, hist, a.contextual_len, a.max_attn_len, cand);
-          c = g.kt_hi - g.kt_lo + 1 + kCostOverhead;
-          cost[k] = c;
-          iseq[k] = b;
-          s_geo[k] = make_int2(g.kt_lo, g.qt * H + g.h);
-        }
+        const int c = k < n ? cost[dealt_pos(k, n, n_wg)] : 0;
         I tot;
         const I ex = block_excl_scan((I)c, s_ws, tot);
-        if (k < n) line[k] = lcarry + ex;
+        if (k < n) {
+          line[k] = c;
+          ub[k] = lcarry + ex;
+        }
         lcarry += tot;
       }
       __syncthreads();
       // XCD x starts at the first item whose cost midpoint is at or past
-      // x C / 8; `reached` counts the x in 1 .. 7 an item's midpoint passes
+      // x C / 8: `reached` counts the x in 1 .. 7 with x C <= 4 (2 P + c),
+      // P the item's prefix and c its cost
       auto reached = [&](int k) {
-        const int64_t m2 = 2 * (int64_t)line[k] + cost[k];   // twice the midpoint
-        return (int)min((int64_t)(kXcds - 1), 4 * m2 / (int64_t)C);
+        const int64_t m4 = 4 * (2 * (int64_t)ub[k] + (int64_t)line[k]);
+        int r = 0;
+#pragma unroll
+        for (int x = 1; x < kXcds; ++x) r += (int64_t)x * (int64_t)C <= m4 ? 1 : 0;
+        return r;
       };
       for (int k = tid; k < n; k += kPlanThreads) {
         const int hi = reached(k), lo = k > 0 ? reached(k - 1) : 0;
         for (int x = lo + 1; x <= hi; ++x) s_xb[x] = k;
       }
       __syncthreads();
+      int xb[kXcds];
+#pragma unroll
+      for (int x = 1; x < kXcds; ++x) xb[x] = s_xb[x];
       for (int k = tid; k < n; k += kPlanThreads) {
-        int x = 0;
-        while (x < kXcds - 1 && s_xb[x + 1] <= k) ++x;
+        int x = 0;   // the range holding k: the last x with start <= k
+#pragma unroll
+        for (int y = 1; y < kXcds; ++y) x += xb[y] <= k ? 1 : 0;
         const int r_lo = s_xb[x], r_hi = s_xb[x + 1];
         const int tail = min(xcd_wgs(n_wg, x), r_hi - r_lo);
+        const int c = (int)line[k];
         int uix = k;
         if (k >= r_hi - tail) {   // decreasing cost, ties in list order
-          const int c = cost[k];
           int rank = 0;
+#pragma unroll 8
           for (int k2 = r_hi - tail; k2 < r_hi; ++k2) {
-            const int c2 = cost[k2];
+            const int c2 = (int)line[k2];
             rank += (c2 > c || (c2 == c && k2 < k)) ? 1 : 0;
           }
           uix = r_hi - tail + rank;
         }
-        const int b = iseq[k];
-        const int2 gg = s_geo[k];
+        const int j = dealt_pos(k, n, n_wg);
+        const int b = iseq[j];
+        const int2 gg = s_geo[j];
         a.units[2 * uix] = make_int4(start[b], slen[b], hist[b], gg.y);
-        a.units[2 * uix + 1] = make_int4(gg.x, gg.x + cost[k] - kCostOverhead - 1, -1,
+        a.units[2 * uix + 1] = make_int4(gg.x, gg.x + c - kCostOverhead - 1, -1,
                                          (cand ? kUnitCandRows : 0) | 1);
       }
       if (tid == 0) {
