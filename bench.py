@@ -44,9 +44,12 @@ KERNEL_SOURCES = {   # the kernel and the scheduler whose work order sets its tr
                                  "plan.hip"],
     "hstu_attn_fwd_pp_kernel": ["attn_fwd_pp.hip", "attn_common.hpp", "hstu_device.hpp",
                                 "plan.hip"],
+    "hstu_attn_fwd_w32_kernel": ["attn_fwd_w32.hip", "attn_common.hpp", "hstu_device.hpp",
+                                 "plan.hip"],
 }
 KERNEL_OF_CHOICE = {"four_wave": "hstu_attn_fwd_kernel", "sixteen_row": "hstu_attn_fwd_w16_kernel",
-                    "eight_wave": "hstu_attn_fwd_pp_kernel"}
+                    "eight_wave": "hstu_attn_fwd_pp_kernel",
+                    "thirtytwo_row": "hstu_attn_fwd_w32_kernel"}
 
 
 def log(msg: str) -> None:
@@ -335,7 +338,7 @@ def main() -> int:
     ap.add_argument("--saved-o", action="store_true",
                     help="with --backward: take o / n_scale kept by the training forward")
     ap.add_argument("--fwd-kernel", default="auto",
-                    choices=["auto", "four_wave", "eight_wave", "sixteen_row"],
+                    choices=["auto", "four_wave", "eight_wave", "sixteen_row", "thirtytwo_row"],
                     help="forward kernel: chosen by batch shape (auto), or forced")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 256 MiB device copy (counter calibration)")

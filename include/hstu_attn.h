@@ -277,13 +277,15 @@ int64_t hstu_jagged_attn_valid_pairs(int32_t num_seqs, const int32_t* offsets_ho
 int hstu_jagged_attn_grid(const hstu_attn_desc* desc);
 
 /*
- * Forward kernel choice.  Three kernels compute the same forward over the
+ * Forward kernel choice.  Four kernels compute the same forward over the
  * same work list and workspace: a four-wave kernel (32 query rows per wave,
  * two workgroups per CU, every supported dtype and head size) and, for bf16
  * with d_qk = d_v = 128, a sixteen-row kernel (16 query rows per wave, eight
- * waves per workgroup, four waves per SIMD) and an eight-wave kernel (one
- * workgroup per CU whose two waves per SIMD alternate between matrix-core
- * and vector work).  AUTO (the default) takes the sixteen-row kernel where
+ * waves per workgroup, four waves per SIMD), a thirty-two-row kernel (two
+ * 16-row groups per wave sharing every K/V operand read, four waves per
+ * workgroup, two waves per SIMD) and an eight-wave kernel (one workgroup per
+ * CU whose two waves per SIMD alternate between matrix-core and vector
+ * work).  AUTO (the default) takes the sixteen-row kernel where
  * it is built and the four-wave kernel elsewhere; the eight-wave kernel runs
  * only when chosen.  The setting is process-wide; a plan and the runs that
  * use it must see the same setting (the launch size depends on it).  All
@@ -291,7 +293,7 @@ int hstu_jagged_attn_grid(const hstu_attn_desc* desc);
  * in the last bits (different summation order).
  * hstu_jagged_attn_set_fwd_kernel returns HSTU_OK, or HSTU_ERR_INVALID_ARG
  * for an unknown mode.  hstu_jagged_attn_fwd_kernel_of returns the kernel
- * `desc` would run (FOUR_WAVE, EIGHT_WAVE or SIXTEEN_ROW), or -1 on a bad
+ * `desc` would run (FOUR_WAVE, EIGHT_WAVE, SIXTEEN_ROW or THIRTYTWO_ROW), or -1 on a bad
  * desc.  A mode whose kernel does not support `desc` falls back to the
  * four-wave kernel.
  */
@@ -299,7 +301,8 @@ enum {
   HSTU_FWD_KERNEL_AUTO = 0,
   HSTU_FWD_KERNEL_FOUR_WAVE = 1,
   HSTU_FWD_KERNEL_EIGHT_WAVE = 2,
-  HSTU_FWD_KERNEL_SIXTEEN_ROW = 3
+  HSTU_FWD_KERNEL_SIXTEEN_ROW = 3,
+  HSTU_FWD_KERNEL_THIRTYTWO_ROW = 4
 };
 int hstu_jagged_attn_set_fwd_kernel(int32_t mode);
 int hstu_jagged_attn_fwd_kernel_of(const hstu_attn_desc* desc);

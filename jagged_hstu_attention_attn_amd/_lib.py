@@ -26,6 +26,7 @@ HSTU_FWD_KERNEL_AUTO = 0
 HSTU_FWD_KERNEL_FOUR_WAVE = 1
 HSTU_FWD_KERNEL_EIGHT_WAVE = 2
 HSTU_FWD_KERNEL_SIXTEEN_ROW = 3
+HSTU_FWD_KERNEL_THIRTYTWO_ROW = 4
 
 # every function the header declares
 EXPORTS = (

@@ -76,12 +76,13 @@ def make_desc(q, k, v, u, out, num_seqs: int, *, pos_table=None, time_table=None
 
 FWD_KERNELS = {"auto": _lib.HSTU_FWD_KERNEL_AUTO, "four_wave": _lib.HSTU_FWD_KERNEL_FOUR_WAVE,
                "eight_wave": _lib.HSTU_FWD_KERNEL_EIGHT_WAVE,
-               "sixteen_row": _lib.HSTU_FWD_KERNEL_SIXTEEN_ROW}
+               "sixteen_row": _lib.HSTU_FWD_KERNEL_SIXTEEN_ROW,
+               "thirtytwo_row": _lib.HSTU_FWD_KERNEL_THIRTYTWO_ROW}
 
 
 def set_fwd_kernel(name: str) -> None:
     """Process-wide forward kernel choice ("auto", "four_wave", "eight_wave",
-    "sixteen_row");
+    "sixteen_row", "thirtytwo_row");
     a plan and the runs that use it must see the same choice."""
     _lib.check(_lib.load().hstu_jagged_attn_set_fwd_kernel(FWD_KERNELS[name]))
 

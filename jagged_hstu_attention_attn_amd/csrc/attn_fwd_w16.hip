@@ -581,7 +581,9 @@ hstu_attn_fwd_w16_kernel(AttnArgs a) {
   // One pipeline step on the walk's blocks s, s + 1 held in buffers `bufc`,
   // `bufc` + 1: copy blocks s + 2, s + 3 into the other two buffers (freed
   // by the previous barrier), compute both blocks, then (this wave's copies
-  // landed) finish the next two and synchronise.
+  // landed) finish the next two and synchronise.  The second copy is issued
+  // after the first block: every wave leaves the barrier together, and
+  // issuing all copies at once queues them behind each other.
   auto step = [&](auto bufc, int s) __attribute__((always_inline)) {
     constexpr int b = decltype(bufc)::value;
     using N1 = std::integral_constant<int, (b + 1) % kW16Stages>;
@@ -591,8 +593,8 @@ hstu_attn_fwd_w16_kernel(AttnArgs a) {
     const int kt = blk(s), kt1 = blk(s + 1), kt2 = blk(s + 2), kt3 = blk(s + 3);
     if (next0) issue_stage(N2{}, kt2);
     else issue_u();
-    if (next1) issue_stage(N3{}, kt3);
     if (needs(kt)) block(stage(bufc), kt);
+    if (next1) issue_stage(N3{}, kt3);
     if (has1 && needs(kt1)) block(stage(N1{}), kt1);
     if (next0) {
       wait_vmem<0>();

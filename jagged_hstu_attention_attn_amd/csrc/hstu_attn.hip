@@ -138,6 +138,8 @@ int fwd_kernel_choice(const hstu_attn_desc* d) {
     return HSTU_FWD_KERNEL_EIGHT_WAVE;
   const bool w16 = hstu::attn_w16_supported(d->dtype, d->d_qk, d->d_v);
   if (mode == HSTU_FWD_KERNEL_SIXTEEN_ROW && w16) return HSTU_FWD_KERNEL_SIXTEEN_ROW;
+  if (mode == HSTU_FWD_KERNEL_THIRTYTWO_ROW && hstu::attn_w32_supported(d->dtype, d->d_qk, d->d_v))
+    return HSTU_FWD_KERNEL_THIRTYTWO_ROW;
   if (mode == HSTU_FWD_KERNEL_AUTO && w16 && hstu::kW16Auto) return HSTU_FWD_KERNEL_SIXTEEN_ROW;
   return HSTU_FWD_KERNEL_FOUR_WAVE;
 }
@@ -171,6 +173,8 @@ int persistent_grid(const hstu_attn_desc* d) {
             ? hstu::attn_pp_grid(d->pos_table_len, d->time_table_len, clamp != 0)
         : kern == HSTU_FWD_KERNEL_SIXTEEN_ROW
             ? hstu::attn_w16_grid(d->pos_table_len, d->time_table_len, clamp != 0)
+        : kern == HSTU_FWD_KERNEL_THIRTYTWO_ROW
+            ? hstu::attn_w32_grid(d->pos_table_len, d->time_table_len, clamp != 0)
             : hstu::attn_grid(d->dtype, d->d_qk, d->d_v, d->pos_table_len, d->time_table_len,
                               clamp != 0);
     if (g <= 0) return g;
@@ -337,6 +341,7 @@ static int run_impl(const hstu_attn_desc* desc, const void* q, const void* k, co
   const hipError_t e =
       kern == HSTU_FWD_KERNEL_EIGHT_WAVE    ? hstu::launch_attn_pp(a, n_wg, st, e0, e1)
       : kern == HSTU_FWD_KERNEL_SIXTEEN_ROW ? hstu::launch_attn_w16(a, n_wg, st, e0, e1)
+      : kern == HSTU_FWD_KERNEL_THIRTYTWO_ROW ? hstu::launch_attn_w32(a, n_wg, st, e0, e1)
           : hstu::launch_attn(a, desc->dtype, desc->d_qk, desc->d_v, n_wg, st, e0, e1);
   if (e != hipSuccess)
     return fail(HSTU_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
@@ -559,7 +564,8 @@ int64_t hstu_jagged_attn_valid_pairs(int32_t num_seqs, const int32_t* offsets_ho
 
 int hstu_jagged_attn_set_fwd_kernel(int32_t mode) {
   if (mode != HSTU_FWD_KERNEL_AUTO && mode != HSTU_FWD_KERNEL_FOUR_WAVE &&
-      mode != HSTU_FWD_KERNEL_EIGHT_WAVE && mode != HSTU_FWD_KERNEL_SIXTEEN_ROW)
+      mode != HSTU_FWD_KERNEL_EIGHT_WAVE && mode != HSTU_FWD_KERNEL_SIXTEEN_ROW &&
+      mode != HSTU_FWD_KERNEL_THIRTYTWO_ROW)
     return fail(HSTU_ERR_INVALID_ARG, "unknown forward kernel mode %d", mode);
   g_fwd_kernel.store(mode, std::memory_order_relaxed);
   return HSTU_OK;

@@ -390,6 +390,13 @@ bool attn_w16_supported(int dtype, int d_qk, int d_v);
 int attn_w16_grid(int pos_len, int time_len, bool clamp);
 hipError_t launch_attn_w16(const AttnArgs& a, int n_wg, hipStream_t stream,
                            hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
+// The thirty-two-row forward (attn_fwd_w32.hip): bf16, d_qk = d_v = 128; four
+// waves of two 16-row groups per workgroup, two waves per SIMD; same units,
+// workspace and arguments as launch_attn.
+bool attn_w32_supported(int dtype, int d_qk, int d_v);
+int attn_w32_grid(int pos_len, int time_len, bool clamp);
+hipError_t launch_attn_w32(const AttnArgs& a, int n_wg, hipStream_t stream,
+                           hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 // Batches whose mean sequence length reaches this many tokens take the
 // eight-wave kernel (short sequences give it too few key blocks per item to
 // fill its pipeline; the four-wave kernel runs two workgroups per CU).

@@ -324,6 +324,10 @@ def test_forward_kernel_choice(lib):
         assert lib.hstu_jagged_attn_set_fwd_kernel(w16) == _lib.HSTU_OK
         assert lib.hstu_jagged_attn_fwd_kernel_of(ctypes.byref(long_d)) == w16
         assert lib.hstu_jagged_attn_fwd_kernel_of(ctypes.byref(d64)) == four      # unsupported
+        w32 = _lib.HSTU_FWD_KERNEL_THIRTYTWO_ROW
+        assert lib.hstu_jagged_attn_set_fwd_kernel(w32) == _lib.HSTU_OK
+        assert lib.hstu_jagged_attn_fwd_kernel_of(ctypes.byref(long_d)) == w32
+        assert lib.hstu_jagged_attn_fwd_kernel_of(ctypes.byref(f32_d)) == four    # unsupported
         assert lib.hstu_jagged_attn_set_fwd_kernel(7) == _lib.HSTU_ERR_INVALID_ARG
         assert lib.hstu_jagged_attn_fwd_kernel_of(ctypes.byref(_desc(num_heads=0))) == -1
     finally:

@@ -1,4 +1,5 @@
-"""Each bf16 d = 128 forward kernel (four-wave, eight-wave, sixteen-row)
+"""Each bf16 d = 128 forward kernel (four-wave, eight-wave, sixteen-row,
+thirty-two-row)
 against the fp64 oracle.
 
 The library picks a forward kernel by shape (see the header: the sixteen-row
@@ -22,7 +23,7 @@ from jagged_hstu_attention_attn_amd.inputs import make_custom, make_inputs
 pytestmark = pytest.mark.gpu
 
 
-@pytest.fixture(params=["four_wave", "eight_wave", "sixteen_row"], autouse=True)
+@pytest.fixture(params=["four_wave", "eight_wave", "sixteen_row", "thirtytwo_row"], autouse=True)
 def kernel(request):
     """The forward kernel every call of the test is forced to."""
     global _KERNEL
