@@ -285,16 +285,16 @@ int hstu_jagged_attn_grid(const hstu_attn_desc* desc);
  * 16-row groups per wave sharing every K/V operand read, four waves per
  * workgroup, two waves per SIMD) and an eight-wave kernel (one workgroup per
  * CU whose two waves per SIMD alternate between matrix-core and vector
- * work).  AUTO (the default) takes the sixteen-row kernel where
- * it is built and the four-wave kernel elsewhere; the eight-wave kernel runs
- * only when chosen.  The setting is process-wide; a plan and the runs that
- * use it must see the same setting (the launch size depends on it).  All
- * kernels meet the same tolerance against the oracle; their outputs differ
- * in the last bits (different summation order).
+ * work).  AUTO (the default) takes the sixteen-row kernel where it is built
+ * and the four-wave kernel elsewhere; the eight-wave and thirty-two-row
+ * kernels run only when chosen.  The setting is process-wide; a plan and the
+ * runs that use it must see the same setting (the launch size depends on
+ * it).  All kernels meet the same tolerance against the oracle; their
+ * outputs differ in the last bits (different summation order).
  * hstu_jagged_attn_set_fwd_kernel returns HSTU_OK, or HSTU_ERR_INVALID_ARG
  * for an unknown mode.  hstu_jagged_attn_fwd_kernel_of returns the kernel
- * `desc` would run (FOUR_WAVE, EIGHT_WAVE, SIXTEEN_ROW or THIRTYTWO_ROW), or -1 on a bad
- * desc.  A mode whose kernel does not support `desc` falls back to the
+ * `desc` would run (FOUR_WAVE, EIGHT_WAVE, SIXTEEN_ROW or THIRTYTWO_ROW), or
+ * -1 on a bad desc.  A mode whose kernel does not support `desc` falls back to the
  * four-wave kernel.
  */
 enum {
