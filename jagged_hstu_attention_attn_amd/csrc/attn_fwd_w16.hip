@@ -112,15 +112,16 @@ hstu_attn_fwd_w16_kernel(AttnArgs a) {
   const float pscale = kLog2e / am;              // position bias in accumulator units
   const uint32_t ldk_b = (uint32_t)(a.ld_k * 2), ldv_b = (uint32_t)(a.ld_v * 2);
   // copies of one stage: wave w copies 1 KB chunk w of the keys and of the
-  // values (rows 4w .. 4w + 3); the bias inputs go to "role" waves, which a
-  // stage in an odd buffer maps to wave role ^ 4 (the two stages of a step
-  // split that work between the two halves of the workgroup, which would
-  // otherwise wait at the barrier for one half): roles 5-7 gather the
-  // position-bias diagonal (part role - 5), role 4 the raw timestamps, role
-  // 3 the clamped-position bias
-  constexpr int kTsW = 4, kCposW = 3, kDiagW0 = 5;
+  // values (rows 4w .. 4w + 3); the bias inputs go to "role" waves among
+  // waves 0-3, which a stage in an odd buffer maps to wave 3 - role (the two
+  // stages of a step spread that work over the four): roles 1-3 gather the
+  // position-bias diagonal (part role - 1), role 0 the raw timestamps and
+  // the clamped-position bias.  Waves w and w + 4 share a SIMD, whose
+  // arbiter favours the older wave, so waves 4-7 compute more slowly and
+  // reach each barrier last; the extra copies go to the waves that wait.
+  constexpr int kTsW = 0, kCposW = 0, kDiagW0 = 1;
   auto role_wave = [&](auto bufc) __attribute__((always_inline)) {
-    return (decltype(bufc)::value & 1) ? (wave ^ 4) : wave;
+    return ((decltype(bufc)::value & 1) && wave < 4) ? 3 - wave : wave;
   };
   static_assert(kDiagW0 + kDiagCopies <= kW16Waves, "enough waves for the bias copies");
 
@@ -244,7 +245,7 @@ hstu_attn_fwd_w16_kernel(AttnArgs a) {
     }
     const int rw = role_wave(bufc);
     if constexpr (POS) {
-      if (rw >= kDiagW0) {
+      if (rw >= kDiagW0 && rw < kDiagW0 + kDiagCopies) {   // part rw - kDiagW0 of the diagonal
         const int p = rw - kDiagW0;
         const int d = i0 - j0 + (kBM - 1) - (64 * p + ln);
         const int ix = min(d < 0 ? -d : d, P - 1);
@@ -278,7 +279,7 @@ hstu_attn_fwd_w16_kernel(AttnArgs a) {
     const int ln = opaque_lane();
     const int rw = role_wave(bufc);
     if constexpr (POS) {
-      if (rw >= kDiagW0) {
+      if (rw >= kDiagW0 && rw < kDiagW0 + kDiagCopies) {
         const int e = 64 * (rw - kDiagW0) + ln;
         if (e < kDiag) sb.diag[e] *= pscale;
       }
