@@ -125,7 +125,9 @@ def bench_layer(args, inp) -> int:
     f_attn = 2.0 * (dqk + dv) * H * pairs
     flops = f_proj + f_attn + f_out
     flush = None if args.no_flush else torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-    for _ in range(args.warmup):
+    for s in range(args.warmup):   # warm-up steps are the timed steps, flush included
+        if flush is not None:
+            flush.fill_(s & 0xFF)
         lay()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
@@ -192,7 +194,9 @@ def bench_backward(args, inp) -> int:
     flush = None if args.no_flush else torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
     log(f"backward: {inp.num_seqs} sequences, {inp.total_tokens} tokens, {pairs} valid "
         f"pairs/head; warmup {args.warmup}")
-    for _ in range(args.warmup):
+    for s in range(args.warmup):   # warm-up steps are the timed steps, flush included
+        if flush is not None:
+            flush.fill_(s & 0xFF)
         call(dout, o_saved)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
@@ -316,7 +320,7 @@ def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="windowed",
                     choices=["tiny", "ranking", "longtail", "windowed", "layer"])
     ap.add_argument("--seed", type=int, default=None)
@@ -383,8 +387,7 @@ def main() -> int:
         del inp
         log("secondary record: ranking batch")
         sec_inp = make_inputs("ranking")
-        sec = measure_forward(args, sec_inp, "ranking", args.secondary_steps,
-                              min(args.warmup, 10))
+        sec = measure_forward(args, sec_inp, "ranking", args.secondary_steps, args.warmup)
         keep = ("value", "unit", "ms_per_step", "steps", "warmup", "config", "tokens_per_s",
                 "pct_bf16_mfma_peak", "pct_hbm_peak", "plan_us", "roofline")
         result["secondary"] = {k: sec[k] for k in keep}
@@ -416,8 +419,14 @@ def measure_forward(args, inp, workload: str, steps: int, warmup: int) -> dict:
 
     log(f"{workload}: {inp.num_seqs} sequences, {inp.total_tokens} tokens, {pairs} valid "
         f"pairs/head; warmup {warmup}")
-    for _ in range(warmup):
-        call()
+    # Warm-up steps are the timed steps (flush, scheduler, attention): the
+    # first steps that rewrite the flush buffer run measurably slower, and
+    # a warm-up without the flush left that transient inside the timed loop.
+    for s in range(warmup):
+        if flush is not None:
+            flush.fill_(s & 0xFF)
+        call.plan()
+        call.run()
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
