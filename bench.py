@@ -65,9 +65,10 @@ def kernel_source_hash(kernel: str) -> str:
 
 
 def algorithmic(inp, valid_pairs: int):
-    """Algorithmic flops and HBM bytes of one forward (definitions in the
-    design notes): 2*(d_qk+d_v) flops per valid pair and head; q, k, v, u read
-    once, out written once, plus timestamps, metadata and bias tables."""
+    """Algorithmic flops and HBM bytes of one forward: 2*(d_qk+d_v) flops per
+    valid pair and head (the two products Q K^T and A V; masked pairs inside a
+    computed tile are not counted); q, k, v, u read once, out written once,
+    plus timestamps, offsets and candidate counts, and the bias tables."""
     H, dqk, dv, N, B = inp.num_heads, inp.d_qk, inp.d_v, inp.total_tokens, inp.num_seqs
     es = 2 if inp.dtype == "bf16" else 4
     flops = 2.0 * (dqk + dv) * H * valid_pairs
@@ -350,7 +351,8 @@ def main() -> int:
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the forward shards by sequence with no exchange; see the design notes)",
+              "(the forward shards by sequence with no exchange, so each GPU would run this "
+              "same measurement on its own batch)",
               file=sys.stderr)
         return 2
 

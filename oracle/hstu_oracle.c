@@ -36,7 +36,7 @@
  * "Mathematical Equivalence" (contextual bidirectional prefix, candidate
  * position clamping, target-group masking, max attention length) with the
  * causal indicator 1_{j<=i} of the teaching equation.  Readings taken where the
- * pages are silent (all listed with the design notes):
+ * pages are silent:
  *   - L = seq length, T = clamp(num_targets[b], 0, L), n_h = L - T history
  *     tokens, c = clamp(contextual_len, 0, n_h) prefix tokens.
  *   - prefix rows i < c see j < c (bidirectional);
