@@ -121,7 +121,9 @@ typedef struct {
  * the fp32 shapes with d_qk == d_v.  (BF16,256,256)
  * runs one workgroup per CU (its 32 x 256 output tile per wave needs the
  * registers of two).  Alignment: q, k, v, u, out 16-byte aligned and
- * ld_x * sizeof(element) a multiple of 16 bytes with ld_x >= H * d.
+ * ld_x * sizeof(element) a multiple of 16 bytes with ld_x >= H * d; a token
+ * row may span at most 16 MiB (ld_x * sizeof(element) <= 2^24), larger
+ * strides are refused with HSTU_ERR_UNSUPPORTED.
  * Returns 1 if supported, 0 if not (no message is set).
  */
 int hstu_jagged_attn_supported(int32_t dtype, int32_t d_qk, int32_t d_v);

@@ -36,6 +36,8 @@ hstu::PlanLayout fwd_layout(const hstu_attn_desc* d, bool no_split = false) {
   return hstu::plan_layout(d->num_seqs, d->total_tokens, d->num_heads, d->d_v, splits);
 }
 
+constexpr int64_t kMaxRowBytes = int64_t(1) << 24;   // bytes of one token row, any tensor
+
 int check_desc(const hstu_attn_desc* d) {
   if (!d) return fail(HSTU_ERR_INVALID_ARG, "desc is NULL");
   if (d->num_seqs < 0) return fail(HSTU_ERR_INVALID_ARG, "num_seqs < 0 (%d)", d->num_seqs);
@@ -82,6 +84,11 @@ int check_desc(const hstu_attn_desc* d) {
     if ((x.ld * (int64_t)es) % 16 != 0)
       return fail(HSTU_ERR_INVALID_ARG, "%s * element size must be a multiple of 16 bytes",
                   x.name);
+    // the kernels form a copy's offset within a tile as a 32-bit row * stride
+    // (rows below 256), so a token row may span at most 16 MiB
+    if (x.ld * (int64_t)es > kMaxRowBytes)
+      return fail(HSTU_ERR_UNSUPPORTED, "%s * element size = %lld bytes exceeds %lld", x.name,
+                  (long long)(x.ld * (int64_t)es), (long long)kMaxRowBytes);
   }
   const hstu::PlanLayout pl = fwd_layout(d);
   if (2 * pl.units_max > 0x7fffffffLL || (int64_t)d->num_seqs * H > 0x7fffffffLL)

@@ -92,6 +92,8 @@ def _fwd(lib, d, ws_bytes=None, **kw):
     ("ln_eps", 0.0, _lib.HSTU_ERR_INVALID_ARG),
     ("pos_table_len", 9000, _lib.HSTU_ERR_UNSUPPORTED),
     ("pos_clamp", 2, _lib.HSTU_ERR_INVALID_ARG),
+    ("ld_v", (1 << 23) + 8, _lib.HSTU_ERR_UNSUPPORTED),  # a bf16 token row past 16 MiB
+    ("ld_out", 1 << 24, _lib.HSTU_ERR_UNSUPPORTED),
 ])
 def test_bad_descriptor(lib, field, value, code):
     d = _desc(**{field: value})
@@ -99,6 +101,14 @@ def test_bad_descriptor(lib, field, value, code):
     assert _lib.last_error() != ""
     if code == _lib.HSTU_ERR_INVALID_ARG or code == _lib.HSTU_ERR_UNSUPPORTED:
         assert lib.hstu_jagged_attn_workspace_bytes(ctypes.byref(d)) == 0
+
+
+def test_token_row_of_16_mib_is_accepted(lib):
+    """Kernels form a tile copy's offset as a 32-bit row * stride (rows below
+    256): a token row of exactly 2^24 bytes is the largest the descriptor
+    takes."""
+    d = _desc(ld_q=1 << 23, ld_k=1 << 23, ld_v=1 << 23, ld_u=1 << 23, ld_out=1 << 23)
+    assert lib.hstu_jagged_attn_workspace_bytes(ctypes.byref(d)) > 0
 
 
 @pytest.mark.parametrize("kw,code", [
