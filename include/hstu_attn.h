@@ -117,8 +117,8 @@ typedef struct {
 /*
  * Supported (dtype, d_qk, d_v) of the forward: (BF16,128,128), (BF16,64,64),
  * (BF16,64,128), (BF16,128,64), (BF16,256,256), (F32,128,128), (F32,64,64),
- * (F32,8,8); the backward takes every bf16 shape but (BF16,256,256) and
- * the fp32 shapes with d_qk == d_v.  (BF16,256,256)
+ * (F32,8,8); the backward takes every bf16 shape (d = 256 through its
+ * per-token kernels) and the fp32 shapes with d_qk == d_v.  (BF16,256,256)
  * runs one workgroup per CU (its 32 x 256 output tile per wave needs the
  * registers of two).  Alignment: q, k, v, u, out 16-byte aligned and
  * ld_x * sizeof(element) a multiple of 16 bytes with ld_x >= H * d; a token
@@ -380,16 +380,19 @@ int hstu_layer_fwd(const hstu_layer_desc* desc, const void* x, const void* w_uvq
  * given, else recomputed (one forward pass with epilogue NONE, rounded to
  * dtype) inside the call.
  *
- * Shapes: d_qk, d_v in {64, 128} for bf16 (equal or not) and d_qk == d_v in
- * {8, 64, 128} for fp32; other head sizes return HSTU_ERR_UNSUPPORTED before
- * any HIP call.
+ * Shapes: d_qk, d_v in {64, 128} for bf16 (equal or not), d_qk = d_v = 256
+ * for bf16, and d_qk == d_v in {8, 64, 128} for fp32; other head sizes
+ * return HSTU_ERR_UNSUPPORTED before any HIP call.
  *
- * Execution: a scheduler kernel, then for bf16 (d = 64, 128) a dQ pass over
- * query tiles and a dK/dV pass over key tiles (bf16 MFMA, fp32 accumulation;
- * each token gradient written by one workgroup, so those are deterministic)
- * and a reduction of the table gradients (fp32 sums whose order depends on
- * the schedule only through LDS atomics within a workgroup); for fp32 two
- * plain kernels with fp32 atomics on the tables.  Ownership, streams, error
+ * Execution: for bf16 with d = 64, 128 a scheduler kernel, then a dQ pass
+ * over query tiles and a dK/dV pass over key tiles (bf16 MFMA, fp32
+ * accumulation; each token gradient written by one workgroup, so those are
+ * deterministic) and a reduction of the table gradients (fp32 sums whose
+ * order depends on the schedule only through LDS atomics within a
+ * workgroup).  For fp32, and for bf16 with d = 256, two per-token kernels
+ * (one wave per token and head, fp32 arithmetic, bf16 or fp32 loads and
+ * stores) with fp64 atomics on the table sums, rounded to fp32 at the end:
+ * a correctness path, far slower than the matrix-core passes.  Ownership, streams, error
  * behaviour and trusted device data as for the forward.  Workspace:
  * hstu_jagged_attn_bwd_workspace_bytes(desc) bytes, 16-byte aligned; B == 0
  * or total_tokens == 0 only zeroes the tables.

@@ -1353,8 +1353,14 @@ __global__ __launch_bounds__(256) void hstu_fill_zero_kernel(float* p, int64_t n
 }
 
 // ---------------------------------------------------------------------------
-// fp32 passes: one wave per (token, head), lanes over the head dimension.
+// Per-token passes: one wave per (token, head), lanes over the head dimension,
+// fp32 arithmetic on inputs of element type T (fp32, or bf16 for the head
+// size the matrix-core passes are not built for).
 // ---------------------------------------------------------------------------
+template <typename T>
+__device__ inline float elt(const void* p, int64_t ix) {
+  return (float)static_cast<const T*>(p)[ix];
+}
 __device__ inline int seq_of(const int32_t* offsets, int num_seqs, int t) {
   int lo = 0, hi = num_seqs - 1;   // last b with offsets[b] <= t
   while (lo < hi) {
@@ -1393,7 +1399,7 @@ __device__ inline float f32_score(const BwdArgs& a, const float* qi, const float
   return s;
 }
 
-template <int D>
+template <int D, typename T>
 __global__ __launch_bounds__(256) void hstu_bwd_dq_f32_kernel(BwdArgs a, int num_seqs) {
   constexpr int E = (D + 63) / 64;
   const int lane = threadIdx.x & 63;
@@ -1405,16 +1411,12 @@ __global__ __launch_bounds__(256) void hstu_bwd_dq_f32_kernel(BwdArgs a, int num
   const SeqGeom geo = seq_geom(L, a.num_targets ? a.num_targets[b] : 0, a.contextual_len,
                                a.max_attn_len);
   const RowBounds rb = row_bounds(geo, i);
-  const float* q = static_cast<const float*>(a.q);
-  const float* k = static_cast<const float*>(a.k);
-  const float* v = static_cast<const float*>(a.v);
-  const float* dO = static_cast<const float*>(a.dout);
   float qi[E], doi[E], acc[E];
 #pragma unroll
   for (int m = 0; m < E; ++m) {
     const int e = lane + 64 * m;
-    qi[m] = e < D ? q[(int64_t)tok * a.ld_q + h * D + e] : 0.0f;
-    doi[m] = e < D ? dO[(int64_t)tok * a.ld_do + h * D + e] : 0.0f;
+    qi[m] = e < D ? elt<T>(a.q, (int64_t)tok * a.ld_q + h * D + e) : 0.0f;
+    doi[m] = e < D ? elt<T>(a.dout, (int64_t)tok * a.ld_do + h * D + e) : 0.0f;
     acc[m] = 0.0f;
   }
   const int64_t ti = a.time_len > 0 ? a.timestamps[tok] : 0;
@@ -1425,8 +1427,8 @@ __global__ __launch_bounds__(256) void hstu_bwd_dq_f32_kernel(BwdArgs a, int num
 #pragma unroll
     for (int m = 0; m < E; ++m) {
       const int e = lane + 64 * m;
-      kj[m] = e < D ? k[(int64_t)(seq0 + j) * a.ld_k + h * D + e] : 0.0f;
-      vj[m] = e < D ? v[(int64_t)(seq0 + j) * a.ld_v + h * D + e] : 0.0f;
+      kj[m] = e < D ? elt<T>(a.k, (int64_t)(seq0 + j) * a.ld_k + h * D + e) : 0.0f;
+      vj[m] = e < D ? elt<T>(a.v, (int64_t)(seq0 + j) * a.ld_v + h * D + e) : 0.0f;
     }
     int pidx = 0, tidx = 0;
     const int64_t tj = a.time_len > 0 ? a.timestamps[seq0 + j] : 0;
@@ -1445,15 +1447,15 @@ __global__ __launch_bounds__(256) void hstu_bwd_dq_f32_kernel(BwdArgs a, int num
       if (a.time_len > 0) atomicAdd(&a.tab64[a.pos_len + tidx], (double)ds);
     }
   }
-  float* dq = static_cast<float*>(a.dq);
+  T* dq = static_cast<T*>(a.dq);
 #pragma unroll
   for (int m = 0; m < E; ++m) {
     const int e = lane + 64 * m;
-    if (e < D) dq[(int64_t)tok * a.ld_q + h * D + e] = acc[m];
+    if (e < D) dq[(int64_t)tok * a.ld_q + h * D + e] = (T)acc[m];
   }
 }
 
-template <int D>
+template <int D, typename T>
 __global__ __launch_bounds__(256) void hstu_bwd_dkv_f32_kernel(BwdArgs a, int num_seqs) {
   constexpr int E = (D + 63) / 64;
   const int lane = threadIdx.x & 63;
@@ -1465,16 +1467,12 @@ __global__ __launch_bounds__(256) void hstu_bwd_dkv_f32_kernel(BwdArgs a, int nu
   const SeqGeom geo = seq_geom(L, a.num_targets ? a.num_targets[b] : 0, a.contextual_len,
                                a.max_attn_len);
   const RowBounds cb = col_bounds(geo, j);
-  const float* q = static_cast<const float*>(a.q);
-  const float* k = static_cast<const float*>(a.k);
-  const float* v = static_cast<const float*>(a.v);
-  const float* dO = static_cast<const float*>(a.dout);
   float kj[E], vj[E], ak[E], av[E];
 #pragma unroll
   for (int m = 0; m < E; ++m) {
     const int e = lane + 64 * m;
-    kj[m] = e < D ? k[(int64_t)tok * a.ld_k + h * D + e] : 0.0f;
-    vj[m] = e < D ? v[(int64_t)tok * a.ld_v + h * D + e] : 0.0f;
+    kj[m] = e < D ? elt<T>(a.k, (int64_t)tok * a.ld_k + h * D + e) : 0.0f;
+    vj[m] = e < D ? elt<T>(a.v, (int64_t)tok * a.ld_v + h * D + e) : 0.0f;
     ak[m] = 0.0f;
     av[m] = 0.0f;
   }
@@ -1486,8 +1484,8 @@ __global__ __launch_bounds__(256) void hstu_bwd_dkv_f32_kernel(BwdArgs a, int nu
 #pragma unroll
     for (int m = 0; m < E; ++m) {
       const int e = lane + 64 * m;
-      qi[m] = e < D ? q[(int64_t)(seq0 + i) * a.ld_q + h * D + e] : 0.0f;
-      doi[m] = e < D ? dO[(int64_t)(seq0 + i) * a.ld_do + h * D + e] : 0.0f;
+      qi[m] = e < D ? elt<T>(a.q, (int64_t)(seq0 + i) * a.ld_q + h * D + e) : 0.0f;
+      doi[m] = e < D ? elt<T>(a.dout, (int64_t)(seq0 + i) * a.ld_do + h * D + e) : 0.0f;
     }
     int pidx = 0, tidx = 0;
     const int64_t ti = a.time_len > 0 ? a.timestamps[seq0 + i] : 0;
@@ -1505,14 +1503,14 @@ __global__ __launch_bounds__(256) void hstu_bwd_dkv_f32_kernel(BwdArgs a, int nu
       ak[m] += a.alpha * ds * qi[m];
     }
   }
-  float* dk = static_cast<float*>(a.dk);
-  float* dv = static_cast<float*>(a.dv);
+  T* dk = static_cast<T*>(a.dk);
+  T* dv = static_cast<T*>(a.dv);
 #pragma unroll
   for (int m = 0; m < E; ++m) {
     const int e = lane + 64 * m;
     if (e < D) {
-      dk[(int64_t)tok * a.ld_k + h * D + e] = ak[m];
-      dv[(int64_t)tok * a.ld_v + h * D + e] = av[m];
+      dk[(int64_t)tok * a.ld_k + h * D + e] = (T)ak[m];
+      dv[(int64_t)tok * a.ld_v + h * D + e] = (T)av[m];
     }
   }
 }
@@ -1588,14 +1586,14 @@ hipError_t launch_mfma_d(const BwdArgs& a, int which, int n_wg, hipStream_t stre
   return launch_mfma_one<DQK, DV, false, false, false>(a, which, n_wg, stream);
 }
 
-template <int D>
+template <int D, typename T>
 hipError_t launch_f32_d(const BwdArgs& a, bool kv, int num_seqs, hipStream_t stream) {
   const int64_t waves = (int64_t)a.n_tok * a.num_heads;
   const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
   if (kv)
-    hipLaunchKernelGGL((hstu_bwd_dkv_f32_kernel<D>), grid, block, 0, stream, a, num_seqs);
+    hipLaunchKernelGGL((hstu_bwd_dkv_f32_kernel<D, T>), grid, block, 0, stream, a, num_seqs);
   else
-    hipLaunchKernelGGL((hstu_bwd_dq_f32_kernel<D>), grid, block, 0, stream, a, num_seqs);
+    hipLaunchKernelGGL((hstu_bwd_dq_f32_kernel<D, T>), grid, block, 0, stream, a, num_seqs);
   return hipGetLastError();
 }
 
@@ -1659,15 +1657,26 @@ int bwd_grid(int dtype, int d_qk, int d_v, int pos_len, int time_len, int which,
 }
 
 // Head sizes the backward is built for: bf16 MFMA passes for d_qk, d_v in
-// {64, 128} (equal or not), the fp32 kernels for d_qk == d_v in {8, 64, 128}.
+// {64, 128} (equal or not); the per-token kernels for fp32 with d_qk == d_v
+// in {8, 64, 128} and for bf16 with d_qk = d_v = 256.
 bool bwd_supported(int dtype, int d_qk, int d_v) {
-  if (dtype == 1) return (d_qk == 64 || d_qk == 128) && (d_v == 64 || d_v == 128);
+  if (dtype == 1)
+    return ((d_qk == 64 || d_qk == 128) && (d_v == 64 || d_v == 128)) ||
+           (d_qk == 256 && d_v == 256);
   if (dtype == 0) return d_qk == d_v && (d_qk == 8 || d_qk == 64 || d_qk == 128);
   return false;
 }
 
+bool bwd_per_token(int dtype, int d_qk, int d_v) {
+  return dtype != 1 || (d_qk == 256 && d_v == 256);
+}
+
 hipError_t launch_bwd(const BwdArgs& a, int dtype, int d_qk, int d_v, int which, int n_wg,
                       hipStream_t stream) {
+  if (dtype == 1 && d_qk == 256 && d_v == 256) {   // per-token kernels, n_wg = sequences
+    if (which == 2) return hipSuccess;
+    return launch_f32_d<256, __bf16>(a, which == 1, n_wg, stream);
+  }
   if (dtype == 1) {
     if (d_qk == 128 && d_v == 128) return launch_mfma_d<128, 128>(a, which, n_wg, stream);
     if (d_qk == 64 && d_v == 64) return launch_mfma_d<64, 64>(a, which, n_wg, stream);
@@ -1679,9 +1688,9 @@ hipError_t launch_bwd(const BwdArgs& a, int dtype, int d_qk, int d_v, int which,
   if (which == 2) return hipSuccess;
   if (d_qk != d_v) return hipErrorInvalidValue;
   const bool kv = which == 1;
-  if (d_qk == 128) return launch_f32_d<128>(a, kv, n_wg, stream);
-  if (d_qk == 64) return launch_f32_d<64>(a, kv, n_wg, stream);
-  if (d_qk == 8) return launch_f32_d<8>(a, kv, n_wg, stream);
+  if (d_qk == 128) return launch_f32_d<128, float>(a, kv, n_wg, stream);
+  if (d_qk == 64) return launch_f32_d<64, float>(a, kv, n_wg, stream);
+  if (d_qk == 8) return launch_f32_d<8, float>(a, kv, n_wg, stream);
   return hipErrorInvalidValue;
 }
 

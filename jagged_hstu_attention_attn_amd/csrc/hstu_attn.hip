@@ -781,10 +781,10 @@ BwdLayout bwd_layout(const hstu_attn_desc* d) {
   const bool tables = d->pos_table_len > 0 || d->time_table_len > 0;
   const size_t stride = (size_t)(d->pos_table_len + 64);
   l.part2_off = l.part_off;
-  if (d->dtype == HSTU_DTYPE_BF16 && tables) {
+  if (!hstu::bwd_per_token(d->dtype, d->d_qk, d->d_v) && tables) {
     l.part2_off = hstu::align256(l.part_off + sizeof(float) * (size_t)hstu::kMaxGrid * stride);
     off = l.part2_off + sizeof(float) * (size_t)((hstu::kMaxGrid + 63) / 64) * stride;
-  } else if (tables) {   // fp32: the fp64 table sums
+  } else if (tables) {   // per-token kernels: the fp64 table sums
     off = l.part_off + sizeof(double) * (size_t)(d->pos_table_len + d->time_table_len);
   }
   l.total = hstu::align256(off);
@@ -837,8 +837,8 @@ int hstu_jagged_attn_bwd(const hstu_attn_desc* desc, const void* q, const void* 
   if (rc != HSTU_OK) return rc;
   if (!hstu::bwd_supported(desc->dtype, desc->d_qk, desc->d_v))
     return fail(HSTU_ERR_UNSUPPORTED,
-                "the backward is built for d_qk, d_v in {64, 128} (bf16) and d_qk == d_v in "
-                "{8, 64, 128} (fp32), not (%d, %d)",
+                "the backward is built for d_qk, d_v in {64, 128} and d_qk = d_v = 256 (bf16) "
+                "and d_qk == d_v in {8, 64, 128} (fp32), not (%d, %d)",
                 desc->d_qk, desc->d_v);
   if (desc->num_seqs > 0 && !offsets) return fail(HSTU_ERR_INVALID_ARG, "offsets is NULL");
   if (contextual_len < 0) return fail(HSTU_ERR_INVALID_ARG, "contextual_len < 0");
@@ -873,11 +873,12 @@ int hstu_jagged_attn_bwd(const hstu_attn_desc* desc, const void* q, const void* 
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
-  const bool bf16 = desc->dtype == HSTU_DTYPE_BF16;
+  // matrix-core passes, or the per-token kernels (fp32; bf16 with d = 256)
+  const bool pertok = hstu::bwd_per_token(desc->dtype, desc->d_qk, desc->d_v);
   // the table gradients are sums: zero them where no pass writes them whole
   const bool tables = desc->pos_table_len > 0 || desc->time_table_len > 0;
   double* tab64 = reinterpret_cast<double*>(static_cast<char*>(workspace) + bl.part_off);
-  if (!empty && !bf16 && tables) {
+  if (!empty && pertok && tables) {
     e = hstu::launch_fill_zero(reinterpret_cast<float*>(tab64),
                                2 * (int64_t)(desc->pos_table_len + desc->time_table_len), s);
     if (e != hipSuccess) return fail(HSTU_ERR_HIP, "fill launch failed: %s", hipGetErrorString(e));
@@ -891,7 +892,7 @@ int hstu_jagged_attn_bwd(const hstu_attn_desc* desc, const void* q, const void* 
   if (empty) return HSTU_OK;
 
   int n_q = 0, n_kv = 0, n_v = 0;
-  if (bf16) {
+  if (!pertok) {
     n_q = bwd_pass_grid(desc, 0);
     n_kv = bwd_pass_grid(desc, 1);
     n_v = bwd_pass_grid(desc, 2);
@@ -968,7 +969,7 @@ int hstu_jagged_attn_bwd(const hstu_attn_desc* desc, const void* q, const void* 
   ba.alpha = alpha;
   ba.inv_scale = (float)(1.0 / (double)n_scale);
   ba.pos_clamp = desc->pos_clamp != 0 && desc->pos_table_len > 0;
-  if (!bf16) {
+  if (pertok) {
     e = hstu::launch_bwd(ba, desc->dtype, desc->d_qk, desc->d_v, 0, desc->num_seqs, s);
     if (e == hipSuccess) e = hstu::launch_bwd(ba, desc->dtype, desc->d_qk, desc->d_v, 1, desc->num_seqs, s);
     if (e == hipSuccess && tables)

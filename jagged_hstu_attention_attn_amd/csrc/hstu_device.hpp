@@ -410,6 +410,9 @@ constexpr bool kW16Auto = true;
 int ln_all_heads_max_width(int dtype);
 hipError_t launch_ln_all_heads(const LnArgs& a, int dtype, hipStream_t stream);
 bool bwd_supported(int dtype, int d_qk, int d_v);
+// Shapes whose backward runs the per-token kernels (fp64 table sums) rather
+// than the matrix-core passes.
+bool bwd_per_token(int dtype, int d_qk, int d_v);
 hipError_t launch_bwd_plan(const BwdPlanArgs& a, hipStream_t stream);
 hipError_t launch_gate_bwd(const GateBwdArgs& a, int dtype, hipStream_t stream);
 // Backward passes: which = 0 (dQ), 1 (dK with the table sums; also dV for

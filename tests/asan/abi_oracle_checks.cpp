@@ -212,9 +212,11 @@ static void abi_checks() {
     CHECK(bwd(b, kFake, kFake, 1u << 30) == HSTU_ERR_UNSUPPORTED);   // no such forward
     check_message();
     b = base_desc();
-    b.d_qk = b.d_v = 256;
+    b.d_qk = b.d_v = 256;   // per-token backward: its workspace is checked before any HIP call
     b.ld_q = b.ld_k = b.ld_v = b.ld_u = b.ld_out = 1024;
-    CHECK(bwd(b, kFake, kFake, 1u << 30) == HSTU_ERR_UNSUPPORTED);   // forward-only shape
+    const size_t bws256 = hstu_jagged_attn_bwd_workspace_bytes(&b);
+    CHECK(bws256 > 0);
+    CHECK(bwd(b, kFake, kFake, bws256 - 1) == HSTU_ERR_WORKSPACE);
     check_message();
     b = base_desc();
     b.pos_clamp = 2;   // a flag: 0 or 1

@@ -249,11 +249,15 @@ def test_backward_validation(lib):
     # the clamped-position bias passes the checks (and then needs a GPU)
     assert _bwd(lib, _desc(pos_clamp=1)) in (_lib.HSTU_OK, _lib.HSTU_ERR_HIP)
     assert _bwd(lib, _desc(pos_clamp=2)) == _lib.HSTU_ERR_INVALID_ARG
-    # d = 256: forward only
+    # bf16 d = 256 (per-token kernels) passes the shape check (and then needs a GPU);
+    # unequal sizes with a 256-wide side are refused before any HIP call
     d256 = _desc(d_qk=256, d_v=256, ld_q=1024, ld_k=1024, ld_v=1024, ld_u=1024, ld_out=1024)
     assert lib.hstu_jagged_attn_workspace_bytes(ctypes.byref(d256)) > 0
-    assert _bwd(lib, d256) == _lib.HSTU_ERR_UNSUPPORTED
-    assert "d_qk, d_v in {64, 128} (bf16)" in _lib.last_error()
+    assert lib.hstu_jagged_attn_bwd_workspace_bytes(ctypes.byref(d256)) > 0
+    assert _bwd(lib, d256) in (_lib.HSTU_OK, _lib.HSTU_ERR_HIP)
+    d256x = _desc(d_qk=256, d_v=128, ld_q=1024, ld_k=1024)
+    assert _bwd(lib, d256x) == _lib.HSTU_ERR_UNSUPPORTED
+    assert "d_qk=256, d_v=128" in _lib.last_error()
     # fp32 d = 8 is built: it passes the shape check (and then needs a GPU)
     d8 = _desc(d_qk=8, d_v=8, dtype=_lib.HSTU_DTYPE_F32, ld_q=32, ld_k=32, ld_v=32, ld_u=32,
                ld_out=32)

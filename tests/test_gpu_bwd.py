@@ -128,6 +128,29 @@ def test_bwd_unequal_head_dims_clamped_long():
 
 
 @pytest.mark.parametrize("epilogue", ["ln_u", "none", "ln_all_u"])
+@pytest.mark.parametrize("W", [0, 100])
+def test_bwd_small_bf16_d256(epilogue, W):
+    """bf16 with d_qk = d_v = 256 (the forward's widest head; the backward
+    runs its per-token kernels): every gradient and both tables against the
+    oracle, every mask rule, ragged lengths past several 128-row tiles."""
+    print(f"case bwd bf16 d=256 W={W} {epilogue}", flush=True)
+    inp = _small("bf16", 256, W=W, seed=11)
+    dout = make_dout(inp, 12)
+    ref = oracle.backward(inp, dout, epilogue=_EP[epilogue])
+    assert_grads(gpu_backward(inp, dout, epilogue), ref, "bf16", epilogue)
+
+
+def test_bwd_bf16_d256_clamped_position_bias():
+    print("case bwd bf16 d=256 pos_clamp", flush=True)
+    inp = make_custom([300, 129, 40, 5], num_heads=2, d_qk=256, d_v=256, dtype="bf16", seed=24,
+                      num_targets=[150, 40, 7, 2], contextual_len=3, max_attn_len=96,
+                      pos_len=320, pos_std=0.3, time_len=32, time_std=0.3, alpha=1.0 / 16)
+    dout = make_dout(inp, seed=5)
+    ref = oracle.backward(inp, dout, epilogue=_EP["ln_u"], pos_clamp=True)
+    assert_grads(gpu_backward(inp, dout, "ln_u", pos_clamp=True), ref, "bf16", "ln_u")
+
+
+@pytest.mark.parametrize("epilogue", ["ln_u", "none", "ln_all_u"])
 @pytest.mark.parametrize("d", [8, 64])
 def test_bwd_small_f32(epilogue, d):
     inp = _small("f32", d, W=40)
