@@ -389,7 +389,10 @@ int hstu_layer_fwd(const hstu_layer_desc* desc, const void* x, const void* w_uvq
  * accumulation; each token gradient written by one workgroup, so those are
  * deterministic) and a reduction of the table gradients (fp32 sums whose
  * order depends on the schedule only through LDS atomics within a
- * workgroup).  For fp32, and for bf16 with d = 256, two per-token kernels
+ * workgroup); for d_qk = d_v = 128 without the clamped-position bias, dV is
+ * the forward's sixteen-row kernel walking key tiles (dV_j = sum_i a_ij dO_i
+ * is the forward with queries and keys exchanged), planned by the forward's
+ * scheduler in the same workspace.  For fp32, and for bf16 with d = 256, two per-token kernels
  * (one wave per token and head, fp32 arithmetic, bf16 or fp32 loads and
  * stores) with fp64 atomics on the table sums, rounded to fp32 at the end:
  * a correctness path, far slower than the matrix-core passes.  Ownership, streams, error

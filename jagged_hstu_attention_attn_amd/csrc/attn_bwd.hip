@@ -173,22 +173,6 @@ __device__ inline int opaque_lane() {
   return l;
 }
 
-// Query rows [rlo, rhi] that keys [j0, j1) can be seen by (col_bounds is
-// nondecreasing in both ends over the history keys; candidate keys are seen
-// by their own rows only).
-__host__ __device__ inline void tile_row_range(const SeqGeom& g, int j0, int j1, int& rlo,
-                                               int& rhi) {
-  const RowBounds f = col_bounds(g, j0);
-  rlo = f.lo != kEmptyLo ? f.lo : f.self_j;
-  const int jl = (j1 < g.n_h ? j1 : g.n_h) - 1;   // last history key of the tile
-  rhi = -1;
-  if (jl >= j0) {
-    const RowBounds e = col_bounds(g, jl);
-    rhi = e.lo + e.span;
-  }
-  if (j1 - 1 >= g.n_h && j1 - 1 > rhi) rhi = j1 - 1;
-}
-
 // ---------------------------------------------------------------------------
 // Scheduler: (sequence, tile) groups sorted by decreasing cost, one list per
 // pass, by a counting sort over cost bins in one workgroup.

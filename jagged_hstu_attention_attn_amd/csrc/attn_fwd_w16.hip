@@ -75,11 +75,22 @@ __device__ inline int w16_vchunk(int c, int row) { return c ^ (2 * (row & 7)); }
 
 // POSM: 0 = no position bias, 1 = position bias of |i - j|, 2 = of the
 // clamped positions |p_i - p_j| (candidate rows take it from cpos).
-template <int POSM, bool TIME>
+// TR: the transposed walk of the backward's value gradient, dV_j = sum_i
+// a_ij dO_i: a tile's "rows" are keys j (their k rows in place of q), the
+// streamed blocks are the query rows i that can see them (q rows as keys,
+// dO rows as values), each lane's allowed partners are the key's column of
+// the mask (col_bounds) and the epilogue is none; the position and time
+// biases depend on |i - j| and |t_i - t_j| only, so they are unchanged.
+template <int POSM, bool TIME, bool TR>
 __global__ __launch_bounds__(kW16Threads) __attribute__((amdgpu_waves_per_eu(4))) void
 hstu_attn_fwd_w16_kernel(AttnArgs a) {
   constexpr bool POS = POSM != 0;
   constexpr bool clamp = POSM == 2;
+  static_assert(!(TR && clamp), "the transposed walk takes the plain position bias");
+  // the allowed partners of this lane's row (of its key, transposed)
+  auto bounds = [](const SeqGeom& g, int x) __attribute__((always_inline)) {
+    return TR ? col_bounds(g, x) : row_bounds(g, x);
+  };
   using SB = W16Stage<clamp>;
   constexpr int ROWB = 256;          // staged row bytes (128 bf16)
   using B0 = std::integral_constant<int, 0>;
@@ -169,7 +180,7 @@ hstu_attn_fwd_w16_kernel(AttnArgs a) {
   const int i0 = ((ch.w & kUnitCandRows) ? geo.n_h : 0) + qt * kBM;
   const int i1 = min(i0 + kBM, L);
   int jlo, jhi;
-  tile_key_range(geo, i0, i1, jlo, jhi);
+  tile_range(geo, i0, i1, TR, jlo, jhi);
   const int kt_lo = max(jlo / kBN, ch.x), kt_hi = min(jhi / kBN, ch.y);
   // Key blocks are walked from a rotation of [kt_lo, kt_hi]: no softmax, so
   // the order is free.  Under a window a tile's range starts four blocks
@@ -192,7 +203,7 @@ hstu_attn_fwd_w16_kernel(AttnArgs a) {
   const bool wave_rows = wr0 < i1;
   int w_jmin, w_jmax, w_lomax, w_himin;
   {
-    const RowBounds rb = row_valid ? row_bounds(geo, i) : RowBounds{kEmptyLo, 0, -1};
+    const RowBounds rb = row_valid ? bounds(geo, i) : RowBounds{kEmptyLo, 0, -1};
     const bool nonempty = rb.lo != kEmptyLo;
     const int hi = rb.lo + rb.span;
     int jmin = nonempty ? rb.lo : (rb.self_j >= 0 ? rb.self_j : 0x7fffffff);
@@ -464,7 +475,7 @@ hstu_attn_fwd_w16_kernel(AttnArgs a) {
     }
     // ---- illegal pairs: an argument whose SiLU is exactly -0 ----
     if (!is_full(kt)) {
-      const RowBounds rb = row_valid ? row_bounds(geo, i) : RowBounds{kEmptyLo, 0, -1};
+      const RowBounds rb = row_valid ? bounds(geo, i) : RowBounds{kEmptyLo, 0, -1};
       int jl = jb + 4 * g4 - rb.lo, js = jb + 4 * g4 - rb.self_j;
       asm volatile("" : "+v"(jl), "+v"(js));
 #pragma unroll
@@ -747,10 +758,10 @@ hstu_attn_fwd_w16_kernel(AttnArgs a) {
   }  // planned workgroups
 }
 
-template <int POSM, bool TIME>
+template <int POSM, bool TIME, bool TR>
 static hipError_t launch_w16_one(const AttnArgs& a, int n_wg, hipStream_t stream,
                                  hipEvent_t start, hipEvent_t stop) {
-  auto kern = hstu_attn_fwd_w16_kernel<POSM, TIME>;
+  auto kern = hstu_attn_fwd_w16_kernel<POSM, TIME, TR>;
   if (start || stop)
     hipExtLaunchKernelGGL(kern, dim3((unsigned)n_wg), dim3(kW16Threads), 0, stream, start, stop,
                           0, a);
@@ -759,9 +770,9 @@ static hipError_t launch_w16_one(const AttnArgs& a, int n_wg, hipStream_t stream
   return hipGetLastError();
 }
 
-template <int POSM, bool TIME>
+template <int POSM, bool TIME, bool TR>
 static int w16_blocks_per_cu() {
-  auto kern = hstu_attn_fwd_w16_kernel<POSM, TIME>;
+  auto kern = hstu_attn_fwd_w16_kernel<POSM, TIME, TR>;
   int nb = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, kW16Threads, 0) != hipSuccess)
     return -1;
@@ -772,15 +783,21 @@ bool attn_w16_supported(int dtype, int d_qk, int d_v) {
   return dtype == 1 && d_qk == 128 && d_v == 128;
 }
 
-int attn_w16_grid(int pos_len, int time_len, bool clamp) {
+int attn_w16_grid(int pos_len, int time_len, bool clamp, bool transposed) {
   const bool pos = pos_len > 0, tim = time_len > 0;
   int bpc;
-  if (pos && clamp && tim) bpc = w16_blocks_per_cu<2, true>();
-  else if (pos && clamp) bpc = w16_blocks_per_cu<2, false>();
-  else if (pos && tim) bpc = w16_blocks_per_cu<1, true>();
-  else if (pos) bpc = w16_blocks_per_cu<1, false>();
-  else if (tim) bpc = w16_blocks_per_cu<0, true>();
-  else bpc = w16_blocks_per_cu<0, false>();
+  if (transposed) {
+    if (clamp) return -1;
+    if (pos && tim) bpc = w16_blocks_per_cu<1, true, true>();
+    else if (pos) bpc = w16_blocks_per_cu<1, false, true>();
+    else if (tim) bpc = w16_blocks_per_cu<0, true, true>();
+    else bpc = w16_blocks_per_cu<0, false, true>();
+  } else if (pos && clamp && tim) bpc = w16_blocks_per_cu<2, true, false>();
+  else if (pos && clamp) bpc = w16_blocks_per_cu<2, false, false>();
+  else if (pos && tim) bpc = w16_blocks_per_cu<1, true, false>();
+  else if (pos) bpc = w16_blocks_per_cu<1, false, false>();
+  else if (tim) bpc = w16_blocks_per_cu<0, true, false>();
+  else bpc = w16_blocks_per_cu<0, false, false>();
   if (bpc <= 0) return -1;
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess) return -1;
@@ -790,14 +807,21 @@ int attn_w16_grid(int pos_len, int time_len, bool clamp) {
 }
 
 hipError_t launch_attn_w16(const AttnArgs& a, int n_wg, hipStream_t stream, hipEvent_t t0,
-                           hipEvent_t t1) {
+                           hipEvent_t t1, bool transposed) {
   const bool pos = a.pos_len > 0, tim = a.time_len > 0, cl = a.pos_clamp != 0;
-  if (pos && cl && tim) return launch_w16_one<2, true>(a, n_wg, stream, t0, t1);
-  if (pos && cl) return launch_w16_one<2, false>(a, n_wg, stream, t0, t1);
-  if (pos && tim) return launch_w16_one<1, true>(a, n_wg, stream, t0, t1);
-  if (pos) return launch_w16_one<1, false>(a, n_wg, stream, t0, t1);
-  if (tim) return launch_w16_one<0, true>(a, n_wg, stream, t0, t1);
-  return launch_w16_one<0, false>(a, n_wg, stream, t0, t1);
+  if (transposed) {
+    if (cl) return hipErrorInvalidValue;
+    if (pos && tim) return launch_w16_one<1, true, true>(a, n_wg, stream, t0, t1);
+    if (pos) return launch_w16_one<1, false, true>(a, n_wg, stream, t0, t1);
+    if (tim) return launch_w16_one<0, true, true>(a, n_wg, stream, t0, t1);
+    return launch_w16_one<0, false, true>(a, n_wg, stream, t0, t1);
+  }
+  if (pos && cl && tim) return launch_w16_one<2, true, false>(a, n_wg, stream, t0, t1);
+  if (pos && cl) return launch_w16_one<2, false, false>(a, n_wg, stream, t0, t1);
+  if (pos && tim) return launch_w16_one<1, true, false>(a, n_wg, stream, t0, t1);
+  if (pos) return launch_w16_one<1, false, false>(a, n_wg, stream, t0, t1);
+  if (tim) return launch_w16_one<0, true, false>(a, n_wg, stream, t0, t1);
+  return launch_w16_one<0, false, false>(a, n_wg, stream, t0, t1);
 }
 
 }  // namespace hstu

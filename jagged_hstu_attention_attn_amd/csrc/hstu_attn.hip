@@ -1,6 +1,7 @@
 // hstu_attn.hip -- host side of the C ABI declared in include/hstu_attn.h:
 // argument validation (before any HIP call), workspace sizing, launches of the
 // scheduler and attention kernels on the caller's stream, error reporting.
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdarg>
@@ -139,7 +140,8 @@ int check_run_args(const hstu_attn_desc* d, const void* q, const void* k, const 
 // elsewhere; the eight-wave kernel runs only when chosen explicitly.
 std::atomic<int> g_fwd_kernel{HSTU_FWD_KERNEL_AUTO};
 
-int fwd_kernel_choice(const hstu_attn_desc* d) {
+int fwd_kernel_choice(const hstu_attn_desc* d, bool transposed = false) {
+  if (transposed) return HSTU_FWD_KERNEL_SIXTEEN_ROW;   // the only kernel with that walk
   const int mode = g_fwd_kernel.load(std::memory_order_relaxed);
   if (mode == HSTU_FWD_KERNEL_EIGHT_WAVE && hstu::attn_pp_supported(d->dtype, d->d_qk, d->d_v))
     return HSTU_FWD_KERNEL_EIGHT_WAVE;
@@ -154,7 +156,7 @@ int fwd_kernel_choice(const hstu_attn_desc* d) {
 // Workgroups of the persistent attention launch: CUs x resident workgroups
 // per CU (cached per device and kernel variant), between 8 (one per XCD) and
 // kMaxGrid (the most a plan serves).  <= 0 on a HIP error.
-int persistent_grid(const hstu_attn_desc* d) {
+int persistent_grid(const hstu_attn_desc* d, bool transposed = false) {
   struct Entry {
     int dev, dtype, d_qk, d_v, pos_len, has_time, clamp, kern, grid;
   };
@@ -164,7 +166,7 @@ int persistent_grid(const hstu_attn_desc* d) {
   if (hipGetDevice(&dev) != hipSuccess) return -1;
   const int has_time = d->time_table_len > 0;
   const int clamp = d->pos_clamp != 0 && d->pos_table_len > 0;
-  const int kern = fwd_kernel_choice(d);
+  const int kern = fwd_kernel_choice(d, transposed) + (transposed ? 100 : 0);   // cache key
   int g = -1;
   for (int i = 0; i < cache_n && i < 16; ++i) {
     const Entry& e = cache[i];
@@ -178,8 +180,8 @@ int persistent_grid(const hstu_attn_desc* d) {
   if (g < 0) {
     g = kern == HSTU_FWD_KERNEL_EIGHT_WAVE
             ? hstu::attn_pp_grid(d->pos_table_len, d->time_table_len, clamp != 0)
-        : kern == HSTU_FWD_KERNEL_SIXTEEN_ROW
-            ? hstu::attn_w16_grid(d->pos_table_len, d->time_table_len, clamp != 0)
+        : kern == HSTU_FWD_KERNEL_SIXTEEN_ROW || transposed
+            ? hstu::attn_w16_grid(d->pos_table_len, d->time_table_len, clamp != 0, transposed)
         : kern == HSTU_FWD_KERNEL_THIRTYTWO_ROW
             ? hstu::attn_w32_grid(d->pos_table_len, d->time_table_len, clamp != 0)
             : hstu::attn_grid(d->dtype, d->d_qk, d->d_v, d->pos_table_len, d->time_table_len,
@@ -235,7 +237,7 @@ size_t hstu_jagged_attn_workspace_bytes(const hstu_attn_desc* desc) {
 static int plan_impl(const hstu_attn_desc* desc, const int32_t* offsets,
                      const int32_t* num_targets, int32_t contextual_len, int32_t max_attn_len,
                      void* workspace, size_t workspace_bytes, void* stream, bool cand_only,
-                     bool no_split = false) {
+                     bool no_split = false, bool transposed = false) {
   int rc = check_desc(desc);
   if (rc != HSTU_OK) return rc;
   rc = check_plan_args(desc, offsets, contextual_len, max_attn_len, workspace, workspace_bytes,
@@ -244,7 +246,7 @@ static int plan_impl(const hstu_attn_desc* desc, const int32_t* offsets,
   if (desc->num_seqs == 0 || desc->total_tokens == 0) return HSTU_OK;
   const hstu::PlanLayout pl = fwd_layout(desc, no_split);
   const PlanPtrs pp = plan_ptrs(desc, workspace, no_split);
-  const int n_wg = persistent_grid(desc);
+  const int n_wg = persistent_grid(desc, transposed);
   if (n_wg <= 0) return fail(HSTU_ERR_HIP, "cannot query the device for the launch size");
   hstu::PlanArgs a;
   a.offsets = offsets;
@@ -257,6 +259,7 @@ static int plan_impl(const hstu_attn_desc* desc, const int32_t* offsets,
   a.n_wg = n_wg;
   a.cand_only = cand_only ? 1 : 0;
   a.no_split = pl.slots_max == 0 ? 1 : 0;
+  a.transposed = transposed ? 1 : 0;
   a.hdr = pp.hdr;
   a.units = pp.units;
   a.wg = pp.wg;
@@ -292,7 +295,7 @@ static int run_impl(const hstu_attn_desc* desc, const void* q, const void* k, co
                     float alpha, float n_scale, const float* pos_table,
                     const float* time_table, void* out, void* o_raw, void* workspace,
                     size_t workspace_bytes, void* stream, void* t_start = nullptr,
-                    void* t_stop = nullptr, bool no_split = false) {
+                    void* t_stop = nullptr, bool no_split = false, bool transposed = false) {
   int rc = check_desc(desc);
   if (rc != HSTU_OK) return rc;
   rc = check_plan_args(desc, offsets, contextual_len, max_attn_len, workspace, workspace_bytes,
@@ -302,7 +305,7 @@ static int run_impl(const hstu_attn_desc* desc, const void* q, const void* k, co
   rc = check_run_args(desc, q, k, v, u, timestamps, alpha, n_scale, pos_table, time_table, out);
   if (rc != HSTU_OK) return rc;
 
-  const int n_wg = persistent_grid(desc);
+  const int n_wg = persistent_grid(desc, transposed);
   if (n_wg <= 0) return fail(HSTU_ERR_HIP, "cannot query the device for the launch size");
   const PlanPtrs pp = plan_ptrs(desc, workspace, no_split);
   hstu::AttnArgs a;
@@ -342,12 +345,12 @@ static int run_impl(const hstu_attn_desc* desc, const void* q, const void* k, co
   a.alpha = alpha;
   a.out_scale = (float)(0.69314718055994530942 / (double)n_scale);
   a.ln_eps = desc->ln_eps;
-  const int kern = fwd_kernel_choice(desc);
+  const int kern = fwd_kernel_choice(desc, transposed);
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipEvent_t e0 = static_cast<hipEvent_t>(t_start), e1 = static_cast<hipEvent_t>(t_stop);
   const hipError_t e =
       kern == HSTU_FWD_KERNEL_EIGHT_WAVE    ? hstu::launch_attn_pp(a, n_wg, st, e0, e1)
-      : kern == HSTU_FWD_KERNEL_SIXTEEN_ROW ? hstu::launch_attn_w16(a, n_wg, st, e0, e1)
+      : kern == HSTU_FWD_KERNEL_SIXTEEN_ROW ? hstu::launch_attn_w16(a, n_wg, st, e0, e1, transposed)
       : kern == HSTU_FWD_KERNEL_THIRTYTWO_ROW ? hstu::launch_attn_w32(a, n_wg, st, e0, e1)
           : hstu::launch_attn(a, desc->dtype, desc->d_qk, desc->d_v, n_wg, st, e0, e1);
   if (e != hipSuccess)
@@ -752,19 +755,48 @@ int hstu_layer_fwd(const hstu_layer_desc* desc, const void* x, const void* w_uvq
 
 namespace {
 
+// The backward's value gradient dV_j = sum_i a_ij dO_i is the forward with
+// the roles of queries and keys exchanged; for bf16 d = 128 with the plain
+// position bias it runs as the sixteen-row forward's transposed walk (k rows
+// as the tile, q and dO rows streamed, epilogue none) instead of a pass of
+// its own.  `ld_do`: token stride of dO.
+bool bwd_tr_dv(const hstu_attn_desc* d) {
+  return d->dtype == HSTU_DTYPE_BF16 && d->d_qk == 128 && d->d_v == 128 &&
+         !(d->pos_clamp != 0 && d->pos_table_len > 0);
+}
+hstu_attn_desc tr_dv_desc(const hstu_attn_desc* d, int64_t ld_do) {
+  hstu_attn_desc t = *d;
+  t.ld_q = d->ld_k;
+  t.ld_k = d->ld_q;
+  t.ld_v = ld_do;
+  t.ld_u = ld_do;   // unused (epilogue none)
+  t.ld_out = d->ld_v;
+  t.epilogue = HSTU_EPILOGUE_NONE;
+  t.pos_clamp = 0;
+  return t;
+}
+
 struct BwdLayout {
   size_t o_off, do_off, hdr_off, gstart_off, lq_off, lkv_off, part_off, part2_off, total;
-  bool gate;
+  bool gate;    // the LayerNorm * U gate: o recomputed (or saved), dO from the gate kernel
+  bool tr_dv;   // dV by the forward's transposed walk
 };
 
 BwdLayout bwd_layout(const hstu_attn_desc* d) {
   BwdLayout l;
   l.gate = d->epilogue != HSTU_EPILOGUE_NONE;
+  l.tr_dv = bwd_tr_dv(d);
   const int64_t N = d->total_tokens, H = d->num_heads;
   const size_t es = elem_size(d->dtype);
   const size_t rows = (size_t)(N * H * d->d_v) * es;
   const int64_t G = hstu::bwd_groups_max(d->num_seqs, N);
-  size_t off = l.gate ? fwd_layout(d).total : 0;
+  // the forward's workspace: the recompute of o (gate) and the transposed dV walk
+  size_t off = 0;
+  if (l.gate) off = fwd_layout(d).total;
+  if (l.tr_dv) {
+    const hstu_attn_desc t = tr_dv_desc(d, H * d->d_v);
+    off = std::max(off, fwd_layout(&t).total);
+  }
   l.o_off = hstu::align256(off);
   off = l.o_off + (l.gate ? rows : 0);
   l.do_off = hstu::align256(off);
@@ -998,7 +1030,8 @@ int hstu_jagged_attn_bwd(const hstu_attn_desc* desc, const void* q, const void* 
   if (e != hipSuccess) return fail(HSTU_ERR_HIP, "dQ launch failed: %s", hipGetErrorString(e));
   ba.list = pa.list_kv;
   e = hstu::launch_bwd(ba, desc->dtype, desc->d_qk, desc->d_v, 1, n_kv, s);
-  if (e == hipSuccess && n_v > 0) e = hstu::launch_bwd(ba, desc->dtype, desc->d_qk, desc->d_v, 2, n_v, s);
+  if (e == hipSuccess && n_v > 0 && !bl.tr_dv)
+    e = hstu::launch_bwd(ba, desc->dtype, desc->d_qk, desc->d_v, 2, n_v, s);
   if (e != hipSuccess) return fail(HSTU_ERR_HIP, "dK/dV launch failed: %s", hipGetErrorString(e));
   if (desc->pos_table_len > 0 || desc->time_table_len > 0) {
     hstu::TabReduceArgs ra;
@@ -1014,6 +1047,16 @@ int hstu_jagged_attn_bwd(const hstu_attn_desc* desc, const void* q, const void* 
     e = hstu::launch_tab_reduce(ra, s);
     if (e != hipSuccess)
       return fail(HSTU_ERR_HIP, "table reduction launch failed: %s", hipGetErrorString(e));
+  }
+  if (bl.tr_dv) {   // dV: the forward's transposed walk over key tiles
+    const hstu_attn_desc td = tr_dv_desc(desc, ld_do);
+    rc = plan_impl(&td, offsets, num_targets, contextual_len, max_attn_len, ws, bl.o_off, stream,
+                   false, false, true);
+    if (rc != HSTU_OK) return rc;
+    rc = run_impl(&td, k, q, d_o, nullptr, offsets, timestamps, num_targets, contextual_len,
+                  max_attn_len, alpha, n_scale, pos_table, time_table, dv, nullptr, ws, bl.o_off,
+                  stream, nullptr, nullptr, false, true);
+    if (rc != HSTU_OK) return rc;
   }
   return HSTU_OK;
 }

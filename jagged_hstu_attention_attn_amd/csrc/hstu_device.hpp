@@ -215,6 +215,7 @@ struct PlanArgs {
   int32_t n_wg;          // workgroups of the attention launch (<= kMaxGrid)
   int32_t cand_only;     // 1: only the candidate rows [n_h, L), tiled from n_h
   int32_t no_split;      // 1: keep every item whole (no partial-output slots)
+  int32_t transposed;    // 1: items are key tiles walking the query rows they reach
   int32_t* hdr;
   int4* units;
   int32_t* wg;
@@ -289,6 +290,32 @@ __host__ __device__ inline RowBounds col_bounds(const SeqGeom& g, int j) {
   r.span = hi - lo;
   r.self_j = -1;
   return r;
+}
+
+// Query rows [ilo, ihi] that keys [j0, j1) (j0 < j1 <= L) can reach: the
+// union of their col_bounds.  A history key's interval starts at 0 (prefix
+// keys) or at the key and ends at j + W or L - 1, nondecreasing in j; a
+// candidate key reaches only its own row.
+__host__ __device__ inline void tile_row_range(const SeqGeom& g, int j0, int j1, int& ilo,
+                                               int& ihi) {
+  if (j0 < g.n_h) {
+    ilo = j0 < g.c ? 0 : j0;
+    const int jl = (j1 < g.n_h ? j1 : g.n_h) - 1;
+    ihi = (g.W == 0 || jl + g.W >= g.n_h) ? g.L - 1 : jl + g.W;
+    if (j1 - 1 > ihi) ihi = j1 - 1;   // candidate keys of the tile: their own rows
+  } else {
+    ilo = j0;
+    ihi = j1 - 1;
+  }
+}
+
+// The range a tile of 128 rows reaches: keys for the forward, or with
+// `transposed` (a tile of keys) the query rows, as the key-side passes of
+// the backward walk them.
+__host__ __device__ inline void tile_range(const SeqGeom& g, int i0, int i1, bool transposed,
+                                           int& lo, int& hi) {
+  if (transposed) tile_row_range(g, i0, i1, lo, hi);
+  else tile_key_range(g, i0, i1, lo, hi);
 }
 
 // Backward.  Work is listed as (sequence, 128-token tile) groups, sorted by
@@ -386,10 +413,13 @@ hipError_t launch_attn_pp(const AttnArgs& a, int n_wg, hipStream_t stream,
 // The sixteen-row forward (attn_fwd_w16.hip): bf16, d_qk = d_v = 128; eight
 // waves of 16 query rows per workgroup, four waves per SIMD; same units,
 // workspace and arguments as launch_attn.
+// `transposed`: the key-side walk of the backward's value gradient (plan
+// made with PlanArgs::transposed; epilogue none; no clamped position bias).
 bool attn_w16_supported(int dtype, int d_qk, int d_v);
-int attn_w16_grid(int pos_len, int time_len, bool clamp);
+int attn_w16_grid(int pos_len, int time_len, bool clamp, bool transposed = false);
 hipError_t launch_attn_w16(const AttnArgs& a, int n_wg, hipStream_t stream,
-                           hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
+                           hipEvent_t start = nullptr, hipEvent_t stop = nullptr,
+                           bool transposed = false);
 // The thirty-two-row forward (attn_fwd_w32.hip): bf16, d_qk = d_v = 128; four
 // waves of two 16-row groups per workgroup, two waves per SIMD; same units,
 // workspace and arguments as launch_attn.

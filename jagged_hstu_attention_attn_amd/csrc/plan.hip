@@ -152,7 +152,7 @@ __device__ inline int row_base(int n_h, bool cand_only) { return cand_only ? n_h
 // Item k of sequence b (head-major, last query tile first).
 __device__ inline ItemGeo item_geo_of(int k, int b, const int32_t* base, const int32_t* slen,
                                       const int32_t* hist, int contextual_len,
-                                      int max_attn_len, bool cand_only) {
+                                      int max_attn_len, bool cand_only, bool tr) {
   ItemGeo r;
   r.b = b;
   const int L = slen[b], i_b = row_base(hist[b], cand_only);
@@ -167,7 +167,7 @@ __device__ inline ItemGeo item_geo_of(int k, int b, const int32_t* base, const i
   g.W = max_attn_len;
   const int i0 = i_b + r.qt * kBM, i1 = min(i0 + kBM, L);
   int jlo, jhi;
-  tile_key_range(g, i0, i1, jlo, jhi);
+  tile_range(g, i0, i1, tr, jlo, jhi);
   r.kt_lo = jlo / kBN;
   r.kt_hi = jhi / kBN;
   r.n_h = g.n_h;
@@ -223,10 +223,11 @@ __device__ inline SeqGeom seq_geom(int b, const int32_t* slen, const int32_t* hi
 // reach, as item_geo_of counts them, and its queue-order bucket (0 = the most
 // key tiles).  The count and the scatter of the queue order both use it, so
 // they agree on every bucket.
-__device__ inline int tile_bucket(const SeqGeom& g, int i_b, int qt, int& kt_lo, int& kt_hi) {
+__device__ inline int tile_bucket(const SeqGeom& g, int i_b, int qt, bool tr, int& kt_lo,
+                                  int& kt_hi) {
   const int i0 = i_b + qt * kBM, i1 = min(i0 + kBM, g.L);
   int jlo, jhi;
-  tile_key_range(g, i0, i1, jlo, jhi);
+  tile_range(g, i0, i1, tr, jlo, jhi);
   kt_lo = jlo / kBN;
   kt_hi = jhi / kBN;
   return kSortBuckets - min(kt_hi - kt_lo + 1, kSortBuckets);
@@ -257,6 +258,7 @@ __global__ __launch_bounds__(kPlanThreads) void hstu_plan_kernel(PlanArgs a) {
   const int tid = threadIdx.x;
   const int B = a.num_seqs, H = a.num_heads, n_wg = a.n_wg;
   const bool cand = a.cand_only != 0;
+  const bool tr = a.transposed != 0;
   int32_t* seq = B <= kPlanLdsSeqs ? s_seq : a.seq_scratch;
   const int LD = B <= kPlanLdsSeqs ? kPlanLdsSeqs + 1 : B + 1;
   int32_t* base = seq;            // [B + 1] first item of each sequence
@@ -290,7 +292,7 @@ __global__ __launch_bounds__(kPlanThreads) void hstu_plan_kernel(PlanArgs a) {
         const int i_b = row_base(g.n_h, cand);
         int kt_lo, kt_hi;
         for (int qt = 0; i_b + qt * kBM < L; ++qt) {
-          atomicAdd(&s_bcnt[tile_bucket(g, i_b, qt, kt_lo, kt_hi)], H);
+          atomicAdd(&s_bcnt[tile_bucket(g, i_b, qt, tr, kt_lo, kt_hi)], H);
           if (kt_hi - kt_lo + 1 >= 2 * kMinChunk) s_long = 1;   // the static plan would split it
         }
       }
@@ -317,7 +319,7 @@ __global__ __launch_bounds__(kPlanThreads) void hstu_plan_kernel(PlanArgs a) {
       const int i_b = row_base(g.n_h, cand);
       for (int qt = 0; i_b + qt * kBM < g.L; ++qt) {
         int kt_lo, kt_hi;
-        const int pos = atomicAdd(&s_bcnt[tile_bucket(g, i_b, qt, kt_lo, kt_hi)], H);
+        const int pos = atomicAdd(&s_bcnt[tile_bucket(g, i_b, qt, tr, kt_lo, kt_hi)], H);
         const int4 ch = make_int4(kt_lo, kt_hi, -1, (cand ? kUnitCandRows : 0) | 1);
         for (int h = 0; h < H; ++h) {
           a.units[2 * (pos + h)] = make_int4(start[b], g.L, g.n_h, qt * H + h);
@@ -356,7 +358,7 @@ __global__ __launch_bounds__(kPlanThreads) void hstu_plan_kernel(PlanArgs a) {
     if (j < n) {
       const int k = dealt_item(j, n, n_wg);
       const int b = seq_of(k, base, B);
-      const ItemGeo g = item_geo_of(k, b, base, slen, hist, a.contextual_len, a.max_attn_len, cand);
+      const ItemGeo g = item_geo_of(k, b, base, slen, hist, a.contextual_len, a.max_attn_len, cand, tr);
       c = g.kt_hi - g.kt_lo + 1 + kCostOverhead;
       cost[j] = c;
       iseq[j] = b;
@@ -485,7 +487,7 @@ __global__ __launch_bounds__(kPlanThreads) void hstu_plan_kernel(PlanArgs a) {
       qh = gg.y;
     } else {
       const ItemGeo g = item_geo_of(dealt_item(j, n, n_wg), b, base, slen, hist,
-                                    a.contextual_len, a.max_attn_len, cand);
+                                    a.contextual_len, a.max_attn_len, cand, tr);
       kt_lo = g.kt_lo;
       qh = g.qt * H + g.h;
     }
