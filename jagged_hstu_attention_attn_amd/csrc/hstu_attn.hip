@@ -350,7 +350,8 @@ static int run_impl(const hstu_attn_desc* desc, const void* q, const void* k, co
   hipEvent_t e0 = static_cast<hipEvent_t>(t_start), e1 = static_cast<hipEvent_t>(t_stop);
   const hipError_t e =
       kern == HSTU_FWD_KERNEL_EIGHT_WAVE    ? hstu::launch_attn_pp(a, n_wg, st, e0, e1)
-      : kern == HSTU_FWD_KERNEL_SIXTEEN_ROW ? hstu::launch_attn_w16(a, n_wg, st, e0, e1, transposed)
+      : kern == HSTU_FWD_KERNEL_SIXTEEN_ROW
+          ? hstu::launch_attn_w16(a, n_wg, st, e0, e1, transposed)
       : kern == HSTU_FWD_KERNEL_THIRTYTWO_ROW ? hstu::launch_attn_w32(a, n_wg, st, e0, e1)
           : hstu::launch_attn(a, desc->dtype, desc->d_qk, desc->d_v, n_wg, st, e0, e1);
   if (e != hipSuccess)
