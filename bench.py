@@ -56,6 +56,30 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def settle(step, flush, seconds: float) -> dict:
+    """Untimed steps of the workload itself (cache flush included) for
+    `seconds` of wall time, before the warm-up steps.  From a fresh start the
+    first few dozen steps run up to ~15% slower however the warm-up count is
+    set (measured on the windowed batch: steps 1-20 at 364 us, 41-60 at 310
+    us; a one-off fill of the flush buffer does not remove it), so the timed
+    steps start from steady state.  Reported in the JSON line as `settle`."""
+    import torch
+    if seconds <= 0:
+        return {"steps": 0, "seconds": 0.0}
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        for _ in range(10):
+            if flush is not None:
+                flush.fill_(n & 0xFF)
+            step()
+            n += 1
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            break
+    return {"steps": n, "seconds": round(time.perf_counter() - t0, 3)}
+
+
 def kernel_source_hash(kernel: str) -> str:
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES[kernel]:
@@ -126,6 +150,7 @@ def bench_layer(args, inp) -> int:
     f_attn = 2.0 * (dqk + dv) * H * pairs
     flops = f_proj + f_attn + f_out
     flush = None if args.no_flush else torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    settled = settle(lay, flush, args.settle_s)
     for s in range(args.warmup):   # warm-up steps are the timed steps, flush included
         if flush is not None:
             flush.fill_(s & 0xFF)
@@ -148,7 +173,8 @@ def bench_layer(args, inp) -> int:
     result = {
         "metric": "HSTU layer forward TFLOP/s (projections + valid-pair attention)",
         "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "warmup": args.warmup, "settle": settled, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "layer (full HSTU layer)", "num_seqs": inp.num_seqs,
                    "total_tokens": N, "hidden": D, "num_heads": H, "d_qk": dqk, "d_v": dv,
@@ -195,6 +221,7 @@ def bench_backward(args, inp) -> int:
     flush = None if args.no_flush else torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
     log(f"backward: {inp.num_seqs} sequences, {inp.total_tokens} tokens, {pairs} valid "
         f"pairs/head; warmup {args.warmup}")
+    settled = settle(lambda: call(dout, o_saved), flush, args.settle_s)
     for s in range(args.warmup):   # warm-up steps are the timed steps, flush included
         if flush is not None:
             flush.fill_(s & 0xFF)
@@ -218,7 +245,8 @@ def bench_backward(args, inp) -> int:
     result = {
         "metric": "jagged HSTU attn bwd TFLOP/s (valid pairs, 5 contractions)",
         "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "warmup": args.warmup, "settle": settled, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak",
         "vs_baseline": None, "dtype": inp.dtype, "data": "synthetic",
         "config": {"workload": args.workload, "pass": "backward", "epilogue": args.epilogue,
                    "o": "saved by the training forward" if args.saved_o else "recomputed",
@@ -322,6 +350,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--settle-s", type=float, default=0.3,
+                    help="seconds of untimed steps before the warm-up (0: none)")
     ap.add_argument("--workload", default="windowed",
                     choices=["tiny", "ranking", "longtail", "windowed", "layer"])
     ap.add_argument("--seed", type=int, default=None)
@@ -390,7 +420,8 @@ def main() -> int:
         log("secondary record: ranking batch")
         sec_inp = make_inputs("ranking")
         sec = measure_forward(args, sec_inp, "ranking", args.secondary_steps, args.warmup)
-        keep = ("value", "unit", "ms_per_step", "steps", "warmup", "config", "tokens_per_s",
+        keep = ("value", "unit", "ms_per_step", "steps", "warmup", "settle", "config",
+                "tokens_per_s",
                 "pct_bf16_mfma_peak", "pct_hbm_peak", "plan_us", "roofline")
         result["secondary"] = {k: sec[k] for k in keep}
         result["secondary"]["why"] = ("the short ranking batch, whose attention is bound by HBM "
@@ -421,9 +452,12 @@ def measure_forward(args, inp, workload: str, steps: int, warmup: int) -> dict:
 
     log(f"{workload}: {inp.num_seqs} sequences, {inp.total_tokens} tokens, {pairs} valid "
         f"pairs/head; warmup {warmup}")
-    # Warm-up steps are the timed steps (flush, scheduler, attention): the
-    # first steps that rewrite the flush buffer run measurably slower, and
-    # a warm-up without the flush left that transient inside the timed loop.
+    def fwd_step():
+        call.plan()
+        call.run()
+    settled = settle(fwd_step, flush, args.settle_s)
+    log(f"{workload}: settled over {settled['steps']} untimed steps ({settled['seconds']} s)")
+    # Warm-up steps are the timed steps (flush, scheduler, attention).
     for s in range(warmup):
         if flush is not None:
             flush.fill_(s & 0xFF)
@@ -518,6 +552,7 @@ def measure_forward(args, inp, workload: str, steps: int, warmup: int) -> dict:
         "n_gpus": 1,
         "steps": steps,
         "warmup": warmup,
+        "settle": settled,
         "ms_per_step": ms,
         "higher_is_better": True,
         "scaling": "weak",
