@@ -553,14 +553,21 @@ struct Pipe {
         const int64_t rel = tj - tbase;
         const bool ok = rel > -kT32Range && rel < kT32Range;
         const uint32_t t32 = ok ? uint32_t(rel + kT32Range) : 0u;
-        const bool valid = lane < min(kStep, L - p0);
+        const int nvalid = min(kStep, L - p0);
         if (lane < kStep) sb.ts32[kl] = t32;
         const bool bad = __ballot(!ok) != 0;
-        const uint32_t mn = wave_min_u(valid ? t32 : 0xffffffffu);
-        const uint32_t mx = wave_max_u(valid ? t32 : 0u);
+        // When the valid partner times ascend (as times along a sequence
+        // usually do) their range is [first, last]; otherwise the step
+        // claims every 32-bit time, so no pair is taken for a shared bucket.
+        const uint32_t nxt = (uint32_t)__builtin_amdgcn_update_dpp(
+            (int)t32, (int)t32, 0x130, 0xf, 0xf, false);   // lane l gets lane l+1
+        const bool desc = lane + 1 < nvalid && nxt < t32;
+        const bool sorted = __ballot(desc) == 0;
+        const uint32_t first = (uint32_t)__builtin_amdgcn_readlane((int)t32, 0);
+        const uint32_t last = (uint32_t)__builtin_amdgcn_readlane((int)t32, nvalid - 1);
         if (lane == 0) {
-          sb.tmin = mn;
-          sb.tmax = mx;
+          sb.tmin = sorted ? first : 0u;
+          sb.tmax = sorted ? last : 0xffffffffu;
           sb.tbad = bad;
         }
       }
@@ -578,9 +585,10 @@ struct Pipe {
     w_tmax = wave_max_u(valid ? tf32 : 0u);
   }
 
-  // Whether every (fixed, partner) time gap of the step falls in one bucket;
-  // then z is its clz(1 + dt).
-  __device__ bool time_const(const SB& sb, int& z) const {
+  // The buckets the step's (fixed, partner) time gaps can fall in: every gap
+  // of a valid pair lies in [dmin, dmax] of the two time ranges, so its
+  // clz(1 + dt) lies in [z1, z0].  False when some time needs 64 bits.
+  __device__ bool time_span(const SB& sb, int& z0, int& z1) const {
     if (!w_t_ok || uni(sb.tbad) != 0) return false;
     const uint32_t kmin = (uint32_t)uni((int)sb.tmin), kmax = (uint32_t)uni((int)sb.tmax);
     uint32_t dmin = 0;
@@ -588,38 +596,50 @@ struct Pipe {
     if (kmin > w_tmax) dmin = kmin - w_tmax;
     const uint32_t dmax = max(w_tmax > kmin ? w_tmax - kmin : 0u,
                               kmax > w_tmin ? kmax - w_tmin : 0u);
-    const int z0 = uni(__builtin_clz(dmin + 1u)), z1 = uni(__builtin_clz(dmax + 1u));
-    z = z0;
-    return z0 == z1;
+    z0 = uni(__builtin_clz(dmin + 1u));
+    z1 = uni(__builtin_clz(dmax + 1u));
+    return true;
   }
 
   // How a step's time bias is found, for this wave: 0 = no time bias, or
-  // one bucket for every pair of the step (its value tb and bin cb); 1 = per
-  // pair from 32-bit times; 2 = per pair from 64-bit times.
-  __device__ int time_mode(const SB& sb, float& tb, int& cb) const {
+  // one bucket for every pair of the step (its value tb and bin cb); 3 = two
+  // adjacent buckets, told apart by one compare per pair (tb and cb are the
+  // lower one's, t_hi and t_thr the upper one's value and first gap + 1);
+  // 1 = per pair from 32-bit times and the table; 2 = per pair from 64-bit
+  // times.
+  __device__ int time_mode(const SB& sb, float& tb, int& cb) {
     tb = 0.0f;
     cb = 0;
     if constexpr (TIME) {
-      int z;
-      if (time_const(sb, z)) {
-        tb = __builtin_bit_cast(float, uni(__builtin_bit_cast(int, trev[z])));
-        cb = 31 - z;
-        return 0;
-      }
-      if (w_t_ok && uni(sb.tbad) == 0) return 1;
-      return 2;
+      int z0, z1;
+      if (!time_span(sb, z0, z1)) return 2;
+      tb = __builtin_bit_cast(float, uni(__builtin_bit_cast(int, trev[z0])));
+      cb = 31 - z0;
+      if (z0 == z1) return 0;
+      if (z0 != z1 + 1) return 1;
+      t_hi = __builtin_bit_cast(float, uni(__builtin_bit_cast(int, trev[z1])));
+      t_thr = 1u << (31 - z1);
+      return 3;
     }
     return 0;
   }
-  // Time bias and bin of register r's pair (modes 1 and 2); t4 holds the
-  // 32-bit partner times of registers 4(r/4) .. 4(r/4)+3.
+  float t_hi;
+  uint32_t t_thr;
+  // Time bias and bin of register r's pair (modes 1, 2 and 3); t4 holds the
+  // 32-bit partner times of registers 4(r/4) .. 4(r/4)+3.  Mode 3 takes cb
+  // (the lower bin) and tb (its value).
   template <int MODE>
   __device__ float pair_time(const SB& sb, const uint4& t4, int r, int hh, int64_t t_fix64,
-                             int& bin) const {
-    if constexpr (MODE == 1) {
+                             int& bin, int cb = 0, float tb = 0.0f) const {
+    if constexpr (MODE == 1 || MODE == 3) {
       const int e = r & 3;
       const uint32_t tv = e == 0 ? t4.x : (e == 1 ? t4.y : (e == 2 ? t4.z : t4.w));
       const uint32_t d1 = (tf32 > tv ? tf32 - tv : tv - tf32) + 1u;
+      if constexpr (MODE == 3) {
+        const bool up = d1 >= t_thr;
+        bin = cb + (up ? 1 : 0);
+        return up ? t_hi : tb;
+      }
       const int z = __builtin_clz(d1);
       bin = 31 - z;
       return trev[z];
@@ -847,12 +867,14 @@ hstu_bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
             for (int gq = 0; gq < 4; ++gq) {
               uint4 t4 = {};
-              if constexpr (MODE == 1) t4 = *reinterpret_cast<const uint4*>(&sb.ts32[8 * gq + 4 * hh]);
+              if constexpr (MODE == 1 || MODE == 3)
+                t4 = *reinterpret_cast<const uint4*>(&sb.ts32[8 * gq + 4 * hh]);
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
                 const int r = 4 * gq + e;
                 int bin;
-                const float t = MODE == 0 ? tb : pp.template pair_time<MODE>(sb, t4, r, hh, ti64, bin);
+                const float t =
+                    MODE == 0 ? tb : pp.template pair_time<MODE>(sb, t4, r, hh, ti64, bin, cbin, tb);
                 const float x = fmaf(s[r], am, t);
                 const float sg = sigm(x);
                 float d = da[r] * (sg * fmaf(x, 1.0f - sg, 1.0f));
@@ -866,6 +888,7 @@ hstu_bwd_dq_kernel(BwdArgs a) {
             }
           };
           if (mode == 0) elem(std::integral_constant<int, 0>{});
+          else if (mode == 3) elem(std::integral_constant<int, 3>{});
           else if (mode == 1) elem(std::integral_constant<int, 1>{});
           else elem(std::integral_constant<int, 2>{});
         }
@@ -1144,13 +1167,15 @@ hstu_bwd_dkv_kernel(BwdArgs a) {
 #pragma unroll
             for (int gq = 0; gq < 4; ++gq) {
               uint4 t4 = {};
-              if constexpr (MODE == 1) t4 = *reinterpret_cast<const uint4*>(&sb.ts32[8 * gq + 4 * hh]);
+              if constexpr (MODE == 1 || MODE == 3)
+                t4 = *reinterpret_cast<const uint4*>(&sb.ts32[8 * gq + 4 * hh]);
               float dg[4];
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
                 const int r = 4 * gq + e, kk = 8 * gq + e;
                 int bin = 0;
-                const float t = MODE == 0 ? tb : pp.template pair_time<MODE>(sb, t4, r, hh, tj64, bin);
+                const float t =
+                    MODE == 0 ? tb : pp.template pair_time<MODE>(sb, t4, r, hh, tj64, bin, cbin, tb);
                 const float x = fmaf(s[r], am, t);
                 const float sg = sigm(x);
                 float aa = x * sg, d = DK ? da[r] * (sg * fmaf(x, 1.0f - sg, 1.0f)) : 0.0f;
@@ -1186,6 +1211,7 @@ hstu_bwd_dkv_kernel(BwdArgs a) {
             if constexpr (TIME && TABS) tflush(prev, run);
           };
           if (mode == 0) elem(std::integral_constant<int, 0>{});
+          else if (mode == 3) elem(std::integral_constant<int, 3>{});
           else if (mode == 1) elem(std::integral_constant<int, 1>{});
           else elem(std::integral_constant<int, 2>{});
           if constexpr (POS && TABS) {
