@@ -330,23 +330,27 @@ hstu_attn_fwd_w16_kernel(AttnArgs a) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc[t][e] = 0.0f;
 
-  // Whether every (row, key) time gap of this wave and a block falls in one
-  // bucket, from the block's key-time range `kr` (tmin, tmax, tbad as the
-  // stage holds them, loaded with the block's first LDS reads); then `tb` is
-  // that bucket's bias.  Uniform values throughout: the distances between
-  // the wave's and the block's time ranges are written as max - b (scalar
-  // ALU) rather than saturating differences (vector ALU).
-  auto time_const = [&](const uint4& kr, float& tb) __attribute__((always_inline)) -> bool {
+  // The buckets the (row, key) time gaps of this wave and a block can fall
+  // in, from the block's key-time range `kr` (tmin, tmax, tbad as the stage
+  // holds them, loaded with the block's first LDS reads) and the wave's
+  // row-time range: the gap of every valid pair lies between the two ranges'
+  // smallest and largest distance, so its clz(1 + dt) lies in [z1, z0].
+  // False when some time needs the 64-bit path.  Uniform values throughout:
+  // the distances between the ranges are written as max - b (scalar ALU)
+  // rather than saturating differences (vector ALU).
+  auto time_span = [&](const uint4& kr, int& z0, int& z1) __attribute__((always_inline)) -> bool {
     if (!w_t_ok || uni((int)kr.z) != 0) return false;
     const uint32_t kmin = (uint32_t)uni((int)kr.x), kmax = (uint32_t)uni((int)kr.y);
     const uint32_t wmin = (uint32_t)uni((int)w_tmin), wmax = (uint32_t)uni((int)w_tmax);
     // ranges [wmin, wmax] and [kmin, kmax]: at most one of the two gaps is positive
     const uint32_t dmin = (max(wmin, kmax) - kmax) + (max(kmin, wmax) - wmax);
     const uint32_t dmax = max(max(wmax, kmin) - kmin, max(kmax, wmin) - wmin);
-    const int z0 = __builtin_clz(dmin + 1u), z1 = __builtin_clz(dmax + 1u);
-    if (z0 != z1) return false;
-    tb = __builtin_bit_cast(float, uni(__builtin_bit_cast(int, tt.trev[z0])));
+    z0 = __builtin_clz(dmin + 1u);
+    z1 = __builtin_clz(dmax + 1u);
     return true;
+  };
+  auto trev_u = [&](int z) __attribute__((always_inline)) -> float {   // a uniform table entry
+    return __builtin_bit_cast(float, uni(__builtin_bit_cast(int, tt.trev[z])));
   };
 
   // One 32-key block from stage buffer `sb`.  The lane parts of its LDS
@@ -434,17 +438,33 @@ hstu_attn_fwd_w16_kernel(AttnArgs a) {
     // ---- x2 = am * S + log2e * time ----
     float x[8];
     if constexpr (TIME) {
-      float tb = 0.0f;
-      if (time_const(kr, tb)) {
+      int z0 = 0, z1 = 0;
+      const bool t32 = time_span(kr, z0, z1);
+      if (t32 && z0 == z1) {   // one bucket for the whole block
+        const float tb = trev_u(z0);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           x[e] = fmaf(s0[e], am, tb);
           x[4 + e] = fmaf(s1[e], am, tb);
         }
-      } else if (w_t_ok && uni(sb.tbad) == 0) {
+      } else if (t32 && z0 == z1 + 1) {
+        // two adjacent buckets: a gap + 1 from 2^(31 - z1) on is in the upper one
+        const float tlo = trev_u(z0), thi = trev_u(z1);
+        const uint32_t thr = 1u << (31 - z1);
 #pragma unroll
         for (int tk = 0; tk < 2; ++tk) {
-          const uint4 t4 = *reinterpret_cast<const uint4*>(&sb.ts32[16 * tk + 4 * g4]);
+          const uint4 t4 = *reinterpret_cast<const uint4*>(&sb.ts32[16 * tk + 4 * (opaque_lane() >> 4)]);
+          const uint32_t tv[4] = {t4.x, t4.y, t4.z, t4.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t d1 = (ti32 > tv[e] ? ti32 - tv[e] : tv[e] - ti32) + 1u;
+            x[4 * tk + e] = fmaf(tk ? s1[e] : s0[e], am, d1 >= thr ? thi : tlo);
+          }
+        }
+      } else if (t32) {
+#pragma unroll
+        for (int tk = 0; tk < 2; ++tk) {
+          const uint4 t4 = *reinterpret_cast<const uint4*>(&sb.ts32[16 * tk + 4 * (opaque_lane() >> 4)]);
           const uint32_t tv[4] = {t4.x, t4.y, t4.z, t4.w};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
