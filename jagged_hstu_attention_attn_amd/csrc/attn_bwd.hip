@@ -1162,7 +1162,7 @@ hstu_bwd_dkv_kernel(BwdArgs a) {
           };
           auto elem = [&](auto mc) __attribute__((always_inline)) {
             constexpr int MODE = decltype(mc)::value;
-            float run = 0.0f;
+            float run = 0.0f, run_hi = 0.0f;   // run_hi: bin cbin + 1 (mode 3)
             int prev = cbin;
 #pragma unroll
             for (int gq = 0; gq < 4; ++gq) {
@@ -1193,7 +1193,12 @@ hstu_bwd_dkv_kernel(BwdArgs a) {
                     dg[e] = 0.0f;
                   }
                 }
-                if constexpr (TIME && TABS) {
+                if constexpr (TIME && TABS && MODE == 3) {
+                  // two bins only: one sum each, no run breaks
+                  const bool up = bin != cbin;
+                  run_hi += up ? d : 0.0f;
+                  run += up ? 0.0f : d;
+                } else if constexpr (TIME && TABS) {
                   if constexpr (MODE != 0) {
                     if (r == 0) {
                       prev = bin;
@@ -1209,6 +1214,7 @@ hstu_bwd_dkv_kernel(BwdArgs a) {
               if constexpr (POS && TABS) pgroup(gq, dg);
             }
             if constexpr (TIME && TABS) tflush(prev, run);
+            if constexpr (TIME && TABS && MODE == 3) tflush(cbin + 1, run_hi);
           };
           if (mode == 0) elem(std::integral_constant<int, 0>{});
           else if (mode == 3) elem(std::integral_constant<int, 3>{});
